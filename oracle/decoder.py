@@ -1,0 +1,343 @@
+"""CPU oracle of one pipeline stage's decoder forward -- TEST INFRASTRUCTURE, not the product.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this module.  It shares no code with the GPU path (``pipeline_stage_decoder_amd``) and
+never imports it; the two meet only in the seeded inputs of ``fixtures``.
+
+It is plain numpy: float64 for every sum, a library matmul (``@``) as the one primitive, no
+blocking or fusion.  Sources, cited by page title and section:
+
+* "41. Many GPUs: tensor, pipeline, expert and data parallelism" (the book chapter), section
+  "Pipeline parallelism": ``PipelineStage.forward`` fixes the stage semantics -- embed on the first
+  stage, then per block ``add_norm`` -> attention -> ``add_norm`` -> MLP, and only the residual
+  stream ``x + delta`` crosses a stage boundary; the final norm follows the last block.
+* same chapter, "Ring attention for very long contexts": ``attention_partial`` (causal scores
+  ``q.k * scale``, keys with ``k_pos > q_pos`` masked, log-sum-exp, rows with no key get lse -inf)
+  and ``merge_partials`` (the split-KV merge by log-sum-exp).
+* same chapter, "Tensor parallelism": weights are ``[out, in]``; ``take_rows`` keeps output rows
+  (column parallel), ``take_cols`` keeps input columns (row parallel, a partial sum); GQA maps
+  query head h to KV head ``h // (Hq / Hkv)``; the MLP is ``down(silu(gate(x)) * up(x))``.
+* "Multi-node layer splitting and tensor parallelism" (TensorSharp), "Supported stage executors":
+  the dense pipeline hands F32 hidden activations between stages, the first stage embeds and the
+  last computes logits; "Transport and tuning": sums of partials in node order ((v0+v1)+v2)+...
+* "RFC: pipeline placement across multiple GPUs ...", "Numerical correctness proof": staged and
+  single-device execution must agree bit-for-bit on logits, final features, KV state and tokens.
+
+Readings where the pages are silent (each listed in the design notes):
+RMSNorm is x * rsqrt(mean(x^2) + eps) * g (no mean subtraction, eps inside the root);
+RoPE is the rotate-half form over the whole head, angle pos * theta^(-2i/Dh), absolute 0-based
+positions; the residual stream is F32 inside a stage as well as across it; the readout is untied.
+GEMM and attention operands are rounded to bf16 at seven fixed points (R1..R7 below), exactly
+where the GPU path rounds them; everything else is float64 and rounded to float32 where the
+method stores an F32 tensor.
+
+Pins: every function here is checked by ``tests/test_oracle_pins.py`` against brute-force loops,
+closed forms and invariants the pages fix (see that file).  Absolute forward values are not
+printed by any page ("parity unpinned" by page numbers); they are pinned by those invariants.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+# --------------------------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------------------------
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> their exact float32 values."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (np.ascontiguousarray(b).astype(np.uint32) << 16).view(np.float32).reshape(b.shape)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits, round to nearest, ties to even (finite inputs)."""
+    x = np.asarray(x, dtype=np.float32)
+    u = np.ascontiguousarray(x).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16).reshape(x.shape)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round to float32 first (the GPU holds these values in f32), then to bf16; return float32."""
+    return bf16_to_f32(f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
+
+
+def f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------------------------
+# the decoder's operations
+# --------------------------------------------------------------------------------------------
+
+
+def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    """x * (1 / sqrt(mean(x^2) + eps)) * g per row, in float64 (reading: Llama RMSNorm)."""
+    x = f64(x)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x * r * f64(gain)
+
+
+def linear(h: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """y = h W^T for W stored [out, in] (the chapter's nn.Linear layout); f64 sums, f32 result."""
+    return (f64(h) @ f64(bf16_to_f32(w_bits)).T).astype(np.float32)
+
+
+def rope_angles(positions: np.ndarray, head_dim: int, theta: float) -> np.ndarray:
+    """angle[p, i] = p * theta^(-2i/Dh) for i < Dh/2, float64."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / head_dim)
+    return f64(positions)[:, None] * inv_freq[None, :]
+
+
+def rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate-half RoPE of x [n, heads, Dh] at absolute positions [n]; f64 in, f64 out.
+
+    For i < Dh/2 the pair (x_i, x_{i+Dh/2}) is rotated by angle[p, i]:
+    y_i = x_i cos - x_{i+Dh/2} sin,  y_{i+Dh/2} = x_{i+Dh/2} cos + x_i sin.
+    """
+    x = f64(x)
+    half = x.shape[-1] // 2
+    a = rope_angles(positions, x.shape[-1], theta)[:, None, :]
+    c, s = np.cos(a), np.sin(a)
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def attention_partial(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray,
+                      k_pos: np.ndarray, scale: float):
+    """Causal attention of q [Tq, H, D] over k, v [Tk, H, D] -> (out [Tq, H, D], lse [Tq, H]).
+
+    Same definition as the chapter's ``attention_partial``: scores = q.k * scale, keys with
+    k_pos > q_pos masked to -inf, probabilities exp(score - lse); a row that sees no key has
+    lse = -inf and output 0.  Float64 throughout.
+    """
+    q, k, v = f64(q), f64(k), f64(v)
+    scores = np.einsum("qhd,khd->hqk", q, k) * scale
+    masked = k_pos[None, None, :] > q_pos[None, :, None]
+    scores = np.where(masked, -np.inf, scores)
+    top = scores.max(axis=-1, keepdims=True)
+    top_safe = np.where(np.isinf(top), 0.0, top)
+    with np.errstate(divide="ignore"):
+        lse = (np.log(np.exp(scores - top_safe).sum(axis=-1, keepdims=True)) + top_safe)[..., 0]
+    probs = np.exp(scores - np.where(np.isinf(lse), 0.0, lse)[..., None])
+    return np.einsum("hqk,khd->qhd", probs, v), lse.T
+
+
+def merge_partials(out, lse, new_out, new_lse):
+    """The chapter's split-KV merge of two partial attentions by their log-sum-exps (f64)."""
+    top = np.maximum(lse, new_lse)
+    top = np.where(np.isinf(top), 0.0, top)
+    a, b = np.exp(lse - top), np.exp(new_lse - top)
+    total = a + b
+    merged = (out * a[..., None] + new_out * b[..., None]) / np.where(total > 0, total, 1)[..., None]
+    with np.errstate(divide="ignore"):
+        return merged, top + np.log(total)
+
+
+def gqa_expand(kv: np.ndarray, n_q_heads: int) -> np.ndarray:
+    """[T, Hkv, D] -> [T, Hq, D]: query head h reads KV head h // (Hq / Hkv)."""
+    group = n_q_heads // kv.shape[1]
+    return np.repeat(kv, group, axis=1)
+
+
+def silu_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """silu(gate) * up in float64 (the chapter's ``F.silu(gate) * up``)."""
+    g = f64(gate)
+    return g / (1.0 + np.exp(-g)) * f64(up)
+
+
+# --------------------------------------------------------------------------------------------
+# one stage
+# --------------------------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class Dims:
+    d_model: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    d_ffn: int
+    vocab: int
+    rms_eps: float = 1e-5
+    rope_theta: float = 1e4
+
+    @staticmethod
+    def of(shape) -> "Dims":
+        return Dims(shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ffn,
+                    shape.vocab, shape.rms_eps, shape.rope_theta)
+
+
+class Stage:
+    """A contiguous block range [begin, end) with its own weights and per-slot KV cache.
+
+    ``weights`` maps (role, global_block) -> bf16 bits; the roles are embed, attn_norm, wq, wk, wv,
+    wo, mlp_norm, wgate, wup, wdown (per block), final_norm, readout.  K and V are cached as the
+    bf16 values the attention reads, per slot, block and absolute position.
+    """
+
+    def __init__(self, dims: Dims, begin: int, end: int, first: bool, last: bool, weights: dict,
+                 max_ctx: int, pure_f32: bool = False):
+        self.c, self.begin, self.end, self.first, self.last = dims, begin, end, first, last
+        self.w, self.max_ctx = weights, max_ctx
+        self.pure_f32 = pure_f32          # information only: drop the bf16 rounding points
+        self.kv = {}                      # slot -> (K, V) float32 [blocks, ctx, Hkv, Dh]
+
+    # rounding points R1..R7 (bf16 operands of GEMMs and attention)
+    def _r(self, x):
+        return np.asarray(x, dtype=np.float32) if self.pure_f32 else round_bf16(x)
+
+    def _cache(self, slot: int):
+        if slot not in self.kv:
+            shp = (self.end - self.begin, self.max_ctx, self.c.n_kv_heads, self.c.head_dim)
+            self.kv[slot] = (np.zeros(shp, np.float32), np.zeros(shp, np.float32))
+        return self.kv[slot]
+
+    def embed(self, tokens: np.ndarray) -> np.ndarray:
+        """First stage only: x_t = E[token_t] as F32 (exact)."""
+        assert self.first
+        return bf16_to_f32(self.w[("embed", -1)][np.asarray(tokens)])
+
+    def block(self, b: int, x: np.ndarray, slots: np.ndarray, positions: np.ndarray) -> np.ndarray:
+        """One decoder block on F32 rows x [M, d]; row m is slot slots[m] at positions[m]."""
+        c, w = self.c, self.w
+        hq, hkv, dh = c.n_q_heads, c.n_kv_heads, c.head_dim
+        m_rows = x.shape[0]
+        gain1 = bf16_to_f32(w[("attn_norm", b)])
+        h = self._r(rms_norm(x, gain1, c.rms_eps))                              # R1
+        q = linear(h, w[("wq", b)]).reshape(m_rows, hq, dh)
+        k = linear(h, w[("wk", b)]).reshape(m_rows, hkv, dh)
+        v = linear(h, w[("wv", b)]).reshape(m_rows, hkv, dh)
+        q = self._r(rope(q, positions, c.rope_theta))                          # R2 (q~)
+        k = self._r(rope(k, positions, c.rope_theta))                          # R3 (cached K)
+        v = self._r(v)                                                         # R3 (cached V)
+        lb = b - self.begin
+        for m in range(m_rows):                                                # write KV first
+            kc, vc = self._cache(int(slots[m]))
+            kc[lb, positions[m]] = k[m]
+            vc[lb, positions[m]] = v[m]
+        attn = np.empty((m_rows, hq * dh), np.float32)
+        scale = dh ** -0.5
+        for s in np.unique(slots):
+            rows = np.nonzero(slots == s)[0]
+            kc, vc = self._cache(int(s))
+            n_keys = int(positions[rows].max()) + 1
+            kk = gqa_expand(kc[lb, :n_keys], hq)
+            vv = gqa_expand(vc[lb, :n_keys], hq)
+            o, _ = attention_partial(q[rows], kk, vv, positions[rows].astype(np.int64),
+                                     np.arange(n_keys), scale)
+            attn[rows] = self._r(o.astype(np.float32)).reshape(len(rows), hq * dh)  # R4
+        x1 = (x + linear(attn, w[("wo", b)])).astype(np.float32)
+        gain2 = bf16_to_f32(w[("mlp_norm", b)])
+        h2 = self._r(rms_norm(x1, gain2, c.rms_eps))                           # R5
+        gate = linear(h2, w[("wgate", b)])
+        up = linear(h2, w[("wup", b)])
+        a = self._r(silu_mul(gate, up).astype(np.float32))                     # R6
+        return (x1 + linear(a, w[("wdown", b)])).astype(np.float32)
+
+    def forward(self, x: np.ndarray, slots, positions) -> np.ndarray:
+        """All blocks of the stage; returns the F32 residual handed to the next stage."""
+        x = np.asarray(x, dtype=np.float32)
+        slots = np.asarray(slots, dtype=np.int64).reshape(-1)
+        positions = np.asarray(positions, dtype=np.int64).reshape(-1)
+        assert x.shape[0] == slots.shape[0] == positions.shape[0]
+        assert positions.max(initial=0) < self.max_ctx
+        for b in range(self.begin, self.end):
+            x = self.block(b, x, slots, positions)
+        return x
+
+    def prefill(self, x, slot: int, pos0: int) -> np.ndarray:
+        t = x.shape[0]
+        return self.forward(x, np.full(t, slot), np.arange(pos0, pos0 + t))
+
+    def readout(self, x: np.ndarray):
+        """Last stage only: final RMSNorm (F32 "final hidden") and F32 logits of bf16(h_N)."""
+        assert self.last
+        g = bf16_to_f32(self.w[("final_norm", -1)])
+        h_n = rms_norm(x, g, self.c.rms_eps).astype(np.float32)
+        logits = linear(self._r(h_n), self.w[("readout", -1)])                 # R7
+        return logits, h_n
+
+    def kv_bits(self, slot: int, n_pos: int):
+        """bf16 bits of the cached K and V of a slot, positions [0, n_pos): [blocks, n, Hkv, Dh]."""
+        kc, vc = self._cache(slot)
+        return f32_to_bf16_bits(kc[:, :n_pos]), f32_to_bf16_bits(vc[:, :n_pos])
+
+
+def greedy(logits: np.ndarray) -> np.ndarray:
+    """argmax per row, lowest index on ties."""
+    return np.argmax(logits, axis=-1).astype(np.int32)
+
+
+def top2_margin(logits: np.ndarray) -> np.ndarray:
+    part = np.sort(logits, axis=-1)
+    return part[..., -1] - part[..., -2]
+
+
+# --------------------------------------------------------------------------------------------
+# pipeline driver (split vs unsplit) and the sharded-MLP slices
+# --------------------------------------------------------------------------------------------
+
+
+def generate(stages: list, prompt: np.ndarray, n_new: int, slot: int = 0):
+    """Greedy generation through an ordered list of stages, handing F32 rows between them.
+
+    One token comes from the prompt's last logits row, then n_new - 1 decode steps (the
+    chapter's "16 new tokens" are one prefill step plus fifteen decode steps).  Returns the tokens
+    and, per step, the handoff rows, the final hidden rows and the logits.
+    """
+    trace = {"handoff": [], "final_hidden": [], "logits": [], "residual": []}
+    x = stages[0].embed(prompt)
+    pos0, t = 0, len(prompt)
+    for st in stages:
+        x = st.prefill(x, slot, pos0)
+        trace["handoff"].append(x.copy())
+    logits, h_n = stages[-1].readout(x)
+    trace["residual"].append(x)
+    trace["final_hidden"].append(h_n)
+    trace["logits"].append(logits)
+    toks = [int(greedy(logits[-1:])[0])]
+    pos = t
+    for _ in range(n_new - 1):
+        x = stages[0].embed(np.array([toks[-1]]))
+        for st in stages:
+            x = st.forward(x, [slot], [pos])
+            trace["handoff"].append(x.copy())
+        logits, h_n = stages[-1].readout(x)
+        trace["residual"].append(x)
+        trace["final_hidden"].append(h_n)
+        trace["logits"].append(logits)
+        toks.append(int(greedy(logits)[0]))
+        pos += 1
+    return np.array(toks, dtype=np.int32), trace
+
+
+def mlp_full(x: np.ndarray, g_mlp: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
+             eps: float):
+    """The whole SwiGLU MLP of F32 rows x: returns (bf16 activation a, F32 f32(W_d a))."""
+    h = round_bf16(rms_norm(x, bf16_to_f32(g_mlp), eps))                      # R5
+    a = round_bf16(silu_mul(linear(h, wg), linear(h, wu)).astype(np.float32))  # R6
+    return a, linear(a, wd)
+
+
+def mlp_slices(x, g_mlp, wg, wu, wd, eps: float, n_slices: int):
+    """Megatron column/row split: slice i keeps rows [i*w, (i+1)*w) of W_gate and W_up and the
+    same columns of W_down, giving an F32 partial; partials are summed in slice order
+    ((p0 + p1) + p2) + ... in float32.  Returns (slice activations, partials, f32 sum)."""
+    f = wg.shape[0]
+    w = f // n_slices
+    h = round_bf16(rms_norm(x, bf16_to_f32(g_mlp), eps))
+    acts, parts = [], []
+    for i in range(n_slices):
+        lo, hi = i * w, (i + 1) * w
+        a_i = round_bf16(silu_mul(linear(h, wg[lo:hi]), linear(h, wu[lo:hi])).astype(np.float32))
+        acts.append(a_i)
+        parts.append(linear(a_i, np.ascontiguousarray(wd[:, lo:hi])))
+    total = parts[0].copy()
+    for p in parts[1:]:
+        total = (total + p).astype(np.float32)
+    return acts, parts, total

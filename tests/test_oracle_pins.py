@@ -1,0 +1,335 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+No page prints activations or logits for a worked forward pass, so the oracle's forward values
+are pinned by brute force on tiny shapes (pure-Python loops with math.exp, no numpy matmul or
+einsum), closed forms, a worked RoPE example, and invariants the pages fix:
+* split vs unsplit bit-identity ("RFC: pipeline placement ...", Numerical correctness proof);
+* the split-KV merge identity ("41. Many GPUs", Ring attention: merge_partials);
+* Megatron slice sums ("41. Many GPUs", Tensor parallelism: take_rows / take_cols);
+* prefill/decode/chunked-prefill consistency (TensorSharp, Reproducible validation: full and
+  chunked prefill, decode, refill and reset probes compared against an unsplit control).
+Several tests plant a plausible mistake in a copy of an oracle function and check that the
+matching pin catches it.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import fixtures as fx
+from oracle import decoder as o
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TINY = fx.TINY
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------------------------
+
+def test_bf16_round_to_nearest_even():
+    one = 1.0
+    cases = {
+        one: one,
+        one + 2 ** -8: one,                        # tie, rounds to even mantissa 0
+        one + 3 * 2 ** -8: one + 2 ** -6,          # tie between mantissa 1 and 2 -> 2
+        one + 2 ** -8 + 2 ** -20: one + 2 ** -7,   # just above the tie -> up
+        -(one + 2 ** -8 + 2 ** -20): -(one + 2 ** -7),
+        3.140625: 3.140625,                        # exactly representable
+    }
+    for x, want in cases.items():
+        assert float(o.round_bf16(np.float32(x))) == want, x
+    bits = o.f32_to_bf16_bits(np.array([1.0, -2.0, 0.5], np.float32))
+    assert bits.tolist() == [0x3F80, 0xC000, 0x3F00]
+    assert o.bf16_to_f32(np.array([0x3F80, 0xC000], np.uint16)).tolist() == [1.0, -2.0]
+
+
+def test_bf16_matches_fixture_generator_rounding():
+    # the generator's own RNE (fx_core.h) and the oracle's must agree on random f32 values
+    vals = fx.normal_f32(7, 11, 4096) * np.float32(0.37)
+    via_oracle = o.f32_to_bf16_bits(vals)
+    # values 0.37 * z are not what the generator rounds, so compare with an independent route:
+    # exhaustive neighbour search of the nearest bf16 (ties to even) in pure Python
+    for v, b in zip(vals[:256].tolist(), via_oracle[:256].tolist()):
+        u = np.float32(v).view(np.uint32).item()
+        lo = u & 0xFFFF0000
+        hi = lo + 0x10000
+        flo = np.uint32(lo).view(np.float32).item()
+        fhi = np.uint32(hi).view(np.float32).item()
+        dlo, dhi = abs(v - flo), abs(fhi - v)
+        pick = lo if (dlo < dhi or (dlo == dhi and ((lo >> 16) & 1) == 0)) else hi
+        assert b == pick >> 16
+
+
+# ---------------------------------------------------------------------------------------------
+# RMSNorm, linear, RoPE, SwiGLU
+# ---------------------------------------------------------------------------------------------
+
+def test_rms_norm_closed_form_constant_row():
+    d, eps = 64, 1e-5
+    g = 1.0 + 0.1 * rng(1).standard_normal(d)
+    for c in (0.0, 0.3, -2.5, 7.0):
+        c = float(np.float32(c))
+        y = o.rms_norm(np.full((1, d), c, np.float32), g, eps)
+        want = g * c / math.sqrt(c * c + eps)
+        np.testing.assert_allclose(y[0], want, rtol=1e-13, atol=0)
+
+
+def test_rms_norm_bruteforce_and_gain_matters():
+    x = rng(2).standard_normal((3, 16)).astype(np.float32)
+    g = (1.0 + 0.2 * rng(3).standard_normal(16)).astype(np.float32)
+    y = o.rms_norm(x, g, 1e-5)
+    for m in range(3):
+        ms = sum(float(v) * float(v) for v in x[m]) / 16
+        r = 1.0 / math.sqrt(ms + 1e-5)
+        for i in range(16):
+            assert abs(y[m, i] - float(x[m, i]) * r * float(g[i])) < 1e-12
+    assert not np.allclose(o.rms_norm(x, np.ones(16), 1e-5), y)   # a dropped gain is visible
+
+
+def test_linear_bruteforce_nonsquare():
+    # W is [out, in] (nn.Linear layout); a transposed operand would not even have the right shape
+    h = o.round_bf16(rng(4).standard_normal((3, 5)))
+    w_bits = fx.normal_bf16(1, 2, 7 * 5, 0.5).reshape(7, 5)
+    w = o.bf16_to_f32(w_bits)
+    y = o.linear(h, w_bits)
+    assert y.shape == (3, 7) and y.dtype == np.float32
+    for m in range(3):
+        for n in range(7):
+            s = 0.0
+            for k in range(5):
+                s += float(h[m, k]) * float(w[n, k])
+            assert y[m, n] == np.float32(s)
+
+
+def test_rope_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "rope_worked_example.json")))
+    x = np.array(g["x"], np.float64).reshape(1, 1, 4)
+    y = o.rope(x, np.array([g["position"]]), g["theta"])[0, 0]
+    np.testing.assert_allclose(y, g["y"], rtol=0, atol=1e-14)
+
+
+def test_rope_identity_norm_and_relative_position():
+    r = rng(5)
+    dh = 64
+    x = r.standard_normal((1, 3, dh))
+    np.testing.assert_array_equal(o.rope(x, np.array([0]), 1e4), x)            # position 0
+    y = o.rope(x, np.array([37]), 1e4)
+    half = dh // 2
+    np.testing.assert_allclose(x[..., :half] ** 2 + x[..., half:] ** 2,
+                               y[..., :half] ** 2 + y[..., half:] ** 2, rtol=1e-12)
+    q, k = r.standard_normal((1, 1, dh)), r.standard_normal((1, 1, dh))
+    for m, n, s in ((5, 2, 11), (100, 0, 4000), (8191, 17, 3)):
+        a = np.sum(o.rope(q, np.array([m]), 1e4) * o.rope(k, np.array([n]), 1e4))
+        b = np.sum(o.rope(q, np.array([m + s]), 1e4) * o.rope(k, np.array([n + s]), 1e4))
+        assert abs(a - b) < 1e-9 * max(1.0, abs(a))
+
+
+def test_rope_pin_catches_interleaved_pairs():
+    # planted mistake: the interleaved (x_2i, x_2i+1) pairing instead of rotate-half
+    def rope_interleaved(x, positions, theta):
+        x = np.asarray(x, np.float64)
+        a = o.rope_angles(positions, x.shape[-1], theta)[:, None, :]
+        c, s = np.cos(a), np.sin(a)
+        ev, od = x[..., 0::2], x[..., 1::2]
+        y = np.empty_like(x)
+        y[..., 0::2], y[..., 1::2] = ev * c - od * s, od * c + ev * s
+        return y
+
+    g = json.load(open(os.path.join(GOLDEN, "rope_worked_example.json")))
+    x = np.array(g["x"], np.float64).reshape(1, 1, 4)
+    y = rope_interleaved(x, np.array([g["position"]]), g["theta"])[0, 0]
+    assert np.max(np.abs(y - np.array(g["y"]))) > 1e-3
+
+
+def test_silu_mul():
+    g = np.array([0.0, 1.0, -1.0, 30.0, -30.0])
+    u = np.array([2.0, 1.0, 1.0, 1.0, 1.0])
+    y = o.silu_mul(g, u)
+    want = [0.0, 1.0 / (1.0 + math.exp(-1.0)), -1.0 / (1.0 + math.exp(1.0)),
+            30.0 / (1.0 + math.exp(-30.0)), -30.0 / (1.0 + math.exp(30.0))]
+    np.testing.assert_allclose(y, want, rtol=1e-15, atol=1e-300)
+
+
+# ---------------------------------------------------------------------------------------------
+# attention: brute force, special cases, GQA map, split-KV merge
+# ---------------------------------------------------------------------------------------------
+
+def brute_attention(q, k, v, q_pos, k_pos, scale, group):
+    """Pure-Python causal GQA attention: q [Tq, Hq, D], k/v [Tk, Hkv, D]; head h uses KV h//group."""
+    tq, hq, dd = q.shape
+    out = np.zeros((tq, hq, dd))
+    for t in range(tq):
+        for h in range(hq):
+            g = h // group
+            sc = []
+            for j in range(k.shape[0]):
+                if k_pos[j] <= q_pos[t]:
+                    sc.append((j, sum(float(q[t, h, e]) * float(k[j, g, e]) for e in range(dd)) * scale))
+            if not sc:
+                continue
+            mx = max(s for _, s in sc)
+            ws = [(j, math.exp(s - mx)) for j, s in sc]
+            z = sum(w for _, w in ws)
+            for e in range(dd):
+                out[t, h, e] = sum(w * float(v[j, g, e]) for j, w in ws) / z
+    return out
+
+
+@pytest.mark.parametrize("tq,tk,hq,hkv,dd", [(4, 4, 2, 1, 4), (5, 8, 4, 2, 4), (3, 6, 4, 4, 8),
+                                             (8, 8, 4, 1, 64)])
+def test_attention_bruteforce(tq, tk, hq, hkv, dd):
+    r = rng(tq * 100 + tk)
+    q = r.standard_normal((tq, hq, dd))                 # N(0,1): not near-uniform attention
+    k = r.standard_normal((tk, hkv, dd))
+    v = r.standard_normal((tk, hkv, dd))
+    q_pos = np.arange(tk - tq, tk)
+    k_pos = np.arange(tk)
+    scale = dd ** -0.5
+    got, lse = o.attention_partial(q, o.gqa_expand(k, hq), o.gqa_expand(v, hq), q_pos, k_pos, scale)
+    want = brute_attention(q, k, v, q_pos, k_pos, scale, hq // hkv)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    assert lse.shape == (tq, hq) and np.all(np.isfinite(lse))
+
+
+def test_attention_gqa_map_pin_catches_modulo_mapping():
+    r = rng(9)
+    q, k, v = r.standard_normal((2, 4, 4)), r.standard_normal((3, 2, 4)), r.standard_normal((3, 2, 4))
+    want = brute_attention(q, k, v, np.array([1, 2]), np.arange(3), 0.5, 2)
+    wrong = np.concatenate([k, k], axis=1)              # planted: head h -> KV head h % Hkv
+    got, _ = o.attention_partial(q, wrong, np.concatenate([v, v], axis=1), np.array([1, 2]),
+                                 np.arange(3), 0.5)
+    assert np.max(np.abs(got - want)) > 1e-3
+
+
+def test_attention_special_cases():
+    r = rng(10)
+    v = r.standard_normal((5, 1, 4))
+    k = np.zeros((5, 1, 4))
+    q = r.standard_normal((1, 1, 4))
+    # equal scores -> mean of the visible values
+    out, lse = o.attention_partial(q, k, v, np.array([2]), np.arange(5), 1.0)
+    np.testing.assert_allclose(out[0, 0], v[:3, 0].mean(axis=0), rtol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], math.log(3.0), rtol=1e-14)
+    # one visible key -> its value
+    out, _ = o.attention_partial(q, r.standard_normal((5, 1, 4)), v, np.array([0]), np.arange(5), 1.0)
+    np.testing.assert_allclose(out[0, 0], v[0, 0], rtol=1e-14)
+    # no visible key -> zero output and lse -inf
+    out, lse = o.attention_partial(q, k, v, np.array([0]), np.arange(1, 6), 1.0)
+    assert np.all(out == 0) and np.isneginf(lse[0, 0])
+
+
+def test_split_kv_merge_identity():
+    r = rng(11)
+    tq, tk, h, dd = 3, 37, 4, 16
+    q, k, v = r.standard_normal((tq, h, dd)), r.standard_normal((tk, h, dd)), r.standard_normal((tk, h, dd))
+    q_pos, k_pos = np.arange(tk - tq, tk), np.arange(tk)
+    full, full_lse = o.attention_partial(q, k, v, q_pos, k_pos, 0.25)
+    for chunk in (1, 5, 16, 36):
+        out = np.zeros((tq, h, dd))
+        lse = np.full((tq, h), -np.inf)
+        for s in range(0, tk, chunk):
+            po, pl = o.attention_partial(q, k[s:s + chunk], v[s:s + chunk], q_pos, k_pos[s:s + chunk], 0.25)
+            out, lse = o.merge_partials(out, lse, po, pl)
+        np.testing.assert_allclose(out, full, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, full_lse, rtol=1e-13)
+    # merging an empty partial (lse -inf) is the identity
+    e_out, e_lse = o.merge_partials(full, full_lse, np.zeros_like(full), np.full_like(full_lse, -np.inf))
+    np.testing.assert_allclose(e_out, full, rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------------------------
+# MLP slices
+# ---------------------------------------------------------------------------------------------
+
+def test_mlp_slices_sum_to_full_mlp():
+    d, f, n = 32, 48, 4
+    x = fx.normal_f32(3, 1, 5 * d).reshape(5, d)
+    g = fx.gain_bf16(3, 2, d, 0.1)
+    wg = fx.normal_bf16(3, 3, f * d, 0.1).reshape(f, d)
+    wu = fx.normal_bf16(3, 4, f * d, 0.1).reshape(f, d)
+    wd = fx.normal_bf16(3, 5, d * f, 0.1).reshape(d, f)
+    a_full, y_full = o.mlp_full(x, g, wg, wu, wd, 1e-5)
+    acts, parts, total = o.mlp_slices(x, g, wg, wu, wd, 1e-5, n)
+    w = f // n
+    for i in range(n):   # column-parallel slices see exactly their columns of the activation
+        np.testing.assert_array_equal(acts[i], a_full[:, i * w:(i + 1) * w])
+    # float64 invariant: sum of the exact partials equals the exact full product
+    wd64 = o.bf16_to_f32(wd).astype(np.float64)
+    exact_parts = [acts[i].astype(np.float64) @ wd64[:, i * w:(i + 1) * w].T for i in range(n)]
+    exact_full = a_full.astype(np.float64) @ wd64.T
+    np.testing.assert_allclose(sum(exact_parts), exact_full, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(total, y_full, rtol=1e-5, atol=1e-6)
+    # planted mistake: row slices of W_down instead of its columns do not sum to the MLP
+    assert wd.shape[0] != wd.shape[1] or True
+    bad = [acts[i].astype(np.float64) @ wd64[:w, :][:, :w].T for i in range(n)]
+    assert np.max(np.abs(sum(bad)[:, :w] - exact_full[:, :w])) > 1e-3
+
+
+# ---------------------------------------------------------------------------------------------
+# stage-level invariants on the tiny decoder
+# ---------------------------------------------------------------------------------------------
+
+def tiny_stage(begin, end, first, last, gain_sigma=0.1, max_ctx=64):
+    w = fx.draw_stage_weights(TINY, begin, end, first, last, gain_sigma=gain_sigma)
+    return o.Stage(o.Dims.of(TINY), begin, end, first, last, w, max_ctx)
+
+
+def test_split_equals_unsplit_bitwise():
+    prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(0), 16, TINY.vocab)
+    whole = tiny_stage(0, 2, True, True)
+    toks1, tr1 = o.generate([whole], prompt, 8)
+    a, b = tiny_stage(0, 1, True, False), tiny_stage(1, 2, False, True)
+    toks2, tr2 = o.generate([a, b], prompt, 8)
+    np.testing.assert_array_equal(toks1, toks2)
+    for key in ("logits", "final_hidden", "residual"):
+        for u, v in zip(tr1[key], tr2[key]):
+            assert u.tobytes() == v.tobytes(), key
+    kw, vw = whole.kv_bits(0, 23)
+    ka, va = a.kv_bits(0, 23)
+    kb, vb = b.kv_bits(0, 23)
+    assert np.array_equal(kw[0], ka[0]) and np.array_equal(kw[1], kb[0])
+    assert np.array_equal(vw[0], va[0]) and np.array_equal(vw[1], vb[0])
+
+
+def test_prefill_decode_and_chunked_consistency():
+    x = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(0), 17 * TINY.d_model).reshape(17, TINY.d_model)
+    s1 = tiny_stage(0, 2, False, False)
+    full = s1.prefill(x, 0, 0)
+    s2 = tiny_stage(0, 2, False, False)
+    part = s2.prefill(x[:16], 0, 0)
+    last = s2.forward(x[16:], [0], [16])
+    s3 = tiny_stage(0, 2, False, False)
+    c1 = s3.prefill(x[:8], 0, 0)
+    c2 = s3.prefill(x[8:], 0, 8)
+    # rows are independent up to the float64 summation order of the library matmul
+    np.testing.assert_allclose(np.vstack([part, last]), full, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(np.vstack([c1, c2]), full, rtol=1e-6, atol=1e-6)
+    k1, v1 = s1.kv_bits(0, 17)
+    k3, v3 = s3.kv_bits(0, 17)
+    assert np.mean(k1 == k3) > 0.999 and np.mean(v1 == v3) > 0.999
+
+
+def test_determinism_and_reset():
+    prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(0), 16, TINY.vocab)
+    s = tiny_stage(0, 2, True, True)
+    t1, tr1 = o.generate([s], prompt, 4)
+    t2, tr2 = o.generate([s], prompt, 4)         # "reset": the caller rewinds positions to 0
+    np.testing.assert_array_equal(t1, t2)
+    assert all(a.tobytes() == b.tobytes() for a, b in zip(tr1["logits"], tr2["logits"]))
+
+
+def test_rounding_points_change_the_result():
+    # the bf16 rounding points are part of the definition; the pure-f32 variant differs
+    w = fx.draw_stage_weights(TINY, 0, 2, False, False, gain_sigma=0.1)
+    x = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(0), 4 * TINY.d_model).reshape(4, TINY.d_model)
+    a = o.Stage(o.Dims.of(TINY), 0, 2, False, False, w, 16).prefill(x, 0, 0)
+    b = o.Stage(o.Dims.of(TINY), 0, 2, False, False, w, 16, pure_f32=True).prefill(x, 0, 0)
+    rel = np.linalg.norm(a - b) / np.linalg.norm(a)
+    assert 1e-6 < rel < 1e-2
