@@ -1,0 +1,191 @@
+/*
+ * stage.h -- C ABI of one pipeline stage of a decoder-only transformer on an MI355X (gfx950).
+ *
+ * A stage owns a contiguous, half-open range of GLOBAL block ids [block_begin, block_end) with its
+ * own weights and per-slot KV cache, takes F32 hidden rows in and gives F32 hidden rows out.  The
+ * first stage also embeds tokens; the last stage also applies the final RMSNorm and the readout.
+ *
+ * Sources (page title, section):
+ *  - "RFC: pipeline placement across multiple GPUs for models larger than one device",
+ *    What I found / Proposed architecture: each stage owns its resident weights, KV state, heap and
+ *    workspace; only the hidden activation crosses the boundary; a step is accepted only after all
+ *    stages succeed; a placement is a global block range with weight roles, a state plan and a
+ *    resource plan; a model that does not fit returns a typed DoesNotFit.
+ *  - "41. Many GPUs: tensor, pipeline, expert and data parallelism", Pipeline parallelism
+ *    (PipelineStage.forward): embed on the first stage, per block add_norm -> attention ->
+ *    add_norm -> MLP, the residual x + delta is what crosses, final norm at the end; Tensor
+ *    parallelism: [out, in] weights, GQA head map h // (Hq / Hkv), MLP down(silu(gate) * up);
+ *    Ring attention: causal attention with keys k_pos > q_pos masked, split-KV merge by LSE.
+ *  - "Multi-node layer splitting and tensor parallelism" (TensorSharp), Supported stage executors:
+ *    the dense pipeline hands F32 hidden activations; each stage loads only its layer weights and
+ *    KV state; the first embeds, the last computes logits; unsupported families are refused before
+ *    any GPU allocation.
+ *
+ * Conventions for every entry point:
+ *  - Return an int status (STAGE_OK or a STAGE_E_* code); nothing throws across the ABI.
+ *  - Pointers are DEVICE pointers unless marked "host".  Buffers are caller-owned, contiguous and
+ *    row-major; the stage keeps no pointer to them after the call returns.
+ *  - All device work is enqueued asynchronously on the given hipStream_t (0 = default stream);
+ *    a call returns once the work is enqueued.  Arguments are validated on the host before any
+ *    work is enqueued; a call that fails validation enqueues nothing.
+ *  - Positions and sequence lengths belong to the caller and are passed with every call.  A call
+ *    writes KV only at the positions it is given, so a failed step is retried at the same
+ *    positions, and "reset"/"truncate" are rewinds of the caller's positions.
+ *  - One host thread per handle; calls that overlap on one handle are not supported.
+ *  - Values that only the device sees (token ids, decode slots and positions) are checked on the
+ *    device: rows with an out-of-range value are not computed (their outputs are zero) and the
+ *    device error counter (stage_device_errors) is incremented; nothing is written out of bounds.
+ */
+#ifndef PIPELINE_STAGE_DECODER_STAGE_H
+#define PIPELINE_STAGE_DECODER_STAGE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------------------------- */
+enum {
+  STAGE_OK = 0,
+  STAGE_E_INVALID = 1,      /* null pointer, non-positive size, T or B above max_tokens */
+  STAGE_E_UNSUPPORTED = 2,  /* configuration refused before any allocation */
+  STAGE_E_DOES_NOT_FIT = 3, /* arena_bytes below the plan's total_bytes */
+  STAGE_E_ROLE = 4,         /* embed off the first stage, readout off the last, role/block outside range */
+  STAGE_E_RANGE = 5,        /* slot >= max_slots, pos0 + T > max_ctx, n_elems wrong for the role */
+  STAGE_E_HIP = 6           /* a HIP call or kernel launch failed; stage_last_error() has the text */
+};
+
+/* ---- configuration -------------------------------------------------------------------------- */
+/* Decoder dimensions (identical on every stage of one model). */
+typedef struct {
+  int32_t d_model;        /* hidden width d; multiple of 64 */
+  int32_t n_q_heads;      /* Hq */
+  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0 and Hq / Hkv <= 16 */
+  int32_t head_dim;       /* Dh in {64, 128} */
+  int32_t d_ffn;          /* SwiGLU width F; multiple of 16 */
+  int32_t vocab;          /* V */
+  int32_t n_blocks_total; /* blocks of the whole model */
+  float rms_eps;          /* RMSNorm epsilon (inside the square root) */
+  float rope_theta;       /* RoPE base; angle(pos, i) = pos * theta^(-2i/Dh) */
+} stage_model_cfg;
+
+#define STAGE_FIRST 1u /* owns the token embedding */
+#define STAGE_LAST 2u  /* owns the final RMSNorm and the readout */
+
+typedef struct {
+  int32_t block_begin; /* first GLOBAL block id (inclusive) */
+  int32_t block_end;   /* one past the last GLOBAL block id; block_begin <= block_end */
+  uint32_t flags;      /* STAGE_FIRST | STAGE_LAST */
+  int32_t max_slots;   /* KV slots (sequences) */
+  int32_t max_ctx;     /* positions per slot: every position used is < max_ctx */
+  int32_t max_tokens;  /* rows per call: prefill T and decode B are <= max_tokens */
+} stage_stage_cfg;
+
+typedef struct {
+  uint64_t weight_bytes;    /* bf16 matrices, F32 norm gains */
+  uint64_t kv_bytes;        /* bf16 K and V for every owned block and slot */
+  uint64_t table_bytes;     /* RoPE cos/sin table (F32) */
+  uint64_t workspace_bytes; /* per-call activations, split-K and split-KV partials, counters */
+  uint64_t total_bytes;     /* arena size stage_create needs (sum of the above with alignment) */
+} stage_plan_t;
+
+typedef struct stage stage_t;
+
+/* ---- weight roles ----------------------------------------------------------------------------- */
+/* Every matrix is bf16 [out, in] row-major (the nn.Linear layout); gains are bf16 [d]. */
+enum {
+  STAGE_ROLE_EMBED = 0,      /* [V, d], first stage, global_block = -1 */
+  STAGE_ROLE_ATTN_NORM = 1,  /* [d] */
+  STAGE_ROLE_WQ = 2,         /* [Hq*Dh, d] */
+  STAGE_ROLE_WK = 3,         /* [Hkv*Dh, d] */
+  STAGE_ROLE_WV = 4,         /* [Hkv*Dh, d] */
+  STAGE_ROLE_WO = 5,         /* [d, Hq*Dh] */
+  STAGE_ROLE_MLP_NORM = 6,   /* [d] */
+  STAGE_ROLE_WGATE = 7,      /* [F, d] */
+  STAGE_ROLE_WUP = 8,        /* [F, d] */
+  STAGE_ROLE_WDOWN = 9,      /* [d, F] */
+  STAGE_ROLE_FINAL_NORM = 10,/* [d], last stage, global_block = -1 */
+  STAGE_ROLE_READOUT = 11    /* [V, d], last stage, global_block = -1 (untied from the embedding) */
+};
+
+/* ---- entry points ------------------------------------------------------------------------------ */
+
+/* Byte plan of a stage (host only, no GPU call).  The arena of stage_create must hold
+ * out->total_bytes.  STAGE_E_UNSUPPORTED for a configuration the kernels do not cover
+ * (checked before anything is allocated), STAGE_E_INVALID for a malformed one. */
+int stage_plan(const stage_model_cfg* model, const stage_stage_cfg* stage, stage_plan_t* out /*host*/);
+
+/* Create a stage inside a caller-allocated device arena (e.g. a torch uint8 tensor) on device
+ * `device`.  The stage sub-allocates weights, KV cache, tables and workspace inside the arena and
+ * never allocates device memory itself.  The arena must stay allocated until stage_destroy.
+ * Zero-fills the KV cache and uploads the RoPE table synchronously.  *out receives a host handle.
+ * STAGE_E_DOES_NOT_FIT if arena_bytes < plan.total_bytes. */
+int stage_create(const stage_model_cfg* model, const stage_stage_cfg* stage, void* arena,
+                 uint64_t arena_bytes, int device, stage_t** out);
+
+/* Copy one weight tensor into the stage.  src: bf16 bits in the role's [out, in] layout, host or
+ * device memory; n_elems must equal the role's element count.  global_block is the GLOBAL block
+ * id for per-block roles (inside [block_begin, block_end)) and -1 for EMBED/FINAL_NORM/READOUT.
+ * The stage stores its own layout (fused QKV, interleaved gate/up, F32 gains).  Host sources are
+ * copied synchronously; device sources are copied on `stream`. */
+int stage_load_weight(stage_t* st, int role, int global_block, const uint16_t* src, uint64_t n_elems,
+                      hipStream_t stream);
+
+/* First stage: hidden_out[i, :] = f32(E[tokens[i], :]) for i < n (exact bf16 -> f32). */
+int stage_embed(stage_t* st, int n, const int32_t* tokens, float* hidden_out, hipStream_t stream);
+
+/* Prefill (or a prefill chunk) of T rows of one slot at positions pos0 .. pos0+T-1: runs every
+ * owned block over hidden_in [T, d] (F32), writes K/V at those positions, attends causally over
+ * positions [0, pos0 + t] for row t, and writes the stage output residual to hidden_out [T, d].
+ * hidden_out may equal hidden_in.  Positions below pos0 must hold KV written earlier. */
+int stage_prefill(stage_t* st, int slot, int pos0, int T, const float* hidden_in, float* hidden_out,
+                  hipStream_t stream);
+
+/* One decode step for B rows: row b is slot slots[b] at position positions[b] (device int32
+ * arrays; slots distinct), attending over positions [0, positions[b]].  hidden_in/out [B, d] F32;
+ * hidden_out may equal hidden_in.  The kernel schedule depends only on B, the shapes and
+ * max_ctx, so the call can be captured in a HIP graph and replayed with new slots/positions. */
+int stage_decode(stage_t* st, int B, const int32_t* slots, const int32_t* positions,
+                 const float* hidden_in, float* hidden_out, hipStream_t stream);
+
+/* Last stage: normed_out = RMSNorm(hidden_in) * g_final (F32 "final hidden", nullable) and
+ * logits_out [n, V] (F32) = bf16(normed) W_readout^T. */
+int stage_readout(stage_t* st, int n, const float* hidden_in, float* logits_out, float* normed_out,
+                  hipStream_t stream);
+
+/* SwiGLU MLP of one owned block without its residual: out [n, d] (F32) = W_down a with
+ * a = bf16(silu(W_gate h) * (W_up h)), h = bf16(RMSNorm(hidden_in) * g_mlp).  With accumulate != 0
+ * the result is added to out (out = out + W_down a, one F32 add per element), so calling it over
+ * column/row slices of one MLP in slice order sums the partials as ((p0 + p1) + p2) + ...
+ * ("41. Many GPUs", Tensor parallelism: take_rows / take_cols and the one all-reduce per MLP;
+ * TensorSharp, Transport and tuning: node-order summation). */
+int stage_mlp(stage_t* st, int global_block, int n, const float* hidden_in, float* out, int accumulate,
+              hipStream_t stream);
+
+/* Copy KV positions [0, n_pos) of every owned block from src_slot to dst_slot. */
+int stage_kv_copy(stage_t* st, int src_slot, int dst_slot, int n_pos, hipStream_t stream);
+
+/* Write / read KV of one owned block and slot at positions [pos0, pos0+n): k, v are device bf16
+ * [n, Hkv, Dh] (K after RoPE, as attention reads it). */
+int stage_kv_import(stage_t* st, int global_block, int slot, int pos0, int n, const uint16_t* k,
+                    const uint16_t* v, hipStream_t stream);
+int stage_kv_export(stage_t* st, int global_block, int slot, int pos0, int n, uint16_t* k, uint16_t* v,
+                    hipStream_t stream);
+
+/* Device-side error counter (rows skipped for out-of-range tokens, slots or positions); reading it
+ * synchronises `stream`.  reset != 0 clears it afterwards. */
+int stage_device_errors(stage_t* st, int reset, uint32_t* count /*host*/, hipStream_t stream);
+
+/* Release the handle (the arena stays the caller's). */
+int stage_destroy(stage_t* st);
+
+const char* stage_status_str(int status);
+/* Text of the last STAGE_E_HIP / validation failure on this handle ("" if none). */
+const char* stage_last_error(const stage_t* st);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -27,9 +27,9 @@ Readings where the pages are silent (each listed in the design notes):
 RMSNorm is x * rsqrt(mean(x^2) + eps) * g (no mean subtraction, eps inside the root);
 RoPE is the rotate-half form over the whole head, angle pos * theta^(-2i/Dh), absolute 0-based
 positions; the residual stream is F32 inside a stage as well as across it; the readout is untied.
-GEMM and attention operands are rounded to bf16 at seven fixed points (R1..R7 below), exactly
-where the GPU path rounds them; everything else is float64 and rounded to float32 where the
-method stores an F32 tensor.
+Precision: weights are bf16 (the seeded inputs), the KV cache stores K (after RoPE) and V as bf16,
+and nothing else is rounded -- every activation, score and sum is float64, and tensors the method
+hands over as F32 (stage output, final hidden, logits, MLP partials) are rounded to float32 once.
 
 Pins: every function here is checked by ``tests/test_oracle_pins.py`` against brute-force loops,
 closed forms and invariants the pages fix (see that file).  Absolute forward values are not
@@ -81,9 +81,14 @@ def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
     return x * r * f64(gain)
 
 
+def linear64(h: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """y = h W^T for W stored [out, in] (the chapter's nn.Linear layout), float64 throughout."""
+    return f64(h) @ f64(bf16_to_f32(w_bits)).T
+
+
 def linear(h: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
-    """y = h W^T for W stored [out, in] (the chapter's nn.Linear layout); f64 sums, f32 result."""
-    return (f64(h) @ f64(bf16_to_f32(w_bits)).T).astype(np.float32)
+    """linear64 rounded once to float32 (an F32 output tensor)."""
+    return linear64(h, w_bits).astype(np.float32)
 
 
 def rope_angles(positions: np.ndarray, head_dim: int, theta: float) -> np.ndarray:
@@ -181,15 +186,10 @@ class Stage:
     """
 
     def __init__(self, dims: Dims, begin: int, end: int, first: bool, last: bool, weights: dict,
-                 max_ctx: int, pure_f32: bool = False):
+                 max_ctx: int):
         self.c, self.begin, self.end, self.first, self.last = dims, begin, end, first, last
         self.w, self.max_ctx = weights, max_ctx
-        self.pure_f32 = pure_f32          # information only: drop the bf16 rounding points
         self.kv = {}                      # slot -> (K, V) float32 [blocks, ctx, Hkv, Dh]
-
-    # rounding points R1..R7 (bf16 operands of GEMMs and attention)
-    def _r(self, x):
-        return np.asarray(x, dtype=np.float32) if self.pure_f32 else round_bf16(x)
 
     def _cache(self, slot: int):
         if slot not in self.kv:
@@ -207,20 +207,19 @@ class Stage:
         c, w = self.c, self.w
         hq, hkv, dh = c.n_q_heads, c.n_kv_heads, c.head_dim
         m_rows = x.shape[0]
-        gain1 = bf16_to_f32(w[("attn_norm", b)])
-        h = self._r(rms_norm(x, gain1, c.rms_eps))                              # R1
-        q = linear(h, w[("wq", b)]).reshape(m_rows, hq, dh)
-        k = linear(h, w[("wk", b)]).reshape(m_rows, hkv, dh)
-        v = linear(h, w[("wv", b)]).reshape(m_rows, hkv, dh)
-        q = self._r(rope(q, positions, c.rope_theta))                          # R2 (q~)
-        k = self._r(rope(k, positions, c.rope_theta))                          # R3 (cached K)
-        v = self._r(v)                                                         # R3 (cached V)
+        h = rms_norm(x, bf16_to_f32(w[("attn_norm", b)]), c.rms_eps)
+        q = linear64(h, w[("wq", b)]).reshape(m_rows, hq, dh)
+        k = linear64(h, w[("wk", b)]).reshape(m_rows, hkv, dh)
+        v = linear64(h, w[("wv", b)]).reshape(m_rows, hkv, dh)
+        q = rope(q, positions, c.rope_theta)
+        k = round_bf16(rope(k, positions, c.rope_theta))                      # bf16 KV cache
+        v = round_bf16(v)
         lb = b - self.begin
         for m in range(m_rows):                                                # write KV first
             kc, vc = self._cache(int(slots[m]))
             kc[lb, positions[m]] = k[m]
             vc[lb, positions[m]] = v[m]
-        attn = np.empty((m_rows, hq * dh), np.float32)
+        attn = np.empty((m_rows, hq * dh), np.float64)
         scale = dh ** -0.5
         for s in np.unique(slots):
             rows = np.nonzero(slots == s)[0]
@@ -230,14 +229,11 @@ class Stage:
             vv = gqa_expand(vc[lb, :n_keys], hq)
             o, _ = attention_partial(q[rows], kk, vv, positions[rows].astype(np.int64),
                                      np.arange(n_keys), scale)
-            attn[rows] = self._r(o.astype(np.float32)).reshape(len(rows), hq * dh)  # R4
-        x1 = (x + linear(attn, w[("wo", b)])).astype(np.float32)
-        gain2 = bf16_to_f32(w[("mlp_norm", b)])
-        h2 = self._r(rms_norm(x1, gain2, c.rms_eps))                           # R5
-        gate = linear(h2, w[("wgate", b)])
-        up = linear(h2, w[("wup", b)])
-        a = self._r(silu_mul(gate, up).astype(np.float32))                     # R6
-        return (x1 + linear(a, w[("wdown", b)])).astype(np.float32)
+            attn[rows] = o.reshape(len(rows), hq * dh)
+        x1 = (x + linear64(attn, w[("wo", b)])).astype(np.float32)
+        h2 = rms_norm(x1, bf16_to_f32(w[("mlp_norm", b)]), c.rms_eps)
+        a = silu_mul(linear64(h2, w[("wgate", b)]), linear64(h2, w[("wup", b)]))
+        return (x1 + linear64(a, w[("wdown", b)])).astype(np.float32)
 
     def forward(self, x: np.ndarray, slots, positions) -> np.ndarray:
         """All blocks of the stage; returns the F32 residual handed to the next stage."""
@@ -258,9 +254,9 @@ class Stage:
         """Last stage only: final RMSNorm (F32 "final hidden") and F32 logits of bf16(h_N)."""
         assert self.last
         g = bf16_to_f32(self.w[("final_norm", -1)])
-        h_n = rms_norm(x, g, self.c.rms_eps).astype(np.float32)
-        logits = linear(self._r(h_n), self.w[("readout", -1)])                 # R7
-        return logits, h_n
+        h_n = rms_norm(x, g, self.c.rms_eps)
+        logits = linear(h_n, self.w[("readout", -1)])
+        return logits, h_n.astype(np.float32)
 
     def kv_bits(self, slot: int, n_pos: int):
         """bf16 bits of the cached K and V of a slot, positions [0, n_pos): [blocks, n, Hkv, Dh]."""
@@ -318,9 +314,9 @@ def generate(stages: list, prompt: np.ndarray, n_new: int, slot: int = 0):
 
 def mlp_full(x: np.ndarray, g_mlp: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
              eps: float):
-    """The whole SwiGLU MLP of F32 rows x: returns (bf16 activation a, F32 f32(W_d a))."""
-    h = round_bf16(rms_norm(x, bf16_to_f32(g_mlp), eps))                      # R5
-    a = round_bf16(silu_mul(linear(h, wg), linear(h, wu)).astype(np.float32))  # R6
+    """The whole SwiGLU MLP of F32 rows x: returns (activation a, f64; F32 output W_d a)."""
+    h = rms_norm(x, bf16_to_f32(g_mlp), eps)
+    a = silu_mul(linear64(h, wg), linear64(h, wu))
     return a, linear(a, wd)
 
 
@@ -330,11 +326,11 @@ def mlp_slices(x, g_mlp, wg, wu, wd, eps: float, n_slices: int):
     ((p0 + p1) + p2) + ... in float32.  Returns (slice activations, partials, f32 sum)."""
     f = wg.shape[0]
     w = f // n_slices
-    h = round_bf16(rms_norm(x, bf16_to_f32(g_mlp), eps))
+    h = rms_norm(x, bf16_to_f32(g_mlp), eps)
     acts, parts = [], []
     for i in range(n_slices):
         lo, hi = i * w, (i + 1) * w
-        a_i = round_bf16(silu_mul(linear(h, wg[lo:hi]), linear(h, wu[lo:hi])).astype(np.float32))
+        a_i = silu_mul(linear64(h, wg[lo:hi]), linear64(h, wu[lo:hi]))
         acts.append(a_i)
         parts.append(linear(a_i, np.ascontiguousarray(wd[:, lo:hi])))
     total = parts[0].copy()

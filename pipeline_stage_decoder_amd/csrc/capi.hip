@@ -1,0 +1,672 @@
+// Host runtime of one pipeline stage: byte plan, arena layout, weight layouts, launch sequence.
+//
+// One stage = one arena ("RFC: pipeline placement ...", What I found: each stage owns its weights,
+// KV state, heap and workspace; there is no unified allocator).  The arena is carved as
+//   [weights | KV cache | RoPE table | workspace]
+// and every call enqueues kernels on the caller's stream.  The per-block sequence follows
+// PipelineStage.forward of "41. Many GPUs" (Pipeline parallelism):
+//   norm -> QKV (+RoPE, KV write) -> attention -> O-proj (+residual) -> norm -> gate/up (+SwiGLU)
+//   -> down (+residual)
+// with rows <= 4 on the GEMV kernels (norm fused in their prologue) and larger row counts on the
+// MFMA GEMM (norm as a row pass that writes the bf16 operand).  The kernel schedule depends only
+// on the row count and the shapes, never on the block range, so a model split into stages runs
+// exactly the kernels of the unsplit model on every block.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "stage.h"
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+constexpr int kMaxCounters = 1 << 16;
+
+uint64_t align_up(uint64_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+struct BlockW {
+  float* attn_norm;
+  float* mlp_norm;
+  uint16_t* wqkv;   // [(Hq + 2 Hkv) Dh, d], RoPE-pair row order within q and k heads
+  uint16_t* wo;     // [d, Hq Dh]
+  uint16_t* wgu;    // [2F, d], gate/up interleaved by 16 rows
+  uint16_t* wd;     // [d, F]
+};
+
+// Byte layout of the arena, computed identically by stage_plan and stage_create.
+struct Layout {
+  // offsets (bytes from the arena base)
+  std::vector<uint64_t> attn_norm, mlp_norm, wqkv, wo, wgu, wd;
+  uint64_t embed = 0, readout = 0, final_norm = 0;
+  uint64_t kcache = 0, vcache = 0, kv_block_elems = 0;
+  uint64_t rope = 0;
+  uint64_t xn = 0, q = 0, attn = 0, act = 0, part_o = 0, part_lse = 0, gemm_part = 0, counters = 0,
+           err = 0, staging = 0;
+  int ctx_cap = 0, qkv_n = 0, nsplit_max_rows = 0;
+  stage_plan_t plan{};
+};
+
+int validate(const stage_model_cfg* m, const stage_stage_cfg* s) {
+  if (!m || !s) return STAGE_E_INVALID;
+  if (m->d_model <= 0 || m->n_q_heads <= 0 || m->n_kv_heads <= 0 || m->head_dim <= 0 || m->d_ffn <= 0 ||
+      m->n_blocks_total < 0 || !(m->rms_eps > 0.0f) || !(m->rope_theta > 0.0f))
+    return STAGE_E_INVALID;
+  if (s->block_begin < 0 || s->block_end < s->block_begin || s->block_end > m->n_blocks_total)
+    return STAGE_E_INVALID;
+  if (s->max_slots <= 0 || s->max_ctx <= 0 || s->max_tokens <= 0) return STAGE_E_INVALID;
+  if ((s->flags & ~(STAGE_FIRST | STAGE_LAST)) != 0) return STAGE_E_INVALID;
+  if ((s->flags & (STAGE_FIRST | STAGE_LAST)) && m->vocab <= 0) return STAGE_E_INVALID;
+  // what the kernels cover (refused before anything is allocated)
+  if (m->head_dim != 64 && m->head_dim != 128) return STAGE_E_UNSUPPORTED;
+  if (m->n_q_heads % m->n_kv_heads != 0 || m->n_q_heads / m->n_kv_heads > 16) return STAGE_E_UNSUPPORTED;
+  if (m->d_model % 64 != 0 || m->d_ffn % 16 != 0) return STAGE_E_UNSUPPORTED;
+  if (s->max_ctx > (1 << 24) || s->max_tokens > (1 << 20) || s->max_slots > (1 << 20)) return STAGE_E_UNSUPPORTED;
+  return STAGE_OK;
+}
+
+int nsplit_for(int B, int ctx_cap) {
+  const int ch = attn_decode_chunk(B);
+  return (ctx_cap + ch - 1) / ch;
+}
+
+Layout make_layout(const stage_model_cfg& m, const stage_stage_cfg& s) {
+  Layout L;
+  const uint64_t d = m.d_model, dh = m.head_dim, hq = m.n_q_heads, hkv = m.n_kv_heads, F = m.d_ffn,
+                 V = m.vocab > 0 ? m.vocab : 0;
+  const int nb = s.block_end - s.block_begin;
+  L.qkv_n = (int)((hq + 2 * hkv) * dh);
+  L.ctx_cap = (int)((s.max_ctx + 63) / 64 * 64);
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  // weights
+  if (s.flags & STAGE_FIRST) L.embed = take(V * d * 2);
+  for (int b = 0; b < nb; ++b) {
+    L.attn_norm.push_back(take(d * 4));
+    L.mlp_norm.push_back(take(d * 4));
+    L.wqkv.push_back(take((uint64_t)L.qkv_n * d * 2));
+    L.wo.push_back(take(d * hq * dh * 2));
+    L.wgu.push_back(take(2 * F * d * 2));
+    L.wd.push_back(take(d * F * 2));
+  }
+  if (s.flags & STAGE_LAST) {
+    L.final_norm = take(d * 4);
+    L.readout = take(V * d * 2);
+  }
+  L.plan.weight_bytes = off;
+  // KV cache
+  const uint64_t kv_start = off;
+  L.kv_block_elems = (uint64_t)s.max_slots * hkv * L.ctx_cap * dh;
+  L.kcache = take(L.kv_block_elems * nb * 2);
+  L.vcache = take(L.kv_block_elems * nb * 2);
+  L.plan.kv_bytes = off - kv_start;
+  // tables
+  const uint64_t tab_start = off;
+  L.rope = take((uint64_t)L.ctx_cap * (dh / 2) * 16);
+  L.plan.table_bytes = off - tab_start;
+  // workspace
+  const uint64_t ws_start = off;
+  const uint64_t M = s.max_tokens;
+  // activation pair buffers (bf16 hi plane, then lo plane)
+  L.xn = take(3 * M * d * 2);
+  L.q = take(2 * M * hq * dh * 2);
+  L.attn = take(2 * M * hq * dh * 2);
+  L.act = take(2 * M * F * 2);
+  uint64_t part_rows = 0;
+  for (int B = 1; B <= s.max_tokens; ++B) {
+    const uint64_t r = (uint64_t)B * nsplit_for(B, L.ctx_cap);
+    if (r > part_rows) part_rows = r;
+  }
+  L.part_o = take(part_rows * hq * dh * 4);
+  L.part_lse = take(part_rows * hq * 4);
+  uint64_t gpart = 0;
+  const int shapes[5][2] = {{L.qkv_n, (int)d}, {(int)d, (int)(hq * dh)}, {(int)(2 * F), (int)d},
+                            {(int)d, (int)F}, {(int)V, (int)d}};
+  for (int Mr = 1; Mr <= s.max_tokens; ++Mr)
+    for (int k = 0; k < 5; ++k) {
+      if (shapes[k][0] <= 0) continue;
+      const GemmPlan p = gemm_plan(Mr, shapes[k][0], shapes[k][1]);
+      if (p.splitk > 1) {
+        const uint64_t need = (uint64_t)p.splitk * Mr * shapes[k][0] * 4;
+        if (need > gpart) gpart = need;
+      }
+    }
+  L.gemm_part = take(gpart);
+  L.counters = take((uint64_t)kMaxCounters * 4);
+  L.err = take(4);
+  L.staging = take(d * 2);
+  L.plan.workspace_bytes = off - ws_start;
+  L.plan.total_bytes = off;
+  return L;
+}
+
+}  // namespace
+
+struct stage {
+  stage_model_cfg m;
+  stage_stage_cfg s;
+  int device;
+  uint8_t* arena;
+  uint64_t arena_bytes;
+  Layout L;
+  int nb;
+  std::vector<BlockW> blocks;
+  uint16_t* embed;
+  uint16_t* readout;
+  float* final_norm;
+  uint16_t *kcache, *vcache;
+  double2* rope;
+  uint16_t *xn, *q, *attn, *act;
+  float *part_o, *part_lse, *gemm_part;
+  uint32_t *counters, *err;
+  uint16_t* staging;
+  std::string last_error;
+};
+
+namespace {
+
+template <typename T>
+T* at(stage* st, uint64_t off) {
+  return reinterpret_cast<T*>(st->arena + off);
+}
+
+int hip_fail(stage* st, hipError_t e, const char* what) {
+  char buf[256];
+  snprintf(buf, sizeof buf, "%s: %s", what, hipGetErrorString(e));
+  if (st) st->last_error = buf;
+  return STAGE_E_HIP;
+}
+
+int fail(stage* st, int code, const char* what) {
+  if (st) st->last_error = what;
+  return code;
+}
+
+#define HIP_TRY(st, expr)                                   \
+  do {                                                      \
+    hipError_t _e = (expr);                                 \
+    if (_e != hipSuccess) return hip_fail((st), _e, #expr); \
+  } while (0)
+
+EpiArgs epi_base(stage* st, int kind) {
+  EpiArgs e{};
+  e.kind = kind;
+  e.hq = st->m.n_q_heads;
+  e.hkv = st->m.n_kv_heads;
+  e.dh = st->m.head_dim;
+  e.ctx_cap = st->L.ctx_cap;
+  e.max_slots = st->s.max_slots;
+  e.rope = st->rope;
+  e.err = st->err;
+  return e;
+}
+
+// plane strides of the workspace pair buffers
+size_t ps_xn(const stage* st) { return (size_t)st->s.max_tokens * st->m.d_model; }
+size_t ps_q(const stage* st) { return (size_t)st->s.max_tokens * st->m.n_q_heads * st->m.head_dim; }
+size_t ps_act(const stage* st) { return (size_t)st->s.max_tokens * st->m.d_ffn; }
+
+// One projection y = x W^T with its epilogue.  x_f32 + gain: the input is RMS-normalised first
+// (fused in the GEMV prologue, or a row pass into the bf16 workspace before the GEMM).
+// planes: bf16 planes of the GEMM operand (2, or 3 for the QKV projection whose K/V outputs are
+// rounded to the bf16 cache).
+hipError_t project(stage* st, int rows, const float* x_f32, const float* gain, const uint16_t* x_pair,
+                   size_t x_ps, const uint16_t* w, int N, int K, const EpiArgs& e, hipStream_t s,
+                   int planes = 2) {
+  if (gemv_fits(rows, K)) {
+    GemvArgs a{};
+    a.x = x_f32 ? x_f32 : nullptr;
+    a.gain = gain;
+    a.eps = st->m.rms_eps;
+    a.xb = x_pair;
+    a.xb_ps = x_ps;
+    a.w = w;
+    a.N = N;
+    a.K = K;
+    a.B = rows;
+    a.e = e;
+    return launch_gemv(a, s);
+  }
+  const uint16_t* A = x_pair;
+  size_t a_ps = x_ps;
+  if (x_f32) {
+    NormArgs n{x_f32, gain, st->m.rms_eps, rows, K, nullptr, st->xn, ps_xn(st)};
+    hipError_t err = launch_rmsnorm(n, s);
+    if (err != hipSuccess) return err;
+    A = st->xn;
+    a_ps = ps_xn(st);
+  }
+  GemmArgs g{};
+  g.a = A;
+  g.a_ps = a_ps;
+  g.planes = x_f32 ? planes : 2;
+  g.w = w;
+  g.M = rows;
+  g.N = N;
+  g.K = K;
+  const GemmPlan p = gemm_plan(rows, N, K);
+  g.splitk = p.splitk;
+  g.part = st->gemm_part;
+  g.counters = st->counters;
+  g.e = e;
+  return launch_gemm(g, p, s);
+}
+
+// The MLP half of a block: out = resid + W_down(silu(W_gate h) * W_up h), h = norm(x).
+hipError_t mlp_half(stage* st, int lb, int rows, const float* x, const float* resid, float* out,
+                    hipStream_t s) {
+  const BlockW& bw = st->blocks[lb];
+  const int d = st->m.d_model, F = st->m.d_ffn;
+  EpiArgs e1 = epi_base(st, EPI_SWIGLU);
+  e1.act = st->act;
+  e1.act_ps = ps_act(st);
+  e1.ldo = F;
+  hipError_t err = project(st, rows, x, bw.mlp_norm, nullptr, 0, bw.wgu, 2 * F, d, e1, s);
+  if (err != hipSuccess) return err;
+  EpiArgs e2 = epi_base(st, resid ? EPI_RESID : EPI_F32);
+  e2.out = out;
+  e2.resid = resid;
+  e2.ldo = d;
+  return project(st, rows, nullptr, nullptr, st->act, ps_act(st), bw.wd, d, F, e2, s);
+}
+
+// One block over `rows` rows.  Prefill: rp = (slot, pos0), attention over keys [0, pos];
+// decode: rp = per-row slots/positions, split-KV attention.
+int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, const RowPos& rp, bool decode,
+              hipStream_t s) {
+  const BlockW& bw = st->blocks[lb];
+  const int d = st->m.d_model, hq = st->m.n_q_heads, hkv = st->m.n_kv_heads, dh = st->m.head_dim;
+  uint16_t* kc = st->kcache + (uint64_t)lb * st->L.kv_block_elems;
+  uint16_t* vc = st->vcache + (uint64_t)lb * st->L.kv_block_elems;
+  EpiArgs e = epi_base(st, EPI_QKV);
+  e.q = st->q;
+  e.q_ps = ps_q(st);
+  e.kc = kc;
+  e.vc = vc;
+  e.rp = rp;
+  HIP_TRY(st, project(st, rows, x_in, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, 3));
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  if (decode) {
+    AttnDecodeArgs a{};
+    a.q = st->q;
+    a.q_ps = ps_q(st);
+    a.out_ps = ps_q(st);
+    a.kc = kc;
+    a.vc = vc;
+    a.slots = rp.slots;
+    a.pos = rp.pos;
+    a.B = rows;
+    a.hq = hq;
+    a.hkv = hkv;
+    a.dh = dh;
+    a.ctx_cap = st->L.ctx_cap;
+    a.max_slots = st->s.max_slots;
+    a.chunk = attn_decode_chunk(rows);
+    a.nsplit = nsplit_for(rows, st->L.ctx_cap);
+    a.scale_log2 = scale_log2;
+    a.part_o = st->part_o;
+    a.part_lse = st->part_lse;
+    a.out = st->attn;
+    a.err = st->err;
+    HIP_TRY(st, launch_attn_decode(a, s));
+  } else {
+    AttnPrefillArgs a{};
+    a.q = st->q;
+    a.q_ps = ps_q(st);
+    a.out_ps = ps_q(st);
+    a.kc = kc;
+    a.vc = vc;
+    a.slot = rp.slot;
+    a.pos0 = rp.pos0;
+    a.T = rows;
+    a.hq = hq;
+    a.hkv = hkv;
+    a.dh = dh;
+    a.ctx_cap = st->L.ctx_cap;
+    a.scale_log2 = scale_log2;
+    a.out = st->attn;
+    HIP_TRY(st, launch_attn_prefill(a, s));
+  }
+  EpiArgs eo = epi_base(st, EPI_RESID);
+  eo.out = x_out;
+  eo.resid = x_in;
+  eo.ldo = d;
+  HIP_TRY(st, project(st, rows, nullptr, nullptr, st->attn, ps_q(st), bw.wo, d, hq * dh, eo, s));
+  HIP_TRY(st, mlp_half(st, lb, rows, x_out, x_out, x_out, s));
+  return STAGE_OK;
+}
+
+int run_blocks(stage* st, int rows, const float* hin, float* hout, const RowPos& rp, bool decode,
+               hipStream_t s) {
+  if (st->nb == 0) {
+    if (hin != hout) HIP_TRY(st, hipMemcpyAsync(hout, hin, (size_t)rows * st->m.d_model * 4,
+                                                 hipMemcpyDeviceToDevice, s));
+    return STAGE_OK;
+  }
+  for (int lb = 0; lb < st->nb; ++lb) {
+    const int rc = run_block(st, lb, rows, lb == 0 ? hin : hout, hout, rp, decode, s);
+    if (rc != STAGE_OK) return rc;
+  }
+  return STAGE_OK;
+}
+
+bool is_device_ptr(const void* p) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice;
+}
+
+uint64_t role_elems(const stage* st, int role) {
+  const uint64_t d = st->m.d_model, dh = st->m.head_dim, hq = st->m.n_q_heads, hkv = st->m.n_kv_heads,
+                 F = st->m.d_ffn, V = st->m.vocab;
+  switch (role) {
+    case STAGE_ROLE_EMBED: case STAGE_ROLE_READOUT: return V * d;
+    case STAGE_ROLE_ATTN_NORM: case STAGE_ROLE_MLP_NORM: case STAGE_ROLE_FINAL_NORM: return d;
+    case STAGE_ROLE_WQ: return hq * dh * d;
+    case STAGE_ROLE_WK: case STAGE_ROLE_WV: return hkv * dh * d;
+    case STAGE_ROLE_WO: return d * hq * dh;
+    case STAGE_ROLE_WGATE: case STAGE_ROLE_WUP: case STAGE_ROLE_WDOWN: return F * d;
+    default: return 0;
+  }
+}
+
+// Copy `rows` rows of q or k weights of one head group into the RoPE-pair row order.
+hipError_t copy_rope_rows(uint16_t* dst_rows, const uint16_t* src_rows, int heads, int dh, int d,
+                          hipStream_t s) {
+  const size_t row_b = (size_t)d * 2;
+  for (int h = 0; h < heads; ++h) {
+    const uint16_t* src = src_rows + (size_t)h * dh * d;
+    uint16_t* dst = dst_rows + (size_t)h * dh * d;
+    for (int half = 0; half < 2; ++half) {
+      // source rows half*Dh/2 + [16b, 16b+16) -> stored rows 32b + 16*half + [0, 16)
+      hipError_t e = hipMemcpy2DAsync(dst + (size_t)16 * half * d, 32 * row_b,
+                                      src + (size_t)half * (dh / 2) * d, 16 * row_b, 16 * row_b, dh / 32,
+                                      hipMemcpyDefault, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* stage_status_str(int status) {
+  switch (status) {
+    case STAGE_OK: return "ok";
+    case STAGE_E_INVALID: return "invalid argument";
+    case STAGE_E_UNSUPPORTED: return "unsupported configuration";
+    case STAGE_E_DOES_NOT_FIT: return "does not fit in the arena";
+    case STAGE_E_ROLE: return "role not owned by this stage";
+    case STAGE_E_RANGE: return "slot, position or size out of range";
+    case STAGE_E_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* stage_last_error(const stage_t* st) { return st ? st->last_error.c_str() : ""; }
+
+int stage_plan(const stage_model_cfg* model, const stage_stage_cfg* stg, stage_plan_t* out) {
+  const int rc = validate(model, stg);
+  if (rc != STAGE_OK) return rc;
+  if (!out) return STAGE_E_INVALID;
+  *out = make_layout(*model, *stg).plan;
+  return STAGE_OK;
+}
+
+int stage_create(const stage_model_cfg* model, const stage_stage_cfg* stg, void* arena, uint64_t arena_bytes,
+                 int device, stage_t** out) {
+  int rc = validate(model, stg);
+  if (rc != STAGE_OK) return rc;
+  if (!arena || !out) return STAGE_E_INVALID;
+  Layout L = make_layout(*model, *stg);
+  if (arena_bytes < L.plan.total_bytes) return STAGE_E_DOES_NOT_FIT;
+  if (reinterpret_cast<uintptr_t>(arena) % kAlign != 0) return STAGE_E_INVALID;
+  stage* st = new (std::nothrow) stage();
+  if (!st) return STAGE_E_INVALID;
+  st->m = *model;
+  st->s = *stg;
+  st->device = device;
+  st->arena = static_cast<uint8_t*>(arena);
+  st->arena_bytes = arena_bytes;
+  st->L = L;
+  st->nb = stg->block_end - stg->block_begin;
+  for (int b = 0; b < st->nb; ++b)
+    st->blocks.push_back(BlockW{at<float>(st, L.attn_norm[b]), at<float>(st, L.mlp_norm[b]),
+                                at<uint16_t>(st, L.wqkv[b]), at<uint16_t>(st, L.wo[b]),
+                                at<uint16_t>(st, L.wgu[b]), at<uint16_t>(st, L.wd[b])});
+  st->embed = (stg->flags & STAGE_FIRST) ? at<uint16_t>(st, L.embed) : nullptr;
+  st->readout = (stg->flags & STAGE_LAST) ? at<uint16_t>(st, L.readout) : nullptr;
+  st->final_norm = (stg->flags & STAGE_LAST) ? at<float>(st, L.final_norm) : nullptr;
+  st->kcache = at<uint16_t>(st, L.kcache);
+  st->vcache = at<uint16_t>(st, L.vcache);
+  st->rope = at<double2>(st, L.rope);
+  st->xn = at<uint16_t>(st, L.xn);
+  st->q = at<uint16_t>(st, L.q);
+  st->attn = at<uint16_t>(st, L.attn);
+  st->act = at<uint16_t>(st, L.act);
+  st->part_o = at<float>(st, L.part_o);
+  st->part_lse = at<float>(st, L.part_lse);
+  st->gemm_part = at<float>(st, L.gemm_part);
+  st->counters = at<uint32_t>(st, L.counters);
+  st->err = at<uint32_t>(st, L.err);
+  st->staging = at<uint16_t>(st, L.staging);
+
+  hipError_t e = hipSetDevice(device);
+  if (e == hipSuccess) e = hipMemset(st->arena + L.kcache, 0, L.plan.kv_bytes);
+  if (e == hipSuccess) e = hipMemset(st->counters, 0, (size_t)kMaxCounters * 4);
+  if (e == hipSuccess) e = hipMemset(st->err, 0, 4);
+  if (e == hipSuccess) {
+    // RoPE table in f64: angle(pos, i) = pos * theta^(-2i/Dh)
+    const int half = model->head_dim / 2;
+    std::vector<double2> tab((size_t)L.ctx_cap * half);
+    for (int p = 0; p < L.ctx_cap; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double inv = std::pow((double)model->rope_theta, -2.0 * i / model->head_dim);
+        const double a = (double)p * inv;
+        tab[(size_t)p * half + i] = make_double2(std::cos(a), std::sin(a));
+      }
+    e = hipMemcpy(st->rope, tab.data(), tab.size() * sizeof(double2), hipMemcpyHostToDevice);
+  }
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    delete st;
+    return STAGE_E_HIP;
+  }
+  *out = st;
+  return STAGE_OK;
+}
+
+int stage_destroy(stage_t* st) {
+  delete st;
+  return STAGE_OK;
+}
+
+int stage_load_weight(stage_t* st, int role, int global_block, const uint16_t* src, uint64_t n_elems,
+                      hipStream_t s) {
+  if (!st || !src) return fail(st, STAGE_E_INVALID, "null handle or source");
+  const bool per_block = !(role == STAGE_ROLE_EMBED || role == STAGE_ROLE_FINAL_NORM || role == STAGE_ROLE_READOUT);
+  if (role < 0 || role > STAGE_ROLE_READOUT) return fail(st, STAGE_E_ROLE, "unknown role");
+  if (per_block && (global_block < st->s.block_begin || global_block >= st->s.block_end))
+    return fail(st, STAGE_E_ROLE, "block outside the stage's range");
+  if (!per_block && global_block != -1) return fail(st, STAGE_E_ROLE, "end tensors take global_block = -1");
+  if (role == STAGE_ROLE_EMBED && !(st->s.flags & STAGE_FIRST)) return fail(st, STAGE_E_ROLE, "embed on a non-first stage");
+  if ((role == STAGE_ROLE_READOUT || role == STAGE_ROLE_FINAL_NORM) && !(st->s.flags & STAGE_LAST))
+    return fail(st, STAGE_E_ROLE, "readout on a non-last stage");
+  if (n_elems != role_elems(st, role)) return fail(st, STAGE_E_RANGE, "n_elems does not match the role");
+  HIP_TRY(st, hipSetDevice(st->device));
+  const int d = st->m.d_model, dh = st->m.head_dim, hq = st->m.n_q_heads, hkv = st->m.n_kv_heads, F = st->m.d_ffn;
+  const BlockW* bw = per_block ? &st->blocks[global_block - st->s.block_begin] : nullptr;
+  const size_t row_b = (size_t)d * 2;
+  switch (role) {
+    case STAGE_ROLE_EMBED:
+      HIP_TRY(st, hipMemcpyAsync(st->embed, src, n_elems * 2, hipMemcpyDefault, s));
+      break;
+    case STAGE_ROLE_READOUT:
+      HIP_TRY(st, hipMemcpyAsync(st->readout, src, n_elems * 2, hipMemcpyDefault, s));
+      break;
+    case STAGE_ROLE_ATTN_NORM: case STAGE_ROLE_MLP_NORM: case STAGE_ROLE_FINAL_NORM: {
+      float* dst = role == STAGE_ROLE_ATTN_NORM ? bw->attn_norm
+                   : role == STAGE_ROLE_MLP_NORM ? bw->mlp_norm : st->final_norm;
+      HIP_TRY(st, hipMemcpyAsync(st->staging, src, n_elems * 2, hipMemcpyDefault, s));
+      HIP_TRY(st, launch_bf16_to_f32(st->staging, dst, d, s));
+      break;
+    }
+    case STAGE_ROLE_WQ:
+      HIP_TRY(st, copy_rope_rows(bw->wqkv, src, hq, dh, d, s));
+      break;
+    case STAGE_ROLE_WK:
+      HIP_TRY(st, copy_rope_rows(bw->wqkv + (size_t)hq * dh * d, src, hkv, dh, d, s));
+      break;
+    case STAGE_ROLE_WV:
+      HIP_TRY(st, hipMemcpyAsync(bw->wqkv + (size_t)(hq + hkv) * dh * d, src, n_elems * 2, hipMemcpyDefault, s));
+      break;
+    case STAGE_ROLE_WO:
+      HIP_TRY(st, hipMemcpyAsync(bw->wo, src, n_elems * 2, hipMemcpyDefault, s));
+      break;
+    case STAGE_ROLE_WGATE: case STAGE_ROLE_WUP:
+      // source row f -> stored row 32*(f/16) + f%16 (+16 for up)
+      HIP_TRY(st, hipMemcpy2DAsync(bw->wgu + (role == STAGE_ROLE_WUP ? (size_t)16 * d : 0), 32 * row_b, src,
+                                   16 * row_b, 16 * row_b, F / 16, hipMemcpyDefault, s));
+      break;
+    case STAGE_ROLE_WDOWN:
+      HIP_TRY(st, hipMemcpyAsync(bw->wd, src, n_elems * 2, hipMemcpyDefault, s));
+      break;
+  }
+  if (!is_device_ptr(src)) HIP_TRY(st, hipStreamSynchronize(s));
+  return STAGE_OK;
+}
+
+int stage_embed(stage_t* st, int n, const int32_t* tokens, float* hidden_out, hipStream_t s) {
+  if (!st || !tokens || !hidden_out || n <= 0) return fail(st, STAGE_E_INVALID, "bad embed arguments");
+  if (!(st->s.flags & STAGE_FIRST)) return fail(st, STAGE_E_ROLE, "embed on a non-first stage");
+  if (n > st->s.max_tokens) return fail(st, STAGE_E_INVALID, "n > max_tokens");
+  HIP_TRY(st, hipSetDevice(st->device));
+  HIP_TRY(st, launch_embed(st->embed, st->m.vocab, st->m.d_model, tokens, n, hidden_out, st->err, s));
+  return STAGE_OK;
+}
+
+int stage_prefill(stage_t* st, int slot, int pos0, int T, const float* hin, float* hout, hipStream_t s) {
+  if (!st || !hin || !hout || T <= 0) return fail(st, STAGE_E_INVALID, "bad prefill arguments");
+  if (T > st->s.max_tokens) return fail(st, STAGE_E_INVALID, "T > max_tokens");
+  if (slot < 0 || slot >= st->s.max_slots || pos0 < 0 || (int64_t)pos0 + T > st->s.max_ctx)
+    return fail(st, STAGE_E_RANGE, "slot or positions out of range");
+  HIP_TRY(st, hipSetDevice(st->device));
+  RowPos rp{nullptr, nullptr, slot, pos0};
+  return run_blocks(st, T, hin, hout, rp, false, s);
+}
+
+int stage_decode(stage_t* st, int B, const int32_t* slots, const int32_t* positions, const float* hin,
+                 float* hout, hipStream_t s) {
+  if (!st || !slots || !positions || !hin || !hout || B <= 0) return fail(st, STAGE_E_INVALID, "bad decode arguments");
+  if (B > st->s.max_tokens) return fail(st, STAGE_E_INVALID, "B > max_tokens");
+  HIP_TRY(st, hipSetDevice(st->device));
+  RowPos rp{slots, positions, 0, 0};
+  return run_blocks(st, B, hin, hout, rp, true, s);
+}
+
+int stage_readout(stage_t* st, int n, const float* hin, float* logits, float* normed, hipStream_t s) {
+  if (!st || !hin || !logits || n <= 0) return fail(st, STAGE_E_INVALID, "bad readout arguments");
+  if (!(st->s.flags & STAGE_LAST)) return fail(st, STAGE_E_ROLE, "readout on a non-last stage");
+  if (n > st->s.max_tokens) return fail(st, STAGE_E_INVALID, "n > max_tokens");
+  HIP_TRY(st, hipSetDevice(st->device));
+  const int d = st->m.d_model;
+  NormArgs na{hin, st->final_norm, st->m.rms_eps, n, d, normed, st->xn, ps_xn(st)};
+  HIP_TRY(st, launch_rmsnorm(na, s));
+  EpiArgs e = epi_base(st, EPI_F32);
+  e.out = logits;
+  e.ldo = st->m.vocab;
+  HIP_TRY(st, project(st, n, nullptr, nullptr, st->xn, ps_xn(st), st->readout, st->m.vocab, d, e, s));
+  return STAGE_OK;
+}
+
+int stage_mlp(stage_t* st, int global_block, int n, const float* hin, float* out, int accumulate, hipStream_t s) {
+  if (!st || !hin || !out || n <= 0) return fail(st, STAGE_E_INVALID, "bad mlp arguments");
+  if (global_block < st->s.block_begin || global_block >= st->s.block_end)
+    return fail(st, STAGE_E_ROLE, "block outside the stage's range");
+  if (n > st->s.max_tokens) return fail(st, STAGE_E_INVALID, "n > max_tokens");
+  HIP_TRY(st, hipSetDevice(st->device));
+  HIP_TRY(st, mlp_half(st, global_block - st->s.block_begin, n, hin, accumulate ? out : nullptr, out, s));
+  return STAGE_OK;
+}
+
+int stage_kv_copy(stage_t* st, int src_slot, int dst_slot, int n_pos, hipStream_t s) {
+  if (!st || n_pos < 0) return fail(st, STAGE_E_INVALID, "bad kv_copy arguments");
+  if (src_slot < 0 || src_slot >= st->s.max_slots || dst_slot < 0 || dst_slot >= st->s.max_slots ||
+      n_pos > st->s.max_ctx)
+    return fail(st, STAGE_E_RANGE, "slot or positions out of range");
+  if (n_pos == 0 || src_slot == dst_slot) return STAGE_OK;
+  HIP_TRY(st, hipSetDevice(st->device));
+  const int hkv = st->m.n_kv_heads, dh = st->m.head_dim, cap = st->L.ctx_cap;
+  const size_t slot_elems = (size_t)hkv * cap * dh;
+  const size_t vgroups = (size_t)(n_pos + 7) / 8;
+  for (int lb = 0; lb < st->nb; ++lb) {
+    uint16_t* kc = st->kcache + (uint64_t)lb * st->L.kv_block_elems;
+    uint16_t* vc = st->vcache + (uint64_t)lb * st->L.kv_block_elems;
+    // per KV head: K rows [0, n_pos) and the V groups covering them are contiguous
+    HIP_TRY(st, hipMemcpy2DAsync(kc + dst_slot * slot_elems, (size_t)cap * dh * 2, kc + src_slot * slot_elems,
+                                 (size_t)cap * dh * 2, (size_t)n_pos * dh * 2, hkv, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(st, hipMemcpy2DAsync(vc + dst_slot * slot_elems, (size_t)cap * dh * 2, vc + src_slot * slot_elems,
+                                 (size_t)cap * dh * 2, vgroups * dh * 8 * 2, hkv, hipMemcpyDeviceToDevice, s));
+  }
+  return STAGE_OK;
+}
+
+static int kv_io_check(stage_t* st, int global_block, int slot, int pos0, int n, const void* k, const void* v) {
+  if (!st || !k || !v || n <= 0) return fail(st, STAGE_E_INVALID, "bad kv arguments");
+  if (global_block < st->s.block_begin || global_block >= st->s.block_end)
+    return fail(st, STAGE_E_ROLE, "block outside the stage's range");
+  if (slot < 0 || slot >= st->s.max_slots || pos0 < 0 || (int64_t)pos0 + n > st->s.max_ctx)
+    return fail(st, STAGE_E_RANGE, "slot or positions out of range");
+  return STAGE_OK;
+}
+
+int stage_kv_import(stage_t* st, int global_block, int slot, int pos0, int n, const uint16_t* k,
+                    const uint16_t* v, hipStream_t s) {
+  const int rc = kv_io_check(st, global_block, slot, pos0, n, k, v);
+  if (rc != STAGE_OK) return rc;
+  HIP_TRY(st, hipSetDevice(st->device));
+  const int lb = global_block - st->s.block_begin;
+  HIP_TRY(st, launch_kv_import(st->kcache + (uint64_t)lb * st->L.kv_block_elems,
+                               st->vcache + (uint64_t)lb * st->L.kv_block_elems, st->m.n_kv_heads,
+                               st->m.head_dim, st->L.ctx_cap, slot, pos0, n, k, v, s));
+  return STAGE_OK;
+}
+
+int stage_kv_export(stage_t* st, int global_block, int slot, int pos0, int n, uint16_t* k, uint16_t* v,
+                    hipStream_t s) {
+  const int rc = kv_io_check(st, global_block, slot, pos0, n, k, v);
+  if (rc != STAGE_OK) return rc;
+  HIP_TRY(st, hipSetDevice(st->device));
+  const int lb = global_block - st->s.block_begin;
+  HIP_TRY(st, launch_kv_export(st->kcache + (uint64_t)lb * st->L.kv_block_elems,
+                               st->vcache + (uint64_t)lb * st->L.kv_block_elems, st->m.n_kv_heads,
+                               st->m.head_dim, st->L.ctx_cap, slot, pos0, n, k, v, s));
+  return STAGE_OK;
+}
+
+int stage_device_errors(stage_t* st, int reset, uint32_t* count, hipStream_t s) {
+  if (!st || !count) return fail(st, STAGE_E_INVALID, "bad arguments");
+  HIP_TRY(st, hipSetDevice(st->device));
+  HIP_TRY(st, hipMemcpyAsync(count, st->err, 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(st, hipStreamSynchronize(s));
+  if (reset) {
+    HIP_TRY(st, hipMemsetAsync(st->err, 0, 4, s));
+    HIP_TRY(st, hipStreamSynchronize(s));
+  }
+  return STAGE_OK;
+}
+
+}  // extern "C"

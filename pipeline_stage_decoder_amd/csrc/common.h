@@ -1,0 +1,170 @@
+// Shared device helpers and launch-argument structs of the stage kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#define PSD_DEV __device__ __forceinline__
+
+// bf16 <-> f32 on raw bits.  f32 -> bf16 rounds to nearest, ties to even; inputs are finite.
+PSD_DEV float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+PSD_DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+PSD_DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+PSD_DEV uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+PSD_DEV uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+PSD_DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+PSD_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+PSD_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// 16x16x32 bf16 MFMA, f32 accumulate.  Lane l holds A[row l%16][k (l/16)*8 .. +8],
+// B[k (l/16)*8 .. +8][col l%16]; C: lane l holds C[rows (l/16)*4 .. +4][col l%16].
+PSD_DEV f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Activations are carried as a pair of bf16 planes, hi = bf16(x) and lo = bf16(x - hi), so the
+// effective operand hi + lo keeps ~16 significant bits and every MFMA product with a bf16 weight
+// is taken twice (hi and lo).  A "pair buffer" is one pointer p with a plane stride ps: hi at
+// p[i], lo at p[ps + i].
+PSD_DEV void split2(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
+PSD_DEV float pair_value(uint32_t hi, uint32_t lo) { return bf2f(hi) + bf2f(lo); }
+// Three planes (hi, mid, lo) carry ~24 significant bits: used for the operand of the projection
+// whose outputs are rounded again (K and V go to the bf16 cache), so that rounding sees f32-grade
+// values.  The first two planes equal the pair split.
+PSD_DEV void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = f2bf(x);
+  const float r = x - bf2f(hi);
+  mid = f2bf(r);
+  lo = f2bf(r - bf2f(mid));
+}
+
+// Split an f32 x8 vector into bf16 hi + bf16 lo (x ~= hi + lo to ~2^-16 relative).
+PSD_DEV void split_hi_lo(const float* x, uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a = f2bf(x[2 * i]), b = f2bf(x[2 * i + 1]);
+    h[i] = a | (b << 16);
+    float ra = x[2 * i] - bf2f(a), rb = x[2 * i + 1] - bf2f(b);
+    l[i] = pack_bf2(ra, rb);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Epilogue kinds shared by the decode GEMV and the MFMA GEMM.
+// ------------------------------------------------------------------------------------------------
+enum EpiKind {
+  EPI_F32 = 0,      // out[m, n] = acc                          (readout logits, MLP partial)
+  EPI_RESID = 1,    // out[m, n] = resid[m, n] + acc            (O-proj, down-proj)
+  EPI_SWIGLU = 2,   // act[m, f] = bf16(silu(gate) * up)        (rows interleaved by 16)
+  EPI_QKV = 3       // RoPE on q/k, q -> bf16 buffer, k/v -> bf16 KV cache
+};
+
+// Where each output row's token sits: slot and absolute position.
+struct RowPos {
+  const int32_t* slots;  // device [M] or null (then every row is `slot`)
+  const int32_t* pos;    // device [M] or null (then row m is at pos0 + m)
+  int slot, pos0;
+};
+
+struct EpiArgs {
+  int kind;
+  int ldo;                     // leading dim of out / resid / act (elements)
+  float* out;                  // EPI_F32 / EPI_RESID
+  const float* resid;          // EPI_RESID (may alias out)
+  uint16_t* act;               // EPI_SWIGLU: pair buffer [M, F]
+  size_t act_ps;
+  // EPI_QKV
+  uint16_t* q;                 // pair buffer [M, Hq*Dh], natural head-dim order
+  size_t q_ps;
+  uint16_t* kc;                // K cache of this block: [slots][Hkv][ctx_cap][Dh]
+  uint16_t* vc;                // V cache of this block: [slots][Hkv][ctx_cap/8][Dh][8]
+  const double2* rope;         // [ctx_cap][Dh/2] (cos, sin), f64
+  RowPos rp;
+  int hq, hkv, dh, ctx_cap, max_slots;
+  uint32_t* err;               // device error counter
+};
+
+// Fused-QKV row layout: within each q and k head, stored rows come in 32-row blocks whose first
+// 16 rows are head dims [16b, 16b+16) and next 16 rows are dims [Dh/2 + 16b, Dh/2 + 16b + 16), so
+// a stored row r with (r % 32) < 16 and row r + 16 are a RoPE pair (i, i + Dh/2).  V rows keep
+// their natural order.  Gate/up are interleaved the same way: stored rows [32j, 32j+16) are gate
+// rows [16j, 16j+16) and [32j+16, 32j+32) the matching up rows.
+PSD_DEV int rope_pair_dim(int s /* stored row within head, s % 32 < 16 */) {
+  return (s >> 5) * 16 + (s & 15);
+}
+
+// Resolve the slot and position of row m; false if out of range (then the row is skipped).
+PSD_DEV bool row_slot_pos(const EpiArgs& e, int m, int& slot, int& pos) {
+  slot = e.rp.slots ? e.rp.slots[m] : e.rp.slot;
+  pos = e.rp.pos ? e.rp.pos[m] : e.rp.pos0 + m;
+  return slot >= 0 && slot < e.max_slots && pos >= 0 && pos < e.ctx_cap;
+}
+
+// Apply the QKV epilogue to one RoPE pair / V pair of outputs of row m.
+// col0 is the stored row index of the first element (col0 % 32 < 16), x0/x1 the two sums of
+// stored rows col0 and col0 + 16.
+PSD_DEV void qkv_epilogue_pair(const EpiArgs& e, int m, int col0, float x0, float x1) {
+  int slot, pos;
+  if (!row_slot_pos(e, m, slot, pos)) return;
+  const int dh = e.dh, qw = e.hq * dh, kw = e.hkv * dh;
+  if (col0 < qw + kw) {
+    const bool is_q = col0 < qw;
+    const int c = is_q ? col0 : col0 - qw;
+    const int head = c / dh, s = c - head * dh;
+    const int i = rope_pair_dim(s);
+    // rotation in f64 from an f64 table, rounded once to f32 and then to bf16
+    const double2 cs = e.rope[(size_t)pos * (dh >> 1) + i];
+    const float y0 = (float)((double)x0 * cs.x - (double)x1 * cs.y);
+    const float y1 = (float)((double)x1 * cs.x + (double)x0 * cs.y);
+    if (is_q) {
+      uint16_t* dst = e.q + (size_t)m * qw + head * dh;
+      uint32_t h0, l0, h1, l1;
+      split2(y0, h0, l0);
+      split2(y1, h1, l1);
+      dst[i] = (uint16_t)h0;
+      dst[i + (dh >> 1)] = (uint16_t)h1;
+      dst[e.q_ps + i] = (uint16_t)l0;
+      dst[e.q_ps + i + (dh >> 1)] = (uint16_t)l1;
+    } else {
+      uint16_t* dst = e.kc + (((size_t)slot * e.hkv + head) * e.ctx_cap + pos) * dh;
+      dst[i] = (uint16_t)f2bf(y0);
+      dst[i + (dh >> 1)] = (uint16_t)f2bf(y1);
+    }
+  } else {
+    const int c = col0 - qw - kw;
+    const int head = c / dh, d0 = c - head * dh;
+    uint16_t* base = e.vc + (((size_t)slot * e.hkv + head) * (e.ctx_cap >> 3) + (pos >> 3)) * dh * 8;
+    base[(size_t)d0 * 8 + (pos & 7)] = (uint16_t)f2bf(x0);
+    base[(size_t)(d0 + 16) * 8 + (pos & 7)] = (uint16_t)f2bf(x1);
+  }
+}
+
+PSD_DEV float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+PSD_DEV void store_pair(uint16_t* p, size_t ps, size_t i, float x) {
+  uint32_t h, l;
+  split2(x, h, l);
+  p[i] = (uint16_t)h;
+  p[ps + i] = (uint16_t)l;
+}

@@ -1,0 +1,97 @@
+// Launch interfaces of the stage kernels (host side).  Every launcher enqueues on `s` and returns
+// the hipError_t of the launch.
+#pragma once
+#include "common.h"
+
+struct NormArgs {
+  const float* x;     // [M][K] f32 rows
+  const float* gain;  // [K] f32
+  float eps;
+  int M, K;
+  float* out_f32;     // [M][K] normalised rows x*r*g (nullable)
+  uint16_t* out_pair; // three bf16 planes [3][M][K] of x*r*g (hi, mid, lo; nullable)
+  size_t pair_ps;     // plane stride
+};
+
+struct GemvArgs {
+  const float* x;      // [B][K] f32 rows (normalised inside: x*r*g)  -- or null
+  const float* gain;   // [K]
+  float eps;
+  const uint16_t* xb;  // pair buffer [B][K] used as is when x is null
+  size_t xb_ps;
+  const uint16_t* w;   // [N][K] bf16
+  int N, K, B;
+  EpiArgs e;
+};
+
+struct GemmArgs {
+  const uint16_t* a;   // activation planes [planes][M][K] (hi, lo or hi, mid, lo), stride a_ps
+  size_t a_ps;
+  int planes;          // 2 or 3
+  const uint16_t* w;   // [N][K] bf16
+  int M, N, K;
+  int splitk;          // K splits; each split's K range is a multiple of 64
+  float* part;         // [splitk][M][N] f32 partials when splitk > 1
+  uint32_t* counters;  // one per output tile, zero between calls (the last arriving tile resets it)
+  EpiArgs e;
+};
+
+struct GemmPlan {
+  int cfg;      // tile configuration index
+  int bm, bn;
+  int splitk;
+  int tiles_m, tiles_n;
+};
+
+struct AttnDecodeArgs {
+  const uint16_t* q;        // pair buffer [B][Hq][Dh]
+  size_t q_ps;
+  const uint16_t* kc;       // K cache of the block
+  const uint16_t* vc;       // V cache of the block
+  const int32_t* slots;     // [B]
+  const int32_t* pos;       // [B]; keys [0, pos] are attended
+  int B, hq, hkv, dh, ctx_cap, max_slots;
+  int chunk;                // keys per work-group, multiple of 128
+  int nsplit;               // splits allocated per row
+  float scale_log2;         // Dh^-1/2 * log2(e)
+  float* part_o;            // [B][Hq][nsplit][Dh]
+  float* part_lse;          // [B][Hq][nsplit]  (base-2 log-sum-exp)
+  uint16_t* out;            // merged output, pair buffer [B][Hq*Dh]
+  size_t out_ps;
+  uint32_t* err;
+};
+
+struct AttnPrefillArgs {
+  const uint16_t* q;        // pair buffer [T][Hq][Dh]
+  size_t q_ps;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  int slot, pos0, T, hq, hkv, dh, ctx_cap;
+  float scale_log2;
+  uint16_t* out;            // pair buffer [T][Hq*Dh]
+  size_t out_ps;
+};
+
+// norm / misc
+hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s);
+hipError_t launch_embed(const uint16_t* table, int V, int d, const int32_t* tokens, int n, float* out,
+                        uint32_t* err, hipStream_t s);
+hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s);
+hipError_t launch_kv_import(uint16_t* kc, uint16_t* vc, int hkv, int dh, int ctx_cap, int slot, int pos0,
+                            int n, const uint16_t* k, const uint16_t* v, hipStream_t s);
+hipError_t launch_kv_export(const uint16_t* kc, const uint16_t* vc, int hkv, int dh, int ctx_cap, int slot,
+                            int pos0, int n, uint16_t* k, uint16_t* v, hipStream_t s);
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s);
+
+// decode GEMV (B <= 4)
+bool gemv_fits(int B, int K);
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
+
+// MFMA GEMM
+GemmPlan gemm_plan(int M, int N, int K);
+hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s);
+
+// attention
+int attn_decode_chunk(int B);
+hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s);
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);

@@ -1,0 +1,289 @@
+// Causal grouped-query attention over a slot's bf16 KV cache, on MFMA.
+//
+// Definition ("41. Many GPUs", Ring attention: attention_partial / merge_partials): scores
+// q.k * Dh^-1/2, keys after the query's position masked, softmax, weighted sum of V; partial
+// results over key ranges merge by their log-sum-exp.  GQA: query head h reads KV head
+// h / (Hq / Hkv) ("41. Many GPUs", Tensor parallelism).
+//
+// Both kernels work on 16 "columns" per wave -- (query, head) pairs that share one KV head -- and
+// 32 keys per step:
+//   S^T[key, col] = K[key, :] . q[col, :]    16x16x32 MFMAs per 32-dim slice of the head, once for
+//       the bf16 hi plane of q and once for its lo plane (q keeps ~16 significant bits); the
+//       A rows are permuted so lane l ends up with the 8 consecutive keys 8*(l/16) .. +8 of its
+//       column l%16 -- exactly the B operand layout of the next product.
+//   O^T[d, col] += V^T[d, key] P^T[key, col]   A = V^T read as 16 bytes from the packed V cache
+//       [pos/8][Dh][8]; B = P^T straight from registers, split into bf16 hi + lo (two MFMAs) so
+//       the probabilities keep ~16 bits.
+// The softmax is online per column (max and rescale), in base 2 with the scale folded in.  O^T
+// puts a column's values in the same lane as its softmax state, so rescaling needs no shuffles.
+//
+// Decode: work-group = (split of `chunk` keys, KV head, batch row); its 4 waves take a quarter of
+// the chunk each and merge through LDS; a second kernel merges the splits in split order.
+// Prefill: work-group = 64 columns (consecutive queries x the group's heads) of one KV head; every
+// wave walks keys 0 .. its last query's position.
+#include "kernels.h"
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Keys of the two S^T MFMAs that A row `rho` (0..15) of chunk c feeds: (rho/4)*8 + c*4 + rho%4.
+PSD_DEV int key_of_row(int rho, int c) { return ((rho >> 2) << 3) + (c << 2) + (rho & 3); }
+
+template <int DH>
+struct Col16 {
+  bf16x8_t qh[DH / 32];    // B operand of S^T: q[col][ks*32 + grp*8 .. +8], hi plane
+  bf16x8_t ql[DH / 32];    // lo plane
+  f32x4_t o[DH / 16];      // O^T[dt*16 + grp*4 + j][col]
+  float m, l;              // running max (base-2 scaled) and this lane's share of the sum
+};
+
+// One 32-key step for a wave's 16 columns.  kb: first key (multiple of 8); key_lim(col, key) gives
+// whether a key is visible to the lane's column; keys >= kend are never touched in V.
+template <int DH, typename Visible>
+PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
+                       int kb, int kend, float scale_log2, Visible visible) {
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  f32x4_t sc[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int key = kb + key_of_row(col, c);
+    const bool ok = key < kend;
+    sc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) {
+      uint4 kv = make_uint4(0, 0, 0, 0);
+      if (ok) kv = *reinterpret_cast<const uint4*>(kbase + (size_t)key * DH + ks * 32 + grp * 8);
+      sc[c] = mfma16(as_bf16x8(kv), st.qh[ks], sc[c]);
+      sc[c] = mfma16(as_bf16x8(kv), st.ql[ks], sc[c]);
+    }
+  }
+  float s[8];
+  float mx = kNegInf;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = kb + grp * 8 + c * 4 + j;
+      const float v = visible(key) ? sc[c][j] * scale_log2 : kNegInf;
+      s[c * 4 + j] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(st.m, mx);
+  // m_new is -inf only if this column has seen no visible key yet; keep everything at zero then.
+  const float base = (m_new == kNegInf) ? 0.0f : m_new;
+  const float alpha = exp2f(st.m - base);
+  float p[8], ps = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = exp2f(s[e] - base);
+    ps += p[e];
+  }
+  st.l = st.l * alpha + ps;
+  st.m = m_new;
+#pragma unroll
+  for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] *= alpha;
+  uint4 phi, plo;
+  split_hi_lo(p, phi, plo);
+  const int kg = kb + grp * 8;              // this lane's 8 keys
+  const int nvalid = kend - kg;             // keys of the group below kend
+#pragma unroll
+  for (int dt = 0; dt < DH / 16; ++dt) {
+    uint4 vv = make_uint4(0, 0, 0, 0);
+    if (nvalid > 0) {
+      vv = *reinterpret_cast<const uint4*>(vbase + ((size_t)(kg >> 3) * DH + dt * 16 + col) * 8);
+      if (nvalid < 8) {
+        uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        vv = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    st.o[dt] = mfma16(as_bf16x8(vv), as_bf16x8(phi), st.o[dt]);
+    st.o[dt] = mfma16(as_bf16x8(vv), as_bf16x8(plo), st.o[dt]);
+  }
+}
+
+template <int DH>
+PSD_DEV void load_q(Col16<DH>& st, const uint16_t* __restrict__ qrow /* null = padded column */, size_t q_ps) {
+  const int grp = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int ks = 0; ks < DH / 32; ++ks) {
+    uint4 h = make_uint4(0, 0, 0, 0), l = make_uint4(0, 0, 0, 0);
+    if (qrow) {
+      h = *reinterpret_cast<const uint4*>(qrow + ks * 32 + grp * 8);
+      l = *reinterpret_cast<const uint4*>(qrow + q_ps + ks * 32 + grp * 8);
+    }
+    st.qh[ks] = as_bf16x8(h);
+    st.ql[ks] = as_bf16x8(l);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = kNegInf;
+  st.l = 0.0f;
+}
+
+// ------------------------------------------------------------------------------------------------
+// decode: partial attention per (split, KV head, row)
+// ------------------------------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
+  __shared__ float sm[4][16], sl[4][16];
+  __shared__ float so[4][DH][17];
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int slot = a.slots[b], pos = a.pos[b];
+  if (slot < 0 || slot >= a.max_slots || pos < 0 || pos >= a.ctx_cap) return;
+  const int ctx = pos + 1;
+  const int k0 = split * a.chunk;
+  if (k0 >= ctx) return;
+  const int k1 = min(k0 + a.chunk, ctx);
+  const int G = a.hq / a.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
+  const int sub = a.chunk >> 2;
+  const int w0 = k0 + wave * sub, w1 = min(w0 + sub, k1);
+
+  Col16<DH> st;
+  load_q(st, col < G ? a.q + ((size_t)b * a.hq + kvh * G + col) * DH : nullptr, a.q_ps);
+  const uint16_t* kbase = a.kc + ((size_t)slot * a.hkv + kvh) * a.ctx_cap * DH;
+  const uint16_t* vbase = a.vc + ((size_t)slot * a.hkv + kvh) * (size_t)(a.ctx_cap >> 3) * DH * 8;
+  for (int kb = w0; kb < w1; kb += 32)
+    attn_step<DH>(st, kbase, vbase, kb, w1, a.scale_log2, [&](int key) { return key < w1; });
+
+  float l = st.l;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (grp == 0) {
+    sm[wave][col] = st.m;
+    sl[wave][col] = l;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DH / 16; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) so[wave][dt * 16 + grp * 4 + j][col] = st.o[dt][j];
+  __syncthreads();
+
+  // merge the four waves (fixed order) and write this split's normalised partial
+  for (int idx = threadIdx.x; idx < G * DH; idx += 256) {
+    const int h = idx / DH, d = idx - h * DH;
+    float mm = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, sm[w][h]);
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (sm[w][h] == kNegInf) ? 0.0f : exp2f(sm[w][h] - mm);
+      L += f * sl[w][h];
+      acc += f * so[w][d][h];
+    }
+    const size_t row = ((size_t)b * a.hq + kvh * G + h) * a.nsplit + split;
+    a.part_o[row * DH + d] = acc / L;
+    if (d == 0) a.part_lse[row] = mm + log2f(L);
+  }
+}
+
+// merge the splits of one (row, head) in split order -> bf16 attention output
+template <int DH>
+__global__ __launch_bounds__(64) void k_attn_merge(AttnDecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int slot = a.slots[b], pos = a.pos[b];
+  uint16_t* out = a.out + (size_t)b * a.hq * DH + (size_t)h * DH;
+  if (slot < 0 || slot >= a.max_slots || pos < 0 || pos >= a.ctx_cap) {
+    for (int d = lane; d < DH; d += 64) out[d] = out[a.out_ps + d] = 0;
+    return;
+  }
+  const int ns = (pos + a.chunk) / a.chunk;   // ceil((pos + 1) / chunk)
+  const size_t row = ((size_t)b * a.hq + h) * a.nsplit;
+  float mm = kNegInf;
+  for (int s = 0; s < ns; ++s) mm = fmaxf(mm, a.part_lse[row + s]);
+  constexpr int PER = DH / 64;
+  float acc[PER] = {};
+  float L = 0.0f;
+  for (int s = 0; s < ns; ++s) {
+    const float f = exp2f(a.part_lse[row + s] - mm);
+    L += f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += f * a.part_o[(row + s) * DH + lane * PER + i];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) store_pair(out, a.out_ps, lane * PER + i, acc[i] / L);
+}
+
+// ------------------------------------------------------------------------------------------------
+// prefill: 64 columns (queries x heads of one KV head) per work-group, all visible keys
+// ------------------------------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
+  const int G = a.hq / a.hkv;
+  const int kvh = blockIdx.y;
+  const int ncols = a.T * G;
+  // heavier (later) column blocks first
+  const int cblk = gridDim.x - 1 - blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
+  const int c0 = cblk * 64 + wave * 16;
+  if (c0 >= ncols) return;
+  const int c = c0 + col;
+  const bool cvalid = c < ncols;
+  const int t = cvalid ? c / G : 0, h = cvalid ? c - (c / G) * G : 0;
+  const int head = kvh * G + h;
+  const int my_pos = a.pos0 + t;
+  const int clast = min(c0 + 15, ncols - 1);
+  const int kend = a.pos0 + clast / G + 1;     // keys [0, kend) cover every column of the wave
+
+  Col16<DH> st;
+  load_q(st, cvalid ? a.q + ((size_t)t * a.hq + head) * DH : nullptr, a.q_ps);
+  const uint16_t* kbase = a.kc + ((size_t)a.slot * a.hkv + kvh) * a.ctx_cap * DH;
+  const uint16_t* vbase = a.vc + ((size_t)a.slot * a.hkv + kvh) * (size_t)(a.ctx_cap >> 3) * DH * 8;
+  for (int kb = 0; kb < kend; kb += 32)
+    attn_step<DH>(st, kbase, vbase, kb, kend, a.scale_log2,
+                  [&](int key) { return key < kend && key <= my_pos; });
+
+  float l = st.l;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (!cvalid) return;
+  const float inv = 1.0f / l;
+  uint16_t* out = a.out + (size_t)t * a.hq * DH + (size_t)head * DH;
+#pragma unroll
+  for (int dt = 0; dt < DH / 16; ++dt) {
+    const int d = dt * 16 + grp * 4;
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) split2(st.o[dt][j] * inv, h[j], l[j]);
+    *reinterpret_cast<uint2*>(out + d) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    *reinterpret_cast<uint2*>(out + a.out_ps + d) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+  }
+}
+
+}  // namespace
+
+// keys per decode work-group: more splits when few rows must fill the chip
+int attn_decode_chunk(int B) {
+  if (B <= 1) return 128;
+  if (B <= 4) return 256;
+  return 512;
+}
+
+hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
+  dim3 grid(a.nsplit, a.hkv, a.B);
+  if (a.dh == 128) {
+    k_attn_decode<128><<<grid, 256, 0, s>>>(a);
+    k_attn_merge<128><<<dim3(a.hq, a.B), 64, 0, s>>>(a);
+  } else {
+    k_attn_decode<64><<<grid, 256, 0, s>>>(a);
+    k_attn_merge<64><<<dim3(a.hq, a.B), 64, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
+  const int G = a.hq / a.hkv;
+  dim3 grid((a.T * G + 63) / 64, a.hkv);
+  if (a.dh == 128)
+    k_attn_prefill<128><<<grid, 256, 0, s>>>(a);
+  else
+    k_attn_prefill<64><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}

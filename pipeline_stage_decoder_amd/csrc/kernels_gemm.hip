@@ -1,0 +1,232 @@
+// C[M, N] = A[M, K] W[N, K]^T on bf16 MFMA (16x16x32, f32 accumulate), with the stage's epilogues.
+// A is an activation plane buffer (bf16 hi + lo, or hi + mid + lo for the QKV projection); every W
+// tile meets every plane, so the product keeps the activations' ~16 (~24) significant bits.
+//
+// Prefill projections (M = T tokens) and batched decode (M = B rows) both land here.  Both
+// operands are K-contiguous, the layout the MFMA operands want: lane l takes 8 consecutive k of
+// row l%16.  A work-group of 4 waves owns a BM x BN tile; BK = 64 slices of A and W are staged
+// global -> registers -> LDS (double-buffered, 16-byte chunks XOR-swizzled by row so the
+// ds_read_b128 of 16 rows hits distinct banks) while the previous slice feeds the MFMAs.
+// Small tile counts (skinny decode GEMMs) split K: every split writes an f32 partial, and the last
+// split to arrive for a tile (one atomic counter per tile) sums the partials in split order -- a
+// fixed order, so results never depend on arrival -- applies the epilogue and re-arms the counter.
+#include "kernels.h"
+
+namespace {
+
+constexpr int BK = 64;
+
+template <int BM, int BN, int WM, int WN, int NP>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
+  static_assert(WM * WN == 4, "4 waves");
+  constexpr int WTM = BM / WM, WTN = BN / WN;       // wave tile
+  constexpr int TM = WTM / 16, TN = WTN / 16;       // MFMA tiles per wave
+  static_assert(WTN % 32 == 0, "paired epilogues need 32-aligned wave columns");
+  constexpr int A_ITERS = (BM * 8 + 255) / 256, B_ITERS = (BN * 8 + 255) / 256;
+  __shared__ uint4 As[2][NP][BM * 8];  // [buffer][plane][row * 8 + swizzled chunk]
+  __shared__ uint4 Bs[2][BN * 8];
+  __shared__ int last_flag;
+
+  const int M = g.M, N = g.N, K = g.K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int tile = blockIdx.x;
+  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  const int split = blockIdx.y;
+  const int kper = ((K + g.splitk - 1) / g.splitk + BK - 1) / BK * BK;
+  const int kbeg = split * kper;
+  const int kend = min(K, kbeg + kper);
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+  uint4 ra[NP][A_ITERS], rb[B_ITERS];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_ITERS; ++i) {
+      const int q = tid + i * 256, row = q >> 3, c8 = q & 7;
+      const int gm = m0 + row, gk = k0 + c8 * 8;
+      const bool ok = q < BM * 8 && gm < M && gk < kend;
+      const uint16_t* src = g.a + (size_t)gm * K + gk;
+#pragma unroll
+      for (int pl = 0; pl < NP; ++pl)
+        ra[pl][i] = ok ? *reinterpret_cast<const uint4*>(src + pl * g.a_ps) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < B_ITERS; ++i) {
+      const int q = tid + i * 256, row = q >> 3, c8 = q & 7;
+      const int gn = n0 + row, gk = k0 + c8 * 8;
+      rb[i] = (q < BN * 8 && gn < N && gk < kend)
+                  ? *reinterpret_cast<const uint4*>(g.w + (size_t)gn * K + gk) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_ITERS; ++i) {
+      const int q = tid + i * 256, row = q >> 3, c8 = q & 7;
+      if (q < BM * 8) {
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl) As[buf][pl][row * 8 + (c8 ^ (row & 7))] = ra[pl][i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B_ITERS; ++i) {
+      const int q = tid + i * 256, row = q >> 3, c8 = q & 7;
+      if (q < BN * 8) Bs[buf][row * 8 + (c8 ^ (row & 7))] = rb[i];
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (nk > 0) {
+    gload(kbeg);
+    sstore(0);
+    __syncthreads();
+  }
+  for (int it = 0; it < nk; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < nk) gload(kbeg + (it + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c8 = kk * 4 + (lane >> 4);
+      bf16x8_t af[NP][TM], bw[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * WTM + i * 16 + (lane & 15);
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl) af[pl][i] = as_bf16x8(As[cur][pl][row * 8 + (c8 ^ (row & 7))]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = wn * WTN + j * 16 + (lane & 15);
+        bw[j] = as_bf16x8(Bs[cur][row * 8 + (c8 ^ (row & 7))]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+          for (int pl = 0; pl < NP; ++pl) acc[i][j] = mfma16(af[pl][i], bw[j], acc[i][j]);
+        }
+    }
+    if (it + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- split-K: partials, last-arriving split reduces in split order ----------------------------
+  if (g.splitk > 1) {
+    float* part = g.part + (size_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = m0 + wm * WTM + i * 16 + (lane >> 4) * 4 + jj;
+          const int c = n0 + wn * WTN + j * 16 + (lane & 15);
+          if (r < M && c < N) part[(size_t)r * N + c] = acc[i][j][jj];
+        }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned prev = atomicAdd(&g.counters[tile], 1u);
+      last_flag = (prev == (unsigned)g.splitk - 1u);
+      if (last_flag) g.counters[tile] = 0u;
+    }
+    __syncthreads();
+    if (!last_flag) return;
+    __threadfence();
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = m0 + wm * WTM + i * 16 + (lane >> 4) * 4 + jj;
+          const int c = n0 + wn * WTN + j * 16 + (lane & 15);
+          float s = 0.0f;
+          if (r < M && c < N)
+            for (int sp = 0; sp < g.splitk; ++sp) s += __builtin_nontemporal_load(g.part + ((size_t)sp * M + r) * N + c);
+          acc[i][j][jj] = s;
+        }
+  }
+
+  // ---- epilogue ----------------------------------------------------------------------------------
+  const EpiArgs& e = g.e;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = m0 + wm * WTM + i * 16 + (lane >> 4) * 4 + jj;
+      if (r >= M) continue;
+      if (e.kind == EPI_F32 || e.kind == EPI_RESID) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int c = n0 + wn * WTN + j * 16 + (lane & 15);
+          if (c >= N) continue;
+          float v = acc[i][j][jj];
+          if (e.kind == EPI_RESID) v += e.resid[(size_t)r * e.ldo + c];
+          e.out[(size_t)r * e.ldo + c] = v;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; j += 2) {
+          const int c = n0 + wn * WTN + j * 16 + (lane & 15);   // c % 32 < 16, partner c + 16
+          if (c >= N) continue;
+          const float x0 = acc[i][j][jj], x1 = acc[i][j + 1][jj];
+          if (e.kind == EPI_SWIGLU) {
+            store_pair(e.act, e.act_ps, (size_t)r * e.ldo + (c >> 5) * 16 + (c & 15), silu_mul(x0, x1));
+          } else {
+            int slot, pos;
+            if (!row_slot_pos(e, r, slot, pos)) {
+              if (c == 0) atomicAdd(e.err, 1u);
+            } else {
+              qkv_epilogue_pair(e, r, c, x0, x1);
+            }
+          }
+        }
+      }
+    }
+}
+
+struct Cfg {
+  int bm, bn;
+};
+constexpr Cfg kCfgs[] = {{128, 128}, {64, 128}, {32, 128}, {16, 128}};
+
+}  // namespace
+
+GemmPlan gemm_plan(int M, int N, int K) {
+  GemmPlan p{};
+  p.cfg = M > 64 ? 0 : (M > 32 ? 1 : (M > 16 ? 2 : 3));
+  p.bm = kCfgs[p.cfg].bm;
+  p.bn = kCfgs[p.cfg].bn;
+  p.tiles_m = (M + p.bm - 1) / p.bm;
+  p.tiles_n = (N + p.bn - 1) / p.bn;
+  const int tiles = p.tiles_m * p.tiles_n;
+  p.splitk = 1;
+  while (tiles * p.splitk < 256 && K / (p.splitk * 2) >= 4 * BK && p.splitk < 16) p.splitk *= 2;
+  return p;
+}
+
+template <int NP>
+void launch_np(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) {
+  switch (p.cfg) {
+    case 0: k_gemm<128, 128, 2, 2, NP><<<grid, 256, 0, s>>>(a); break;
+    case 1: k_gemm<64, 128, 1, 4, NP><<<grid, 256, 0, s>>>(a); break;
+    case 2: k_gemm<32, 128, 1, 4, NP><<<grid, 256, 0, s>>>(a); break;
+    default: k_gemm<16, 128, 1, 4, NP><<<grid, 256, 0, s>>>(a); break;
+  }
+}
+
+hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+  dim3 grid(p.tiles_m * p.tiles_n, p.splitk);
+  if (a.planes == 3)
+    launch_np<3>(a, p, grid, s);
+  else
+    launch_np<2>(a, p, grid, s);
+  return hipGetLastError();
+}

@@ -1,0 +1,165 @@
+// Decode GEMV for up to four rows: y[b, n] = sum_k x[b, k] W[n, k] with bf16 W streamed once.
+//
+// HBM-bound: every weight byte is read once per step.  A wave owns a pair of output rows
+// (n, n + 16) -- a RoPE pair of the fused QKV layout or a gate/up pair of the interleaved MLP
+// layout, so the epilogue finds both operands in the wave -- and streams the two rows along K with
+// 16-byte loads (one 1 KiB contiguous segment per row per wave load), up to eight loads per row in
+// flight.  f32 FMAs on bf16 operands, then a 64-lane butterfly reduces each sum.
+// Fused prologue: the f32 input rows are RMS-normalised and scaled by the gain into LDS (f32) once
+// per work-group, or an activation pair buffer is expanded to f32 (hi + lo); the grid is sized so
+// each work-group covers many row pairs.
+#include "kernels.h"
+#include "norm.h"
+
+namespace {
+
+constexpr int kGemvThreads = 256;
+constexpr int kGemvUnroll = 8;
+constexpr int kGemvMaxLds = 64 * 1024;
+
+PSD_DEV void dot8(const uint4& w, const float4& x0, const float4& x1, float& acc) {
+  acc = fmaf(bf_lo(w.x), x0.x, acc);
+  acc = fmaf(bf_hi(w.x), x0.y, acc);
+  acc = fmaf(bf_lo(w.y), x0.z, acc);
+  acc = fmaf(bf_hi(w.y), x0.w, acc);
+  acc = fmaf(bf_lo(w.z), x1.x, acc);
+  acc = fmaf(bf_hi(w.z), x1.y, acc);
+  acc = fmaf(bf_lo(w.w), x1.z, acc);
+  acc = fmaf(bf_hi(w.w), x1.w, acc);
+}
+
+template <int NB>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
+  extern __shared__ float4 lds_x[];                // NB rows of K f32 (operand values)
+  __shared__ double red[4];
+  const int K = a.K, K8 = K >> 3, B = a.B;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* xs = reinterpret_cast<float*>(lds_x);
+
+  // ---- prologue: input rows -> f32 operand values in LDS ---------------------------------------
+  if (a.x) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < B) {
+        const float* xr = a.x + (size_t)b * K;
+        const double r = block_rms_scale(xr, K, a.eps, red);
+        for (int i = threadIdx.x * 4; i < K; i += 1024) {
+          const float4 v = *(const float4*)(xr + i);
+          const float4 g = *(const float4*)(a.gain + i);
+          *(float4*)(xs + (size_t)b * K + i) = make_float4(norm_mul(v.x, r, g.x), norm_mul(v.y, r, g.y),
+                                                           norm_mul(v.z, r, g.z), norm_mul(v.w, r, g.w));
+        }
+      } else {
+        for (int i = threadIdx.x * 4; i < K; i += 1024)
+          *(float4*)(xs + (size_t)b * K + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  } else {
+    for (int i = threadIdx.x * 4; i < NB * K; i += 1024) {
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i / K < B) {
+        const uint2 h = *(const uint2*)(a.xb + i);
+        const uint2 l = *(const uint2*)(a.xb + a.xb_ps + i);
+        o = make_float4(bf_lo(h.x) + bf_lo(l.x), bf_hi(h.x) + bf_hi(l.x), bf_lo(h.y) + bf_lo(l.y),
+                        bf_hi(h.y) + bf_hi(l.y));
+      }
+      *(float4*)(xs + i) = o;
+    }
+  }
+  __syncthreads();
+
+  // ---- row pairs ------------------------------------------------------------------------------
+  const int N = a.N;
+  const int npairs = ((N + 31) >> 5) << 4;
+  const int nwaves = gridDim.x * (kGemvThreads / 64);
+  for (int p = blockIdx.x * (kGemvThreads / 64) + wave; p < npairs; p += nwaves) {
+    const int r0 = ((p >> 4) << 5) + (p & 15), r1 = r0 + 16;
+    const bool v0 = r0 < N, v1 = r1 < N;
+    const uint4* w0 = reinterpret_cast<const uint4*>(a.w + (size_t)(v0 ? r0 : 0) * K);
+    const uint4* w1 = reinterpret_cast<const uint4*>(a.w + (size_t)(v1 ? r1 : 0) * K);
+    float acc0[NB], acc1[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc0[b] = acc1[b] = 0.0f;
+
+    for (int base = 0; base < K8; base += 64 * kGemvUnroll) {
+      uint4 q0[kGemvUnroll], q1[kGemvUnroll];
+#pragma unroll
+      for (int u = 0; u < kGemvUnroll; ++u) {
+        const int idx = base + u * 64 + lane;
+        const bool ok = idx < K8;
+        q0[u] = (ok && v0) ? w0[idx] : make_uint4(0, 0, 0, 0);
+        q1[u] = (ok && v1) ? w1[idx] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kGemvUnroll; ++u) {
+        const int idx = base + u * 64 + lane;
+        if (idx < K8) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const float4 xa = lds_x[(b * K8 + idx) * 2], xb = lds_x[(b * K8 + idx) * 2 + 1];
+            dot8(q0[u], xa, xb, acc0[b]);
+            dot8(q1[u], xa, xb, acc1[b]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      acc0[b] = wave_sum(acc0[b]);
+      acc1[b] = wave_sum(acc1[b]);
+    }
+
+    // ---- epilogue: lane b writes row b -------------------------------------------------------
+    const EpiArgs& e = a.e;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < B && lane == b) {
+        const float x0 = acc0[b], x1 = acc1[b];
+        switch (e.kind) {
+          case EPI_F32:
+            if (v0) e.out[(size_t)b * e.ldo + r0] = x0;
+            if (v1) e.out[(size_t)b * e.ldo + r1] = x1;
+            break;
+          case EPI_RESID:
+            if (v0) e.out[(size_t)b * e.ldo + r0] = e.resid[(size_t)b * e.ldo + r0] + x0;
+            if (v1) e.out[(size_t)b * e.ldo + r1] = e.resid[(size_t)b * e.ldo + r1] + x1;
+            break;
+          case EPI_SWIGLU:
+            if (v1) store_pair(e.act, e.act_ps, (size_t)b * e.ldo + (p >> 4) * 16 + (p & 15), silu_mul(x0, x1));
+            break;
+          case EPI_QKV:
+            if (v1) {
+              int slot, pos;
+              if (!row_slot_pos(e, b, slot, pos)) {
+                if (r0 == 0) atomicAdd(e.err, 1u);
+              } else {
+                qkv_epilogue_pair(e, b, r0, x0, x1);
+              }
+            }
+            break;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool gemv_fits(int B, int K) {
+  const int nb = B <= 1 ? 1 : (B <= 2 ? 2 : 4);
+  return B >= 1 && B <= 4 && (size_t)nb * K * 4 <= (size_t)kGemvMaxLds && K % 8 == 0;
+}
+
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t s) {
+  const int npairs = ((a.N + 31) >> 5) << 4;
+  int grid = (npairs + 3) / 4;
+  if (grid > 1024) grid = 1024;
+  const int nb = a.B <= 1 ? 1 : (a.B <= 2 ? 2 : 4);
+  const size_t lds = (size_t)nb * a.K * 4;
+  switch (nb) {
+    case 1: k_gemv<1><<<grid, kGemvThreads, lds, s>>>(a); break;
+    case 2: k_gemv<2><<<grid, kGemvThreads, lds, s>>>(a); break;
+    default: k_gemv<4><<<grid, kGemvThreads, lds, s>>>(a); break;
+  }
+  return hipGetLastError();
+}

@@ -1,0 +1,120 @@
+// RMSNorm rows, token embedding, KV import/export and small conversions.
+#include "kernels.h"
+#include "norm.h"
+
+namespace {
+
+__global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
+  __shared__ double red[4];
+  const int m = blockIdx.x;
+  const float* x = a.x + (size_t)m * a.K;
+  const double r = block_rms_scale(x, a.K, a.eps, red);
+  for (int i = threadIdx.x * 4; i < a.K; i += 1024) {
+    const float4 v = *(const float4*)(x + i);
+    const float4 g = *(const float4*)(a.gain + i);
+    const float y0 = norm_mul(v.x, r, g.x), y1 = norm_mul(v.y, r, g.y), y2 = norm_mul(v.z, r, g.z),
+                y3 = norm_mul(v.w, r, g.w);
+    if (a.out_f32) *(float4*)(a.out_f32 + (size_t)m * a.K + i) = make_float4(y0, y1, y2, y3);
+    if (a.out_pair) {
+      uint32_t h[4], md[4], l[4];
+      split3(y0, h[0], md[0], l[0]);
+      split3(y1, h[1], md[1], l[1]);
+      split3(y2, h[2], md[2], l[2]);
+      split3(y3, h[3], md[3], l[3]);
+      uint16_t* p = a.out_pair + (size_t)m * a.K + i;
+      *(uint2*)p = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      *(uint2*)(p + a.pair_ps) = make_uint2(md[0] | (md[1] << 16), md[2] | (md[3] << 16));
+      *(uint2*)(p + 2 * a.pair_ps) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_embed(const uint16_t* __restrict__ table, int V, int d,
+                                               const int32_t* __restrict__ tokens, float* __restrict__ out,
+                                               uint32_t* err) {
+  const int i = blockIdx.x;
+  const int tok = tokens[i];
+  float* o = out + (size_t)i * d;
+  if (tok < 0 || tok >= V) {
+    for (int j = threadIdx.x; j < d; j += 256) o[j] = 0.0f;
+    if (threadIdx.x == 0) atomicAdd(err, 1u);
+    return;
+  }
+  const uint16_t* e = table + (size_t)tok * d;
+  for (int j = threadIdx.x * 4; j < d; j += 1024) {
+    const uint2 w = *(const uint2*)(e + j);
+    *(float4*)(o + j) = make_float4(bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y));
+  }
+}
+
+__global__ void k_bf16_to_f32(const uint16_t* __restrict__ src, float* __restrict__ dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = bf2f(src[i]);
+}
+
+__global__ void k_zero_f32(float* __restrict__ p, size_t n) {
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
+}
+
+// K cache [slot][kvh][ctx_cap][Dh]; V cache [slot][kvh][ctx_cap/8][Dh][8].
+__global__ void k_kv_import(uint16_t* kc, uint16_t* vc, int hkv, int dh, int ctx_cap, int slot, int pos0,
+                            const uint16_t* __restrict__ k, const uint16_t* __restrict__ v) {
+  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const int pos = pos0 + t;
+  const size_t src = ((size_t)t * hkv + h) * dh + d;
+  kc[(((size_t)slot * hkv + h) * ctx_cap + pos) * dh + d] = k[src];
+  vc[((((size_t)slot * hkv + h) * (ctx_cap >> 3) + (pos >> 3)) * dh + d) * 8 + (pos & 7)] = v[src];
+}
+
+__global__ void k_kv_export(const uint16_t* kc, const uint16_t* vc, int hkv, int dh, int ctx_cap, int slot,
+                            int pos0, uint16_t* __restrict__ k, uint16_t* __restrict__ v) {
+  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const int pos = pos0 + t;
+  const size_t dst = ((size_t)t * hkv + h) * dh + d;
+  k[dst] = kc[(((size_t)slot * hkv + h) * ctx_cap + pos) * dh + d];
+  v[dst] = vc[((((size_t)slot * hkv + h) * (ctx_cap >> 3) + (pos >> 3)) * dh + d) * 8 + (pos & 7)];
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  k_rmsnorm<<<a.M, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const uint16_t* table, int V, int d, const int32_t* tokens, int n, float* out,
+                        uint32_t* err, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_embed<<<n, 256, 0, s>>>(table, V, d, tokens, out, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_bf16_to_f32<<<(n + 255) / 256, 256, 0, s>>>(src, dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t g = (n + 255) / 256;
+  if (g > 4096) g = 4096;
+  k_zero_f32<<<(unsigned)g, 256, 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_import(uint16_t* kc, uint16_t* vc, int hkv, int dh, int ctx_cap, int slot, int pos0,
+                            int n, const uint16_t* k, const uint16_t* v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_kv_import<<<dim3(n, hkv), dh, 0, s>>>(kc, vc, hkv, dh, ctx_cap, slot, pos0, k, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_export(const uint16_t* kc, const uint16_t* vc, int hkv, int dh, int ctx_cap, int slot,
+                            int pos0, int n, uint16_t* k, uint16_t* v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_kv_export<<<dim3(n, hkv), dh, 0, s>>>(kc, vc, hkv, dh, ctx_cap, slot, pos0, k, v);
+  return hipGetLastError();
+}

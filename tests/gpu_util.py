@@ -1,0 +1,78 @@
+"""Helpers of the GPU parity tests: build stages from seeded weights, drive them like the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import fixtures as fx
+from pipeline_stage_decoder_amd.stage import Stage
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(got, want) -> float:
+    g = np.asarray(got, dtype=np.float64)
+    w = np.asarray(want, dtype=np.float64)
+    den = np.linalg.norm(w)
+    return float(np.linalg.norm(g - w) / (den if den > 0 else 1.0))
+
+
+def make_stage(shape, begin, end, first, last, weights: dict, **kw) -> Stage:
+    st = Stage(shape, begin, end, first, last, **kw)
+    for (role, block), w in weights.items():
+        if role == "embed" and not first:
+            continue
+        if role in ("final_norm", "readout") and not last:
+            continue
+        if block >= 0 and not (begin <= block < end):
+            continue
+        st.load_weight(role, block, w)
+    torch.cuda.synchronize()
+    return st
+
+
+def gpu_generate(stages: list, prompt: np.ndarray, n_new: int, slot: int = 0):
+    """Greedy generation through GPU stages with F32 handoff; same trace keys as oracle.generate."""
+    dev = stages[0].arena.device
+    trace = {"handoff": [], "final_hidden": [], "logits": [], "residual": []}
+    toks_in = torch.tensor(np.asarray(prompt, np.int32), device=dev)
+    x = stages[0].embed(toks_in)
+    for st in stages:
+        x = st.prefill(x, slot, 0)
+        trace["handoff"].append(x.cpu().numpy())
+    logits, hn = stages[-1].readout(x)
+    trace["residual"].append(x.cpu().numpy())
+    trace["final_hidden"].append(hn.cpu().numpy())
+    trace["logits"].append(logits.cpu().numpy())
+    toks = [int(torch.argmax(logits[-1]).item())]
+    pos = len(prompt)
+    slots = torch.tensor([slot], dtype=torch.int32, device=dev)
+    for _ in range(n_new - 1):
+        x = stages[0].embed(torch.tensor([toks[-1]], dtype=torch.int32, device=dev))
+        positions = torch.tensor([pos], dtype=torch.int32, device=dev)
+        for st in stages:
+            x = st.decode(x, slots, positions)
+            trace["handoff"].append(x.cpu().numpy())
+        logits, hn = stages[-1].readout(x)
+        trace["residual"].append(x.cpu().numpy())
+        trace["final_hidden"].append(hn.cpu().numpy())
+        trace["logits"].append(logits.cpu().numpy())
+        toks.append(int(torch.argmax(logits[0]).item()))
+        pos += 1
+    return np.array(toks, dtype=np.int32), trace
+
+
+def kv_bits(st: Stage, block: int, slot: int, n: int):
+    k, v = st.kv_export(block, slot, 0, n)
+    torch.cuda.synchronize()
+    return k.cpu().numpy().view(np.uint16), v.cpu().numpy().view(np.uint16)
+
+
+def hidden_rows(seed_slot: int, n: int, d: int, offset_pos: int = 0) -> np.ndarray:
+    """Seeded F32 N(0,1) hidden rows of a slot at positions offset_pos .. offset_pos+n."""
+    return fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(seed_slot), n * d, offset_pos * d).reshape(n, d)

@@ -1,0 +1,149 @@
+"""GPU parity on the tiny decoder (2 blocks, d 256, 4 q / 2 KV heads, Dh 64, F 688, V 1024).
+
+Compares the HIP path (through the C ABI) with the CPU oracle on the same seeded weights and
+inputs: relative L2 <= 1e-3 on hidden rows and logits, identical greedy tokens, and bit-identical
+split-vs-unsplit results on the GPU itself ("RFC: pipeline placement ...", Numerical correctness
+proof: logits, final features, KV state and generated tokens must match bit for bit).
+"""
+import numpy as np
+import pytest
+import torch
+
+import fixtures as fx
+from oracle import decoder as o
+from tests.gpu_util import gpu_generate, hidden_rows, kv_bits, make_stage, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+TINY = fx.TINY
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def weights():
+    return fx.draw_stage_weights(TINY, 0, 2, True, True, gain_sigma=0.1)
+
+
+def oracle_stage(w, begin, end, first, last, max_ctx=64):
+    return o.Stage(o.Dims.of(TINY), begin, end, first, last, w, max_ctx)
+
+
+def test_tiny_greedy_parity(weights):
+    prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(0), 16, TINY.vocab)
+    say("tiny greedy: oracle")
+    want_toks, want = o.generate([oracle_stage(weights, 0, 2, True, True)], prompt, 8)
+    say("tiny greedy: gpu")
+    st = make_stage(TINY, 0, 2, True, True, weights, max_slots=2, max_ctx=64, max_tokens=16)
+    got_toks, got = gpu_generate([st], prompt, 8)
+    for step in range(8):
+        for key in ("logits", "final_hidden", "residual"):
+            e = rel_l2(got[key][step], want[key][step])
+            assert e <= TOL, (step, key, e)
+    margins = [float(o.top2_margin(l[-1:])[0]) for l in want["logits"]]
+    say("tokens", got_toks.tolist(), "oracle", want_toks.tolist(), "margins", [round(m, 4) for m in margins])
+    np.testing.assert_array_equal(got_toks, want_toks)
+    assert st.device_errors() == 0
+
+
+def test_tiny_split_equals_unsplit_on_gpu(weights):
+    prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(1), 16, TINY.vocab)
+    whole = make_stage(TINY, 0, 2, True, True, weights, max_slots=1, max_ctx=64, max_tokens=16)
+    t1, tr1 = gpu_generate([whole], prompt, 8)
+    a = make_stage(TINY, 0, 1, True, False, weights, max_slots=1, max_ctx=64, max_tokens=16)
+    b = make_stage(TINY, 1, 2, False, True, weights, max_slots=1, max_ctx=64, max_tokens=16)
+    t2, tr2 = gpu_generate([a, b], prompt, 8)
+    np.testing.assert_array_equal(t1, t2)
+    for key in ("logits", "final_hidden", "residual"):
+        for u, v in zip(tr1[key], tr2[key]):
+            assert u.tobytes() == v.tobytes(), key
+    kw0, vw0 = kv_bits(whole, 0, 0, 23)
+    kw1, vw1 = kv_bits(whole, 1, 0, 23)
+    ka, va = kv_bits(a, 0, 0, 23)
+    kb, vb = kv_bits(b, 1, 0, 23)
+    assert np.array_equal(kw0, ka) and np.array_equal(vw0, va)
+    assert np.array_equal(kw1, kb) and np.array_equal(vw1, vb)
+
+
+def test_tiny_kv_matches_oracle(weights):
+    x = hidden_rows(0, 16, TINY.d_model)
+    ost = oracle_stage(weights, 0, 2, False, False)
+    want = ost.prefill(x, 0, 0)
+    st = make_stage(TINY, 0, 2, False, False, weights, max_slots=1, max_ctx=64, max_tokens=16)
+    got = st.prefill(torch.from_numpy(x).cuda(), 0, 0).cpu().numpy()
+    assert rel_l2(got, want) <= TOL
+    kw, vw = ost.kv_bits(0, 16)
+    for blk in range(2):
+        kg, vg = kv_bits(st, blk, 0, 16)
+        for g_bits, w_bits in ((kg, kw[blk]), (vg, vw[blk])):
+            gv, wv = o.bf16_to_f32(g_bits), o.bf16_to_f32(w_bits)
+            assert rel_l2(gv, wv) <= TOL
+            assert np.mean(g_bits == w_bits) > 0.99      # bf16 rounding flips are rare
+
+
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 16, 40])
+def test_tiny_prefill_row_counts(weights, T):
+    # T <= 4 runs the GEMV kernels, larger T the MFMA GEMM; 40 leaves a ragged GEMM tile
+    x = hidden_rows(1, T, TINY.d_model)
+    want = oracle_stage(weights, 0, 2, False, False).prefill(x, 0, 0)
+    st = make_stage(TINY, 0, 2, False, False, weights, max_slots=1, max_ctx=64, max_tokens=64)
+    got = st.prefill(torch.from_numpy(x).cuda(), 0, 0).cpu().numpy()
+    assert rel_l2(got, want) <= TOL, T
+
+
+def test_tiny_chunked_prefill_and_decode(weights):
+    x = hidden_rows(2, 20, TINY.d_model)
+    ost = oracle_stage(weights, 0, 2, False, False)
+    w1 = ost.prefill(x[:8], 0, 0)
+    w2 = ost.prefill(x[8:19], 0, 8)
+    w3 = ost.forward(x[19:], [0], [19])
+    st = make_stage(TINY, 0, 2, False, False, weights, max_slots=1, max_ctx=64, max_tokens=16)
+    xt = torch.from_numpy(x).cuda()
+    g1 = st.prefill(xt[:8], 0, 0).cpu().numpy()
+    g2 = st.prefill(xt[8:19], 0, 8).cpu().numpy()
+    dev = xt.device
+    g3 = st.decode(xt[19:], torch.tensor([0], dtype=torch.int32, device=dev),
+                   torch.tensor([19], dtype=torch.int32, device=dev)).cpu().numpy()
+    for g, w in ((g1, w1), (g2, w2), (g3, w3)):
+        assert rel_l2(g, w) <= TOL
+
+
+@pytest.mark.parametrize("B", [2, 4, 6, 9])
+def test_tiny_batched_decode(weights, B):
+    # slots prefilled to different lengths, then one decode step for all rows at once
+    ost = oracle_stage(weights, 0, 2, False, False)
+    st = make_stage(TINY, 0, 2, False, False, weights, max_slots=B, max_ctx=64, max_tokens=64)
+    lens = [3 + 5 * b for b in range(B)]
+    for b, n in enumerate(lens):
+        x = hidden_rows(10 + b, n, TINY.d_model)
+        ost.prefill(x, b, 0)
+        st.prefill(torch.from_numpy(x).cuda(), b, 0)
+    xd = np.vstack([hidden_rows(10 + b, 1, TINY.d_model, offset_pos=n) for b, n in enumerate(lens)])
+    slots = np.arange(B)[::-1].copy()
+    xd = xd[slots]
+    pos = np.array(lens)[slots]
+    want = ost.forward(xd, slots, pos)
+    dev = torch.device("cuda")
+    got = st.decode(torch.from_numpy(xd).to(dev), torch.tensor(slots, dtype=torch.int32, device=dev),
+                    torch.tensor(pos, dtype=torch.int32, device=dev)).cpu().numpy()
+    assert rel_l2(got, want) <= TOL
+    assert st.device_errors() == 0
+
+
+def test_tiny_determinism(weights):
+    prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(3), 16, TINY.vocab)
+    st = make_stage(TINY, 0, 2, True, True, weights, max_slots=1, max_ctx=64, max_tokens=16)
+    t1, tr1 = gpu_generate([st], prompt, 6)
+    t2, tr2 = gpu_generate([st], prompt, 6)       # the caller rewinds positions: "reset"
+    np.testing.assert_array_equal(t1, t2)
+    assert all(a.tobytes() == b.tobytes() for a, b in zip(tr1["logits"], tr2["logits"]))
+
+
+def test_device_side_range_checks(weights):
+    st = make_stage(TINY, 0, 2, True, False, weights, max_slots=2, max_ctx=64, max_tokens=4)
+    dev = torch.device("cuda")
+    st.device_errors(reset=True)
+    st.embed(torch.tensor([5, TINY.vocab, -1], dtype=torch.int32, device=dev))
+    x = torch.zeros((2, TINY.d_model), dtype=torch.float32, device=dev)
+    st.decode(x, torch.tensor([0, 7], dtype=torch.int32, device=dev), torch.tensor([3, 1], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert st.device_errors() >= 3
