@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of one pipeline stage's decoder forward on one MI355X.
+
+Workload (default): the 8B-shaped first stage -- token embedding + blocks 0..15 of a 32-block
+decoder (d 4096, 32 q / 8 KV heads, head dim 128, SwiGLU 14336, vocabulary 128256), seeded
+synthetic bf16 weights N(0, 0.02) and uniform tokens, batch 1: prefill of a 512-token prompt, then
+teacher-forced decode one token at a time up to context 2048.  One step = that whole request.
+
+Prints ONE JSON line.  `value` is the decode throughput (tokens/s, inputs resident in HBM); the
+line also carries the prefill throughput, the dominant decode kernel's roofline (HBM bytes per
+launch / its average duration, timed live with HIP events on the launch stream) and the CPU
+oracle timed on this host's cores over a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fill_weights(st, shape, blocks, first, last, seed, gain_sigma=0.0):
+    """Draw every weight tensor of the stage on the GPU and load it (device-to-device copies)."""
+    import torch
+
+    import fixtures as fx
+
+    roles = fx.stage_roles(blocks[0], blocks[1], first, last)
+    biggest = max(int(__import__("numpy").prod(fx.role_shape(shape, r))) for r, _ in roles)
+    scratch = torch.empty(biggest, dtype=torch.int16, device="cuda")
+    for role, b in roles:
+        n = int(__import__("numpy").prod(fx.role_shape(shape, role)))
+        t = scratch[:n]
+        if role in fx.GAIN_ROLES:
+            fx.gain_bf16_gpu(t, seed, fx.weight_stream(role, b), gain_sigma)
+        else:
+            fx.normal_bf16_gpu(t, seed, fx.weight_stream(role, b), 0.02)
+        st.load_weight(role, b, t)
+    torch.cuda.synchronize()
+    del scratch
+
+
+def cpu_baseline_decode(shape, ctx: int, n_blocks: int, reps: int = 2):
+    """The oracle, as it stands, on this host: one block's decode step at context `ctx`,
+    `reps` times; per-token time = n_blocks x the per-block time."""
+    import numpy as np
+
+    import fixtures as fx
+    from oracle import decoder as o
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    w = fx.draw_stage_weights(shape, 0, 1, False, False)
+    st = o.Stage(o.Dims.of(shape), 0, 1, False, False, w, ctx + 1)
+    kshape = (1, ctx + 1, shape.n_kv_heads, shape.head_dim)
+    kv = o.round_bf16(fx.normal_f32(fx.SEED_HIDDEN, 0x7000, int(np.prod(kshape))).reshape(kshape))
+    st.kv[0] = (kv.copy(), kv.copy())
+    x = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(0), shape.d_model).reshape(1, shape.d_model)
+    st.forward(x, [0], [ctx])                     # warm caches
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        st.forward(x, [0], [ctx])
+    per_block = (time.perf_counter() - t0) / reps
+    per_token = per_block * n_blocks
+    return {"value": 1.0 / per_token, "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} decode steps of 1 of {n_blocks} blocks at context {ctx} (B=1); "
+                      f"tok/s = 1 / ({n_blocks} x {per_block:.2f} s per block-step)",
+            "seconds_per_block_step": per_block}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--prefill", type=int, default=512, help="prompt tokens")
+    ap.add_argument("--ctx", type=int, default=2048, help="decode up to this context")
+    ap.add_argument("--graph", choices=("on", "off"), default="on", help="replay decode steps from a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs one pipeline stage on one GPU; "
+                                   "--gpus above 1 is not supported (the stage has no cross-GPU path)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fixtures as fx
+    from pipeline_stage_decoder_amd import accounting as acc
+    from pipeline_stage_decoder_amd.stage import Stage
+
+    shape = fx.LLAMA8B
+    blocks = (0, 16)
+    T, ctx = args.prefill, args.ctx
+    n_dec = ctx - T
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    log(f"[bench] creating stage: blocks {blocks}, embedding, max_ctx {ctx}, max_tokens {T}")
+    st = Stage(shape, blocks[0], blocks[1], True, False, max_slots=1, max_ctx=ctx, max_tokens=T, device=0)
+    fill_weights(st, shape, blocks, True, False, fx.SEED_WEIGHTS)
+    prompt = fx.tokens_gpu(torch.empty(T, dtype=torch.int32, device=dev), fx.SEED_TOKENS, fx.token_stream(0),
+                           shape.vocab)
+    dec_tok = fx.tokens_gpu(torch.empty(n_dec, dtype=torch.int32, device=dev), fx.SEED_TOKENS,
+                            fx.token_stream(1), shape.vocab)
+    positions = torch.arange(T, ctx, dtype=torch.int32, device=dev)
+    slot0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    xin = torch.empty((T, shape.d_model), dtype=torch.float32, device=dev)
+    hout = torch.empty_like(xin)
+    x1 = torch.empty((1, shape.d_model), dtype=torch.float32, device=dev)
+    h1 = torch.empty_like(x1)
+    torch.cuda.synchronize()
+
+    # decode step as a HIP graph: token and position come from device scalars advanced in-graph
+    use_graph = args.graph == "on"
+    graph = None
+    pos_buf = torch.full((1,), T, dtype=torch.int32, device=dev)
+    idx_buf = torch.zeros(1, dtype=torch.int64, device=dev)
+    tok_buf = torch.zeros(1, dtype=torch.int32, device=dev)
+    if use_graph:
+        # warm the kernels once outside capture
+        torch.index_select(dec_tok, 0, idx_buf, out=tok_buf)
+        st.embed(tok_buf, out=x1)
+        st.decode(x1, slot0, pos_buf, out=h1)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        with torch.cuda.graph(graph, stream=cs):
+            torch.index_select(dec_tok, 0, idx_buf, out=tok_buf)
+            st.embed(tok_buf, out=x1)
+            st.decode(x1, slot0, pos_buf, out=h1)
+            pos_buf.add_(1)
+            idx_buf.add_(1)
+        torch.cuda.synchronize()
+
+    def run_step(ev):
+        ev[0].record(stream)
+        st.embed(prompt, out=xin)
+        st.prefill(xin, 0, 0, out=hout)
+        ev[1].record(stream)
+        if use_graph:
+            pos_buf.fill_(T)
+            idx_buf.zero_()
+            for _ in range(n_dec):
+                graph.replay()
+        else:
+            for i in range(n_dec):
+                st.embed(dec_tok[i:i + 1], out=x1)
+                st.decode(x1, slot0, positions[i:i + 1], out=h1)
+        ev[2].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]  # noqa: E731
+    for w in range(args.warmup):
+        log(f"[bench] warmup step {w + 1}/{args.warmup}")
+        run_step(mk())
+    torch.cuda.synchronize()
+
+    evs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev = mk()
+        run_step(ev)
+        evs.append(ev)
+        log(f"[bench] timed step {k + 1}/{args.steps} enqueued")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prefill_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+
+    # dominant decode kernel (gate/up GEMV + SwiGLU, ~54% of the bytes), timed live with HIP events
+    # on the launch stream over one eager decode pass of the request
+    log("[bench] timing the decode kernels over one eager decode pass")
+    kinds = ("gateup", "qkv", "o", "down", "attn")
+    st.embed(prompt, out=xin)
+    st.prefill(xin, 0, 0, out=hout)
+    st.timing(list(kinds))
+    kern = {k: [0, 0.0] for k in kinds}
+    for i in range(n_dec):
+        st.embed(dec_tok[i:i + 1], out=x1)
+        st.decode(x1, slot0, positions[i:i + 1], out=h1)
+        if i % 64 == 63 or i == n_dec - 1:
+            for k in kinds:
+                n, ms = st.timing_read(k)
+                kern[k][0] += n
+                kern[k][1] += ms
+    st.timing([])
+
+    n_gu, ms_gu = kern["gateup"]
+    gu_bytes = acc.projection_bytes(shape, "gateup", 1)
+    gu_avg_s = ms_gu / 1e3 / max(n_gu, 1)
+    achieved = gu_bytes / gu_avg_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "k_gemv<1, EPI_SWIGLU> (gate/up projection + SwiGLU, B=1)",
+                "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 2), "launches": n_gu}
+    kernel_avg_us = {k: round(v[1] * 1e3 / max(v[0], 1), 2) for k, v in kern.items()}
+
+    dec_ms = float(np.median(decode_ms))
+    pre_ms = float(np.median(prefill_ms))
+    dec_tok_s = n_dec / (dec_ms / 1e3)
+    dec_bytes = sum(acc.decode_step_bytes(shape, 16, [c], first=True) for c in range(T, ctx))
+    dec_gbs = dec_bytes / (dec_ms / 1e3) / 1e9
+    pre_flops = acc.prefill_flops(shape, 16, T)
+    pre_tflops = pre_flops / (pre_ms / 1e3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline_decode(shape, ctx - 1, 16)
+
+    out = {
+        "metric": "stage decode tok/s & HBM GB/s %peak; prefill tok/s & MFMA util",
+        "value": round(dec_tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.median(step_ms)), 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,0.02) bf16 weights, uniform tokens",
+        "config": {"workload": "8B-shaped first stage: embedding + blocks 0..15 of 32, d 4096, 32q/8kv heads, "
+                               "head dim 128, SwiGLU 14336, vocab 128256; batch 1, prefill 512 then decode to ctx 2048",
+                   "prefill_tokens": T, "decode_ctx": ctx, "batch": 1, "decode_graph": use_graph},
+        "decode_ms_per_token": round(dec_ms / n_dec, 4),
+        "decode_hbm_gbs": round(dec_gbs, 1),
+        "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "prefill_tok_s": round(T / (pre_ms / 1e3), 1),
+        "prefill_ms": round(pre_ms, 3),
+        "prefill_tflops": round(pre_tflops, 1),
+        "prefill_mfma_frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kernel_avg_us": kernel_avg_us,
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

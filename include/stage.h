@@ -178,6 +178,29 @@ int stage_kv_export(stage_t* st, int global_block, int slot, int pos0, int n, ui
  * synchronises `stream`.  reset != 0 clears it afterwards. */
 int stage_device_errors(stage_t* st, int reset, uint32_t* count /*host*/, hipStream_t stream);
 
+/* ---- kernel timing for benchmarks ------------------------------------------------------------
+ * When enabled for a set of kernel kinds, the stage records a HIP event pair on the call's stream
+ * around every launch of those kinds and keeps the pairs until they are read.  Off by default;
+ * the events add a few microseconds per timed launch.  Not for use while a stream is being
+ * captured into a graph. */
+enum {
+  STAGE_KT_EMBED = 0,   /* token embedding */
+  STAGE_KT_NORM = 1,    /* RMSNorm row pass (MFMA path and readout) */
+  STAGE_KT_QKV = 2,     /* QKV projection + RoPE + KV write */
+  STAGE_KT_ATTN = 3,    /* attention (decode: partials + merge) */
+  STAGE_KT_O = 4,       /* output projection + residual */
+  STAGE_KT_GATEUP = 5,  /* gate/up projection + SwiGLU */
+  STAGE_KT_DOWN = 6,    /* down projection + residual */
+  STAGE_KT_READOUT = 7, /* readout projection */
+  STAGE_KT_COUNT = 8
+};
+/* Enable timing for the kinds whose bit (1u << kind) is set in kind_mask; 0 disables.  Discards
+ * any recorded pairs. */
+int stage_timing(stage_t* st, uint32_t kind_mask);
+/* Launch count and summed duration (ms) of one kind since timing was enabled or last read;
+ * waits for the recorded events, then forgets them. */
+int stage_timing_read(stage_t* st, int kind, uint64_t* launches /*host*/, double* total_ms /*host*/);
+
 /* Release the handle (the arena stays the caller's). */
 int stage_destroy(stage_t* st);
 

@@ -168,6 +168,10 @@ struct stage {
   uint32_t *counters, *err;
   uint16_t* staging;
   std::string last_error;
+  // kernel timing (benchmarks)
+  uint32_t tmask = 0;
+  std::vector<hipEvent_t> ev_pool;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> recs[STAGE_KT_COUNT];
 };
 
 namespace {
@@ -195,6 +199,38 @@ int fail(stage* st, int code, const char* what) {
     if (_e != hipSuccess) return hip_fail((st), _e, #expr); \
   } while (0)
 
+hipEvent_t take_event(stage* st) {
+  if (st->ev_pool.empty()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  hipEvent_t e = st->ev_pool.back();
+  st->ev_pool.pop_back();
+  return e;
+}
+
+// Event pair around the launches of one kernel kind while timing is enabled for it.
+struct Timed {
+  stage* st;
+  int kind;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  Timed(stage* st_, int kind_, hipStream_t s_) : st(st_), kind(kind_), s(s_) {
+    if (st->tmask & (1u << kind)) {
+      a = take_event(st);
+      b = take_event(st);
+      if (a) (void)hipEventRecord(a, s);
+    }
+  }
+  ~Timed() {
+    if (a && b) {
+      (void)hipEventRecord(b, s);
+      st->recs[kind].push_back({a, b});
+    }
+  }
+};
+
 EpiArgs epi_base(stage* st, int kind) {
   EpiArgs e{};
   e.kind = kind;
@@ -217,10 +253,11 @@ size_t ps_act(const stage* st) { return (size_t)st->s.max_tokens * st->m.d_ffn; 
 // (fused in the GEMV prologue, or a row pass into the bf16 workspace before the GEMM).
 // planes: bf16 planes of the GEMM operand (2, or 3 for the QKV projection whose K/V outputs are
 // rounded to the bf16 cache).
-hipError_t project(stage* st, int rows, const float* x_f32, const float* gain, const uint16_t* x_pair,
+hipError_t project(stage* st, int kind, int rows, const float* x_f32, const float* gain, const uint16_t* x_pair,
                    size_t x_ps, const uint16_t* w, int N, int K, const EpiArgs& e, hipStream_t s,
                    int planes = 2) {
   if (gemv_fits(rows, K)) {
+    Timed t(st, kind, s);
     GemvArgs a{};
     a.x = x_f32 ? x_f32 : nullptr;
     a.gain = gain;
@@ -238,7 +275,11 @@ hipError_t project(stage* st, int rows, const float* x_f32, const float* gain, c
   size_t a_ps = x_ps;
   if (x_f32) {
     NormArgs n{x_f32, gain, st->m.rms_eps, rows, K, nullptr, st->xn, ps_xn(st)};
-    hipError_t err = launch_rmsnorm(n, s);
+    hipError_t err;
+    {
+      Timed t(st, STAGE_KT_NORM, s);
+      err = launch_rmsnorm(n, s);
+    }
     if (err != hipSuccess) return err;
     A = st->xn;
     a_ps = ps_xn(st);
@@ -256,6 +297,7 @@ hipError_t project(stage* st, int rows, const float* x_f32, const float* gain, c
   g.part = st->gemm_part;
   g.counters = st->counters;
   g.e = e;
+  Timed t(st, kind, s);
   return launch_gemm(g, p, s);
 }
 
@@ -268,13 +310,13 @@ hipError_t mlp_half(stage* st, int lb, int rows, const float* x, const float* re
   e1.act = st->act;
   e1.act_ps = ps_act(st);
   e1.ldo = F;
-  hipError_t err = project(st, rows, x, bw.mlp_norm, nullptr, 0, bw.wgu, 2 * F, d, e1, s);
+  hipError_t err = project(st, STAGE_KT_GATEUP, rows, x, bw.mlp_norm, nullptr, 0, bw.wgu, 2 * F, d, e1, s);
   if (err != hipSuccess) return err;
   EpiArgs e2 = epi_base(st, resid ? EPI_RESID : EPI_F32);
   e2.out = out;
   e2.resid = resid;
   e2.ldo = d;
-  return project(st, rows, nullptr, nullptr, st->act, ps_act(st), bw.wd, d, F, e2, s);
+  return project(st, STAGE_KT_DOWN, rows, nullptr, nullptr, st->act, ps_act(st), bw.wd, d, F, e2, s);
 }
 
 // One block over `rows` rows.  Prefill: rp = (slot, pos0), attention over keys [0, pos];
@@ -291,7 +333,7 @@ int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, cons
   e.kc = kc;
   e.vc = vc;
   e.rp = rp;
-  HIP_TRY(st, project(st, rows, x_in, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, 3));
+  HIP_TRY(st, project(st, STAGE_KT_QKV, rows, x_in, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, 3));
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   if (decode) {
     AttnDecodeArgs a{};
@@ -315,6 +357,7 @@ int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, cons
     a.part_lse = st->part_lse;
     a.out = st->attn;
     a.err = st->err;
+    Timed t(st, STAGE_KT_ATTN, s);
     HIP_TRY(st, launch_attn_decode(a, s));
   } else {
     AttnPrefillArgs a{};
@@ -332,13 +375,14 @@ int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, cons
     a.ctx_cap = st->L.ctx_cap;
     a.scale_log2 = scale_log2;
     a.out = st->attn;
+    Timed t(st, STAGE_KT_ATTN, s);
     HIP_TRY(st, launch_attn_prefill(a, s));
   }
   EpiArgs eo = epi_base(st, EPI_RESID);
   eo.out = x_out;
   eo.resid = x_in;
   eo.ldo = d;
-  HIP_TRY(st, project(st, rows, nullptr, nullptr, st->attn, ps_q(st), bw.wo, d, hq * dh, eo, s));
+  HIP_TRY(st, project(st, STAGE_KT_O, rows, nullptr, nullptr, st->attn, ps_q(st), bw.wo, d, hq * dh, eo, s));
   HIP_TRY(st, mlp_half(st, lb, rows, x_out, x_out, x_out, s));
   return STAGE_OK;
 }
@@ -490,7 +534,47 @@ int stage_create(const stage_model_cfg* model, const stage_stage_cfg* stg, void*
 }
 
 int stage_destroy(stage_t* st) {
+  if (!st) return STAGE_OK;
+  for (auto& v : st->recs)
+    for (auto& pr : v) {
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
+  for (auto e : st->ev_pool) (void)hipEventDestroy(e);
   delete st;
+  return STAGE_OK;
+}
+
+int stage_timing(stage_t* st, uint32_t kind_mask) {
+  if (!st) return STAGE_E_INVALID;
+  if (kind_mask >> STAGE_KT_COUNT) return fail(st, STAGE_E_INVALID, "unknown kernel kind in mask");
+  for (auto& v : st->recs) {
+    for (auto& pr : v) {
+      st->ev_pool.push_back(pr.first);
+      st->ev_pool.push_back(pr.second);
+    }
+    v.clear();
+  }
+  st->tmask = kind_mask;
+  return STAGE_OK;
+}
+
+int stage_timing_read(stage_t* st, int kind, uint64_t* launches, double* total_ms) {
+  if (!st || !launches || !total_ms || kind < 0 || kind >= STAGE_KT_COUNT)
+    return fail(st, STAGE_E_INVALID, "bad timing arguments");
+  double tot = 0.0;
+  auto& v = st->recs[kind];
+  for (auto& pr : v) {
+    HIP_TRY(st, hipEventSynchronize(pr.second));
+    float ms = 0.0f;
+    HIP_TRY(st, hipEventElapsedTime(&ms, pr.first, pr.second));
+    tot += ms;
+    st->ev_pool.push_back(pr.first);
+    st->ev_pool.push_back(pr.second);
+  }
+  *launches = v.size();
+  *total_ms = tot;
+  v.clear();
   return STAGE_OK;
 }
 
@@ -554,6 +638,7 @@ int stage_embed(stage_t* st, int n, const int32_t* tokens, float* hidden_out, hi
   if (!(st->s.flags & STAGE_FIRST)) return fail(st, STAGE_E_ROLE, "embed on a non-first stage");
   if (n > st->s.max_tokens) return fail(st, STAGE_E_INVALID, "n > max_tokens");
   HIP_TRY(st, hipSetDevice(st->device));
+  Timed t(st, STAGE_KT_EMBED, s);
   HIP_TRY(st, launch_embed(st->embed, st->m.vocab, st->m.d_model, tokens, n, hidden_out, st->err, s));
   return STAGE_OK;
 }
@@ -584,11 +669,14 @@ int stage_readout(stage_t* st, int n, const float* hin, float* logits, float* no
   HIP_TRY(st, hipSetDevice(st->device));
   const int d = st->m.d_model;
   NormArgs na{hin, st->final_norm, st->m.rms_eps, n, d, normed, st->xn, ps_xn(st)};
-  HIP_TRY(st, launch_rmsnorm(na, s));
+  {
+    Timed t(st, STAGE_KT_NORM, s);
+    HIP_TRY(st, launch_rmsnorm(na, s));
+  }
   EpiArgs e = epi_base(st, EPI_F32);
   e.out = logits;
   e.ldo = st->m.vocab;
-  HIP_TRY(st, project(st, n, nullptr, nullptr, st->xn, ps_xn(st), st->readout, st->m.vocab, d, e, s));
+  HIP_TRY(st, project(st, STAGE_KT_READOUT, n, nullptr, nullptr, st->xn, ps_xn(st), st->readout, st->m.vocab, d, e, s));
   return STAGE_OK;
 }
 

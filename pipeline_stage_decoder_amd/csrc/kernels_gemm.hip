@@ -16,7 +16,7 @@ namespace {
 
 constexpr int BK = 64;
 
-template <int BM, int BN, int WM, int WN, int NP>
+template <int BM, int BN, int WM, int WN, int NP, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   static_assert(WM * WN == 4, "4 waves");
   constexpr int WTM = BM / WM, WTN = BN / WN;       // wave tile
@@ -162,13 +162,13 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     for (int jj = 0; jj < 4; ++jj) {
       const int r = m0 + wm * WTM + i * 16 + (lane >> 4) * 4 + jj;
       if (r >= M) continue;
-      if (e.kind == EPI_F32 || e.kind == EPI_RESID) {
+      if (EPI == EPI_F32 || EPI == EPI_RESID) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int c = n0 + wn * WTN + j * 16 + (lane & 15);
           if (c >= N) continue;
           float v = acc[i][j][jj];
-          if (e.kind == EPI_RESID) v += e.resid[(size_t)r * e.ldo + c];
+          if (EPI == EPI_RESID) v += e.resid[(size_t)r * e.ldo + c];
           e.out[(size_t)r * e.ldo + c] = v;
         }
       } else {
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
           const int c = n0 + wn * WTN + j * 16 + (lane & 15);   // c % 32 < 16, partner c + 16
           if (c >= N) continue;
           const float x0 = acc[i][j][jj], x1 = acc[i][j + 1][jj];
-          if (e.kind == EPI_SWIGLU) {
+          if (EPI == EPI_SWIGLU) {
             store_pair(e.act, e.act_ps, (size_t)r * e.ldo + (c >> 5) * 16 + (c & 15), silu_mul(x0, x1));
           } else {
             int slot, pos;
@@ -212,21 +212,30 @@ GemmPlan gemm_plan(int M, int N, int K) {
   return p;
 }
 
-template <int NP>
-void launch_np(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) {
+namespace {
+
+template <int NP, int EPI>
+void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) {
   switch (p.cfg) {
-    case 0: k_gemm<128, 128, 2, 2, NP><<<grid, 256, 0, s>>>(a); break;
-    case 1: k_gemm<64, 128, 1, 4, NP><<<grid, 256, 0, s>>>(a); break;
-    case 2: k_gemm<32, 128, 1, 4, NP><<<grid, 256, 0, s>>>(a); break;
-    default: k_gemm<16, 128, 1, 4, NP><<<grid, 256, 0, s>>>(a); break;
+    case 0: k_gemm<128, 128, 2, 2, NP, EPI><<<grid, 256, 0, s>>>(a); break;
+    case 1: k_gemm<64, 128, 1, 4, NP, EPI><<<grid, 256, 0, s>>>(a); break;
+    case 2: k_gemm<32, 128, 1, 4, NP, EPI><<<grid, 256, 0, s>>>(a); break;
+    default: k_gemm<16, 128, 1, 4, NP, EPI><<<grid, 256, 0, s>>>(a); break;
   }
 }
 
+}  // namespace
+
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n, p.splitk);
-  if (a.planes == 3)
-    launch_np<3>(a, p, grid, s);
-  else
-    launch_np<2>(a, p, grid, s);
+  switch (a.e.kind) {
+    case EPI_QKV:
+      if (a.planes == 3) launch_cfg<3, EPI_QKV>(a, p, grid, s);
+      else launch_cfg<2, EPI_QKV>(a, p, grid, s);
+      break;
+    case EPI_SWIGLU: launch_cfg<2, EPI_SWIGLU>(a, p, grid, s); break;
+    case EPI_RESID: launch_cfg<2, EPI_RESID>(a, p, grid, s); break;
+    default: launch_cfg<2, EPI_F32>(a, p, grid, s); break;
+  }
   return hipGetLastError();
 }

@@ -28,7 +28,7 @@ PSD_DEV void dot8(const uint4& w, const float4& x0, const float4& x1, float& acc
   acc = fmaf(bf_hi(w.w), x1.w, acc);
 }
 
-template <int NB>
+template <int NB, int EPI>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
   extern __shared__ float4 lds_x[];                // NB rows of K f32 (operand values)
   __shared__ double red[4];
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
     for (int b = 0; b < NB; ++b) {
       if (b < B && lane == b) {
         const float x0 = acc0[b], x1 = acc1[b];
-        switch (e.kind) {
+        switch (EPI) {
           case EPI_F32:
             if (v0) e.out[(size_t)b * e.ldo + r0] = x0;
             if (v1) e.out[(size_t)b * e.ldo + r1] = x1;
@@ -143,6 +143,15 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
   }
 }
 
+template <int EPI>
+void launch_nb(const GemvArgs& a, int nb, int grid, size_t lds, hipStream_t s) {
+  switch (nb) {
+    case 1: k_gemv<1, EPI><<<grid, kGemvThreads, lds, s>>>(a); break;
+    case 2: k_gemv<2, EPI><<<grid, kGemvThreads, lds, s>>>(a); break;
+    default: k_gemv<4, EPI><<<grid, kGemvThreads, lds, s>>>(a); break;
+  }
+}
+
 }  // namespace
 
 bool gemv_fits(int B, int K) {
@@ -156,10 +165,11 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t s) {
   if (grid > 1024) grid = 1024;
   const int nb = a.B <= 1 ? 1 : (a.B <= 2 ? 2 : 4);
   const size_t lds = (size_t)nb * a.K * 4;
-  switch (nb) {
-    case 1: k_gemv<1><<<grid, kGemvThreads, lds, s>>>(a); break;
-    case 2: k_gemv<2><<<grid, kGemvThreads, lds, s>>>(a); break;
-    default: k_gemv<4><<<grid, kGemvThreads, lds, s>>>(a); break;
+  switch (a.e.kind) {
+    case EPI_F32: launch_nb<EPI_F32>(a, nb, grid, lds, s); break;
+    case EPI_RESID: launch_nb<EPI_RESID>(a, nb, grid, lds, s); break;
+    case EPI_SWIGLU: launch_nb<EPI_SWIGLU>(a, nb, grid, lds, s); break;
+    default: launch_nb<EPI_QKV>(a, nb, grid, lds, s); break;
   }
   return hipGetLastError();
 }

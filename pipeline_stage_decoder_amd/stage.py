@@ -18,6 +18,8 @@ STAGE_OK, STAGE_E_INVALID, STAGE_E_UNSUPPORTED, STAGE_E_DOES_NOT_FIT, STAGE_E_RO
     STAGE_E_HIP = range(7)
 STAGE_FIRST, STAGE_LAST = 1, 2
 
+KERNEL_KINDS = {"embed": 0, "norm": 1, "qkv": 2, "attn": 3, "o": 4, "gateup": 5, "down": 6, "readout": 7}
+
 ROLES = {
     "embed": 0, "attn_norm": 1, "wq": 2, "wk": 3, "wv": 4, "wo": 5, "mlp_norm": 6, "wgate": 7,
     "wup": 8, "wdown": 9, "final_norm": 10, "readout": 11,
@@ -65,6 +67,8 @@ EXPORTS = {
     "stage_kv_import": [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp],
     "stage_kv_export": [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp],
     "stage_device_errors": [_vp, _i32, ctypes.POINTER(ctypes.c_uint32), _vp],
+    "stage_timing": [_vp, ctypes.c_uint32],
+    "stage_timing_read": [_vp, _i32, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_double)],
     "stage_destroy": [_vp],
     "stage_status_str": [_i32],
     "stage_last_error": [_vp],
@@ -255,3 +259,19 @@ class Stage:
         self._check(lib().stage_device_errors(self._h, int(reset), ctypes.byref(c), _stream(stream)),
                     "stage_device_errors")
         return int(c.value)
+
+    # -- kernel timing -----------------------------------------------------------------------------
+    def timing(self, kinds=()):
+        """Record HIP event pairs around the launches of the given kernel kinds (names of KERNEL_KINDS)."""
+        mask = 0
+        for k in kinds:
+            mask |= 1 << KERNEL_KINDS[k]
+        self._check(lib().stage_timing(self._h, mask), "stage_timing")
+
+    def timing_read(self, kind: str):
+        """(launches, total ms) of one kind since timing was enabled or last read."""
+        n = ctypes.c_uint64(0)
+        ms = ctypes.c_double(0.0)
+        self._check(lib().stage_timing_read(self._h, KERNEL_KINDS[kind], ctypes.byref(n), ctypes.byref(ms)),
+                    "stage_timing_read")
+        return int(n.value), float(ms.value)
