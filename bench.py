@@ -130,42 +130,38 @@ def main():
     h1 = torch.empty_like(x1)
     torch.cuda.synchronize()
 
-    # decode step as a HIP graph: token and position come from device scalars advanced in-graph
+    # decode steps as HIP graphs: each graph replays GRAPH_STEPS consecutive decode steps with their
+    # token and position pointers baked in, so a replay launches only the stage's own kernels
     use_graph = args.graph == "on"
-    graph = None
-    pos_buf = torch.full((1,), T, dtype=torch.int32, device=dev)
-    idx_buf = torch.zeros(1, dtype=torch.int64, device=dev)
-    tok_buf = torch.zeros(1, dtype=torch.int32, device=dev)
+    graph_steps = 128
+    graphs = []
     if use_graph:
-        # warm the kernels once outside capture
-        torch.index_select(dec_tok, 0, idx_buf, out=tok_buf)
-        st.embed(tok_buf, out=x1)
-        st.decode(x1, slot0, pos_buf, out=h1)
+        st.embed(dec_tok[:1], out=x1)                # warm every kernel once outside capture
+        st.decode(x1, slot0, positions[:1], out=h1)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
         cs = torch.cuda.Stream()
-        with torch.cuda.graph(graph, stream=cs):
-            torch.index_select(dec_tok, 0, idx_buf, out=tok_buf)
-            st.embed(tok_buf, out=x1)
-            st.decode(x1, slot0, pos_buf, out=h1)
-            pos_buf.add_(1)
-            idx_buf.add_(1)
+        for g0 in range(0, n_dec - n_dec % graph_steps, graph_steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                for i in range(g0, g0 + graph_steps):
+                    st.embed(dec_tok[i:i + 1], out=x1)
+                    st.decode(x1, slot0, positions[i:i + 1], out=h1)
+            graphs.append(g)
         torch.cuda.synchronize()
+        log(f"[bench] captured {len(graphs)} decode graphs of {graph_steps} steps")
 
     def run_step(ev):
         ev[0].record(stream)
         st.embed(prompt, out=xin)
         st.prefill(xin, 0, 0, out=hout)
         ev[1].record(stream)
-        if use_graph:
-            pos_buf.fill_(T)
-            idx_buf.zero_()
-            for _ in range(n_dec):
-                graph.replay()
-        else:
-            for i in range(n_dec):
-                st.embed(dec_tok[i:i + 1], out=x1)
-                st.decode(x1, slot0, positions[i:i + 1], out=h1)
+        done = 0
+        for g in graphs:
+            g.replay()
+            done += graph_steps
+        for i in range(done, n_dec):
+            st.embed(dec_tok[i:i + 1], out=x1)
+            st.decode(x1, slot0, positions[i:i + 1], out=h1)
         ev[2].record(stream)
 
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]  # noqa: E731

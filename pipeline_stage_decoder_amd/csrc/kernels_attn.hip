@@ -18,7 +18,9 @@
 // puts a column's values in the same lane as its softmax state, so rescaling needs no shuffles.
 //
 // Decode: work-group = (split of `chunk` keys, KV head, batch row); its 4 waves take a quarter of
-// the chunk each and merge through LDS; a second kernel merges the splits in split order.
+// the chunk each and merge through LDS; the last split of a (row, KV head) to finish (one atomic
+// counter each, re-armed by that split) merges all splits in split order, so the result does not
+// depend on which split finishes last.
 // Prefill: work-group = 64 columns (consecutive queries x the group's heads) of one KV head; every
 // wave walks keys 0 .. its last query's position.
 #include "kernels.h"
@@ -44,18 +46,32 @@ template <int DH, typename Visible>
 PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
                        int kb, int kend, float scale_log2, Visible visible) {
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-  f32x4_t sc[2];
+  // issue every K and V load of the step first: one memory round trip per step
+  uint4 kr[2][DH / 32];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int key = kb + key_of_row(col, c);
     const bool ok = key < kend;
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks)
+      kr[c][ks] = ok ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * DH + ks * 32 + grp * 8)
+                     : make_uint4(0, 0, 0, 0);
+  }
+  const int kg = kb + grp * 8;              // this lane's 8 keys in the PV product
+  const int nvalid = kend - kg;             // keys of the group below kend
+  uint4 vr[DH / 16];
+#pragma unroll
+  for (int dt = 0; dt < DH / 16; ++dt)
+    vr[dt] = nvalid > 0 ? *reinterpret_cast<const uint4*>(vbase + ((size_t)(kg >> 3) * DH + dt * 16 + col) * 8)
+                        : make_uint4(0, 0, 0, 0);
+  f32x4_t sc[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
     sc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DH / 32; ++ks) {
-      uint4 kv = make_uint4(0, 0, 0, 0);
-      if (ok) kv = *reinterpret_cast<const uint4*>(kbase + (size_t)key * DH + ks * 32 + grp * 8);
-      sc[c] = mfma16(as_bf16x8(kv), st.qh[ks], sc[c]);
-      sc[c] = mfma16(as_bf16x8(kv), st.ql[ks], sc[c]);
+      sc[c] = mfma16(as_bf16x8(kr[c][ks]), st.qh[ks], sc[c]);
+      sc[c] = mfma16(as_bf16x8(kr[c][ks]), st.ql[ks], sc[c]);
     }
   }
   float s[8];
@@ -87,20 +103,15 @@ PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const 
   for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] *= alpha;
   uint4 phi, plo;
   split_hi_lo(p, phi, plo);
-  const int kg = kb + grp * 8;              // this lane's 8 keys
-  const int nvalid = kend - kg;             // keys of the group below kend
 #pragma unroll
   for (int dt = 0; dt < DH / 16; ++dt) {
-    uint4 vv = make_uint4(0, 0, 0, 0);
-    if (nvalid > 0) {
-      vv = *reinterpret_cast<const uint4*>(vbase + ((size_t)(kg >> 3) * DH + dt * 16 + col) * 8);
-      if (nvalid < 8) {
-        uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+    uint4 vv = vr[dt];
+    if (nvalid < 8) {
+      uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        vv = make_uint4(w[0], w[1], w[2], w[3]);
-      }
+      for (int e = 0; e < 8; ++e)
+        if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      vv = make_uint4(w[0], w[1], w[2], w[3]);
     }
     st.o[dt] = mfma16(as_bf16x8(vv), as_bf16x8(phi), st.o[dt]);
     st.o[dt] = mfma16(as_bf16x8(vv), as_bf16x8(plo), st.o[dt]);
@@ -133,14 +144,25 @@ template <int DH>
 __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
   __shared__ float sm[4][16], sl[4][16];
   __shared__ float so[4][DH][17];
+  __shared__ int last_flag;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int slot = a.slots[b], pos = a.pos[b];
-  if (slot < 0 || slot >= a.max_slots || pos < 0 || pos >= a.ctx_cap) return;
+  const int G = a.hq / a.hkv;
+  if (slot < 0 || slot >= a.max_slots || pos < 0 || pos >= a.ctx_cap) {
+    // out-of-range row: zero attention output (written once, by split 0)
+    if (split == 0)
+      for (int idx = threadIdx.x; idx < G * DH; idx += 256) {
+        const size_t o = (size_t)b * a.hq * DH + (size_t)kvh * G * DH + idx;
+        a.out[o] = 0;
+        a.out[a.out_ps + o] = 0;
+      }
+    return;
+  }
   const int ctx = pos + 1;
   const int k0 = split * a.chunk;
   if (k0 >= ctx) return;
+  const int ns = (ctx + a.chunk - 1) / a.chunk;
   const int k1 = min(k0 + a.chunk, ctx);
-  const int G = a.hq / a.hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int sub = a.chunk >> 2;
   const int w0 = k0 + wave * sub, w1 = min(w0 + sub, k1);
@@ -182,33 +204,49 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
     a.part_o[row * DH + d] = acc / L;
     if (d == 0) a.part_lse[row] = mm + log2f(L);
   }
-}
 
-// merge the splits of one (row, head) in split order -> bf16 attention output
-template <int DH>
-__global__ __launch_bounds__(64) void k_attn_merge(AttnDecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int slot = a.slots[b], pos = a.pos[b];
-  uint16_t* out = a.out + (size_t)b * a.hq * DH + (size_t)h * DH;
-  if (slot < 0 || slot >= a.max_slots || pos < 0 || pos >= a.ctx_cap) {
-    for (int d = lane; d < DH; d += 64) out[d] = out[a.out_ps + d] = 0;
-    return;
+  // the last split of this (row, KV head) to finish merges all splits in split order
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(&a.counters[b * a.hkv + kvh], 1u);
+    last_flag = prev == (unsigned)(ns - 1);
+    if (last_flag) a.counters[b * a.hkv + kvh] = 0u;
   }
-  const int ns = (pos + a.chunk) / a.chunk;   // ceil((pos + 1) / chunk)
-  const size_t row = ((size_t)b * a.hq + h) * a.nsplit;
-  float mm = kNegInf;
-  for (int s = 0; s < ns; ++s) mm = fmaxf(mm, a.part_lse[row + s]);
-  constexpr int PER = DH / 64;
-  float acc[PER] = {};
-  float L = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float f = exp2f(a.part_lse[row + s] - mm);
-    L += f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += f * a.part_o[(row + s) * DH + lane * PER + i];
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+  // split weights w[h][sp] = exp2(lse - max) through LDS, then every output reads its ns partials
+  // with independent loads
+  float* wts = &so[0][0][0];                 // reuse: G * ns <= 16 * nsplit floats
+  float* tot = &sl[0][0];
+  const size_t row0 = ((size_t)b * a.hq + kvh * G) * a.nsplit;
+  for (int idx = threadIdx.x; idx < G * ns; idx += 256) {
+    const int h = idx / ns, sp = idx - h * ns;
+    wts[idx] = __builtin_nontemporal_load(a.part_lse + row0 + (size_t)h * a.nsplit + sp);
   }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) store_pair(out, a.out_ps, lane * PER + i, acc[i] / L);
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float mm = kNegInf;
+    for (int sp = 0; sp < ns; ++sp) mm = fmaxf(mm, wts[h * ns + sp]);
+    float L = 0.0f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float f = exp2f(wts[h * ns + sp] - mm);
+      wts[h * ns + sp] = f;
+      L += f;
+    }
+    tot[h] = L;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * DH; idx += 256) {
+    const int h = idx / DH, d = idx - h * DH;
+    const float* po = a.part_o + (row0 + (size_t)h * a.nsplit) * DH + d;
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int sp = 0; sp < ns; ++sp) acc += wts[h * ns + sp] * __builtin_nontemporal_load(po + (size_t)sp * DH);
+    store_pair(a.out, a.out_ps, (size_t)b * a.hq * DH + (size_t)(kvh * G + h) * DH + d, acc / tot[h]);
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -270,10 +308,8 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
   dim3 grid(a.nsplit, a.hkv, a.B);
   if (a.dh == 128) {
     k_attn_decode<128><<<grid, 256, 0, s>>>(a);
-    k_attn_merge<128><<<dim3(a.hq, a.B), 64, 0, s>>>(a);
   } else {
     k_attn_decode<64><<<grid, 256, 0, s>>>(a);
-    k_attn_merge<64><<<dim3(a.hq, a.B), 64, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -13,6 +13,8 @@
 
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kGemvThreads = 256;
 constexpr int kGemvUnroll = 8;
 constexpr int kGemvMaxLds = 64 * 1024;
@@ -35,6 +37,31 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
   const int K = a.K, K8 = K >> 3, B = a.B;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* xs = reinterpret_cast<float*>(lds_x);
+
+  const int N = a.N;
+  const int npairs = ((N + 31) >> 5) << 4;
+  const int nwaves = gridDim.x * (kGemvThreads / 64);
+  const int p_first = blockIdx.x * (kGemvThreads / 64) + wave;
+  const int nchunks = (K8 + 64 * kGemvUnroll - 1) / (64 * kGemvUnroll);
+  // weights of (pair pp, chunk cc), zero outside the matrix
+  auto load_item = [&](int pp, int cc, uint4* d0, uint4* d1) {
+    const int q0r = ((pp >> 4) << 5) + (pp & 15), q1r = q0r + 16;
+    const bool ok0 = pp < npairs && q0r < N, ok1 = pp < npairs && q1r < N;
+    const u32x4* w0 = reinterpret_cast<const u32x4*>(a.w + (size_t)(ok0 ? q0r : 0) * K);
+    const u32x4* w1 = reinterpret_cast<const u32x4*>(a.w + (size_t)(ok1 ? q1r : 0) * K);
+#pragma unroll
+    for (int u = 0; u < kGemvUnroll; ++u) {
+      const int idx = cc * 64 * kGemvUnroll + u * 64 + lane;
+      const bool in = idx < K8;
+      u32x4 t0 = {0, 0, 0, 0}, t1 = {0, 0, 0, 0};
+      if (in && ok0) t0 = __builtin_nontemporal_load(w0 + idx);
+      if (in && ok1) t1 = __builtin_nontemporal_load(w1 + idx);
+      d0[u] = make_uint4(t0.x, t0.y, t0.z, t0.w);
+      d1[u] = make_uint4(t1.x, t1.y, t1.z, t1.w);
+    }
+  };
+  uint4 c0[kGemvUnroll], c1[kGemvUnroll];
+  load_item(p_first, 0, c0, c1);
 
   // ---- prologue: input rows -> f32 operand values in LDS ---------------------------------------
   if (a.x) {
@@ -68,28 +95,25 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
   }
   __syncthreads();
 
-  // ---- row pairs ------------------------------------------------------------------------------
-  const int N = a.N;
-  const int npairs = ((N + 31) >> 5) << 4;
-  const int nwaves = gridDim.x * (kGemvThreads / 64);
-  for (int p = blockIdx.x * (kGemvThreads / 64) + wave; p < npairs; p += nwaves) {
-    const int r0 = ((p >> 4) << 5) + (p & 15), r1 = r0 + 16;
-    const bool v0 = r0 < N, v1 = r1 < N;
-    const uint4* w0 = reinterpret_cast<const uint4*>(a.w + (size_t)(v0 ? r0 : 0) * K);
-    const uint4* w1 = reinterpret_cast<const uint4*>(a.w + (size_t)(v1 ? r1 : 0) * K);
+  // ---- row pairs -------------------------------------------------------------------------------
+  // Work items are (pair, K chunk of 64 * kGemvUnroll 16-byte loads per row); the next item's
+  // weights are loaded before the current one is consumed, and the first item's before the
+  // prologue above, so the weight stream never waits on the norm or on a reduction.
+  for (int p = p_first; p < npairs; p += nwaves) {
     float acc0[NB], acc1[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc0[b] = acc1[b] = 0.0f;
-
-    for (int base = 0; base < K8; base += 64 * kGemvUnroll) {
-      uint4 q0[kGemvUnroll], q1[kGemvUnroll];
-#pragma unroll
-      for (int u = 0; u < kGemvUnroll; ++u) {
-        const int idx = base + u * 64 + lane;
-        const bool ok = idx < K8;
-        q0[u] = (ok && v0) ? w0[idx] : make_uint4(0, 0, 0, 0);
-        q1[u] = (ok && v1) ? w1[idx] : make_uint4(0, 0, 0, 0);
+    const int r0 = ((p >> 4) << 5) + (p & 15), r1 = r0 + 16;
+    const bool v0 = r0 < N, v1 = r1 < N;
+    for (int c = 0; c < nchunks; ++c) {
+      int pn = p, cn = c + 1;
+      if (cn == nchunks) {
+        pn = p + nwaves;
+        cn = 0;
       }
+      uint4 n0[kGemvUnroll], n1[kGemvUnroll];
+      load_item(pn, cn, n0, n1);
+      const int base = c * 64 * kGemvUnroll;
 #pragma unroll
       for (int u = 0; u < kGemvUnroll; ++u) {
         const int idx = base + u * 64 + lane;
@@ -97,10 +121,15 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             const float4 xa = lds_x[(b * K8 + idx) * 2], xb = lds_x[(b * K8 + idx) * 2 + 1];
-            dot8(q0[u], xa, xb, acc0[b]);
-            dot8(q1[u], xa, xb, acc1[b]);
+            dot8(c0[u], xa, xb, acc0[b]);
+            dot8(c1[u], xa, xb, acc1[b]);
           }
         }
+      }
+#pragma unroll
+      for (int u = 0; u < kGemvUnroll; ++u) {
+        c0[u] = n0[u];
+        c1[u] = n1[u];
       }
     }
 #pragma unroll
