@@ -71,13 +71,18 @@ typedef struct {
   float rope_theta;       /* RoPE base; angle(pos, i) = pos * theta^(-2i/Dh) */
 } stage_model_cfg;
 
-#define STAGE_FIRST 1u /* owns the token embedding */
-#define STAGE_LAST 2u  /* owns the final RMSNorm and the readout */
+#define STAGE_FIRST 1u  /* owns the token embedding */
+#define STAGE_LAST 2u   /* owns the final RMSNorm and the readout */
+#define STAGE_KV_F32 4u /* KV cache elements are F32 instead of bf16 (twice the bytes).  With bf16,
+                           a K/V value that a float64 reference and the GPU's f32 sums put on
+                           different sides of a bf16 rounding boundary perturbs attention, which
+                           flips more roundings in later blocks; F32 storage keeps a deep stage
+                           within 1e-3 of a float64 reference. */
 
 typedef struct {
   int32_t block_begin; /* first GLOBAL block id (inclusive) */
   int32_t block_end;   /* one past the last GLOBAL block id; block_begin <= block_end */
-  uint32_t flags;      /* STAGE_FIRST | STAGE_LAST */
+  uint32_t flags;      /* STAGE_FIRST | STAGE_LAST | STAGE_KV_F32 */
   int32_t max_slots;   /* KV slots (sequences) */
   int32_t max_ctx;     /* positions per slot: every position used is < max_ctx */
   int32_t max_tokens;  /* rows per call: prefill T and decode B are <= max_tokens */
@@ -85,7 +90,7 @@ typedef struct {
 
 typedef struct {
   uint64_t weight_bytes;    /* bf16 matrices, F32 norm gains */
-  uint64_t kv_bytes;        /* bf16 K and V for every owned block and slot */
+  uint64_t kv_bytes;        /* K and V (bf16, or F32 with STAGE_KV_F32) for every owned block and slot */
   uint64_t table_bytes;     /* RoPE cos/sin table (F32) */
   uint64_t workspace_bytes; /* per-call activations, split-K and split-KV partials, counters */
   uint64_t total_bytes;     /* arena size stage_create needs (sum of the above with alignment) */
@@ -167,11 +172,12 @@ int stage_mlp(stage_t* st, int global_block, int n, const float* hidden_in, floa
 /* Copy KV positions [0, n_pos) of every owned block from src_slot to dst_slot. */
 int stage_kv_copy(stage_t* st, int src_slot, int dst_slot, int n_pos, hipStream_t stream);
 
-/* Write / read KV of one owned block and slot at positions [pos0, pos0+n): k, v are device bf16
- * [n, Hkv, Dh] (K after RoPE, as attention reads it). */
-int stage_kv_import(stage_t* st, int global_block, int slot, int pos0, int n, const uint16_t* k,
-                    const uint16_t* v, hipStream_t stream);
-int stage_kv_export(stage_t* st, int global_block, int slot, int pos0, int n, uint16_t* k, uint16_t* v,
+/* Write / read KV of one owned block and slot at positions [pos0, pos0+n): k, v are device
+ * [n, Hkv, Dh] arrays in the cache's element type -- bf16 bits, or F32 with STAGE_KV_F32 -- with K
+ * after RoPE, as attention reads it. */
+int stage_kv_import(stage_t* st, int global_block, int slot, int pos0, int n, const void* k, const void* v,
+                    hipStream_t stream);
+int stage_kv_export(stage_t* st, int global_block, int slot, int pos0, int n, void* k, void* v,
                     hipStream_t stream);
 
 /* Device-side error counter (rows skipped for out-of-range tokens, slots or positions); reading it

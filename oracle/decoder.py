@@ -27,9 +27,10 @@ Readings where the pages are silent (each listed in the design notes):
 RMSNorm is x * rsqrt(mean(x^2) + eps) * g (no mean subtraction, eps inside the root);
 RoPE is the rotate-half form over the whole head, angle pos * theta^(-2i/Dh), absolute 0-based
 positions; the residual stream is F32 inside a stage as well as across it; the readout is untied.
-Precision: weights are bf16 (the seeded inputs), the KV cache stores K (after RoPE) and V as bf16,
-and nothing else is rounded -- every activation, score and sum is float64, and tensors the method
-hands over as F32 (stage output, final hidden, logits, MLP partials) are rounded to float32 once.
+Precision: weights are bf16 (the seeded inputs), the KV cache stores K (after RoPE) and V as bf16
+(or, for a stage built with an F32 cache, as float32), and nothing else is rounded -- every
+activation, score and sum is float64, and tensors the method hands over as F32 (stage output, final
+hidden, logits, MLP partials) are rounded to float32 once.
 
 Pins: every function here is checked by ``tests/test_oracle_pins.py`` against brute-force loops,
 closed forms and invariants the pages fix (see that file).  Absolute forward values are not
@@ -149,6 +150,24 @@ def gqa_expand(kv: np.ndarray, n_q_heads: int) -> np.ndarray:
     return np.repeat(kv, group, axis=1)
 
 
+def attention_gqa(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray, k_pos: np.ndarray,
+                  scale: float) -> np.ndarray:
+    """attention_partial's output for GQA without repeating K/V: q [Tq, Hq, D] over k, v
+    [Tk, Hkv, D], query head h reading KV head h // (Hq / Hkv).  Float64 throughout."""
+    tq, hq, dd = q.shape
+    hkv = k.shape[1]
+    qg = f64(q).reshape(tq, hkv, hq // hkv, dd)                    # [Tq, Hkv, G, D]
+    scores = np.einsum("qcgd,kcd->cgqk", qg, f64(k)) * scale       # [Hkv, G, Tq, Tk]
+    masked = k_pos[None, None, None, :] > q_pos[None, None, :, None]
+    scores = np.where(masked, -np.inf, scores)
+    top = scores.max(axis=-1, keepdims=True)
+    top = np.where(np.isinf(top), 0.0, top)
+    w = np.exp(scores - top)
+    z = w.sum(axis=-1, keepdims=True)
+    out = np.einsum("cgqk,kcd->qcgd", w / np.where(z > 0, z, 1.0), f64(v))
+    return out.reshape(tq, hq, dd)
+
+
 def silu_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
     """silu(gate) * up in float64 (the chapter's ``F.silu(gate) * up``)."""
     g = f64(gate)
@@ -186,9 +205,11 @@ class Stage:
     """
 
     def __init__(self, dims: Dims, begin: int, end: int, first: bool, last: bool, weights: dict,
-                 max_ctx: int):
+                 max_ctx: int, kv_dtype: str = "bf16"):
+        assert kv_dtype in ("bf16", "f32")
         self.c, self.begin, self.end, self.first, self.last = dims, begin, end, first, last
         self.w, self.max_ctx = weights, max_ctx
+        self.kv_dtype = kv_dtype
         self.kv = {}                      # slot -> (K, V) float32 [blocks, ctx, Hkv, Dh]
 
     def _cache(self, slot: int):
@@ -212,8 +233,9 @@ class Stage:
         k = linear64(h, w[("wk", b)]).reshape(m_rows, hkv, dh)
         v = linear64(h, w[("wv", b)]).reshape(m_rows, hkv, dh)
         q = rope(q, positions, c.rope_theta)
-        k = round_bf16(rope(k, positions, c.rope_theta))                      # bf16 KV cache
-        v = round_bf16(v)
+        store = round_bf16 if self.kv_dtype == "bf16" else (lambda t: np.asarray(t, np.float32))
+        k = store(rope(k, positions, c.rope_theta))                           # the KV cache's format
+        v = store(v)
         lb = b - self.begin
         for m in range(m_rows):                                                # write KV first
             kc, vc = self._cache(int(slots[m]))
@@ -225,10 +247,8 @@ class Stage:
             rows = np.nonzero(slots == s)[0]
             kc, vc = self._cache(int(s))
             n_keys = int(positions[rows].max()) + 1
-            kk = gqa_expand(kc[lb, :n_keys], hq)
-            vv = gqa_expand(vc[lb, :n_keys], hq)
-            o, _ = attention_partial(q[rows], kk, vv, positions[rows].astype(np.int64),
-                                     np.arange(n_keys), scale)
+            o = attention_gqa(q[rows], kc[lb, :n_keys], vc[lb, :n_keys], positions[rows].astype(np.int64),
+                              np.arange(n_keys), scale)
             attn[rows] = o.reshape(len(rows), hq * dh)
         x1 = (x + linear64(attn, w[("wo", b)])).astype(np.float32)
         h2 = rms_norm(x1, bf16_to_f32(w[("mlp_norm", b)]), c.rms_eps)

@@ -58,7 +58,7 @@ int validate(const stage_model_cfg* m, const stage_stage_cfg* s) {
   if (s->block_begin < 0 || s->block_end < s->block_begin || s->block_end > m->n_blocks_total)
     return STAGE_E_INVALID;
   if (s->max_slots <= 0 || s->max_ctx <= 0 || s->max_tokens <= 0) return STAGE_E_INVALID;
-  if ((s->flags & ~(STAGE_FIRST | STAGE_LAST)) != 0) return STAGE_E_INVALID;
+  if ((s->flags & ~(STAGE_FIRST | STAGE_LAST | STAGE_KV_F32)) != 0) return STAGE_E_INVALID;
   if ((s->flags & (STAGE_FIRST | STAGE_LAST)) && m->vocab <= 0) return STAGE_E_INVALID;
   // what the kernels cover (refused before anything is allocated)
   if (m->head_dim != 64 && m->head_dim != 128) return STAGE_E_UNSUPPORTED;
@@ -110,9 +110,10 @@ Layout make_layout(const stage_model_cfg& m, const stage_stage_cfg& s) {
   L.plan.weight_bytes = off;
   // KV cache
   const uint64_t kv_start = off;
+  const uint64_t kvb = (s.flags & STAGE_KV_F32) ? 4 : 2;
   L.kv_block_elems = (uint64_t)s.max_slots * hkv * L.ctx_cap * dh;
-  L.kcache = take(L.kv_block_elems * nb * 2);
-  L.vcache = take(L.kv_block_elems * nb * 2);
+  L.kcache = take(L.kv_block_elems * nb * kvb);
+  L.vcache = take(L.kv_block_elems * nb * kvb);
   L.plan.kv_bytes = off - kv_start;
   // tables
   const uint64_t tab_start = off;
@@ -169,7 +170,9 @@ struct stage {
   uint16_t* embed;
   uint16_t* readout;
   float* final_norm;
-  uint16_t *kcache, *vcache;
+  uint8_t *kcache, *vcache;
+  int kv_f32;
+  size_t kvb;  // bytes per KV element
   double2* rope;
   uint16_t *xn, *q, *attn, *act;
   float *part_o, *part_lse, *gemm_part;
@@ -333,9 +336,10 @@ int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, cons
               hipStream_t s) {
   const BlockW& bw = st->blocks[lb];
   const int d = st->m.d_model, hq = st->m.n_q_heads, hkv = st->m.n_kv_heads, dh = st->m.head_dim;
-  uint16_t* kc = st->kcache + (uint64_t)lb * st->L.kv_block_elems;
-  uint16_t* vc = st->vcache + (uint64_t)lb * st->L.kv_block_elems;
+  uint8_t* kc = st->kcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb;
+  uint8_t* vc = st->vcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb;
   EpiArgs e = epi_base(st, EPI_QKV);
+  e.kv_f32 = st->kv_f32;
   e.q = st->q;
   e.q_ps = ps_q(st);
   e.kc = kc;
@@ -350,6 +354,7 @@ int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, cons
     a.out_ps = ps_q(st);
     a.kc = kc;
     a.vc = vc;
+    a.kv_f32 = st->kv_f32;
     a.slots = rp.slots;
     a.pos = rp.pos;
     a.B = rows;
@@ -375,6 +380,7 @@ int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, cons
     a.out_ps = ps_q(st);
     a.kc = kc;
     a.vc = vc;
+    a.kv_f32 = st->kv_f32;
     a.slot = rp.slot;
     a.pos0 = rp.pos0;
     a.T = rows;
@@ -503,8 +509,10 @@ int stage_create(const stage_model_cfg* model, const stage_stage_cfg* stg, void*
   st->embed = (stg->flags & STAGE_FIRST) ? at<uint16_t>(st, L.embed) : nullptr;
   st->readout = (stg->flags & STAGE_LAST) ? at<uint16_t>(st, L.readout) : nullptr;
   st->final_norm = (stg->flags & STAGE_LAST) ? at<float>(st, L.final_norm) : nullptr;
-  st->kcache = at<uint16_t>(st, L.kcache);
-  st->vcache = at<uint16_t>(st, L.vcache);
+  st->kcache = at<uint8_t>(st, L.kcache);
+  st->vcache = at<uint8_t>(st, L.vcache);
+  st->kv_f32 = (stg->flags & STAGE_KV_F32) ? 1 : 0;
+  st->kvb = st->kv_f32 ? 4 : 2;
   st->rope = at<double2>(st, L.rope);
   st->xn = at<uint16_t>(st, L.xn);
   st->q = at<uint16_t>(st, L.q);
@@ -711,14 +719,15 @@ int stage_kv_copy(stage_t* st, int src_slot, int dst_slot, int n_pos, hipStream_
   const int hkv = st->m.n_kv_heads, dh = st->m.head_dim, cap = st->L.ctx_cap;
   const size_t slot_elems = (size_t)hkv * cap * dh;
   const size_t vgroups = (size_t)(n_pos + 7) / 8;
+  const size_t eb = st->kvb;
   for (int lb = 0; lb < st->nb; ++lb) {
-    uint16_t* kc = st->kcache + (uint64_t)lb * st->L.kv_block_elems;
-    uint16_t* vc = st->vcache + (uint64_t)lb * st->L.kv_block_elems;
+    uint8_t* kc = st->kcache + (uint64_t)lb * st->L.kv_block_elems * eb;
+    uint8_t* vc = st->vcache + (uint64_t)lb * st->L.kv_block_elems * eb;
     // per KV head: K rows [0, n_pos) and the V groups covering them are contiguous
-    HIP_TRY(st, hipMemcpy2DAsync(kc + dst_slot * slot_elems, (size_t)cap * dh * 2, kc + src_slot * slot_elems,
-                                 (size_t)cap * dh * 2, (size_t)n_pos * dh * 2, hkv, hipMemcpyDeviceToDevice, s));
-    HIP_TRY(st, hipMemcpy2DAsync(vc + dst_slot * slot_elems, (size_t)cap * dh * 2, vc + src_slot * slot_elems,
-                                 (size_t)cap * dh * 2, vgroups * dh * 8 * 2, hkv, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(st, hipMemcpy2DAsync(kc + dst_slot * slot_elems * eb, (size_t)cap * dh * eb, kc + src_slot * slot_elems * eb,
+                                 (size_t)cap * dh * eb, (size_t)n_pos * dh * eb, hkv, hipMemcpyDeviceToDevice, s));
+    HIP_TRY(st, hipMemcpy2DAsync(vc + dst_slot * slot_elems * eb, (size_t)cap * dh * eb, vc + src_slot * slot_elems * eb,
+                                 (size_t)cap * dh * eb, vgroups * dh * 8 * eb, hkv, hipMemcpyDeviceToDevice, s));
   }
   return STAGE_OK;
 }
@@ -732,26 +741,26 @@ static int kv_io_check(stage_t* st, int global_block, int slot, int pos0, int n,
   return STAGE_OK;
 }
 
-int stage_kv_import(stage_t* st, int global_block, int slot, int pos0, int n, const uint16_t* k,
-                    const uint16_t* v, hipStream_t s) {
-  const int rc = kv_io_check(st, global_block, slot, pos0, n, k, v);
-  if (rc != STAGE_OK) return rc;
-  HIP_TRY(st, hipSetDevice(st->device));
-  const int lb = global_block - st->s.block_begin;
-  HIP_TRY(st, launch_kv_import(st->kcache + (uint64_t)lb * st->L.kv_block_elems,
-                               st->vcache + (uint64_t)lb * st->L.kv_block_elems, st->m.n_kv_heads,
-                               st->m.head_dim, st->L.ctx_cap, slot, pos0, n, k, v, s));
-  return STAGE_OK;
-}
-
-int stage_kv_export(stage_t* st, int global_block, int slot, int pos0, int n, uint16_t* k, uint16_t* v,
+int stage_kv_import(stage_t* st, int global_block, int slot, int pos0, int n, const void* k, const void* v,
                     hipStream_t s) {
   const int rc = kv_io_check(st, global_block, slot, pos0, n, k, v);
   if (rc != STAGE_OK) return rc;
   HIP_TRY(st, hipSetDevice(st->device));
   const int lb = global_block - st->s.block_begin;
-  HIP_TRY(st, launch_kv_export(st->kcache + (uint64_t)lb * st->L.kv_block_elems,
-                               st->vcache + (uint64_t)lb * st->L.kv_block_elems, st->m.n_kv_heads,
+  HIP_TRY(st, launch_kv_import(st->kcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb,
+                               st->vcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb, st->kv_f32, st->m.n_kv_heads,
+                               st->m.head_dim, st->L.ctx_cap, slot, pos0, n, k, v, s));
+  return STAGE_OK;
+}
+
+int stage_kv_export(stage_t* st, int global_block, int slot, int pos0, int n, void* k, void* v,
+                    hipStream_t s) {
+  const int rc = kv_io_check(st, global_block, slot, pos0, n, k, v);
+  if (rc != STAGE_OK) return rc;
+  HIP_TRY(st, hipSetDevice(st->device));
+  const int lb = global_block - st->s.block_begin;
+  HIP_TRY(st, launch_kv_export(st->kcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb,
+                               st->vcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb, st->kv_f32, st->m.n_kv_heads,
                                st->m.head_dim, st->L.ctx_cap, slot, pos0, n, k, v, s));
   return STAGE_OK;
 }

@@ -97,8 +97,9 @@ struct EpiArgs {
   // EPI_QKV
   uint16_t* q;                 // pair buffer [M, Hq*Dh], natural head-dim order
   size_t q_ps;
-  uint16_t* kc;                // K cache of this block: [slots][Hkv][ctx_cap][Dh]
-  uint16_t* vc;                // V cache of this block: [slots][Hkv][ctx_cap/8][Dh][8]
+  void* kc;                    // K cache of this block: [slots][Hkv][ctx_cap][Dh]
+  void* vc;                    // V cache of this block: [slots][Hkv][ctx_cap/8][Dh][8]
+  int kv_f32;                  // cache elements are F32 (else bf16)
   const double2* rope;         // [ctx_cap][Dh/2] (cos, sin), f64
   RowPos rp;
   int hq, hkv, dh, ctx_cap, max_slots;
@@ -147,16 +148,31 @@ PSD_DEV void qkv_epilogue_pair(const EpiArgs& e, int m, int col0, float x0, floa
       dst[e.q_ps + i] = (uint16_t)l0;
       dst[e.q_ps + i + (dh >> 1)] = (uint16_t)l1;
     } else {
-      uint16_t* dst = e.kc + (((size_t)slot * e.hkv + head) * e.ctx_cap + pos) * dh;
-      dst[i] = (uint16_t)f2bf(y0);
-      dst[i + (dh >> 1)] = (uint16_t)f2bf(y1);
+      const size_t o = (((size_t)slot * e.hkv + head) * e.ctx_cap + pos) * dh;
+      if (e.kv_f32) {
+        float* dst = static_cast<float*>(e.kc) + o;
+        dst[i] = y0;
+        dst[i + (dh >> 1)] = y1;
+      } else {
+        uint16_t* dst = static_cast<uint16_t*>(e.kc) + o;
+        dst[i] = (uint16_t)f2bf(y0);
+        dst[i + (dh >> 1)] = (uint16_t)f2bf(y1);
+      }
     }
   } else {
     const int c = col0 - qw - kw;
     const int head = c / dh, d0 = c - head * dh;
-    uint16_t* base = e.vc + (((size_t)slot * e.hkv + head) * (e.ctx_cap >> 3) + (pos >> 3)) * dh * 8;
-    base[(size_t)d0 * 8 + (pos & 7)] = (uint16_t)f2bf(x0);
-    base[(size_t)(d0 + 16) * 8 + (pos & 7)] = (uint16_t)f2bf(x1);
+    const size_t o = (((size_t)slot * e.hkv + head) * (e.ctx_cap >> 3) + (pos >> 3)) * dh * 8;
+    const size_t i0 = (size_t)d0 * 8 + (pos & 7), i1 = (size_t)(d0 + 16) * 8 + (pos & 7);
+    if (e.kv_f32) {
+      float* base = static_cast<float*>(e.vc) + o;
+      base[i0] = x0;
+      base[i1] = x1;
+    } else {
+      uint16_t* base = static_cast<uint16_t*>(e.vc) + o;
+      base[i0] = (uint16_t)f2bf(x0);
+      base[i1] = (uint16_t)f2bf(x1);
+    }
   }
 }
 

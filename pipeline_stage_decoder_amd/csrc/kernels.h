@@ -46,8 +46,9 @@ struct GemmPlan {
 struct AttnDecodeArgs {
   const uint16_t* q;        // pair buffer [B][Hq][Dh]
   size_t q_ps;
-  const uint16_t* kc;       // K cache of the block
-  const uint16_t* vc;       // V cache of the block
+  const void* kc;           // K cache of the block
+  const void* vc;           // V cache of the block
+  int kv_f32;               // cache elements are F32 (else bf16)
   const int32_t* slots;     // [B]
   const int32_t* pos;       // [B]; keys [0, pos] are attended
   int B, hq, hkv, dh, ctx_cap, max_slots;
@@ -65,8 +66,9 @@ struct AttnDecodeArgs {
 struct AttnPrefillArgs {
   const uint16_t* q;        // pair buffer [T][Hq][Dh]
   size_t q_ps;
-  const uint16_t* kc;
-  const uint16_t* vc;
+  const void* kc;
+  const void* vc;
+  int kv_f32;
   int slot, pos0, T, hq, hkv, dh, ctx_cap;
   float scale_log2;
   uint16_t* out;            // pair buffer [T][Hq*Dh]
@@ -78,10 +80,11 @@ hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s);
 hipError_t launch_embed(const uint16_t* table, int V, int d, const int32_t* tokens, int n, float* out,
                         uint32_t* err, hipStream_t s);
 hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s);
-hipError_t launch_kv_import(uint16_t* kc, uint16_t* vc, int hkv, int dh, int ctx_cap, int slot, int pos0,
-                            int n, const uint16_t* k, const uint16_t* v, hipStream_t s);
-hipError_t launch_kv_export(const uint16_t* kc, const uint16_t* vc, int hkv, int dh, int ctx_cap, int slot,
-                            int pos0, int n, uint16_t* k, uint16_t* v, hipStream_t s);
+// k, v: [n][Hkv][Dh] in the cache's element type (bf16 bits or F32)
+hipError_t launch_kv_import(void* kc, void* vc, int kv_f32, int hkv, int dh, int ctx_cap, int slot, int pos0,
+                            int n, const void* k, const void* v, hipStream_t s);
+hipError_t launch_kv_export(const void* kc, const void* vc, int kv_f32, int hkv, int dh, int ctx_cap, int slot,
+                            int pos0, int n, void* k, void* v, hipStream_t s);
 hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s);
 
 // decode GEMV (B <= 4)

@@ -1,4 +1,4 @@
-// Causal grouped-query attention over a slot's bf16 KV cache, on MFMA.
+// Causal grouped-query attention over a slot's KV cache (bf16 or F32 elements), on MFMA.
 //
 // Definition ("41. Many GPUs", Ring attention: attention_partial / merge_partials): scores
 // q.k * Dh^-1/2, keys after the query's position masked, softmax, weighted sum of V; partial
@@ -11,9 +11,10 @@
 //       the bf16 hi plane of q and once for its lo plane (q keeps ~16 significant bits); the
 //       A rows are permuted so lane l ends up with the 8 consecutive keys 8*(l/16) .. +8 of its
 //       column l%16 -- exactly the B operand layout of the next product.
-//   O^T[d, col] += V^T[d, key] P^T[key, col]   A = V^T read as 16 bytes from the packed V cache
-//       [pos/8][Dh][8]; B = P^T straight from registers, split into bf16 hi + lo (two MFMAs) so
-//       the probabilities keep ~16 bits.
+//   O^T[d, col] += V^T[d, key] P^T[key, col]   A = V^T read as 8 consecutive elements from the
+//       packed V cache [pos/8][Dh][8]; B = P^T straight from registers, split into bf16 hi + lo
+//       (two MFMAs) so the probabilities keep ~16 bits.
+//   An F32 cache is split into bf16 hi + lo on load and adds the K_lo.q_hi and V_lo.P_hi MFMAs.
 // The softmax is online per column (max and rescale), in base 2 with the scale folded in.  O^T
 // puts a column's values in the same lane as its softmax state, so rescaling needs no shuffles.
 //
@@ -32,6 +33,32 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // Keys of the two S^T MFMAs that A row `rho` (0..15) of chunk c feeds: (rho/4)*8 + c*4 + rho%4.
 PSD_DEV int key_of_row(int rho, int c) { return ((rho >> 2) << 3) + (c << 2) + (rho & 3); }
 
+// 8 consecutive cache elements from element offset `off`: bf16 bits as they are (lo = 0), or F32
+// split into bf16 hi + lo.
+template <bool KF32>
+PSD_DEV void load8(const void* base, size_t off, bool ok, uint4& hi, uint4& lo) {
+  if (KF32) {
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off + 4);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+    split_hi_lo(x, hi, lo);
+  } else {
+    hi = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off) : make_uint4(0, 0, 0, 0);
+    lo = make_uint4(0, 0, 0, 0);
+  }
+}
+
+PSD_DEV uint4 mask_tail(uint4 v, int nvalid) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 template <int DH>
 struct Col16 {
   bf16x8_t qh[DH / 32];    // B operand of S^T: q[col][ks*32 + grp*8 .. +8], hi plane
@@ -40,38 +67,37 @@ struct Col16 {
   float m, l;              // running max (base-2 scaled) and this lane's share of the sum
 };
 
-// One 32-key step for a wave's 16 columns.  kb: first key (multiple of 8); key_lim(col, key) gives
-// whether a key is visible to the lane's column; keys >= kend are never touched in V.
-template <int DH, typename Visible>
-PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
-                       int kb, int kend, float scale_log2, Visible visible) {
+// One 32-key step for a wave's 16 columns.  kb: first key (multiple of 8); visible(key) says
+// whether a key counts for the lane's column; keys >= kend are never read.
+template <int DH, bool KF32, typename Visible>
+PSD_DEV void attn_step(Col16<DH>& st, const void* __restrict__ kbase, const void* __restrict__ vbase, int kb,
+                       int kend, float scale_log2, Visible visible) {
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   // issue every K and V load of the step first: one memory round trip per step
-  uint4 kr[2][DH / 32];
+  uint4 kh[2][DH / 32], kl[2][DH / 32];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int key = kb + key_of_row(col, c);
     const bool ok = key < kend;
 #pragma unroll
     for (int ks = 0; ks < DH / 32; ++ks)
-      kr[c][ks] = ok ? *reinterpret_cast<const uint4*>(kbase + (size_t)key * DH + ks * 32 + grp * 8)
-                     : make_uint4(0, 0, 0, 0);
+      load8<KF32>(kbase, (size_t)key * DH + ks * 32 + grp * 8, ok, kh[c][ks], kl[c][ks]);
   }
   const int kg = kb + grp * 8;              // this lane's 8 keys in the PV product
   const int nvalid = kend - kg;             // keys of the group below kend
-  uint4 vr[DH / 16];
+  uint4 vh[DH / 16], vl[DH / 16];
 #pragma unroll
   for (int dt = 0; dt < DH / 16; ++dt)
-    vr[dt] = nvalid > 0 ? *reinterpret_cast<const uint4*>(vbase + ((size_t)(kg >> 3) * DH + dt * 16 + col) * 8)
-                        : make_uint4(0, 0, 0, 0);
+    load8<KF32>(vbase, ((size_t)(kg >> 3) * DH + dt * 16 + col) * 8, nvalid > 0, vh[dt], vl[dt]);
   f32x4_t sc[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     sc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DH / 32; ++ks) {
-      sc[c] = mfma16(as_bf16x8(kr[c][ks]), st.qh[ks], sc[c]);
-      sc[c] = mfma16(as_bf16x8(kr[c][ks]), st.ql[ks], sc[c]);
+      sc[c] = mfma16(as_bf16x8(kh[c][ks]), st.qh[ks], sc[c]);
+      sc[c] = mfma16(as_bf16x8(kh[c][ks]), st.ql[ks], sc[c]);
+      if (KF32) sc[c] = mfma16(as_bf16x8(kl[c][ks]), st.qh[ks], sc[c]);
     }
   }
   float s[8];
@@ -105,16 +131,14 @@ PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const 
   split_hi_lo(p, phi, plo);
 #pragma unroll
   for (int dt = 0; dt < DH / 16; ++dt) {
-    uint4 vv = vr[dt];
+    uint4 a = vh[dt], b = vl[dt];
     if (nvalid < 8) {
-      uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e >= nvalid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-      vv = make_uint4(w[0], w[1], w[2], w[3]);
+      a = mask_tail(a, nvalid);
+      b = mask_tail(b, nvalid);
     }
-    st.o[dt] = mfma16(as_bf16x8(vv), as_bf16x8(phi), st.o[dt]);
-    st.o[dt] = mfma16(as_bf16x8(vv), as_bf16x8(plo), st.o[dt]);
+    st.o[dt] = mfma16(as_bf16x8(a), as_bf16x8(phi), st.o[dt]);
+    st.o[dt] = mfma16(as_bf16x8(a), as_bf16x8(plo), st.o[dt]);
+    if (KF32) st.o[dt] = mfma16(as_bf16x8(b), as_bf16x8(phi), st.o[dt]);
   }
 }
 
@@ -140,7 +164,7 @@ PSD_DEV void load_q(Col16<DH>& st, const uint16_t* __restrict__ qrow /* null = p
 // ------------------------------------------------------------------------------------------------
 // decode: partial attention per (split, KV head, row)
 // ------------------------------------------------------------------------------------------------
-template <int DH>
+template <int DH, bool KF32>
 __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
   __shared__ float sm[4][16], sl[4][16];
   __shared__ float so[4][DH][17];
@@ -169,10 +193,11 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
 
   Col16<DH> st;
   load_q(st, col < G ? a.q + ((size_t)b * a.hq + kvh * G + col) * DH : nullptr, a.q_ps);
-  const uint16_t* kbase = a.kc + ((size_t)slot * a.hkv + kvh) * a.ctx_cap * DH;
-  const uint16_t* vbase = a.vc + ((size_t)slot * a.hkv + kvh) * (size_t)(a.ctx_cap >> 3) * DH * 8;
+  const size_t eb = KF32 ? 4 : 2;
+  const char* kbase = static_cast<const char*>(a.kc) + ((size_t)slot * a.hkv + kvh) * a.ctx_cap * DH * eb;
+  const char* vbase = static_cast<const char*>(a.vc) + ((size_t)slot * a.hkv + kvh) * (size_t)a.ctx_cap * DH * eb;
   for (int kb = w0; kb < w1; kb += 32)
-    attn_step<DH>(st, kbase, vbase, kb, w1, a.scale_log2, [&](int key) { return key < w1; });
+    attn_step<DH, KF32>(st, kbase, vbase, kb, w1, a.scale_log2, [&](int key) { return key < w1; });
 
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
@@ -252,7 +277,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
 // ------------------------------------------------------------------------------------------------
 // prefill: 64 columns (queries x heads of one KV head) per work-group, all visible keys
 // ------------------------------------------------------------------------------------------------
-template <int DH>
+template <int DH, bool KF32>
 __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
   const int G = a.hq / a.hkv;
   const int kvh = blockIdx.y;
@@ -272,11 +297,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
 
   Col16<DH> st;
   load_q(st, cvalid ? a.q + ((size_t)t * a.hq + head) * DH : nullptr, a.q_ps);
-  const uint16_t* kbase = a.kc + ((size_t)a.slot * a.hkv + kvh) * a.ctx_cap * DH;
-  const uint16_t* vbase = a.vc + ((size_t)a.slot * a.hkv + kvh) * (size_t)(a.ctx_cap >> 3) * DH * 8;
+  const size_t eb = KF32 ? 4 : 2;
+  const char* kbase = static_cast<const char*>(a.kc) + ((size_t)a.slot * a.hkv + kvh) * a.ctx_cap * DH * eb;
+  const char* vbase = static_cast<const char*>(a.vc) + ((size_t)a.slot * a.hkv + kvh) * (size_t)a.ctx_cap * DH * eb;
   for (int kb = 0; kb < kend; kb += 32)
-    attn_step<DH>(st, kbase, vbase, kb, kend, a.scale_log2,
-                  [&](int key) { return key < kend && key <= my_pos; });
+    attn_step<DH, KF32>(st, kbase, vbase, kb, kend, a.scale_log2,
+                        [&](int key) { return key < kend && key <= my_pos; });
 
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
@@ -307,9 +333,11 @@ int attn_decode_chunk(int B) {
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
   dim3 grid(a.nsplit, a.hkv, a.B);
   if (a.dh == 128) {
-    k_attn_decode<128><<<grid, 256, 0, s>>>(a);
+    if (a.kv_f32) k_attn_decode<128, true><<<grid, 256, 0, s>>>(a);
+    else k_attn_decode<128, false><<<grid, 256, 0, s>>>(a);
   } else {
-    k_attn_decode<64><<<grid, 256, 0, s>>>(a);
+    if (a.kv_f32) k_attn_decode<64, true><<<grid, 256, 0, s>>>(a);
+    else k_attn_decode<64, false><<<grid, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
@@ -317,9 +345,12 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
   const int G = a.hq / a.hkv;
   dim3 grid((a.T * G + 63) / 64, a.hkv);
-  if (a.dh == 128)
-    k_attn_prefill<128><<<grid, 256, 0, s>>>(a);
-  else
-    k_attn_prefill<64><<<grid, 256, 0, s>>>(a);
+  if (a.dh == 128) {
+    if (a.kv_f32) k_attn_prefill<128, true><<<grid, 256, 0, s>>>(a);
+    else k_attn_prefill<128, false><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (a.kv_f32) k_attn_prefill<64, true><<<grid, 256, 0, s>>>(a);
+    else k_attn_prefill<64, false><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }

@@ -57,9 +57,10 @@ __global__ void k_zero_f32(float* __restrict__ p, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
 }
 
-// K cache [slot][kvh][ctx_cap][Dh]; V cache [slot][kvh][ctx_cap/8][Dh][8].
-__global__ void k_kv_import(uint16_t* kc, uint16_t* vc, int hkv, int dh, int ctx_cap, int slot, int pos0,
-                            const uint16_t* __restrict__ k, const uint16_t* __restrict__ v) {
+// K cache [slot][kvh][ctx_cap][Dh]; V cache [slot][kvh][ctx_cap/8][Dh][8]; element type T.
+template <typename T>
+__global__ void k_kv_import(T* kc, T* vc, int hkv, int dh, int ctx_cap, int slot, int pos0,
+                            const T* __restrict__ k, const T* __restrict__ v) {
   const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
   const int pos = pos0 + t;
   const size_t src = ((size_t)t * hkv + h) * dh + d;
@@ -67,8 +68,9 @@ __global__ void k_kv_import(uint16_t* kc, uint16_t* vc, int hkv, int dh, int ctx
   vc[((((size_t)slot * hkv + h) * (ctx_cap >> 3) + (pos >> 3)) * dh + d) * 8 + (pos & 7)] = v[src];
 }
 
-__global__ void k_kv_export(const uint16_t* kc, const uint16_t* vc, int hkv, int dh, int ctx_cap, int slot,
-                            int pos0, uint16_t* __restrict__ k, uint16_t* __restrict__ v) {
+template <typename T>
+__global__ void k_kv_export(const T* kc, const T* vc, int hkv, int dh, int ctx_cap, int slot, int pos0,
+                            T* __restrict__ k, T* __restrict__ v) {
   const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
   const int pos = pos0 + t;
   const size_t dst = ((size_t)t * hkv + h) * dh + d;
@@ -105,16 +107,30 @@ hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_kv_import(uint16_t* kc, uint16_t* vc, int hkv, int dh, int ctx_cap, int slot, int pos0,
-                            int n, const uint16_t* k, const uint16_t* v, hipStream_t s) {
+hipError_t launch_kv_import(void* kc, void* vc, int kv_f32, int hkv, int dh, int ctx_cap, int slot, int pos0,
+                            int n, const void* k, const void* v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  k_kv_import<<<dim3(n, hkv), dh, 0, s>>>(kc, vc, hkv, dh, ctx_cap, slot, pos0, k, v);
+  if (kv_f32)
+    k_kv_import<float><<<dim3(n, hkv), dh, 0, s>>>(static_cast<float*>(kc), static_cast<float*>(vc), hkv, dh,
+                                                   ctx_cap, slot, pos0, static_cast<const float*>(k),
+                                                   static_cast<const float*>(v));
+  else
+    k_kv_import<uint16_t><<<dim3(n, hkv), dh, 0, s>>>(static_cast<uint16_t*>(kc), static_cast<uint16_t*>(vc), hkv,
+                                                      dh, ctx_cap, slot, pos0, static_cast<const uint16_t*>(k),
+                                                      static_cast<const uint16_t*>(v));
   return hipGetLastError();
 }
 
-hipError_t launch_kv_export(const uint16_t* kc, const uint16_t* vc, int hkv, int dh, int ctx_cap, int slot,
-                            int pos0, int n, uint16_t* k, uint16_t* v, hipStream_t s) {
+hipError_t launch_kv_export(const void* kc, const void* vc, int kv_f32, int hkv, int dh, int ctx_cap, int slot,
+                            int pos0, int n, void* k, void* v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  k_kv_export<<<dim3(n, hkv), dh, 0, s>>>(kc, vc, hkv, dh, ctx_cap, slot, pos0, k, v);
+  if (kv_f32)
+    k_kv_export<float><<<dim3(n, hkv), dh, 0, s>>>(static_cast<const float*>(kc), static_cast<const float*>(vc), hkv,
+                                                   dh, ctx_cap, slot, pos0, static_cast<float*>(k),
+                                                   static_cast<float*>(v));
+  else
+    k_kv_export<uint16_t><<<dim3(n, hkv), dh, 0, s>>>(static_cast<const uint16_t*>(kc),
+                                                      static_cast<const uint16_t*>(vc), hkv, dh, ctx_cap, slot, pos0,
+                                                      static_cast<uint16_t*>(k), static_cast<uint16_t*>(v));
   return hipGetLastError();
 }

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpsd_stag
 
 STAGE_OK, STAGE_E_INVALID, STAGE_E_UNSUPPORTED, STAGE_E_DOES_NOT_FIT, STAGE_E_ROLE, STAGE_E_RANGE, \
     STAGE_E_HIP = range(7)
-STAGE_FIRST, STAGE_LAST = 1, 2
+STAGE_FIRST, STAGE_LAST, STAGE_KV_F32 = 1, 2, 4
 
 KERNEL_KINDS = {"embed": 0, "norm": 1, "qkv": 2, "attn": 3, "o": 4, "gateup": 5, "down": 6, "readout": 7}
 
@@ -131,15 +131,16 @@ class Stage:
     """One pipeline stage on one GPU: weights, KV cache and workspace in one torch-owned arena."""
 
     def __init__(self, shape, block_begin: int, block_end: int, first: bool, last: bool, *, max_slots: int = 1,
-                 max_ctx: int = 2048, max_tokens: int = 512, device: int = 0):
+                 max_ctx: int = 2048, max_tokens: int = 512, device: int = 0, kv_f32: bool = False):
         if not torch.cuda.is_available():
             raise RuntimeError("Stage needs a ROCm GPU; none is visible")
         self.shape = shape
         self.spec = StageSpec(block_begin, block_end, first, last, max_slots, max_ctx, max_tokens)
         self.device = device
         self._m = model_cfg(shape)
-        self._s = StageCfg(block_begin, block_end, (STAGE_FIRST if first else 0) | (STAGE_LAST if last else 0),
-                           max_slots, max_ctx, max_tokens)
+        self.kv_f32 = kv_f32
+        self._s = StageCfg(block_begin, block_end, (STAGE_FIRST if first else 0) | (STAGE_LAST if last else 0)
+                           | (STAGE_KV_F32 if kv_f32 else 0), max_slots, max_ctx, max_tokens)
         self.plan = Plan()
         self._check(lib().stage_plan(ctypes.byref(self._m), ctypes.byref(self._s), ctypes.byref(self.plan)),
                     "stage_plan")
@@ -241,15 +242,21 @@ class Stage:
         self._check(lib().stage_kv_copy(self._h, src_slot, dst_slot, n_pos, _stream(stream)), "stage_kv_copy")
 
     def kv_import(self, global_block: int, slot: int, pos0: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+        """k, v: [n, Hkv, Dh] device tensors in the cache's element type (bf16 bits as int16, or float32)."""
+        want = torch.float32 if self.kv_f32 else torch.int16
+        if k.dtype != want or v.dtype != want:
+            raise TypeError(f"kv_import expects {want} tensors for this stage")
         n = k.shape[0]
         self._check(lib().stage_kv_import(self._h, global_block, slot, pos0, n, _ptr(k.contiguous()),
                                           _ptr(v.contiguous()), _stream(stream)), "stage_kv_import")
 
     def kv_export(self, global_block: int, slot: int, pos0: int, n: int, stream=None):
+        """K and V [n, Hkv, Dh] in the cache's element type (int16 bf16 bits, or float32)."""
         shp = (n, self.shape.n_kv_heads, self.shape.head_dim)
         dev = self.arena.device
-        k = torch.empty(shp, dtype=torch.int16, device=dev)
-        v = torch.empty(shp, dtype=torch.int16, device=dev)
+        dt = torch.float32 if self.kv_f32 else torch.int16
+        k = torch.empty(shp, dtype=dt, device=dev)
+        v = torch.empty(shp, dtype=dt, device=dev)
         self._check(lib().stage_kv_export(self._h, global_block, slot, pos0, n, _ptr(k), _ptr(v), _stream(stream)),
                     "stage_kv_export")
         return k, v

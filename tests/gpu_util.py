@@ -68,9 +68,11 @@ def gpu_generate(stages: list, prompt: np.ndarray, n_new: int, slot: int = 0):
 
 
 def kv_bits(st: Stage, block: int, slot: int, n: int):
+    """The cache's K and V of one block and slot as raw bits (uint16 for bf16, uint32 for F32)."""
     k, v = st.kv_export(block, slot, 0, n)
     torch.cuda.synchronize()
-    return k.cpu().numpy().view(np.uint16), v.cpu().numpy().view(np.uint16)
+    view = np.uint32 if st.kv_f32 else np.uint16
+    return k.cpu().numpy().view(view), v.cpu().numpy().view(view)
 
 
 def hidden_rows(seed_slot: int, n: int, d: int, offset_pos: int = 0) -> np.ndarray:

@@ -1,0 +1,215 @@
+"""GPU parity at the workloads' real shapes (relative L2 <= 1e-3 against the float64 oracle).
+
+The oracle cannot run a whole 16- or 20-block stage at these widths in seconds, so each case runs
+the stage's kernels at their real shapes on a slice the oracle can follow:
+* 8B-shaped first stage: embedding + blocks 0..1 at d 4096, prefill T = 512 (the benchmark's
+  launch shapes) and a ragged T = 72, then B = 1 decode steps (the benchmark's decode kernels);
+* 8B-shaped last stage: block 16 + final norm + readout, B = 64 decode at context 4096 over a
+  seeded KV cache imported into both sides;
+* 70B-shaped middle stage: block 20 at d 8192, T = 64 prefill, then B = 128 decode at context
+  8192 over a seeded KV cache;
+* sharded MLP: 8 column/row slices of a d 8192 / F 28672 MLP summed in slice order against the full
+  MLP at T in {1, 64, 4096} (the T = 4096 oracle check on 64 sampled rows; MLP rows are
+  independent).
+Inputs: seeded bf16 N(0, 0.02) weights with norm gains 1 + N(0, 0.1^2), uniform tokens, F32 N(0,1)
+hidden rows, bf16 N(0,1) cached K/V.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fixtures as fx
+from oracle import decoder as o
+from tests.gpu_util import hidden_rows, make_stage, rel_l2, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+TOL = 1e-3
+SEED_KV = 0x5EED0004
+
+
+def seeded_kv(shape, slot: int, n: int):
+    """bf16 bits of K and V [n, Hkv, Dh] for one slot (K stands for post-RoPE keys)."""
+    per = shape.n_kv_heads * shape.head_dim
+    k = fx.normal_bf16(SEED_KV, 2 * slot, n * per, 1.0).reshape(n, shape.n_kv_heads, shape.head_dim)
+    v = fx.normal_bf16(SEED_KV, 2 * slot + 1, n * per, 1.0).reshape(n, shape.n_kv_heads, shape.head_dim)
+    return k, v
+
+
+def import_kv(st, ost, block, slots, n):
+    """Write the same seeded KV (positions 0..n-1) into the GPU stage and the oracle stage."""
+    lb = block - ost.begin
+    for s in slots:
+        k, v = seeded_kv(st.shape, s, n)
+        st.kv_import(block, s, 0, torch.from_numpy(k.view(np.int16)).cuda(), torch.from_numpy(v.view(np.int16)).cuda())
+        kc, vc = ost._cache(s)
+        kc[lb, :n] = o.bf16_to_f32(k)
+        vc[lb, :n] = o.bf16_to_f32(v)
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def w8b_first():
+    return fx.draw_stage_weights(fx.LLAMA8B, 0, 2, True, False, gain_sigma=0.1)
+
+
+@pytest.mark.parametrize("T", [512, 72])
+def test_8b_first_stage_prefill_and_decode(w8b_first, T):
+    s = fx.LLAMA8B
+    prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(0), T, s.vocab)
+    say(f"8B first stage: oracle prefill T={T}")
+    ost = o.Stage(o.Dims.of(s), 0, 2, True, False, w8b_first, T + 4)
+    want = ost.prefill(ost.embed(prompt), 0, 0)
+    st = make_stage(s, 0, 2, True, False, w8b_first, max_slots=1, max_ctx=2048, max_tokens=512)
+    dev = torch.device("cuda")
+    x = st.embed(torch.tensor(prompt, dtype=torch.int32, device=dev))
+    got = st.prefill(x, 0, 0).cpu().numpy()
+    e = rel_l2(got, want)
+    say(f"  prefill rel L2 {e:.2e}")
+    assert e <= TOL
+    toks = fx.tokens(fx.SEED_TOKENS, fx.token_stream(1), 2, s.vocab)
+    for i, tok in enumerate(toks):
+        w = ost.forward(ost.embed(np.array([tok])), [0], [T + i])
+        xg = st.embed(torch.tensor([tok], dtype=torch.int32, device=dev))
+        g = st.decode(xg, torch.tensor([0], dtype=torch.int32, device=dev),
+                      torch.tensor([T + i], dtype=torch.int32, device=dev)).cpu().numpy()
+        e = rel_l2(g, w)
+        say(f"  decode step {i} rel L2 {e:.2e}")
+        assert e <= TOL
+
+
+def test_8b_last_stage_batched_decode_and_readout():
+    s, blk, B, ctx = fx.LLAMA8B, 16, 64, 4096
+    w = fx.draw_stage_weights(s, blk, blk + 1, False, True, gain_sigma=0.1)
+    ost = o.Stage(o.Dims.of(s), blk, blk + 1, False, True, w, ctx + 1)
+    st = make_stage(s, blk, blk + 1, False, True, w, max_slots=B, max_ctx=ctx + 1, max_tokens=B)
+    say("8B last stage: importing KV")
+    import_kv(st, ost, blk, range(B), ctx)
+    slots = np.arange(B)[::-1].copy()
+    x = np.vstack([hidden_rows(100 + int(b), 1, s.d_model, offset_pos=ctx) for b in slots])
+    pos = np.full(B, ctx)
+    say("8B last stage: oracle")
+    want = ost.forward(x, slots, pos)
+    want_logits, want_hn = ost.readout(want)
+    dev = torch.device("cuda")
+    got = st.decode(torch.from_numpy(x).to(dev), torch.tensor(slots, dtype=torch.int32, device=dev),
+                    torch.tensor(pos, dtype=torch.int32, device=dev))
+    logits, hn = st.readout(got)
+    for name, g, wv in (("hidden", got.cpu().numpy(), want), ("final hidden", hn.cpu().numpy(), want_hn),
+                        ("logits", logits.cpu().numpy(), want_logits)):
+        e = rel_l2(g, wv)
+        say(f"  {name} rel L2 {e:.2e}")
+        assert e <= TOL, name
+    assert st.device_errors() == 0
+
+
+def test_70b_mid_stage_prefill_and_batched_decode():
+    s, blk, B, ctx = fx.LLAMA70B, 20, 128, 8192
+    w = fx.draw_stage_weights(s, blk, blk + 1, False, False, gain_sigma=0.1)
+    st = make_stage(s, blk, blk + 1, False, False, w, max_slots=B + 1, max_ctx=ctx + 1, max_tokens=B)
+    # prefill T = 64 into the extra slot B
+    ost = o.Stage(o.Dims.of(s), blk, blk + 1, False, False, w, ctx + 1)
+    xp = hidden_rows(7, 64, s.d_model)
+    say("70B block: oracle prefill")
+    want = ost.prefill(xp, B, 0)
+    got = st.prefill(torch.from_numpy(xp).cuda(), B, 0).cpu().numpy()
+    e = rel_l2(got, want)
+    say(f"  prefill rel L2 {e:.2e}")
+    assert e <= TOL
+    say("70B block: importing KV")
+    import_kv(st, ost, blk, range(B), ctx)
+    slots = np.arange(B)
+    x = np.vstack([hidden_rows(300 + b, 1, s.d_model, offset_pos=ctx) for b in slots])
+    pos = np.full(B, ctx)
+    say("70B block: oracle decode")
+    want = ost.forward(x, slots, pos)
+    dev = torch.device("cuda")
+    got = st.decode(torch.from_numpy(x).to(dev), torch.tensor(slots, dtype=torch.int32, device=dev),
+                    torch.tensor(pos, dtype=torch.int32, device=dev)).cpu().numpy()
+    e = rel_l2(got, want)
+    say(f"  decode B=128 rel L2 {e:.2e}")
+    assert e <= TOL
+    assert st.device_errors() == 0
+
+
+@pytest.fixture(scope="module")
+def mlp70b():
+    s = fx.LLAMA70B
+    g = fx.draw_weight(s, "mlp_norm", 0, gain_sigma=0.1)
+    wg = fx.draw_weight(s, "wgate", 0)
+    wu = fx.draw_weight(s, "wup", 0)
+    wd = fx.draw_weight(s, "wdown", 0)
+    return g, wg, wu, wd
+
+
+def slice_stage(mlp, n_slices):
+    """A stage whose n blocks hold the MLP slices (block i = rows/columns [i w, (i+1) w))."""
+    g, wg, wu, wd = mlp
+    s = fx.LLAMA70B
+    width = s.d_ffn // n_slices
+    sh = fx.Shape(s.d_model, s.n_q_heads, s.n_kv_heads, s.head_dim, width, s.vocab, n_slices)
+    st = make_stage(sh, 0, n_slices, False, False, {}, max_slots=1, max_ctx=64, max_tokens=4096)
+    for i in range(n_slices):
+        lo, hi = i * width, (i + 1) * width
+        st.load_weight("mlp_norm", i, g)
+        st.load_weight("wgate", i, np.ascontiguousarray(wg[lo:hi]))
+        st.load_weight("wup", i, np.ascontiguousarray(wu[lo:hi]))
+        st.load_weight("wdown", i, np.ascontiguousarray(wd[:, lo:hi]))
+    torch.cuda.synchronize()
+    return st
+
+
+@pytest.mark.parametrize("T", [1, 64, 4096])
+def test_mlp_slices_sum_to_full_mlp(mlp70b, T):
+    g, wg, wu, wd = mlp70b
+    s = fx.LLAMA70B
+    x = hidden_rows(40, T, s.d_model)
+    xt = torch.from_numpy(x).cuda()
+    sl = slice_stage(mlp70b, 8)
+    acc = torch.empty_like(xt)
+    for i in range(8):                                   # ((p0 + p1) + p2) + ... in slice order
+        sl.mlp(i, xt, out=acc, accumulate=i > 0)
+    full = make_stage(s, 0, 1, False, False, {("mlp_norm", 0): g, ("wgate", 0): wg, ("wup", 0): wu,
+                                              ("wdown", 0): wd}, max_slots=1, max_ctx=64, max_tokens=4096)
+    y_full = full.mlp(0, xt).cpu().numpy()
+    y_sum = acc.cpu().numpy()
+    # on the GPU the slice sum differs from the full MLP only by F32 reassociation
+    e_gpu = rel_l2(y_sum, y_full)
+    rows = np.arange(T) if T <= 64 else np.linspace(0, T - 1, 64).astype(int)
+    say(f"MLP slices T={T}: oracle on {len(rows)} rows")
+    _, _, want_sum = o.mlp_slices(x[rows], g, wg, wu, wd, s.rms_eps, 8)
+    _, want_full = o.mlp_full(x[rows], g, wg, wu, wd, s.rms_eps)
+    e_sum = rel_l2(y_sum[rows], want_sum)
+    e_full = rel_l2(y_full[rows], want_full)
+    say(f"  slices vs full (gpu) {e_gpu:.2e}; slices vs oracle {e_sum:.2e}; full vs oracle {e_full:.2e}")
+    assert e_gpu <= 1e-5
+    assert e_sum <= TOL and e_full <= TOL
+
+
+def test_8b_first_stage_all_16_blocks_decode_kernels():
+    # the whole first stage (embedding + 16 blocks) with a short prompt, then B = 1 decode steps:
+    # the decode launches are the benchmark's (GEMV kernels, split-KV attention over max_ctx 2048)
+    s = fx.LLAMA8B
+    w = fx.draw_stage_weights(s, 0, 16, True, False, gain_sigma=0.1)
+    T = 24
+    prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(2), T, s.vocab)
+    # an F32 KV cache: with bf16 storage, rounding decisions that the f32 GPU sums and the float64
+    # oracle take differently cascade through 16 blocks past 1e-3 (the bf16 case is covered
+    # block by block above)
+    ost = o.Stage(o.Dims.of(s), 0, 16, True, False, w, T + 4, kv_dtype="f32")
+    say("8B first stage, 16 blocks: oracle")
+    want = [ost.prefill(ost.embed(prompt), 0, 0)]
+    toks = fx.tokens(fx.SEED_TOKENS, fx.token_stream(3), 2, s.vocab)
+    for i, tok in enumerate(toks):
+        want.append(ost.forward(ost.embed(np.array([tok])), [0], [T + i]))
+    st = make_stage(s, 0, 16, True, False, w, max_slots=1, max_ctx=2048, max_tokens=512, kv_f32=True)
+    dev = torch.device("cuda")
+    got = [st.prefill(st.embed(torch.tensor(prompt, dtype=torch.int32, device=dev)), 0, 0).cpu().numpy()]
+    for i, tok in enumerate(toks):
+        xg = st.embed(torch.tensor([tok], dtype=torch.int32, device=dev))
+        got.append(st.decode(xg, torch.tensor([0], dtype=torch.int32, device=dev),
+                             torch.tensor([T + i], dtype=torch.int32, device=dev)).cpu().numpy())
+    for i, (g, wv) in enumerate(zip(got, want)):
+        e = rel_l2(g, wv)
+        say(f"  step {i} rel L2 {e:.2e}")
+        assert e <= TOL

@@ -24,16 +24,18 @@ def weights():
     return fx.draw_stage_weights(TINY, 0, 2, True, True, gain_sigma=0.1)
 
 
-def oracle_stage(w, begin, end, first, last, max_ctx=64):
-    return o.Stage(o.Dims.of(TINY), begin, end, first, last, w, max_ctx)
+def oracle_stage(w, begin, end, first, last, max_ctx=64, kv_dtype="bf16"):
+    return o.Stage(o.Dims.of(TINY), begin, end, first, last, w, max_ctx, kv_dtype=kv_dtype)
 
 
-def test_tiny_greedy_parity(weights):
+@pytest.mark.parametrize("kv_f32", [False, True])
+def test_tiny_greedy_parity(weights, kv_f32):
     prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(0), 16, TINY.vocab)
     say("tiny greedy: oracle")
-    want_toks, want = o.generate([oracle_stage(weights, 0, 2, True, True)], prompt, 8)
+    want_toks, want = o.generate([oracle_stage(weights, 0, 2, True, True, kv_dtype="f32" if kv_f32 else "bf16")],
+                                 prompt, 8)
     say("tiny greedy: gpu")
-    st = make_stage(TINY, 0, 2, True, True, weights, max_slots=2, max_ctx=64, max_tokens=16)
+    st = make_stage(TINY, 0, 2, True, True, weights, max_slots=2, max_ctx=64, max_tokens=16, kv_f32=kv_f32)
     got_toks, got = gpu_generate([st], prompt, 8)
     for step in range(8):
         for key in ("logits", "final_hidden", "residual"):
@@ -45,12 +47,14 @@ def test_tiny_greedy_parity(weights):
     assert st.device_errors() == 0
 
 
-def test_tiny_split_equals_unsplit_on_gpu(weights):
+@pytest.mark.parametrize("kv_f32", [False, True])
+def test_tiny_split_equals_unsplit_on_gpu(weights, kv_f32):
     prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(1), 16, TINY.vocab)
-    whole = make_stage(TINY, 0, 2, True, True, weights, max_slots=1, max_ctx=64, max_tokens=16)
+    kw = dict(max_slots=1, max_ctx=64, max_tokens=16, kv_f32=kv_f32)
+    whole = make_stage(TINY, 0, 2, True, True, weights, **kw)
     t1, tr1 = gpu_generate([whole], prompt, 8)
-    a = make_stage(TINY, 0, 1, True, False, weights, max_slots=1, max_ctx=64, max_tokens=16)
-    b = make_stage(TINY, 1, 2, False, True, weights, max_slots=1, max_ctx=64, max_tokens=16)
+    a = make_stage(TINY, 0, 1, True, False, weights, **kw)
+    b = make_stage(TINY, 1, 2, False, True, weights, **kw)
     t2, tr2 = gpu_generate([a, b], prompt, 8)
     np.testing.assert_array_equal(t1, t2)
     for key in ("logits", "final_hidden", "residual"):
@@ -107,11 +111,11 @@ def test_tiny_chunked_prefill_and_decode(weights):
         assert rel_l2(g, w) <= TOL
 
 
-@pytest.mark.parametrize("B", [2, 4, 6, 9])
-def test_tiny_batched_decode(weights, B):
+@pytest.mark.parametrize("B,kv_f32", [(2, False), (4, False), (6, False), (9, False), (3, True), (9, True)])
+def test_tiny_batched_decode(weights, B, kv_f32):
     # slots prefilled to different lengths, then one decode step for all rows at once
-    ost = oracle_stage(weights, 0, 2, False, False)
-    st = make_stage(TINY, 0, 2, False, False, weights, max_slots=B, max_ctx=64, max_tokens=64)
+    ost = oracle_stage(weights, 0, 2, False, False, kv_dtype="f32" if kv_f32 else "bf16")
+    st = make_stage(TINY, 0, 2, False, False, weights, max_slots=B, max_ctx=64, max_tokens=64, kv_f32=kv_f32)
     lens = [3 + 5 * b for b in range(B)]
     for b, n in enumerate(lens):
         x = hidden_rows(10 + b, n, TINY.d_model)

@@ -198,6 +198,18 @@ def test_attention_bruteforce(tq, tk, hq, hkv, dd):
     assert lse.shape == (tq, hq) and np.all(np.isfinite(lse))
 
 
+@pytest.mark.parametrize("tq,tk,hq,hkv", [(4, 4, 2, 1), (5, 9, 8, 2), (3, 6, 4, 4), (1, 7, 16, 2)])
+def test_attention_gqa_equals_expanded_and_bruteforce(tq, tk, hq, hkv):
+    r = rng(tq * 7 + tk)
+    dd = 8
+    q, k, v = r.standard_normal((tq, hq, dd)), r.standard_normal((tk, hkv, dd)), r.standard_normal((tk, hkv, dd))
+    q_pos, k_pos = np.arange(tk - tq, tk), np.arange(tk)
+    got = o.attention_gqa(q, k, v, q_pos, k_pos, 0.3)
+    ref, _ = o.attention_partial(q, o.gqa_expand(k, hq), o.gqa_expand(v, hq), q_pos, k_pos, 0.3)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(got, brute_attention(q, k, v, q_pos, k_pos, 0.3, hq // hkv), rtol=0, atol=1e-12)
+
+
 def test_attention_gqa_map_pin_catches_modulo_mapping():
     r = rng(9)
     q, k, v = r.standard_normal((2, 4, 4)), r.standard_normal((3, 2, 4)), r.standard_normal((3, 2, 4))
