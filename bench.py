@@ -83,6 +83,32 @@ def cpu_baseline_decode(shape, ctx: int, n_blocks: int, reps: int = 2):
             "seconds_per_block_step": per_block}
 
 
+def summarize_rocprof(path: str, top: int = 12) -> None:
+    """Print a short text summary of rocprofv3 CSV output under `path`: kernel statistics (calls,
+    average and total duration) and, for counter runs, each counter's mean value per dispatch by
+    kernel."""
+    import csv
+    import glob
+    stats = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
+    for f in stats:
+        rows = list(csv.DictReader(open(f)))
+        rows.sort(key=lambda r: -float(r.get("TotalDurationNs", 0)))
+        print(f"# kernel statistics ({os.path.basename(f)}): name | calls | avg us | total ms | %")
+        for r in rows[:top]:
+            print(f"{r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r.get('Percentage', 0)):.1f}")
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        agg = {}
+        for r in csv.DictReader(open(f)):
+            key = (r["Kernel_Name"][:110], r["Counter_Name"])
+            a = agg.setdefault(key, [0, 0.0])
+            a[0] += 1
+            a[1] += float(r["Counter_Value"])
+        print(f"# counters ({os.path.basename(f)}): kernel | counter | dispatches | mean per dispatch")
+        for (k, c), (n, v) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:top]:
+            print(f"{k} | {c} | {n} | {v / n:.1f}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,8 +117,17 @@ def main():
     ap.add_argument("--prefill", type=int, default=512, help="prompt tokens")
     ap.add_argument("--ctx", type=int, default=2048, help="decode up to this context")
     ap.add_argument("--graph", choices=("on", "off"), default="on", help="replay decode steps from a HIP graph")
+    ap.add_argument("--kv", choices=("f32", "bf16"), default="f32",
+                    help="KV cache element type (f32: the configuration validated against the oracle at full depth)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="only summarise the rocprofv3 CSV output under DIR")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -102,6 +137,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")       # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": a.numel() * 4, "bytes_written": b.numel() * 4,
+                          "dispatches": 5}))
+        return
 
     import fixtures as fx
     from pipeline_stage_decoder_amd import accounting as acc
@@ -116,7 +161,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     log(f"[bench] creating stage: blocks {blocks}, embedding, max_ctx {ctx}, max_tokens {T}")
-    st = Stage(shape, blocks[0], blocks[1], True, False, max_slots=1, max_ctx=ctx, max_tokens=T, device=0)
+    kv_f32 = args.kv == "f32"
+    st = Stage(shape, blocks[0], blocks[1], True, False, max_slots=1, max_ctx=ctx, max_tokens=T, device=0,
+               kv_f32=kv_f32)
     fill_weights(st, shape, blocks, True, False, fx.SEED_WEIGHTS)
     prompt = fx.tokens_gpu(torch.empty(T, dtype=torch.int32, device=dev), fx.SEED_TOKENS, fx.token_stream(0),
                            shape.vocab)
@@ -215,7 +262,8 @@ def main():
     dec_ms = float(np.median(decode_ms))
     pre_ms = float(np.median(prefill_ms))
     dec_tok_s = n_dec / (dec_ms / 1e3)
-    dec_bytes = sum(acc.decode_step_bytes(shape, 16, [c], first=True) for c in range(T, ctx))
+    dec_bytes = sum(acc.decode_step_bytes(shape, 16, [c], first=True, kv_elem_bytes=4 if kv_f32 else 2)
+                    for c in range(T, ctx))
     dec_gbs = dec_bytes / (dec_ms / 1e3) / 1e9
     pre_flops = acc.prefill_flops(shape, 16, T)
     pre_tflops = pre_flops / (pre_ms / 1e3) / 1e12
@@ -240,7 +288,8 @@ def main():
         "data": "synthetic: seeded N(0,0.02) bf16 weights, uniform tokens",
         "config": {"workload": "8B-shaped first stage: embedding + blocks 0..15 of 32, d 4096, 32q/8kv heads, "
                                "head dim 128, SwiGLU 14336, vocab 128256; batch 1, prefill 512 then decode to ctx 2048",
-                   "prefill_tokens": T, "decode_ctx": ctx, "batch": 1, "decode_graph": use_graph},
+                   "prefill_tokens": T, "decode_ctx": ctx, "batch": 1, "decode_graph": use_graph,
+                   "kv_cache": args.kv},
         "decode_ms_per_token": round(dec_ms / n_dec, 4),
         "decode_hbm_gbs": round(dec_gbs, 1),
         "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),

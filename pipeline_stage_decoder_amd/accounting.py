@@ -36,8 +36,8 @@ def block_weight_bytes(s) -> int:
     return block_linear_params(s) * BF16
 
 
-def kv_bytes_per_token_block(s) -> int:
-    return 2 * s.n_kv_heads * s.head_dim * BF16
+def kv_bytes_per_token_block(s, kv_elem_bytes: int = BF16) -> int:
+    return 2 * s.n_kv_heads * s.head_dim * kv_elem_bytes
 
 
 def projection_shapes(s) -> dict:
@@ -69,10 +69,11 @@ def projection_bytes(s, kind: str, rows: int) -> int:
 # whole steps
 # ---------------------------------------------------------------------------------------------
 
-def decode_step_bytes(s, n_blocks: int, ctxs, first: bool = False, last: bool = False) -> int:
+def decode_step_bytes(s, n_blocks: int, ctxs, first: bool = False, last: bool = False,
+                      kv_elem_bytes: int = BF16) -> int:
     """One decode step of B = len(ctxs) rows; row b attends ctxs[b] + 1 keys (ctxs[b] cached)."""
     B = len(ctxs)
-    kv_tok = kv_bytes_per_token_block(s)
+    kv_tok = kv_bytes_per_token_block(s, kv_elem_bytes)
     per_block = block_weight_bytes(s) + sum(c + 1 for c in ctxs) * kv_tok
     total = n_blocks * per_block
     total += 2 * B * s.d_model * F32                       # hidden in, hidden out

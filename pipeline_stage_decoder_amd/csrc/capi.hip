@@ -45,7 +45,7 @@ struct Layout {
   uint64_t kcache = 0, vcache = 0, kv_block_elems = 0;
   uint64_t rope = 0;
   uint64_t xn = 0, q = 0, attn = 0, act = 0, part_o = 0, part_lse = 0, gemm_part = 0, counters = 0,
-           attn_counters = 0, err = 0, staging = 0;
+           err = 0, staging = 0;
   int ctx_cap = 0, qkv_n = 0, nsplit_max_rows = 0;
   stage_plan_t plan{};
 };
@@ -65,12 +65,12 @@ int validate(const stage_model_cfg* m, const stage_stage_cfg* s) {
   if (m->n_q_heads % m->n_kv_heads != 0 || m->n_q_heads / m->n_kv_heads > 16) return STAGE_E_UNSUPPORTED;
   if (m->d_model % 64 != 0 || m->d_ffn % 16 != 0) return STAGE_E_UNSUPPORTED;
   if (s->max_ctx > (1 << 24) || s->max_tokens > (1 << 20) || s->max_slots > (1 << 20)) return STAGE_E_UNSUPPORTED;
-  // the decode attention merges up to ceil(ctx / 128) splits per head of a KV group in LDS
-  // (4 * Dh * 17 floats)
+  // the decode attention merge keeps the weights of up to ceil(ctx / 128) splits for each head of
+  // a KV group in LDS (4096 floats)
   {
     const int64_t cap = ((int64_t)s->max_ctx + 63) / 64 * 64;
     const int64_t g = m->n_q_heads / m->n_kv_heads;
-    if (g * ((cap + 127) / 128) > 4 * 17 * (int64_t)m->head_dim) return STAGE_E_UNSUPPORTED;
+    if (g * ((cap + 127) / 128) > 4096) return STAGE_E_UNSUPPORTED;
   }
   return STAGE_OK;
 }
@@ -148,7 +148,6 @@ Layout make_layout(const stage_model_cfg& m, const stage_stage_cfg& s) {
     }
   L.gemm_part = take(gpart);
   L.counters = take((uint64_t)kMaxCounters * 4);
-  L.attn_counters = take(M * hkv * 4);
   L.err = take(4);
   L.staging = take(d * 2);
   L.plan.workspace_bytes = off - ws_start;
@@ -176,7 +175,7 @@ struct stage {
   double2* rope;
   uint16_t *xn, *q, *attn, *act;
   float *part_o, *part_lse, *gemm_part;
-  uint32_t *counters, *attn_counters, *err;
+  uint32_t *counters, *err;
   uint16_t* staging;
   std::string last_error;
   // kernel timing (benchmarks)
@@ -369,7 +368,6 @@ int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, cons
     a.part_o = st->part_o;
     a.part_lse = st->part_lse;
     a.out = st->attn;
-    a.counters = st->attn_counters;
     a.err = st->err;
     Timed t(st, STAGE_KT_ATTN, s);
     HIP_TRY(st, launch_attn_decode(a, s));
@@ -522,14 +520,12 @@ int stage_create(const stage_model_cfg* model, const stage_stage_cfg* stg, void*
   st->part_lse = at<float>(st, L.part_lse);
   st->gemm_part = at<float>(st, L.gemm_part);
   st->counters = at<uint32_t>(st, L.counters);
-  st->attn_counters = at<uint32_t>(st, L.attn_counters);
   st->err = at<uint32_t>(st, L.err);
   st->staging = at<uint16_t>(st, L.staging);
 
   hipError_t e = hipSetDevice(device);
   if (e == hipSuccess) e = hipMemset(st->arena + L.kcache, 0, L.plan.kv_bytes);
   if (e == hipSuccess) e = hipMemset(st->counters, 0, (size_t)kMaxCounters * 4);
-  if (e == hipSuccess) e = hipMemset(st->attn_counters, 0, (size_t)stg->max_tokens * model->n_kv_heads * 4);
   if (e == hipSuccess) e = hipMemset(st->err, 0, 4);
   if (e == hipSuccess) {
     // RoPE table in f64: angle(pos, i) = pos * theta^(-2i/Dh)

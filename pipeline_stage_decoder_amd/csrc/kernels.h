@@ -59,7 +59,6 @@ struct AttnDecodeArgs {
   float* part_lse;          // [B][Hq][nsplit]  (base-2 log-sum-exp)
   uint16_t* out;            // merged output, pair buffer [B][Hq*Dh]
   size_t out_ps;
-  uint32_t* counters;       // [B][Hkv] arrival counters, zero between calls
   uint32_t* err;
 };
 

@@ -19,9 +19,8 @@
 // puts a column's values in the same lane as its softmax state, so rescaling needs no shuffles.
 //
 // Decode: work-group = (split of `chunk` keys, KV head, batch row); its 4 waves take a quarter of
-// the chunk each and merge through LDS; the last split of a (row, KV head) to finish (one atomic
-// counter each, re-armed by that split) merges all splits in split order, so the result does not
-// depend on which split finishes last.
+// the chunk each and merge through LDS into one partial per split; a second kernel merges the
+// splits of each (row, KV head) in split order.
 // Prefill: work-group = 64 columns (consecutive queries x the group's heads) of one KV head; every
 // wave walks keys 0 .. its last query's position.
 #include "kernels.h"
@@ -168,24 +167,13 @@ template <int DH, bool KF32>
 __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
   __shared__ float sm[4][16], sl[4][16];
   __shared__ float so[4][DH][17];
-  __shared__ int last_flag;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int slot = a.slots[b], pos = a.pos[b];
   const int G = a.hq / a.hkv;
-  if (slot < 0 || slot >= a.max_slots || pos < 0 || pos >= a.ctx_cap) {
-    // out-of-range row: zero attention output (written once, by split 0)
-    if (split == 0)
-      for (int idx = threadIdx.x; idx < G * DH; idx += 256) {
-        const size_t o = (size_t)b * a.hq * DH + (size_t)kvh * G * DH + idx;
-        a.out[o] = 0;
-        a.out[a.out_ps + o] = 0;
-      }
-    return;
-  }
+  if (slot < 0 || slot >= a.max_slots || pos < 0 || pos >= a.ctx_cap) return;
   const int ctx = pos + 1;
   const int k0 = split * a.chunk;
   if (k0 >= ctx) return;
-  const int ns = (ctx + a.chunk - 1) / a.chunk;
   const int k1 = min(k0 + a.chunk, ctx);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int sub = a.chunk >> 2;
@@ -230,25 +218,32 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
     if (d == 0) a.part_lse[row] = mm + log2f(L);
   }
 
-  // the last split of this (row, KV head) to finish merges all splits in split order
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(&a.counters[b * a.hkv + kvh], 1u);
-    last_flag = prev == (unsigned)(ns - 1);
-    if (last_flag) a.counters[b * a.hkv + kvh] = 0u;
+}
+
+// Merge the splits of one (row, KV head) in split order -> attention output pair buffer.
+// A separate launch rather than a last-arriving work-group inside the partial kernel: making the
+// partials visible across work-groups inside one kernel takes a device-scope release/acquire,
+// which on gfx950 writes back and invalidates the L2 of every work-group's XCD.
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_merge(AttnDecodeArgs a) {
+  __shared__ float wts[16 * 64 * 4];        // G * ns weights (G <= 16, ns <= 256)
+  __shared__ float tot[16];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int slot = a.slots[b], pos = a.pos[b];
+  const int G = a.hq / a.hkv;
+  if (slot < 0 || slot >= a.max_slots || pos < 0 || pos >= a.ctx_cap) {
+    for (int idx = threadIdx.x; idx < G * DH; idx += 256) {
+      const size_t o = (size_t)b * a.hq * DH + (size_t)kvh * G * DH + idx;
+      a.out[o] = 0;
+      a.out[a.out_ps + o] = 0;
+    }
+    return;
   }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  // split weights w[h][sp] = exp2(lse - max) through LDS, then every output reads its ns partials
-  // with independent loads
-  float* wts = &so[0][0][0];                 // reuse: G * ns <= 16 * nsplit floats
-  float* tot = &sl[0][0];
+  const int ns = (pos + a.chunk) / a.chunk;  // ceil((pos + 1) / chunk)
   const size_t row0 = ((size_t)b * a.hq + kvh * G) * a.nsplit;
   for (int idx = threadIdx.x; idx < G * ns; idx += 256) {
     const int h = idx / ns, sp = idx - h * ns;
-    wts[idx] = __builtin_nontemporal_load(a.part_lse + row0 + (size_t)h * a.nsplit + sp);
+    wts[idx] = a.part_lse[row0 + (size_t)h * a.nsplit + sp];
   }
   __syncthreads();
   if (threadIdx.x < G) {
@@ -269,7 +264,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
     const float* po = a.part_o + (row0 + (size_t)h * a.nsplit) * DH + d;
     float acc = 0.0f;
 #pragma unroll 8
-    for (int sp = 0; sp < ns; ++sp) acc += wts[h * ns + sp] * __builtin_nontemporal_load(po + (size_t)sp * DH);
+    for (int sp = 0; sp < ns; ++sp) acc += wts[h * ns + sp] * po[(size_t)sp * DH];
     store_pair(a.out, a.out_ps, (size_t)b * a.hq * DH + (size_t)(kvh * G + h) * DH + d, acc / tot[h]);
   }
 }
@@ -335,9 +330,11 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
   if (a.dh == 128) {
     if (a.kv_f32) k_attn_decode<128, true><<<grid, 256, 0, s>>>(a);
     else k_attn_decode<128, false><<<grid, 256, 0, s>>>(a);
+    k_attn_merge<128><<<dim3(a.hkv, a.B), 256, 0, s>>>(a);
   } else {
     if (a.kv_f32) k_attn_decode<64, true><<<grid, 256, 0, s>>>(a);
     else k_attn_decode<64, false><<<grid, 256, 0, s>>>(a);
+    k_attn_merge<64><<<dim3(a.hkv, a.B), 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -16,7 +16,8 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemvThreads = 256;
-constexpr int kGemvUnroll = 8;
+constexpr int kGemvUnrollDefault = 4;   // 16-byte loads per row per chunk (swept: 4 ~ 8 > 16)
+constexpr int kGemvMaxGrid = 512;        // two work-groups per CU (swept: 512 beats 256 / 1024 / 2048)
 constexpr int kGemvMaxLds = 64 * 1024;
 
 PSD_DEV void dot8(const uint4& w, const float4& x0, const float4& x1, float& acc) {
@@ -30,7 +31,7 @@ PSD_DEV void dot8(const uint4& w, const float4& x0, const float4& x1, float& acc
   acc = fmaf(bf_hi(w.w), x1.w, acc);
 }
 
-template <int NB, int EPI>
+template <int NB, int EPI, int kGemvUnroll = kGemvUnrollDefault>
 __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
   extern __shared__ float4 lds_x[];                // NB rows of K f32 (operand values)
   __shared__ double red[4];
@@ -191,7 +192,7 @@ bool gemv_fits(int B, int K) {
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s) {
   const int npairs = ((a.N + 31) >> 5) << 4;
   int grid = (npairs + 3) / 4;
-  if (grid > 1024) grid = 1024;
+  if (grid > kGemvMaxGrid) grid = kGemvMaxGrid;
   const int nb = a.B <= 1 ? 1 : (a.B <= 2 ? 2 : 4);
   const size_t lds = (size_t)nb * a.K * 4;
   switch (a.e.kind) {
