@@ -83,6 +83,35 @@ def cpu_baseline_decode(shape, ctx: int, n_blocks: int, reps: int = 2):
             "seconds_per_block_step": per_block}
 
 
+GEMV_SOURCES = ("pipeline_stage_decoder_amd/csrc/kernels_gemv.hip", "pipeline_stage_decoder_amd/csrc/common.h",
+                "pipeline_stage_decoder_amd/csrc/norm.h")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "decode_gemv_gateup_8b_counters.txt")
+
+
+def gemv_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per launch of the gate/up GEMV from the committed counter summary: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) scaled by what the same counters read for a plain 1 GiB copy.
+    None when the summary is missing or was taken on another version of the kernel source."""
+    try:
+        kv = dict(line.split(":", 1) for line in open(COUNTER_FILE) if ":" in line and not line.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if kv.get("kernel_source_sha256_16") != gemv_source_hash():
+            return None
+        fetch = float(kv["gateup_fetch_kib"]) * 1048576.0 / float(kv["copy_fetch_kib"])
+        write = float(kv["gateup_write_kib"]) * 1048576.0 / float(kv["copy_write_kib"])
+        return round((fetch + write) * 1024.0)
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def summarize_rocprof(path: str, top: int = 12) -> None:
     """Print a short text summary of rocprofv3 CSV output under `path`: kernel statistics (calls,
     average and total duration) and, for counter runs, each counter's mean value per dispatch by
@@ -124,9 +153,14 @@ def main():
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="only summarise the rocprofv3 CSV output under DIR")
+    ap.add_argument("--source-hash", action="store_true",
+                    help="only print the hash of the decode GEMV sources the counter summary was taken on")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
+        return
+    if args.source_hash:
+        print(gemv_source_hash())
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -254,7 +288,7 @@ def main():
     gu_avg_s = ms_gu / 1e3 / max(n_gu, 1)
     achieved = gu_bytes / gu_avg_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
                 "kernel": "k_gemv<1, EPI_SWIGLU> (gate/up projection + SwiGLU, B=1)",
                 "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 2), "launches": n_gu}
     kernel_avg_us = {k: round(v[1] * 1e3 / max(v[0], 1), 2) for k, v in kern.items()}
