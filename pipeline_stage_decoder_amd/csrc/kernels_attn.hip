@@ -21,8 +21,9 @@
 // Decode: work-group = (split of `chunk` keys, KV head, batch row); its 4 waves take a quarter of
 // the chunk each and merge through LDS into one partial per split; a second kernel merges the
 // splits of each (row, KV head) in split order.
-// Prefill: work-group = 64 columns (consecutive queries x the group's heads) of one KV head; every
-// wave walks keys 0 .. its last query's position.
+// Prefill: work-group = 64 columns (consecutive queries x the group's heads) of one KV head; the
+// 4 waves share 32-key K/V tiles staged in LDS (double-buffered), each wave skipping tiles past its
+// last query.
 #include "kernels.h"
 
 namespace {
@@ -270,34 +271,173 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnDecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// prefill: 64 columns (queries x heads of one KV head) per work-group, all visible keys
+// prefill: 64 columns (queries x heads of one KV head) per work-group; the 4 waves share 32-key K/V
+// tiles staged in LDS, the next tile's global loads in flight while the current one is consumed
 // ------------------------------------------------------------------------------------------------
+constexpr int kKeyTile = 32;
+
+// XOR applied to the 16-byte chunk index within K tile row `key` (0..31), RC chunks per row.  The
+// 16 keys one A-operand read touches (key_of_row(col, c), col 0..15) have distinct
+// (key & 3) | (key >> 3) << 2 = col; scaled to the row width, the same chunk of those 16 rows lands
+// in 16 distinct 16-byte bank groups (a 128-byte row shares a 256-byte bank line with its neighbour
+// of opposite parity, so there the value is halved).
+template <int RC>
+PSD_DEV int k_swz(int key) {
+  static_assert(RC == 8 || RC == 16 || RC == 32, "row chunks");
+  const int c = (key & 3) | ((key >> 3) << 2);
+  return RC >= 16 ? c * (RC / 16) : c >> 1;
+}
+
 template <int DH, bool KF32>
 __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
+  constexpr int EB = KF32 ? 4 : 2;
+  constexpr int ROW_CHUNKS = DH * EB / 16;                 // 16-byte chunks per K row
+  constexpr int TILE_CHUNKS = kKeyTile * ROW_CHUNKS;       // per K tile (V tile the same)
+  constexpr int PER_THREAD = TILE_CHUNKS / 256;
+  static_assert(TILE_CHUNKS % 256 == 0, "tile chunks per thread");
+  __shared__ uint4 kt[2][TILE_CHUNKS];
+  __shared__ uint4 vt[2][TILE_CHUNKS];
+
   const int G = a.hq / a.hkv;
   const int kvh = blockIdx.y;
   const int ncols = a.T * G;
-  // heavier (later) column blocks first
-  const int cblk = gridDim.x - 1 - blockIdx.x;
+  const int cblk = gridDim.x - 1 - blockIdx.x;               // heavier (later) column blocks first
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int c0 = cblk * 64 + wave * 16;
-  if (c0 >= ncols) return;
   const int c = c0 + col;
   const bool cvalid = c < ncols;
   const int t = cvalid ? c / G : 0, h = cvalid ? c - (c / G) * G : 0;
   const int head = kvh * G + h;
   const int my_pos = a.pos0 + t;
-  const int clast = min(c0 + 15, ncols - 1);
-  const int kend = a.pos0 + clast / G + 1;     // keys [0, kend) cover every column of the wave
+  const bool wave_live = c0 < ncols;
+  const int wlast = wave_live ? min(c0 + 15, ncols - 1) : 0;
+  const int wave_kend = a.pos0 + wlast / G + 1;            // keys [0, wave_kend) matter to this wave
+  const int blast = min(cblk * 64 + 63, ncols - 1);
+  const int kend = a.pos0 + blast / G + 1;                 // keys the work-group walks
+  const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
 
   Col16<DH> st;
   load_q(st, cvalid ? a.q + ((size_t)t * a.hq + head) * DH : nullptr, a.q_ps);
-  const size_t eb = KF32 ? 4 : 2;
-  const char* kbase = static_cast<const char*>(a.kc) + ((size_t)a.slot * a.hkv + kvh) * a.ctx_cap * DH * eb;
-  const char* vbase = static_cast<const char*>(a.vc) + ((size_t)a.slot * a.hkv + kvh) * (size_t)a.ctx_cap * DH * eb;
-  for (int kb = 0; kb < kend; kb += 32)
-    attn_step<DH, KF32>(st, kbase, vbase, kb, kend, a.scale_log2,
-                        [&](int key) { return key < kend && key <= my_pos; });
+  const uint4* kg = reinterpret_cast<const uint4*>(static_cast<const char*>(a.kc) +
+                                                  ((size_t)a.slot * a.hkv + kvh) * a.ctx_cap * DH * EB);
+  const uint4* vg = reinterpret_cast<const uint4*>(static_cast<const char*>(a.vc) +
+                                                  ((size_t)a.slot * a.hkv + kvh) * (size_t)a.ctx_cap * DH * EB);
+  // a tile is one contiguous byte range of K (32 rows of [Dh]) and of V (4 packed 8-key groups)
+  uint4 kr[PER_THREAD], vr[PER_THREAD];
+  auto gload = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int q = threadIdx.x + i * 256;
+      kr[i] = kg[(size_t)tile * TILE_CHUNKS + q];
+      vr[i] = vg[(size_t)tile * TILE_CHUNKS + q];
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int q = threadIdx.x + i * 256;
+      const int row = q / ROW_CHUNKS, ch = q - row * ROW_CHUNKS;
+      kt[buf][row * ROW_CHUNKS + (ch ^ k_swz<ROW_CHUNKS>(row))] = kr[i];
+      vt[buf][q] = vr[i];
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int cur = tile & 1;
+    if (tile + 1 < ntiles) gload(tile + 1);
+    const int kb = tile * kKeyTile;
+    if (wave_live && kb < wave_kend) {
+      // K fragments: A row rho of chunk c is key key_of_row(rho, c); 8 elements at dim ks*32 + grp*8
+      uint4 kh[2][DH / 32], kl[2][DH / 32];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int key = key_of_row(col, cc);
+#pragma unroll
+        for (int ks = 0; ks < DH / 32; ++ks) {
+          const int ch = (ks * 32 + grp * 8) * EB / 16;     // first chunk of the 8 elements
+          const uint4* row = &kt[cur][key * ROW_CHUNKS];
+          const int sw = k_swz<ROW_CHUNKS>(key);
+          if (KF32) {
+            const uint4 x = row[ch ^ sw], y = row[(ch + 1) ^ sw];
+            float f[8] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w),
+                          __uint_as_float(y.x), __uint_as_float(y.y), __uint_as_float(y.z), __uint_as_float(y.w)};
+            split_hi_lo(f, kh[cc][ks], kl[cc][ks]);
+          } else {
+            kh[cc][ks] = row[ch ^ sw];
+            kl[cc][ks] = make_uint4(0, 0, 0, 0);
+          }
+        }
+      }
+      f32x4_t sc[2];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        sc[cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DH / 32; ++ks) {
+          sc[cc] = mfma16(as_bf16x8(kh[cc][ks]), st.qh[ks], sc[cc]);
+          sc[cc] = mfma16(as_bf16x8(kh[cc][ks]), st.ql[ks], sc[cc]);
+          if (KF32) sc[cc] = mfma16(as_bf16x8(kl[cc][ks]), st.qh[ks], sc[cc]);
+        }
+      }
+      float sv[8];
+      float mx = kNegInf;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = kb + grp * 8 + cc * 4 + j;
+          const float v = (key < kend && key <= my_pos) ? sc[cc][j] * a.scale_log2 : kNegInf;
+          sv[cc * 4 + j] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(st.m, mx);
+      const float base = (m_new == kNegInf) ? 0.0f : m_new;
+      const float alpha = exp2f(st.m - base);
+      float p[8], ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = exp2f(sv[e] - base);
+        ps += p[e];
+      }
+      st.l = st.l * alpha + ps;
+      st.m = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] *= alpha;
+      uint4 phi, plo;
+      split_hi_lo(p, phi, plo);
+      // V fragments: 8 keys of group grp at dim dt*16 + col; keys at or past kend (p = 0) are
+      // zeroed so that whatever the cache holds there cannot reach the sum
+      const int nvalid = kend - (kb + grp * 8);
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) {
+        const int q = (grp * DH + dt * 16 + col) * 8 * EB / 16;
+        uint4 vh, vl;
+        if (KF32) {
+          const uint4 x = vt[cur][q], y = vt[cur][q + 1];
+          float f[8] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w),
+                        __uint_as_float(y.x), __uint_as_float(y.y), __uint_as_float(y.z), __uint_as_float(y.w)};
+          split_hi_lo(f, vh, vl);
+        } else {
+          vh = vt[cur][q];
+          vl = make_uint4(0, 0, 0, 0);
+        }
+        if (nvalid < 8) {
+          vh = mask_tail(vh, nvalid);
+          vl = mask_tail(vl, nvalid);
+        }
+        st.o[dt] = mfma16(as_bf16x8(vh), as_bf16x8(phi), st.o[dt]);
+        st.o[dt] = mfma16(as_bf16x8(vh), as_bf16x8(plo), st.o[dt]);
+        if (KF32) st.o[dt] = mfma16(as_bf16x8(vl), as_bf16x8(phi), st.o[dt]);
+      }
+    }
+    if (tile + 1 < ntiles) sstore(cur ^ 1);
+    __syncthreads();
+  }
 
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
@@ -308,11 +448,11 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DH / 16; ++dt) {
     const int d = dt * 16 + grp * 4;
-    uint32_t h[4], l[4];
+    uint32_t hh[4], ll[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) split2(st.o[dt][j] * inv, h[j], l[j]);
-    *reinterpret_cast<uint2*>(out + d) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-    *reinterpret_cast<uint2*>(out + a.out_ps + d) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+    for (int j = 0; j < 4; ++j) split2(st.o[dt][j] * inv, hh[j], ll[j]);
+    *reinterpret_cast<uint2*>(out + d) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+    *reinterpret_cast<uint2*>(out + a.out_ps + d) = make_uint2(ll[0] | (ll[1] << 16), ll[2] | (ll[3] << 16));
   }
 }
 

@@ -7,14 +7,31 @@
 // row l%16.  A work-group of 4 waves owns a BM x BN tile; BK = 64 slices of A and W are staged
 // global -> registers -> LDS (double-buffered, 16-byte chunks XOR-swizzled by row so the
 // ds_read_b128 of 16 rows hits distinct banks) while the previous slice feeds the MFMAs.
-// Small tile counts (skinny decode GEMMs) split K: every split writes an f32 partial, and the last
-// split to arrive for a tile (one atomic counter per tile) sums the partials in split order -- a
-// fixed order, so results never depend on arrival -- applies the epilogue and re-arms the counter.
+// Small tile counts (skinny decode GEMMs) split K: every split writes an f32 partial and a second
+// kernel sums them in split order -- a fixed order, so results never depend on timing -- and
+// applies the epilogue.
 #include "kernels.h"
 
 namespace {
 
 constexpr int BK = 64;
+constexpr int kGroupM = 8;   // M-tiles per group of the tile order
+
+// Tile order.  Work-groups are dealt to the 8 XCDs round-robin (block i runs on XCD i % 8), and
+// each XCD has its own L2; so block i first maps to the logical index that gives every XCD one
+// contiguous range of logical tiles.  Logical tiles then walk groups of kGroupM M-tiles, column by
+// column, so a group's A panels and each W panel are reused from L2 instead of HBM.
+PSD_DEV void tile_coords(int block, int nblocks, int tiles_m, int tiles_n, int& tm, int& tn) {
+  int logical = block;
+  if (nblocks % 8 == 0) logical = (block % 8) * (nblocks / 8) + block / 8;
+  const int per_group = kGroupM * tiles_n;
+  const int group = logical / per_group;
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = logical - group * per_group;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
+}
 
 template <int BM, int BN, int WM, int WN, int NP, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
@@ -25,14 +42,15 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   constexpr int A_ITERS = (BM * 8 + 255) / 256, B_ITERS = (BN * 8 + 255) / 256;
   __shared__ uint4 As[2][NP][BM * 8];  // [buffer][plane][row * 8 + swizzled chunk]
   __shared__ uint4 Bs[2][BN * 8];
-  __shared__ int last_flag;
 
   const int M = g.M, N = g.N, K = g.K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int tiles_n = (N + BN - 1) / BN;
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
   const int tile = blockIdx.x;
-  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  int tm, tn;
+  tile_coords(tile, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const int split = blockIdx.y;
   const int kper = ((K + g.splitk - 1) / g.splitk + BK - 1) / BK * BK;
   const int kbeg = split * kper;
@@ -116,7 +134,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     __syncthreads();
   }
 
-  // ---- split-K: partials, last-arriving split reduces in split order ----------------------------
+  // ---- split-K: write this split's partial; k_splitk_reduce sums them in split order ------------
   if (g.splitk > 1) {
     float* part = g.part + (size_t)split * M * N;
 #pragma unroll
@@ -129,29 +147,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
           const int c = n0 + wn * WTN + j * 16 + (lane & 15);
           if (r < M && c < N) part[(size_t)r * N + c] = acc[i][j][jj];
         }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned prev = atomicAdd(&g.counters[tile], 1u);
-      last_flag = (prev == (unsigned)g.splitk - 1u);
-      if (last_flag) g.counters[tile] = 0u;
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = m0 + wm * WTM + i * 16 + (lane >> 4) * 4 + jj;
-          const int c = n0 + wn * WTN + j * 16 + (lane & 15);
-          float s = 0.0f;
-          if (r < M && c < N)
-            for (int sp = 0; sp < g.splitk; ++sp) s += __builtin_nontemporal_load(g.part + ((size_t)sp * M + r) * N + c);
-          acc[i][j][jj] = s;
-        }
+    return;
   }
 
   // ---- epilogue ----------------------------------------------------------------------------------
@@ -192,6 +188,44 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     }
 }
 
+// Sum the split-K partials of column pairs (c, c + 16), c % 32 < 16, in split order and apply the
+// epilogue.  A separate launch: combining partials inside the GEMM would need device-scope
+// release/acquire fences, which on gfx950 write back and invalidate the XCD's L2 per work-group.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
+  const int M = g.M, N = g.N;
+  const int pairs_per_row = ((N + 31) >> 5) << 4;
+  const size_t total = (size_t)M * pairs_per_row;
+  const size_t plane = (size_t)M * N;
+  for (size_t t = (size_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (size_t)gridDim.x * 256) {
+    const int r = (int)(t / pairs_per_row), pp = (int)(t - (size_t)r * pairs_per_row);
+    const int c0 = ((pp >> 4) << 5) + (pp & 15), c1 = c0 + 16;
+    const bool v0 = c0 < N, v1 = c1 < N;
+    float x0 = 0.0f, x1 = 0.0f;
+    for (int sp = 0; sp < g.splitk; ++sp) {
+      const float* p = g.part + sp * plane + (size_t)r * N;
+      if (v0) x0 += p[c0];
+      if (v1) x1 += p[c1];
+    }
+    const EpiArgs& e = g.e;
+    if (EPI == EPI_F32 || EPI == EPI_RESID) {
+      if (v0) e.out[(size_t)r * e.ldo + c0] = (EPI == EPI_RESID ? e.resid[(size_t)r * e.ldo + c0] : 0.0f) + x0;
+      if (v1) e.out[(size_t)r * e.ldo + c1] = (EPI == EPI_RESID ? e.resid[(size_t)r * e.ldo + c1] : 0.0f) + x1;
+    } else if (v1) {
+      if (EPI == EPI_SWIGLU) {
+        store_pair(e.act, e.act_ps, (size_t)r * e.ldo + (c0 >> 5) * 16 + (c0 & 15), silu_mul(x0, x1));
+      } else {
+        int slot, pos;
+        if (!row_slot_pos(e, r, slot, pos)) {
+          if (c0 == 0) atomicAdd(e.err, 1u);
+        } else {
+          qkv_epilogue_pair(e, r, c0, x0, x1);
+        }
+      }
+    }
+  }
+}
+
 struct Cfg {
   int bm, bn;
 };
@@ -226,16 +260,34 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
 
 }  // namespace
 
+template <int EPI>
+void launch_reduce(const GemmArgs& a, hipStream_t s) {
+  const size_t pairs = (size_t)a.M * ((((size_t)a.N + 31) >> 5) << 4);
+  size_t grid = (pairs + 255) / 256;
+  if (grid > 2048) grid = 2048;
+  k_splitk_reduce<EPI><<<(unsigned)grid, 256, 0, s>>>(a);
+}
+
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
   dim3 grid(p.tiles_m * p.tiles_n, p.splitk);
   switch (a.e.kind) {
     case EPI_QKV:
       if (a.planes == 3) launch_cfg<3, EPI_QKV>(a, p, grid, s);
       else launch_cfg<2, EPI_QKV>(a, p, grid, s);
+      if (p.splitk > 1) launch_reduce<EPI_QKV>(a, s);
       break;
-    case EPI_SWIGLU: launch_cfg<2, EPI_SWIGLU>(a, p, grid, s); break;
-    case EPI_RESID: launch_cfg<2, EPI_RESID>(a, p, grid, s); break;
-    default: launch_cfg<2, EPI_F32>(a, p, grid, s); break;
+    case EPI_SWIGLU:
+      launch_cfg<2, EPI_SWIGLU>(a, p, grid, s);
+      if (p.splitk > 1) launch_reduce<EPI_SWIGLU>(a, s);
+      break;
+    case EPI_RESID:
+      launch_cfg<2, EPI_RESID>(a, p, grid, s);
+      if (p.splitk > 1) launch_reduce<EPI_RESID>(a, s);
+      break;
+    default:
+      launch_cfg<2, EPI_F32>(a, p, grid, s);
+      if (p.splitk > 1) launch_reduce<EPI_F32>(a, s);
+      break;
   }
   return hipGetLastError();
 }
