@@ -283,6 +283,22 @@ def main():
                 kern[k][1] += ms
     st.timing([])
 
+    # prefill per-kernel breakdown: one eager prefill of the same prompt with every kind timed
+    log("[bench] timing the prefill kernels over one eager prefill")
+    pkinds = ("norm", "qkv", "attn", "o", "gateup", "down")
+    st.timing(list(pkinds))
+    st.embed(prompt, out=xin)
+    st.prefill(xin, 0, 0, out=hout)
+    torch.cuda.synchronize()
+    prefill_kernel_ms = {k: round(st.timing_read(k)[1], 4) for k in pkinds}
+    st.timing([])
+    # MFMA work issued: activation operands enter as bf16 hi + lo planes (three for QKV), so the
+    # matrix cores execute planes x the algorithmic linear flops; attention issues 2 products per
+    # score / output term (3 with an F32 cache, whose lo plane adds one)
+    lin = acc.projection_shapes(shape)
+    issued_lin = 16 * 2 * T * sum(n * k * (3 if kind == "qkv" else 2) for kind, (n, k) in lin.items()
+                                  if kind != "readout")
+
     n_gu, ms_gu = kern["gateup"]
     gu_bytes = acc.projection_bytes(shape, "gateup", 1)
     gu_avg_s = ms_gu / 1e3 / max(n_gu, 1)
@@ -331,6 +347,9 @@ def main():
         "prefill_ms": round(pre_ms, 3),
         "prefill_tflops": round(pre_tflops, 1),
         "prefill_mfma_frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "prefill_mfma_issued_frac": round((issued_lin + (pre_flops - acc.prefill_flops(shape, 16, T, attn=False)) * (3 if kv_f32 else 2))
+                                          / (pre_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "prefill_kernel_ms": prefill_kernel_ms,
         "kernel_avg_us": kernel_avg_us,
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,

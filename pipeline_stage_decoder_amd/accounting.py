@@ -84,10 +84,11 @@ def decode_step_bytes(s, n_blocks: int, ctxs, first: bool = False, last: bool = 
     return total
 
 
-def prefill_flops(s, n_blocks: int, T: int, pos0: int = 0, last: bool = False) -> int:
+def prefill_flops(s, n_blocks: int, T: int, pos0: int = 0, last: bool = False, attn: bool = True) -> int:
+    """Linear flops 2 * params * T plus (attn=True) 4 * Hq * Dh * keys attended."""
     lin = 2 * block_linear_params(s) * T
     keys = sum(pos0 + t + 1 for t in range(T))
-    attn = 4 * s.n_q_heads * s.head_dim * keys
+    attn = 4 * s.n_q_heads * s.head_dim * keys if attn else 0
     total = n_blocks * (lin + attn)
     if last:
         total += 2 * s.vocab * s.d_model * T

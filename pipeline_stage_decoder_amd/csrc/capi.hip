@@ -24,7 +24,6 @@
 namespace {
 
 constexpr uint64_t kAlign = 256;
-constexpr int kMaxCounters = 1 << 16;
 
 uint64_t align_up(uint64_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
@@ -44,7 +43,7 @@ struct Layout {
   uint64_t embed = 0, readout = 0, final_norm = 0;
   uint64_t kcache = 0, vcache = 0, kv_block_elems = 0;
   uint64_t rope = 0;
-  uint64_t xn = 0, q = 0, attn = 0, act = 0, part_o = 0, part_lse = 0, gemm_part = 0, counters = 0,
+  uint64_t xn = 0, q = 0, attn = 0, act = 0, part_o = 0, part_lse = 0, gemm_part = 0,
            err = 0, staging = 0;
   int ctx_cap = 0, qkv_n = 0, nsplit_max_rows = 0;
   stage_plan_t plan{};
@@ -147,7 +146,6 @@ Layout make_layout(const stage_model_cfg& m, const stage_stage_cfg& s) {
       }
     }
   L.gemm_part = take(gpart);
-  L.counters = take((uint64_t)kMaxCounters * 4);
   L.err = take(4);
   L.staging = take(d * 2);
   L.plan.workspace_bytes = off - ws_start;
@@ -175,7 +173,7 @@ struct stage {
   double2* rope;
   uint16_t *xn, *q, *attn, *act;
   float *part_o, *part_lse, *gemm_part;
-  uint32_t *counters, *err;
+  uint32_t* err;
   uint16_t* staging;
   std::string last_error;
   // kernel timing (benchmarks)
@@ -305,7 +303,6 @@ hipError_t project(stage* st, int kind, int rows, const float* x_f32, const floa
   const GemmPlan p = gemm_plan(rows, N, K);
   g.splitk = p.splitk;
   g.part = st->gemm_part;
-  g.counters = st->counters;
   g.e = e;
   Timed t(st, kind, s);
   return launch_gemm(g, p, s);
@@ -519,13 +516,11 @@ int stage_create(const stage_model_cfg* model, const stage_stage_cfg* stg, void*
   st->part_o = at<float>(st, L.part_o);
   st->part_lse = at<float>(st, L.part_lse);
   st->gemm_part = at<float>(st, L.gemm_part);
-  st->counters = at<uint32_t>(st, L.counters);
   st->err = at<uint32_t>(st, L.err);
   st->staging = at<uint16_t>(st, L.staging);
 
   hipError_t e = hipSetDevice(device);
   if (e == hipSuccess) e = hipMemset(st->arena + L.kcache, 0, L.plan.kv_bytes);
-  if (e == hipSuccess) e = hipMemset(st->counters, 0, (size_t)kMaxCounters * 4);
   if (e == hipSuccess) e = hipMemset(st->err, 0, 4);
   if (e == hipSuccess) {
     // RoPE table in f64: angle(pos, i) = pos * theta^(-2i/Dh)

@@ -32,7 +32,6 @@ struct GemmArgs {
   int M, N, K;
   int splitk;          // K splits; each split's K range is a multiple of 64
   float* part;         // [splitk][M][N] f32 partials when splitk > 1
-  uint32_t* counters;  // one per output tile, zero between calls (the last arriving tile resets it)
   EpiArgs e;
 };
 

@@ -57,27 +57,37 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   const int kend = min(K, kbeg + kper);
   const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
-  uint4 ra[NP][A_ITERS], rb[B_ITERS];
-  auto gload = [&](int k0) {
+  // Global -> register staging, two sets: the loads of step it + 2 are issued while step it is
+  // computed, so each load has two steps of MFMA work to arrive.  Rows past M / N are clamped to
+  // the last row (their results are never stored) and k past the split's end reads as zero, so
+  // every load is unconditional and in bounds.
+  typedef uint4 ASet[NP][A_ITERS];
+  typedef uint4 BSet[B_ITERS];
+  ASet ra0, ra1;
+  BSet rb0, rb1;
+  auto gload = [&](ASet& ra, BSet& rb, int k0) {
 #pragma unroll
     for (int i = 0; i < A_ITERS; ++i) {
-      const int q = tid + i * 256, row = q >> 3, c8 = q & 7;
-      const int gm = m0 + row, gk = k0 + c8 * 8;
-      const bool ok = q < BM * 8 && gm < M && gk < kend;
-      const uint16_t* src = g.a + (size_t)gm * K + gk;
+      const int q = tid + i * 256, row = (q >> 3) % BM, c8 = q & 7;
+      const int gm = min(m0 + row, M - 1), gk = k0 + c8 * 8;
+      const bool ok = gk < kend;
+      const uint16_t* src = g.a + (size_t)gm * K + (ok ? gk : kbeg);
 #pragma unroll
-      for (int pl = 0; pl < NP; ++pl)
-        ra[pl][i] = ok ? *reinterpret_cast<const uint4*>(src + pl * g.a_ps) : make_uint4(0, 0, 0, 0);
+      for (int pl = 0; pl < NP; ++pl) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + pl * g.a_ps);
+        ra[pl][i] = ok ? v : make_uint4(0, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < B_ITERS; ++i) {
-      const int q = tid + i * 256, row = q >> 3, c8 = q & 7;
-      const int gn = n0 + row, gk = k0 + c8 * 8;
-      rb[i] = (q < BN * 8 && gn < N && gk < kend)
-                  ? *reinterpret_cast<const uint4*>(g.w + (size_t)gn * K + gk) : make_uint4(0, 0, 0, 0);
+      const int q = tid + i * 256, row = (q >> 3) % BN, c8 = q & 7;
+      const int gn = min(n0 + row, N - 1), gk = k0 + c8 * 8;
+      const bool ok = gk < kend;
+      const uint4 v = *reinterpret_cast<const uint4*>(g.w + (size_t)gn * K + (ok ? gk : kbeg));
+      rb[i] = ok ? v : make_uint4(0, 0, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, const ASet& ra, const BSet& rb) {
 #pragma unroll
     for (int i = 0; i < A_ITERS; ++i) {
       const int q = tid + i * 256, row = q >> 3, c8 = q & 7;
@@ -99,14 +109,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (nk > 0) {
-    gload(kbeg);
-    sstore(0);
-    __syncthreads();
-  }
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nk) gload(kbeg + (it + 1) * BK);
+  auto compute = [&](int cur) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int c8 = kk * 4 + (lane >> 4);
@@ -130,7 +133,25 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
           for (int pl = 0; pl < NP; ++pl) acc[i][j] = mfma16(af[pl][i], bw[j], acc[i][j]);
         }
     }
-    if (it + 1 < nk) sstore(cur ^ 1);
+  };
+
+  if (nk > 0) {
+    gload(ra0, rb0, kbeg);
+    if (nk > 1) gload(ra1, rb1, kbeg + BK);
+    sstore(0, ra0, rb0);
+    __syncthreads();
+  }
+  // step it computes LDS buffer it & 1; register set it & 1 is free (stored during step it - 1)
+  // and receives step it + 2; set (it + 1) & 1 holds step it + 1 and goes to LDS after the MFMAs
+  for (int it = 0; it < nk; it += 2) {
+    if (it + 2 < nk) gload(ra0, rb0, kbeg + (it + 2) * BK);
+    compute(0);
+    if (it + 1 < nk) sstore(1, ra1, rb1);
+    __syncthreads();
+    if (it + 1 >= nk) break;
+    if (it + 3 < nk) gload(ra1, rb1, kbeg + (it + 3) * BK);
+    compute(1);
+    if (it + 2 < nk) sstore(0, ra0, rb0);
     __syncthreads();
   }
 
@@ -229,20 +250,24 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
 struct Cfg {
   int bm, bn;
 };
-constexpr Cfg kCfgs[] = {{128, 128}, {64, 128}, {32, 128}, {16, 128}};
+constexpr Cfg kCfgs[] = {{128, 128}, {64, 128}, {32, 128}, {16, 128}, {128, 256}};
 
 }  // namespace
 
 GemmPlan gemm_plan(int M, int N, int K) {
   GemmPlan p{};
-  p.cfg = M > 64 ? 0 : (M > 32 ? 1 : (M > 16 ? 2 : 3));
+  // 64 x 128 tiles from M = 33 up: two work-groups fit a CU (64 KB LDS each), and the second
+  // hides the first's barrier and LDS waits (measured faster than 128 x 128 from M = 128 to 4096).
+  // Split K until the grid holds ~2 work-groups per CU (one for skinny M), each split >= 256 deep.
+  p.cfg = M > 32 ? 1 : (M > 16 ? 2 : 3);
   p.bm = kCfgs[p.cfg].bm;
   p.bn = kCfgs[p.cfg].bn;
   p.tiles_m = (M + p.bm - 1) / p.bm;
   p.tiles_n = (N + p.bn - 1) / p.bn;
   const int tiles = p.tiles_m * p.tiles_n;
+  const int target = M > 64 ? 512 : 256;
   p.splitk = 1;
-  while (tiles * p.splitk < 256 && K / (p.splitk * 2) >= 4 * BK && p.splitk < 16) p.splitk *= 2;
+  while (tiles * p.splitk < target && K / (p.splitk * 2) >= 4 * BK && p.splitk < 16) p.splitk *= 2;
   return p;
 }
 
@@ -254,7 +279,8 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
     case 0: k_gemm<128, 128, 2, 2, NP, EPI><<<grid, 256, 0, s>>>(a); break;
     case 1: k_gemm<64, 128, 1, 4, NP, EPI><<<grid, 256, 0, s>>>(a); break;
     case 2: k_gemm<32, 128, 1, 4, NP, EPI><<<grid, 256, 0, s>>>(a); break;
-    default: k_gemm<16, 128, 1, 4, NP, EPI><<<grid, 256, 0, s>>>(a); break;
+    case 3: k_gemm<16, 128, 1, 4, NP, EPI><<<grid, 256, 0, s>>>(a); break;
+    default: k_gemm<128, 256, 2, 2, NP, EPI><<<grid, 256, 0, s>>>(a); break;
   }
 }
 
