@@ -134,8 +134,93 @@ def summarize_rocprof(path: str, top: int = 12) -> None:
             a[0] += 1
             a[1] += float(r["Counter_Value"])
         print(f"# counters ({os.path.basename(f)}): kernel | counter | dispatches | mean per dispatch")
-        for (k, c), (n, v) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:top]:
+        for (k, c), (n, v) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:4 * top]:
             print(f"{k} | {c} | {n} | {v / n:.1f}")
+        # MFMA utilisation (busy cycles over GPU-active cycles x SIMDs) and bf16 MFMA flops issued;
+        # GRBM_GUI_ACTIVE arrives summed over the 8 XCDs (8x the dispatch's wall-clock cycles)
+        kernels = sorted({k for k, _ in agg})
+        simds = 256 * 4 / 8
+        lines = []
+        for k in kernels:
+            busy, act = agg.get((k, "SQ_VALU_MFMA_BUSY_CYCLES")), agg.get((k, "GRBM_GUI_ACTIVE"))
+            mops = agg.get((k, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+            if busy and act and act[1] > 0:
+                lines.append((busy[1] / (act[1] * simds), k, act[0], (mops[1] * 512 / mops[0]) if mops else 0.0))
+        if lines:
+            print("# derived: kernel | dispatches | MFMA busy / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) | "
+                  "bf16 MFMA flops per dispatch")
+            for u, k, n, fl in sorted(lines, key=lambda t: -t[3]):
+                print(f"{k} | {n} | {100 * u:.1f}% | {fl:.4g}")
+
+
+def time_handoff(rows_prefill, row_decode, reps: int = 50) -> dict:
+    """The stage boundary's cost: the F32 hidden rows a stage hands to the next, copied device to
+    device (the one-GPU handoff), and as a pinned device->host->device round trip (the host-staged
+    transfer of two stages on two PCIe-attached GPUs)."""
+    import torch
+    out = {}
+    for name, src in (("prefill_rows", rows_prefill), ("decode_row", row_decode)):
+        dst = torch.empty_like(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dst.copy_(src)
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"d2d_{name}"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+        host = torch.empty(src.shape, dtype=src.dtype, pin_memory=True)
+        host.copy_(src)
+        dst.copy_(host)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            host.copy_(src)                 # synchronous D2H into pinned memory
+            dst.copy_(host)
+            torch.cuda.synchronize()
+        out[f"pinned_round_trip_{name}"] = round((time.perf_counter() - t0) * 1e6 / reps, 2)
+        out[f"bytes_{name}"] = src.numel() * 4
+    return out
+
+
+def prefill_only(args, shape, blocks, T, dev, stream):
+    """Time the prefill alone: stage sized for one T-token prompt, W warmups then K timed prefills."""
+    import numpy as np
+    import torch
+
+    import fixtures as fx
+    from pipeline_stage_decoder_amd import accounting as acc
+    from pipeline_stage_decoder_amd.stage import Stage
+
+    kv_f32 = args.kv == "f32"
+    st = Stage(shape, blocks[0], blocks[1], True, False, max_slots=1, max_ctx=T, max_tokens=T, device=0,
+               kv_f32=kv_f32)
+    fill_weights(st, shape, blocks, True, False, fx.SEED_WEIGHTS)
+    prompt = fx.tokens_gpu(torch.empty(T, dtype=torch.int32, device=dev), fx.SEED_TOKENS, fx.token_stream(0),
+                           shape.vocab)
+    xin = torch.empty((T, shape.d_model), dtype=torch.float32, device=dev)
+    hout = torch.empty_like(xin)
+    for _ in range(max(args.warmup, 1)):
+        st.embed(prompt, out=xin)
+        st.prefill(xin, 0, 0, out=hout)
+    torch.cuda.synchronize()
+    ms = []
+    for k in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st.embed(prompt, out=xin)
+        st.prefill(xin, 0, 0, out=hout)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+        log(f"[bench] prefill {k + 1}/{args.steps}: {ms[-1]:.3f} ms")
+    pre_ms = float(np.median(ms))
+    flops = acc.prefill_flops(shape, blocks[1] - blocks[0], T)
+    print(json.dumps({"phase": "prefill", "prefill_tokens": T, "kv_cache": args.kv, "prefill_ms": round(pre_ms, 3),
+                      "prefill_tok_s": round(T / (pre_ms / 1e3), 1),
+                      "prefill_tflops": round(flops / (pre_ms / 1e3) / 1e12, 1),
+                      "prefill_mfma_frac": round(flops / (pre_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}),
+          flush=True)
 
 
 def main():
@@ -148,6 +233,8 @@ def main():
     ap.add_argument("--graph", choices=("on", "off"), default="on", help="replay decode steps from a HIP graph")
     ap.add_argument("--kv", choices=("f32", "bf16"), default="f32",
                     help="KV cache element type (f32: the configuration validated against the oracle at full depth)")
+    ap.add_argument("--phase", choices=("both", "prefill"), default="both",
+                    help="prefill: only time the prefill (a short run for hardware-counter passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -193,6 +280,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+
+    if args.phase == "prefill":
+        prefill_only(args, shape, blocks, T, dev, stream)
+        return
 
     log(f"[bench] creating stage: blocks {blocks}, embedding, max_ctx {ctx}, max_tokens {T}")
     kv_f32 = args.kv == "f32"
@@ -318,6 +409,8 @@ def main():
     pre_flops = acc.prefill_flops(shape, 16, T)
     pre_tflops = pre_flops / (pre_ms / 1e3) / 1e12
 
+    handoff = time_handoff(hout, x1)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
@@ -350,6 +443,7 @@ def main():
         "prefill_mfma_issued_frac": round((issued_lin + (pre_flops - acc.prefill_flops(shape, 16, T, attn=False)) * (3 if kv_f32 else 2))
                                           / (pre_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "prefill_kernel_ms": prefill_kernel_ms,
+        "handoff_us": handoff,
         "kernel_avg_us": kernel_avg_us,
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
