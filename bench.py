@@ -223,6 +223,219 @@ def prefill_only(args, shape, blocks, T, dev, stream):
           flush=True)
 
 
+def stage_kernel_ms(st, kinds):
+    """(launches, total ms) per kind from the stage's HIP-event timing, then timing switched off."""
+    out = {k: st.timing_read(k) for k in kinds}
+    st.timing([])
+    return out
+
+
+def graph_of(fn, n: int):
+    """Capture n calls of fn() into one HIP graph (fn is warmed once outside capture)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cs):
+        for _ in range(n):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps: int) -> float:
+    """Median ms of one replay of g over `reps` replays (events on the current stream)."""
+    import numpy as np
+    import torch
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return float(np.median(ms))
+
+
+def fill_kv_by_prefill(st, slot0: int, n_pos: int, chunk: int, other_slots, d: int):
+    """Fill slot0's cache with n_pos positions by chunked prefill of seeded F32 N(0,1) hidden rows,
+    then copy it into the other slots (the decode rows then attend real, distinct-slot caches)."""
+    import torch
+
+    import fixtures as fx
+    x = torch.empty((chunk, d), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for p0 in range(0, n_pos, chunk):
+        t = min(chunk, n_pos - p0)
+        fx.normal_f32_gpu(x[:t], fx.SEED_HIDDEN, fx.hidden_stream(slot0), p0 * d)
+        st.prefill(x[:t], slot0, p0, out=y[:t])
+    torch.cuda.synchronize()
+    for i, s in enumerate(other_slots):
+        st.kv_copy(slot0, s, n_pos)
+        if i % 16 == 15:
+            torch.cuda.synchronize()
+            log(f"[bench] KV copied into {i + 1}/{len(other_slots)} slots")
+    torch.cuda.synchronize()
+
+
+def kernel_roofline(bytes_per_launch: int, launches: int, total_ms: float, name: str) -> dict:
+    avg_s = total_ms / 1e3 / max(launches, 1)
+    ach = bytes_per_launch / avg_s / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": name,
+            "bytes_per_launch": bytes_per_launch, "avg_launch_us": round(avg_s * 1e6, 2), "launches": launches}
+
+
+def batched_decode_line(args, workload: str, shape, blocks, first: bool, last: bool, B: int, ctx: int,
+                        prefill_chunk: int, time_prefill: bool) -> dict:
+    """B rows (distinct slots) decoding at context ctx (positions ctx), every step the same positions
+    (each step rewrites position ctx): per-step bytes are constant, as in the workload's definition."""
+    import torch
+
+    import fixtures as fx
+    from pipeline_stage_decoder_amd import accounting as acc
+    from pipeline_stage_decoder_amd.stage import Stage
+
+    nb = blocks[1] - blocks[0]
+    d = shape.d_model
+    log(f"[bench] {workload}: creating stage {blocks}, {B} slots, ctx {ctx}")
+    st = Stage(shape, blocks[0], blocks[1], first, last, max_slots=B, max_ctx=ctx + 1,
+               max_tokens=max(B, prefill_chunk), device=0)
+    fill_weights(st, shape, blocks, first, last, fx.SEED_WEIGHTS)
+    pre = {}
+    if time_prefill:
+        # the fill itself is the prefill workload: chunks of prefill_chunk tokens at pos0 = 0, chunk, ..
+        x = torch.empty((prefill_chunk, d), dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        ms = []
+        for p0 in range(0, ctx, prefill_chunk):
+            fx.normal_f32_gpu(x, fx.SEED_HIDDEN, fx.hidden_stream(0), p0 * d)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            st.prefill(x, 0, p0, out=y)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+            fl = acc.prefill_flops(shape, nb, prefill_chunk, pos0=p0)
+            log(f"[bench] prefill chunk at pos0 {p0}: {ms[-1]:.1f} ms, {fl / ms[-1] / 1e9:.1f} TFLOP/s")
+        tot_fl = sum(acc.prefill_flops(shape, nb, prefill_chunk, pos0=p0) for p0 in range(0, ctx, prefill_chunk))
+        pre = {"prefill_chunk": prefill_chunk, "prefill_chunk_ms": [round(m, 2) for m in ms],
+               "prefill_tok_s": round(ctx / (sum(ms) / 1e3), 1),
+               "prefill_tflops": round(tot_fl / (sum(ms) / 1e3) / 1e12, 1),
+               "prefill_mfma_frac": round(tot_fl / (sum(ms) / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        for i, s in enumerate(range(1, B)):
+            st.kv_copy(0, s, ctx)
+            if i % 16 == 15:
+                torch.cuda.synchronize()
+                log(f"[bench] KV copied into {i + 1}/{B - 1} slots")
+        torch.cuda.synchronize()
+    else:
+        fill_kv_by_prefill(st, 0, ctx, prefill_chunk, range(1, B), d)
+
+    xin = fx.normal_f32_gpu(torch.empty((B, d), dtype=torch.float32, device="cuda"), fx.SEED_HIDDEN,
+                            fx.hidden_stream(1000), 0)
+    h = torch.empty_like(xin)
+    slots = torch.arange(B, dtype=torch.int32, device="cuda")
+    pos = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, shape.vocab), dtype=torch.float32, device="cuda") if last else None
+
+    def step():
+        st.decode(xin, slots, pos, out=h)
+        if last:
+            st.readout(h, logits=logits)
+
+    per_graph = 4
+    g = graph_of(step, per_graph)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(args.steps, 1)
+    ms = time_graph(g, reps) / per_graph
+    kinds = ("qkv", "attn", "o", "gateup", "down") + (("readout",) if last else ())
+    st.timing(list(kinds))
+    step()
+    torch.cuda.synchronize()
+    kt = stage_kernel_ms(st, kinds)
+    step_bytes = acc.decode_step_bytes(shape, nb, [ctx] * B, first=first, last=last)
+    kv_launch = B * (ctx + 1) * acc.kv_bytes_per_token_block(shape)
+    roof = kernel_roofline(kv_launch, kt["attn"][0], kt["attn"][1],
+                           "k_attn_decode + k_attn_merge (split-KV GQA decode over the slots' bf16 caches)")
+    gbs = step_bytes / (ms / 1e3) / 1e9
+    return {
+        "metric": "stage decode tok/s & HBM GB/s %peak; prefill tok/s & MFMA util",
+        "value": round(B / (ms / 1e3), 1), "unit": "tok/s", "n_gpus": 1, "steps": reps * per_graph,
+        "warmup": args.warmup * per_graph, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,0.02) bf16 weights, F32 N(0,1) hidden rows",
+        "config": {"workload": workload, "batch": B, "decode_ctx": ctx, "blocks": list(blocks),
+                   "kv_cache": "bf16", "decode_graph": True},
+        "decode_step_bytes": step_bytes, "decode_hbm_gbs": round(gbs, 1),
+        "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "kernel_ms_per_step": {k: round(v[1], 3) for k, v in kt.items()},
+        **pre, "roofline": roof, "cpu_baseline": None,
+    }
+
+
+def mlp_slices_line(args) -> dict:
+    """8 column/row slices (width 3584) of a d 8192 / F 28672 SwiGLU MLP, one stage block each;
+    stage_mlp per slice, accumulated in slice order, at T in {1, 64, 4096}."""
+    import torch
+
+    import fixtures as fx
+    from pipeline_stage_decoder_amd import accounting as acc
+    from pipeline_stage_decoder_amd.stage import Stage
+
+    s70 = fx.LLAMA70B
+    n_sl, width = 8, s70.d_ffn // 8
+    sh = fx.Shape(s70.d_model, s70.n_q_heads, s70.n_kv_heads, s70.head_dim, width, s70.vocab, n_sl)
+    st = Stage(sh, 0, n_sl, False, False, max_slots=1, max_ctx=64, max_tokens=4096, device=0)
+    roles = [r for r in fx.stage_roles(0, n_sl, False, False) if r[0] in ("mlp_norm", "wgate", "wup", "wdown")]
+    big = max(int(__import__("numpy").prod(fx.role_shape(sh, r))) for r, _ in roles)
+    scratch = torch.empty(big, dtype=torch.int16, device="cuda")
+    for role, b in roles:
+        n = int(__import__("numpy").prod(fx.role_shape(sh, role)))
+        if role == "mlp_norm":
+            fx.gain_bf16_gpu(scratch[:n], fx.SEED_WEIGHTS, fx.weight_stream(role, b), 0.0)
+        else:
+            fx.normal_bf16_gpu(scratch[:n], fx.SEED_WEIGHTS, fx.weight_stream(role, b), 0.02)
+        st.load_weight(role, b, scratch[:n])
+    torch.cuda.synchronize()
+    del scratch
+    per_T = {}
+    for T in (1, 64, 4096):
+        x = fx.normal_f32_gpu(torch.empty((T, sh.d_model), dtype=torch.float32, device="cuda"), fx.SEED_HIDDEN,
+                              fx.hidden_stream(40), 0)
+        acc_out = torch.empty_like(x)
+
+        def run():
+            for i in range(n_sl):
+                st.mlp(i, x, out=acc_out, accumulate=i > 0)
+
+        g = graph_of(run, 1)
+        ms = time_graph(g, max(args.steps, 3)) / n_sl
+        by = acc.mlp_slice_bytes(sh.d_model, width, T)
+        fl = acc.mlp_slice_flops(sh.d_model, width, T)
+        per_T[str(T)] = {"us_per_slice": round(ms * 1e3, 2), "hbm_gbs": round(by / (ms / 1e3) / 1e9, 1),
+                         "hbm_frac": round(by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "tflops": round(fl / (ms / 1e3) / 1e12, 1),
+                         "mfma_frac": round(fl / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        log(f"[bench] MLP slice T={T}: {per_T[str(T)]}")
+    big_t = per_T["4096"]
+    return {
+        "metric": "stage decode tok/s & HBM GB/s %peak; prefill tok/s & MFMA util",
+        "value": round(4096 / (big_t["us_per_slice"] * n_sl / 1e6), 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": max(args.steps, 3), "warmup": 1, "ms_per_step": round(big_t["us_per_slice"] * n_sl / 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,0.02) bf16 weights, F32 N(0,1) hidden rows",
+        "config": {"workload": "sharded-MLP slices: d 8192, 8 slices of width 3584 (F 28672), "
+                               "T in {1, 64, 4096}, F32 partials summed in slice order; value = "
+                               "T=4096 rows/s through all 8 slices"},
+        "per_T": per_T, "roofline": None, "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +446,8 @@ def main():
     ap.add_argument("--graph", choices=("on", "off"), default="on", help="replay decode steps from a HIP graph")
     ap.add_argument("--kv", choices=("f32", "bf16"), default="f32",
                     help="KV cache element type (f32: the configuration validated against the oracle at full depth)")
+    ap.add_argument("--workload", choices=("first-8b", "last-8b", "mid-70b", "mlp-slices"), default="first-8b",
+                    help="first-8b: the benchmark line; the others report the remaining workloads' rooflines")
     ap.add_argument("--phase", choices=("both", "prefill"), default="both",
                     help="prefill: only time the prefill (a short run for hardware-counter passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -283,6 +498,21 @@ def main():
 
     if args.phase == "prefill":
         prefill_only(args, shape, blocks, T, dev, stream)
+        return
+    if args.workload == "last-8b":
+        print(json.dumps(batched_decode_line(
+            args, "8B-shaped last stage: blocks 16..31 of 32 + final norm + readout (vocab 128256); "
+                  "batched decode B=64 at context 4096, F32 hidden in, F32 logits out",
+            shape, (16, 32), False, True, 64, 4096, 1024, False)), flush=True)
+        return
+    if args.workload == "mid-70b":
+        print(json.dumps(batched_decode_line(
+            args, "70B-shaped middle stage: blocks 20..39 of 80, d 8192, 64q/8kv, SwiGLU 28672; "
+                  "prefill in 4096-token chunks to context 8192, then batched decode B=128 at context 8192",
+            fx.LLAMA70B, (20, 40), False, False, 128, 8192, 4096, True)), flush=True)
+        return
+    if args.workload == "mlp-slices":
+        print(json.dumps(mlp_slices_line(args)), flush=True)
         return
 
     log(f"[bench] creating stage: blocks {blocks}, embedding, max_ctx {ctx}, max_tokens {T}")

@@ -5,8 +5,10 @@
 // Prefill projections (M = T tokens) and batched decode (M = B rows) both land here.  Both
 // operands are K-contiguous, the layout the MFMA operands want: lane l takes 8 consecutive k of
 // row l%16.  A work-group of 4 waves owns a BM x BN tile; BK = 64 slices of A and W are staged
-// global -> registers -> LDS (double-buffered, 16-byte chunks XOR-swizzled by row so the
-// ds_read_b128 of 16 rows hits distinct banks) while the previous slice feeds the MFMAs.
+// global -> registers -> LDS (16-byte chunks XOR-swizzled by row so the ds_read_b128 of 16 rows
+// hits distinct banks), the next slices' loads in flight while the current slice feeds the MFMAs.
+// STAGES = LDS buffers (1: a barrier separates the last reads from the next store), DEPTH =
+// register staging sets (loads issued DEPTH slices ahead).
 // Small tile counts (skinny decode GEMMs) split K: every split writes an f32 partial and a second
 // kernel sums them in split order -- a fixed order, so results never depend on timing -- and
 // applies the epilogue.
@@ -33,15 +35,17 @@ PSD_DEV void tile_coords(int block, int nblocks, int tiles_m, int tiles_n, int& 
   tn = in_group / gm;
 }
 
-template <int BM, int BN, int WM, int WN, int NP, int EPI>
+template <int BM, int BN, int WM, int WN, int NP, int EPI, int STAGES, int DEPTH>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
+  static_assert(DEPTH == 1 || DEPTH == 2, "register staging sets");
   static_assert(WM * WN == 4, "4 waves");
+  static_assert(STAGES == 1 || STAGES == 2, "LDS buffers");
   constexpr int WTM = BM / WM, WTN = BN / WN;       // wave tile
   constexpr int TM = WTM / 16, TN = WTN / 16;       // MFMA tiles per wave
   static_assert(WTN % 32 == 0, "paired epilogues need 32-aligned wave columns");
   constexpr int A_ITERS = (BM * 8 + 255) / 256, B_ITERS = (BN * 8 + 255) / 256;
-  __shared__ uint4 As[2][NP][BM * 8];  // [buffer][plane][row * 8 + swizzled chunk]
-  __shared__ uint4 Bs[2][BN * 8];
+  __shared__ uint4 As[STAGES][NP][BM * 8];  // [buffer][plane][row * 8 + swizzled chunk]
+  __shared__ uint4 Bs[STAGES][BN * 8];
 
   const int M = g.M, N = g.N, K = g.K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -135,24 +139,45 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     }
   };
 
+  if (DEPTH == 1) {
+    // one staging set: step it + 1's loads are issued while step it is computed
+    if (nk > 0) {
+      gload(ra0, rb0, kbeg);
+      sstore(0, ra0, rb0);
+      __syncthreads();
+    }
+    for (int it = 0; it < nk; ++it) {
+      const int cur = STAGES == 2 ? (it & 1) : 0;
+      if (it + 1 < nk) gload(ra0, rb0, kbeg + (it + 1) * BK);
+      compute(cur);
+      if (STAGES == 1) __syncthreads();
+      if (it + 1 < nk) sstore(STAGES == 2 ? cur ^ 1 : 0, ra0, rb0);
+      __syncthreads();
+    }
+  } else {
   if (nk > 0) {
     gload(ra0, rb0, kbeg);
     if (nk > 1) gload(ra1, rb1, kbeg + BK);
     sstore(0, ra0, rb0);
     __syncthreads();
   }
-  // step it computes LDS buffer it & 1; register set it & 1 is free (stored during step it - 1)
-  // and receives step it + 2; set (it + 1) & 1 holds step it + 1 and goes to LDS after the MFMAs
+  // step it computes LDS buffer it & 1 (buffer 0 with one buffer); register set it & 1 is free
+  // (stored during step it - 1) and receives step it + 2; set (it + 1) & 1 holds step it + 1 and goes
+  // to LDS after the MFMAs -- with one LDS buffer, after a barrier that ends every wave's reads
+  constexpr int B1 = STAGES == 2 ? 1 : 0;
   for (int it = 0; it < nk; it += 2) {
     if (it + 2 < nk) gload(ra0, rb0, kbeg + (it + 2) * BK);
     compute(0);
-    if (it + 1 < nk) sstore(1, ra1, rb1);
+    if (STAGES == 1) __syncthreads();
+    if (it + 1 < nk) sstore(B1, ra1, rb1);
     __syncthreads();
     if (it + 1 >= nk) break;
     if (it + 3 < nk) gload(ra1, rb1, kbeg + (it + 3) * BK);
-    compute(1);
+    compute(B1);
+    if (STAGES == 1) __syncthreads();
     if (it + 2 < nk) sstore(0, ra0, rb0);
     __syncthreads();
+  }
   }
 
   // ---- split-K: write this split's partial; k_splitk_reduce sums them in split order ------------
@@ -250,22 +275,25 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
 struct Cfg {
   int bm, bn;
 };
-constexpr Cfg kCfgs[] = {{128, 128}, {64, 128}, {32, 128}, {16, 128}, {128, 256}};
+constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128}};
 
 }  // namespace
 
 GemmPlan gemm_plan(int M, int N, int K) {
+  // Tile shapes from a sweep on MI355X over the prefill and batched-decode projections.  The big
+  // tiles keep one LDS buffer and one register staging set so that two work-groups fit a CU (the
+  // second hides the first's barrier, LDS and load waits) while each wave owns a 64 x 64 tile:
+  // 128 x 128 up to M = 512 and 64 x 256 above (its 4 MB weight panels kept the long-K 70B
+  // projections 1.5x faster than 128 x 128).  Skinny M uses 64 / 32 / 16 x 128 tiles.  Split K
+  // until the grid holds ~400 work-groups (256 for skinny tiles), each split >= 256 deep.
   GemmPlan p{};
-  // 64 x 128 tiles from M = 33 up: two work-groups fit a CU (64 KB LDS each), and the second
-  // hides the first's barrier and LDS waits (measured faster than 128 x 128 from M = 128 to 4096).
-  // Split K until the grid holds ~2 work-groups per CU (one for skinny M), each split >= 256 deep.
-  p.cfg = M > 32 ? 1 : (M > 16 ? 2 : 3);
+  p.cfg = M > 512 ? 1 : (M > 64 ? 0 : (M > 32 ? 2 : (M > 16 ? 3 : 4)));
   p.bm = kCfgs[p.cfg].bm;
   p.bn = kCfgs[p.cfg].bn;
   p.tiles_m = (M + p.bm - 1) / p.bm;
   p.tiles_n = (N + p.bn - 1) / p.bn;
   const int tiles = p.tiles_m * p.tiles_n;
-  const int target = M > 64 ? 512 : 256;
+  const int target = M > 64 ? 400 : 256;
   p.splitk = 1;
   while (tiles * p.splitk < target && K / (p.splitk * 2) >= 4 * BK && p.splitk < 16) p.splitk *= 2;
   return p;
@@ -276,11 +304,11 @@ namespace {
 template <int NP, int EPI>
 void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) {
   switch (p.cfg) {
-    case 0: k_gemm<128, 128, 2, 2, NP, EPI><<<grid, 256, 0, s>>>(a); break;
-    case 1: k_gemm<64, 128, 1, 4, NP, EPI><<<grid, 256, 0, s>>>(a); break;
-    case 2: k_gemm<32, 128, 1, 4, NP, EPI><<<grid, 256, 0, s>>>(a); break;
-    case 3: k_gemm<16, 128, 1, 4, NP, EPI><<<grid, 256, 0, s>>>(a); break;
-    default: k_gemm<128, 256, 2, 2, NP, EPI><<<grid, 256, 0, s>>>(a); break;
+    case 0: k_gemm<128, 128, 2, 2, NP, EPI, 1, 1><<<grid, 256, 0, s>>>(a); break;
+    case 1: k_gemm<64, 256, 1, 4, NP, EPI, 1, 1><<<grid, 256, 0, s>>>(a); break;
+    case 2: k_gemm<64, 128, 1, 4, NP, EPI, 2, 1><<<grid, 256, 0, s>>>(a); break;
+    case 3: k_gemm<32, 128, 1, 4, NP, EPI, 2, 2><<<grid, 256, 0, s>>>(a); break;
+    default: k_gemm<16, 128, 1, 4, NP, EPI, 2, 2><<<grid, 256, 0, s>>>(a); break;
   }
 }
 
