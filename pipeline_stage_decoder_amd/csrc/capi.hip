@@ -64,13 +64,6 @@ int validate(const stage_model_cfg* m, const stage_stage_cfg* s) {
   if (m->n_q_heads % m->n_kv_heads != 0 || m->n_q_heads / m->n_kv_heads > 16) return STAGE_E_UNSUPPORTED;
   if (m->d_model % 64 != 0 || m->d_ffn % 16 != 0) return STAGE_E_UNSUPPORTED;
   if (s->max_ctx > (1 << 24) || s->max_tokens > (1 << 20) || s->max_slots > (1 << 20)) return STAGE_E_UNSUPPORTED;
-  // the decode attention merge keeps the weights of up to ceil(ctx / 128) splits for each head of
-  // a KV group in LDS (4096 floats)
-  {
-    const int64_t cap = ((int64_t)s->max_ctx + 63) / 64 * 64;
-    const int64_t g = m->n_q_heads / m->n_kv_heads;
-    if (g * ((cap + 127) / 128) > 4096) return STAGE_E_UNSUPPORTED;
-  }
   return STAGE_OK;
 }
 

@@ -20,7 +20,7 @@
 //
 // Decode: work-group = (split of `chunk` keys, KV head, batch row); its 4 waves take a quarter of
 // the chunk each and merge through LDS into one partial per split; a second kernel merges the
-// splits of each (row, KV head) in split order.
+// splits of each (row, query head) in split order.
 // Prefill: work-group = 64 columns (consecutive queries x the group's heads) of one KV head; the
 // 4 waves share 32-key K/V tiles staged in LDS (double-buffered), each wave skipping tiles past its
 // last query.
@@ -221,53 +221,70 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
 
 }
 
-// Merge the splits of one (row, KV head) in split order -> attention output pair buffer.
+// Merge the splits of one (row, query head) in split order -> attention output pair buffer.  A
+// thread owns one output dim: it loads the head's split log-sum-exps and its dim of every split's
+// partial together (up to 16 splits per round trip), takes the maximum, then sums the weighted
+// partials in split order.
 // A separate launch rather than a last-arriving work-group inside the partial kernel: making the
 // partials visible across work-groups inside one kernel takes a device-scope release/acquire,
 // which on gfx950 writes back and invalidates the L2 of every work-group's XCD.
 template <int DH>
-__global__ __launch_bounds__(256) void k_attn_merge(AttnDecodeArgs a) {
-  __shared__ float wts[16 * 64 * 4];        // G * ns weights (G <= 16, ns <= 256)
-  __shared__ float tot[16];
-  const int kvh = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(DH) void k_attn_merge(AttnDecodeArgs a) {
+  constexpr int R = 16;                       // splits per round of loads
+  const int head = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int slot = a.slots[b], pos = a.pos[b];
-  const int G = a.hq / a.hkv;
+  const size_t o = ((size_t)b * a.hq + head) * DH + d;
   if (slot < 0 || slot >= a.max_slots || pos < 0 || pos >= a.ctx_cap) {
-    for (int idx = threadIdx.x; idx < G * DH; idx += 256) {
-      const size_t o = (size_t)b * a.hq * DH + (size_t)kvh * G * DH + idx;
-      a.out[o] = 0;
-      a.out[a.out_ps + o] = 0;
-    }
+    a.out[o] = 0;
+    a.out[a.out_ps + o] = 0;
     return;
   }
-  const int ns = (pos + a.chunk) / a.chunk;  // ceil((pos + 1) / chunk)
-  const size_t row0 = ((size_t)b * a.hq + kvh * G) * a.nsplit;
-  for (int idx = threadIdx.x; idx < G * ns; idx += 256) {
-    const int h = idx / ns, sp = idx - h * ns;
-    wts[idx] = a.part_lse[row0 + (size_t)h * a.nsplit + sp];
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
+  const int ns = (pos + a.chunk) / a.chunk;  // ceil((pos + 1) / chunk); every split holds a key
+  const size_t row0 = ((size_t)b * a.hq + head) * a.nsplit;
+  const float* lse = a.part_lse + row0;
+  const float* po = a.part_o + row0 * DH + d;
+  float L = 0.0f, acc = 0.0f;
+  if (ns <= R) {
+    float l[R], v[R];
     float mm = kNegInf;
-    for (int sp = 0; sp < ns; ++sp) mm = fmaxf(mm, wts[h * ns + sp]);
-    float L = 0.0f;
-    for (int sp = 0; sp < ns; ++sp) {
-      const float f = exp2f(wts[h * ns + sp] - mm);
-      wts[h * ns + sp] = f;
-      L += f;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      l[j] = j < ns ? lse[j] : kNegInf;
+      v[j] = j < ns ? po[(size_t)j * DH] : 0.0f;
     }
-    tot[h] = L;
+#pragma unroll
+    for (int j = 0; j < R; ++j) mm = fmaxf(mm, l[j]);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float f = exp2f(l[j] - mm);        // 0 for the padding
+      L += f;
+      acc += f * v[j];
+    }
+  } else {
+    float mm = kNegInf;
+    for (int s0 = 0; s0 < ns; s0 += R) {
+      float l[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) l[j] = s0 + j < ns ? lse[s0 + j] : kNegInf;
+#pragma unroll
+      for (int j = 0; j < R; ++j) mm = fmaxf(mm, l[j]);
+    }
+    for (int s0 = 0; s0 < ns; s0 += R) {
+      float l[R], v[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        l[j] = s0 + j < ns ? lse[s0 + j] : kNegInf;
+        v[j] = s0 + j < ns ? po[(size_t)(s0 + j) * DH] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const float f = exp2f(l[j] - mm);
+        L += f;
+        acc += f * v[j];
+      }
+    }
   }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * DH; idx += 256) {
-    const int h = idx / DH, d = idx - h * DH;
-    const float* po = a.part_o + (row0 + (size_t)h * a.nsplit) * DH + d;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int sp = 0; sp < ns; ++sp) acc += wts[h * ns + sp] * po[(size_t)sp * DH];
-    store_pair(a.out, a.out_ps, (size_t)b * a.hq * DH + (size_t)(kvh * G + h) * DH + d, acc / tot[h]);
-  }
+  store_pair(a.out, a.out_ps, o, acc / L);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -470,11 +487,11 @@ hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
   if (a.dh == 128) {
     if (a.kv_f32) k_attn_decode<128, true><<<grid, 256, 0, s>>>(a);
     else k_attn_decode<128, false><<<grid, 256, 0, s>>>(a);
-    k_attn_merge<128><<<dim3(a.hkv, a.B), 256, 0, s>>>(a);
+    k_attn_merge<128><<<dim3(a.hq, a.B), 128, 0, s>>>(a);
   } else {
     if (a.kv_f32) k_attn_decode<64, true><<<grid, 256, 0, s>>>(a);
     else k_attn_decode<64, false><<<grid, 256, 0, s>>>(a);
-    k_attn_merge<64><<<dim3(a.hkv, a.B), 256, 0, s>>>(a);
+    k_attn_merge<64><<<dim3(a.hq, a.B), 64, 0, s>>>(a);
   }
   return hipGetLastError();
 }
