@@ -91,8 +91,8 @@ typedef struct {
 typedef struct {
   uint64_t weight_bytes;    /* bf16 matrices, F32 norm gains */
   uint64_t kv_bytes;        /* K and V (bf16, or F32 with STAGE_KV_F32) for every owned block and slot */
-  uint64_t table_bytes;     /* RoPE cos/sin table (F32) */
-  uint64_t workspace_bytes; /* per-call activations, split-K and split-KV partials, counters */
+  uint64_t table_bytes;     /* RoPE cos/sin table (float64) */
+  uint64_t workspace_bytes; /* per-call activations, split-K and split-KV partials, error counter */
   uint64_t total_bytes;     /* arena size stage_create needs (sum of the above with alignment) */
 } stage_plan_t;
 
@@ -179,6 +179,15 @@ int stage_kv_import(stage_t* st, int global_block, int slot, int pos0, int n, co
                     hipStream_t stream);
 int stage_kv_export(stage_t* st, int global_block, int slot, int pos0, int n, void* k, void* v,
                     hipStream_t stream);
+
+/* Greedy sampling: tokens_out[i] = argmax_j logits[i, j] over j < V for i < n, the lowest index
+ * on ties ("41. Many GPUs", Measured: the greedy driver's argmax of the last row's logits).  NaN
+ * never wins (a row of NaN and -inf gives 0).  Needs no stage handle. */
+int stage_greedy(int n, int V, const float* logits, int32_t* tokens_out, hipStream_t stream);
+
+/* The configuration a handle was created with (host copies) and its device. */
+int stage_describe(const stage_t* st, stage_model_cfg* model /*host*/, stage_stage_cfg* stage /*host*/,
+                   int* device /*host*/);
 
 /* Device-side error counter (rows skipped for out-of-range tokens, slots or positions); reading it
  * synchronises `stream`.  reset != 0 clears it afterwards. */

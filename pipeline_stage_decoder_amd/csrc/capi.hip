@@ -450,6 +450,20 @@ hipError_t copy_rope_rows(uint16_t* dst_rows, const uint16_t* src_rows, int head
 
 extern "C" {
 
+int stage_greedy(int n, int V, const float* logits, int32_t* tokens_out, hipStream_t s) {
+  if (n < 0 || V <= 0 || (n > 0 && (!logits || !tokens_out))) return STAGE_E_INVALID;
+  if (n == 0) return STAGE_OK;
+  return launch_argmax(logits, n, V, tokens_out, s) == hipSuccess ? STAGE_OK : STAGE_E_HIP;
+}
+
+int stage_describe(const stage_t* st, stage_model_cfg* model, stage_stage_cfg* stage, int* device) {
+  if (!st) return STAGE_E_INVALID;
+  if (model) *model = st->m;
+  if (stage) *stage = st->s;
+  if (device) *device = st->device;
+  return STAGE_OK;
+}
+
 const char* stage_status_str(int status) {
   switch (status) {
     case STAGE_OK: return "ok";

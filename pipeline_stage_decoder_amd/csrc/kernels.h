@@ -84,6 +84,7 @@ hipError_t launch_kv_import(void* kc, void* vc, int kv_f32, int hkv, int dh, int
 hipError_t launch_kv_export(const void* kc, const void* vc, int kv_f32, int hkv, int dh, int ctx_cap, int slot,
                             int pos0, int n, void* k, void* v, hipStream_t s);
 hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s);
+hipError_t launch_argmax(const float* logits, int n, int V, int32_t* out, hipStream_t s);
 
 // decode GEMV (B <= 4)
 bool gemv_fits(int B, int K);

@@ -78,6 +78,49 @@ __global__ void k_kv_export(const T* kc, const T* vc, int hkv, int dh, int ctx_c
   v[dst] = vc[((((size_t)slot * hkv + h) * (ctx_cap >> 3) + (pos >> 3)) * dh + d) * 8 + (pos & 7)];
 }
 
+
+// Greedy choice per row: the largest logit, the lowest index among equal ones.  Each thread scans
+// a strided subset in ascending index order (a strict > keeps its first maximum), then the
+// (value, index) pairs reduce with the same rule.  NaN compares false and never wins.
+__global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ logits, int V, int32_t* __restrict__ out) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const float* row = logits + (size_t)blockIdx.x * V;
+  float best = -__builtin_huge_valf();
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < V; i += 256) {
+    const float v = row[i];
+    if (v > best) {
+      best = v;
+      bi = i;
+    }
+  }
+  auto better = [](float v, int i, float bv, int bidx) { return v > bv || (v == bv && i < bidx); };
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float v = __shfl_xor(best, o, 64);
+    const int i = __shfl_xor(bi, o, 64);
+    if (better(v, i, best, bi)) {
+      best = v;
+      bi = i;
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sv[wave] = best;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], best, bi)) {
+        best = sv[w];
+        bi = si[w];
+      }
+    out[blockIdx.x] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s) {
@@ -132,5 +175,10 @@ hipError_t launch_kv_export(const void* kc, const void* vc, int kv_f32, int hkv,
     k_kv_export<uint16_t><<<dim3(n, hkv), dh, 0, s>>>(static_cast<const uint16_t*>(kc),
                                                       static_cast<const uint16_t*>(vc), hkv, dh, ctx_cap, slot, pos0,
                                                       static_cast<uint16_t*>(k), static_cast<uint16_t*>(v));
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const float* logits, int n, int V, int32_t* out, hipStream_t s) {
+  k_argmax<<<n, 256, 0, s>>>(logits, V, out);
   return hipGetLastError();
 }

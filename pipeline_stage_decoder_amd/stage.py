@@ -45,6 +45,11 @@ class Plan(ctypes.Structure):
         return {f: int(getattr(self, f)) for f, _ in self._fields_}
 
 
+class GenCfg(ctypes.Structure):
+    _fields_ = [("n_micro", ctypes.c_int32), ("rows", ctypes.c_int32), ("prompt_len", ctypes.c_int32),
+                ("n_new", ctypes.c_int32)]
+
+
 class StageError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(msg)
@@ -69,6 +74,11 @@ EXPORTS = {
     "stage_device_errors": [_vp, _i32, ctypes.POINTER(ctypes.c_uint32), _vp],
     "stage_timing": [_vp, ctypes.c_uint32],
     "stage_timing_read": [_vp, _i32, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_double)],
+    "stage_greedy": [_i32, _i32, _vp, _vp, _vp],
+    "stage_describe": [_vp, ctypes.POINTER(ModelCfg), ctypes.POINTER(StageCfg), ctypes.POINTER(ctypes.c_int)],
+    "stage_pipeline_workspace": [ctypes.POINTER(_vp), _i32, ctypes.POINTER(GenCfg), ctypes.POINTER(ctypes.c_uint64)],
+    "stage_pipeline_generate": [ctypes.POINTER(_vp), _i32, ctypes.POINTER(GenCfg), _vp, _vp, _vp, _u64,
+                                ctypes.POINTER(_vp)],
     "stage_destroy": [_vp],
     "stage_status_str": [_i32],
     "stage_last_error": [_vp],
@@ -282,3 +292,42 @@ class Stage:
         self._check(lib().stage_timing_read(self._h, KERNEL_KINDS[kind], ctypes.byref(n), ctypes.byref(ms)),
                     "stage_timing_read")
         return int(n.value), float(ms.value)
+
+
+def _status(rc: int, what: str):
+    if rc != STAGE_OK:
+        raise StageError(rc, f"{what}: {lib().stage_status_str(rc).decode()}")
+
+
+def greedy(logits: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """int32 [n] = argmax of each row of F32 logits [n, V] (lowest index on ties), on the GPU."""
+    n, v = logits.shape
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=logits.device)
+    _status(lib().stage_greedy(n, v, _ptr(logits.contiguous()), _ptr(out), _stream(stream)), "stage_greedy")
+    return out
+
+
+def pipeline_generate(stages: list, prompts: torch.Tensor, n_new: int, streams=None,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Greedy generation through the ordered stages with micro-batches in flight (include/pipeline.h).
+
+    prompts: int32 [n_micro, rows, prompt_len] on the stages' device; returns int32
+    [n_micro, n_new, rows].  streams: one torch.cuda.Stream per stage, or None for the default
+    stream.  Returns after the run completes."""
+    n_micro, rows, plen = prompts.shape
+    cfg = GenCfg(n_micro, rows, plen, n_new)
+    handles = (_vp * len(stages))(*[s._h.value for s in stages])
+    nbytes = ctypes.c_uint64(0)
+    _status(lib().stage_pipeline_workspace(handles, len(stages), ctypes.byref(cfg), ctypes.byref(nbytes)),
+            "stage_pipeline_workspace")
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = torch.empty(int(nbytes.value), dtype=torch.uint8, device=prompts.device)
+    out = torch.empty((n_micro, n_new, rows), dtype=torch.int32, device=prompts.device)
+    sarr = None
+    if streams is not None:
+        sarr = (_vp * len(stages))(*[_stream(s) for s in streams])
+    _status(lib().stage_pipeline_generate(handles, len(stages), ctypes.byref(cfg), _ptr(prompts.contiguous()),
+                                          _ptr(out), _ptr(workspace), int(workspace.numel()), sarr),
+            "stage_pipeline_generate")
+    return out

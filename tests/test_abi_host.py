@@ -10,11 +10,11 @@ import fixtures as fx
 from pipeline_stage_decoder_amd import stage as S
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "stage.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("stage.h", "pipeline.h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(stage_\w+)\s*\(", text, flags=re.M)))
 
@@ -23,7 +23,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("stage_plan", "stage_create", "stage_load_weight", "stage_embed", "stage_prefill", "stage_decode",
               "stage_readout", "stage_mlp", "stage_kv_copy", "stage_kv_import", "stage_kv_export", "stage_destroy",
-              "stage_status_str", "stage_last_error"):
+              "stage_status_str", "stage_last_error", "stage_greedy", "stage_describe", "stage_pipeline_workspace",
+              "stage_pipeline_generate"):
         assert n in names, n
 
 
@@ -114,3 +115,17 @@ def test_calls_on_a_null_handle_are_refused():
     assert L.stage_readout(None, 1, None, None, None, None) == S.STAGE_E_INVALID
     assert L.stage_embed(None, 1, None, None, None) == S.STAGE_E_INVALID
     assert L.stage_destroy(None) == S.STAGE_OK
+
+
+def test_pipeline_and_greedy_refuse_bad_arguments_on_the_host():
+    L = S.lib()
+    cfg = S.GenCfg(2, 1, 16, 8)
+    nbytes = ctypes.c_uint64(0)
+    assert L.stage_pipeline_workspace(None, 2, ctypes.byref(cfg), ctypes.byref(nbytes)) == S.STAGE_E_INVALID
+    handles = (ctypes.c_void_p * 2)(None, None)
+    assert L.stage_pipeline_workspace(handles, 2, ctypes.byref(cfg), ctypes.byref(nbytes)) == S.STAGE_E_INVALID
+    assert L.stage_pipeline_generate(handles, 0, ctypes.byref(cfg), None, None, None, 0, None) == S.STAGE_E_INVALID
+    assert L.stage_greedy(-1, 10, None, None, None) == S.STAGE_E_INVALID
+    assert L.stage_greedy(2, 0, None, None, None) == S.STAGE_E_INVALID
+    assert L.stage_greedy(0, 10, None, None, None) == S.STAGE_OK          # nothing to do, no GPU call
+    assert L.stage_describe(None, None, None, None) == S.STAGE_E_INVALID
