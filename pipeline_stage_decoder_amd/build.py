@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpsd_stage.so")
-SOURCES = ["capi.hip", "pipeline.hip", "kernels_misc.hip", "kernels_gemv.hip", "kernels_gemm.hip", "kernels_attn.hip"]
+SOURCES = ["capi.hip", "pipeline.hip", "placement.hip", "kernels_misc.hip", "kernels_gemv.hip", "kernels_gemm.hip", "kernels_attn.hip"]
 # Packed FP32 instructions are disabled for all device code; hipcc's host pass warns that it does
 # not know the feature, which is harmless.
 HIPFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -79,6 +79,8 @@ EXPORTS = {
     "stage_pipeline_workspace": [ctypes.POINTER(_vp), _i32, ctypes.POINTER(GenCfg), ctypes.POINTER(ctypes.c_uint64)],
     "stage_pipeline_generate": [ctypes.POINTER(_vp), _i32, ctypes.POINTER(GenCfg), _vp, _vp, _vp, _u64,
                                 ctypes.POINTER(_vp)],
+    "stage_place": [ctypes.POINTER(ModelCfg), ctypes.POINTER(StageCfg), _i32, ctypes.POINTER(ctypes.c_uint64),
+                    ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_uint64)],
     "stage_destroy": [_vp],
     "stage_status_str": [_i32],
     "stage_last_error": [_vp],
@@ -104,6 +106,22 @@ def model_cfg(shape) -> ModelCfg:
     """A stage_model_cfg from any object with the decoder's dimension attributes."""
     return ModelCfg(shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ffn, shape.vocab,
                     shape.n_blocks_total, shape.rms_eps, shape.rope_theta)
+
+
+def place(shape, budgets, *, max_slots: int = 1, max_ctx: int = 2048, max_tokens: int = 512,
+          kv_f32: bool = False):
+    """Contiguous byte-balanced placement over len(budgets) devices (include/placement.h), host only.
+    Returns (cuts, required): device i gets blocks [cuts[i], cuts[i+1])."""
+    n = len(budgets)
+    m = model_cfg(shape)
+    s = StageCfg(0, 0, STAGE_KV_F32 if kv_f32 else 0, max_slots, max_ctx, max_tokens)
+    b = (ctypes.c_uint64 * n)(*[int(x) for x in budgets])
+    cuts = (ctypes.c_int32 * (n + 1))()
+    req = (ctypes.c_uint64 * n)()
+    rc = lib().stage_place(ctypes.byref(m), ctypes.byref(s), n, b, cuts, req)
+    if rc != STAGE_OK:
+        raise StageError(rc, f"stage_place: {lib().stage_status_str(rc).decode()}")
+    return list(cuts), list(req)
 
 
 def plan(shape, block_begin, block_end, first, last, max_slots, max_ctx, max_tokens) -> Plan:

@@ -10,7 +10,7 @@ import fixtures as fx
 from pipeline_stage_decoder_amd import stage as S
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("stage.h", "pipeline.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("stage.h", "pipeline.h", "placement.h")]
 
 
 def declared_functions():
@@ -24,7 +24,7 @@ def test_header_declares_the_boundary():
     for n in ("stage_plan", "stage_create", "stage_load_weight", "stage_embed", "stage_prefill", "stage_decode",
               "stage_readout", "stage_mlp", "stage_kv_copy", "stage_kv_import", "stage_kv_export", "stage_destroy",
               "stage_status_str", "stage_last_error", "stage_greedy", "stage_describe", "stage_pipeline_workspace",
-              "stage_pipeline_generate"):
+              "stage_pipeline_generate", "stage_place"):
         assert n in names, n
 
 
