@@ -169,6 +169,26 @@ int stage_readout(stage_t* st, int n, const float* hidden_in, float* logits_out,
 int stage_mlp(stage_t* st, int global_block, int n, const float* hidden_in, float* out, int accumulate,
               hipStream_t stream);
 
+/* Attention sublayer of one owned block without its residual, for T rows of one slot at positions
+ * pos0 .. pos0+T-1 (as in stage_prefill: K/V written there, row t attends positions
+ * [0, pos0 + t]): out [T, d] (F32) = W_o attention(q, K, V) with q, k, v from
+ * h = RMSNorm(hidden_in) g_attn.  With accumulate != 0 the result is added to out (one F32 add
+ * per element), so stages holding head slices of one attention block -- their query heads' rows
+ * of W_q, their KV heads' rows of W_k / W_v, the matching columns of W_o -- called in slice order
+ * sum the partials as ((p0 + p1) + p2) + ... ("41. Many GPUs", Tensor parallelism: Q, K, V
+ * column-parallel by heads, W_o row-parallel, one all-reduce per attention). */
+int stage_attn(stage_t* st, int global_block, int slot, int pos0, int T, const float* hidden_in, float* out,
+               int accumulate, hipStream_t stream);
+
+/* Embedding of a vocabulary slice on a first stage: the stage's table holds ids
+ * [vocab_lo, vocab_lo + V) of a larger vocabulary.  hidden_out[i, :] = (accumulate ? hidden_out[i, :]
+ * : 0) + (tokens[i] inside ? E[tokens[i] - vocab_lo, :] : 0), so slices called in order assemble
+ * every token's row ("41. Many GPUs", Tensor parallelism: a vocabulary-parallel embedding looks up
+ * zeros outside its slice and the all-reduce sums the slices).  Negative ids count as device
+ * errors. */
+int stage_embed_range(stage_t* st, int n, const int32_t* tokens, int vocab_lo, float* hidden_out, int accumulate,
+                      hipStream_t stream);
+
 /* Copy KV positions [0, n_pos) of every owned block from src_slot to dst_slot. */
 int stage_kv_copy(stage_t* st, int src_slot, int dst_slot, int n_pos, hipStream_t stream);
 

@@ -357,3 +357,91 @@ def mlp_slices(x, g_mlp, wg, wu, wd, eps: float, n_slices: int):
     for p in parts[1:]:
         total = (total + p).astype(np.float32)
     return acts, parts, total
+
+
+# --------------------------------------------------------------------------------------------
+# tensor-parallel slices of attention and of the vocabulary ("41. Many GPUs", Tensor parallelism)
+# --------------------------------------------------------------------------------------------
+
+def attn_sublayer(x: np.ndarray, g_attn, wq, wk, wv, wo, head_dim: int, eps: float, theta: float,
+                  kv_dtype: str = "bf16"):
+    """The attention sublayer of F32 rows x [T, d] at positions 0..T-1 of a fresh sequence, without
+    its residual: W_o . attention(q, K, V), q/k/v from h = RMSNorm(x) * g, K and V stored in the
+    cache format (bf16 or F32) as in Stage.block.  Returns the f64 delta [T, d]."""
+    t = x.shape[0]
+    hq, hkv = wq.shape[0] // head_dim, wk.shape[0] // head_dim
+    pos = np.arange(t)
+    h = rms_norm(x, bf16_to_f32(g_attn), eps)
+    q = rope(linear64(h, wq).reshape(t, hq, head_dim), pos, theta)
+    store = round_bf16 if kv_dtype == "bf16" else (lambda a: np.asarray(a, np.float32))
+    k = store(rope(linear64(h, wk).reshape(t, hkv, head_dim), pos, theta))
+    v = store(linear64(h, wv).reshape(t, hkv, head_dim))
+    o = attention_gqa(q, k, v, pos, pos, head_dim ** -0.5)
+    return linear64(o.reshape(t, hq * head_dim), wo)
+
+
+def head_slices(n_q_heads: int, n_kv_heads: int, n_slices: int):
+    """Slice i's query heads [q0, q0 + hq) and KV heads [kv0, kv0 + hk): query heads split evenly,
+    KV heads split while there are at least as many as slices and otherwise replicated, slice i
+    keeping the KV head its query heads read (kv0 = q0 // (Hq / Hkv))."""
+    if n_q_heads % n_slices or (n_kv_heads % n_slices and n_slices % n_kv_heads):
+        raise ValueError("heads do not split over the slices")
+    hq, hk = n_q_heads // n_slices, max(n_kv_heads // n_slices, 1)
+    out = []
+    for i in range(n_slices):
+        kv0 = i * hk if n_kv_heads >= n_slices else (i * hq) // (n_q_heads // n_kv_heads)
+        out.append((i * hq, hq, kv0, hk))
+    return out
+
+
+def attn_slices(x, g_attn, wq, wk, wv, wo, head_dim: int, eps: float, theta: float, n_slices: int,
+                kv_dtype: str = "bf16"):
+    """Head-sharded attention: slice i keeps its query heads' rows of W_q, its KV heads' rows of
+    W_k / W_v and the matching columns of W_o, and gives an F32 partial; partials are summed in
+    slice order in float32.  Returns (partials, f32 sum)."""
+    hq_all, hkv_all = wq.shape[0] // head_dim, wk.shape[0] // head_dim
+    parts = []
+    for q0, hq, kv0, hk in head_slices(hq_all, hkv_all, n_slices):
+        qr = slice(q0 * head_dim, (q0 + hq) * head_dim)
+        kr = slice(kv0 * head_dim, (kv0 + hk) * head_dim)
+        part = attn_sublayer(x, g_attn, wq[qr], wk[kr], wv[kr], np.ascontiguousarray(wo[:, qr]), head_dim, eps,
+                             theta, kv_dtype)
+        parts.append(part.astype(np.float32))
+    total = parts[0].copy()
+    for p in parts[1:]:
+        total = (total + p).astype(np.float32)
+    return parts, total
+
+
+def vocab_range(vocab: int, n_slices: int, i: int):
+    """(rows per slice, first id, end id) of slice i: the vocabulary padded to a multiple of the
+    slice count, every slice holding the same number of rows."""
+    per = -(-vocab // n_slices)
+    return per, i * per, min(vocab, (i + 1) * per)
+
+
+def vocab_slice(table_bits: np.ndarray, n_slices: int, i: int) -> np.ndarray:
+    """Slice i of a [V, d] bf16 table: its rows, zero rows past V (the padding)."""
+    per, lo, hi = vocab_range(table_bits.shape[0], n_slices, i)
+    out = np.zeros((per, table_bits.shape[1]), table_bits.dtype)
+    out[:hi - lo] = table_bits[lo:hi]
+    return out
+
+
+def embed_slices(table_bits: np.ndarray, tokens: np.ndarray, n_slices: int) -> np.ndarray:
+    """Vocabulary-parallel embedding: slice i looks up its own ids and zeros for the rest; the
+    slices' rows are summed in slice order (F32)."""
+    total = np.zeros((len(tokens), table_bits.shape[1]), np.float32)
+    for i in range(n_slices):
+        per, lo, hi = vocab_range(table_bits.shape[0], n_slices, i)
+        mine = (tokens >= lo) & (tokens < hi)
+        rows = bf16_to_f32(vocab_slice(table_bits, n_slices, i))[np.where(mine, tokens - lo, 0)]
+        total = (total + rows * mine[:, None]).astype(np.float32)
+    return total
+
+
+def readout_slices(h_final: np.ndarray, readout_bits: np.ndarray, n_slices: int) -> np.ndarray:
+    """Vocabulary-parallel head: every slice scores its rows, the scores are concatenated in slice
+    order and cut back to V (F32 logits)."""
+    cols = [linear(h_final, vocab_slice(readout_bits, n_slices, i)) for i in range(n_slices)]
+    return np.concatenate(cols, axis=1)[:, :readout_bits.shape[0]]

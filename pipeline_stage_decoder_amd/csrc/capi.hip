@@ -321,8 +321,10 @@ hipError_t mlp_half(stage* st, int lb, int rows, const float* x, const float* re
 
 // One block over `rows` rows.  Prefill: rp = (slot, pos0), attention over keys [0, pos];
 // decode: rp = per-row slots/positions, split-KV attention.
-int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, const RowPos& rp, bool decode,
-              hipStream_t s) {
+// The attention sublayer of owned block lb: x_out = (resid ? resid : 0) + W_o attention(QKV(norm(x_in))),
+// with K/V written at the rows' positions.
+hipError_t attn_half(stage* st, int lb, int rows, const float* x_in, const float* resid, float* x_out,
+                     const RowPos& rp, bool decode, hipStream_t s) {
   const BlockW& bw = st->blocks[lb];
   const int d = st->m.d_model, hq = st->m.n_q_heads, hkv = st->m.n_kv_heads, dh = st->m.head_dim;
   uint8_t* kc = st->kcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb;
@@ -334,7 +336,8 @@ int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, cons
   e.kc = kc;
   e.vc = vc;
   e.rp = rp;
-  HIP_TRY(st, project(st, STAGE_KT_QKV, rows, x_in, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, 3));
+  hipError_t err = project(st, STAGE_KT_QKV, rows, x_in, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, 3);
+  if (err != hipSuccess) return err;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   if (decode) {
     AttnDecodeArgs a{};
@@ -360,7 +363,7 @@ int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, cons
     a.out = st->attn;
     a.err = st->err;
     Timed t(st, STAGE_KT_ATTN, s);
-    HIP_TRY(st, launch_attn_decode(a, s));
+    err = launch_attn_decode(a, s);
   } else {
     AttnPrefillArgs a{};
     a.q = st->q;
@@ -379,13 +382,19 @@ int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, cons
     a.scale_log2 = scale_log2;
     a.out = st->attn;
     Timed t(st, STAGE_KT_ATTN, s);
-    HIP_TRY(st, launch_attn_prefill(a, s));
+    err = launch_attn_prefill(a, s);
   }
-  EpiArgs eo = epi_base(st, EPI_RESID);
+  if (err != hipSuccess) return err;
+  EpiArgs eo = epi_base(st, resid ? EPI_RESID : EPI_F32);
   eo.out = x_out;
-  eo.resid = x_in;
+  eo.resid = resid;
   eo.ldo = d;
-  HIP_TRY(st, project(st, STAGE_KT_O, rows, nullptr, nullptr, st->attn, ps_q(st), bw.wo, d, hq * dh, eo, s));
+  return project(st, STAGE_KT_O, rows, nullptr, nullptr, st->attn, ps_q(st), bw.wo, d, hq * dh, eo, s);
+}
+
+int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, const RowPos& rp, bool decode,
+              hipStream_t s) {
+  HIP_TRY(st, attn_half(st, lb, rows, x_in, x_in, x_out, rp, decode, s));
   HIP_TRY(st, mlp_half(st, lb, rows, x_out, x_out, x_out, s));
   return STAGE_OK;
 }
@@ -449,6 +458,32 @@ hipError_t copy_rope_rows(uint16_t* dst_rows, const uint16_t* src_rows, int head
 }  // namespace
 
 extern "C" {
+
+int stage_attn(stage_t* st, int global_block, int slot, int pos0, int T, const float* hin, float* out,
+               int accumulate, hipStream_t s) {
+  if (!st || !hin || !out || T <= 0) return fail(st, STAGE_E_INVALID, "bad attn arguments");
+  if (global_block < st->s.block_begin || global_block >= st->s.block_end)
+    return fail(st, STAGE_E_ROLE, "block outside the stage's range");
+  if (T > st->s.max_tokens) return fail(st, STAGE_E_INVALID, "T > max_tokens");
+  if (slot < 0 || slot >= st->s.max_slots || pos0 < 0 || (int64_t)pos0 + T > st->s.max_ctx)
+    return fail(st, STAGE_E_RANGE, "slot or positions out of range");
+  HIP_TRY(st, hipSetDevice(st->device));
+  RowPos rp{nullptr, nullptr, slot, pos0};
+  HIP_TRY(st, attn_half(st, global_block - st->s.block_begin, T, hin, accumulate ? out : nullptr, out, rp, false, s));
+  return STAGE_OK;
+}
+
+int stage_embed_range(stage_t* st, int n, const int32_t* tokens, int vocab_lo, float* hidden_out, int accumulate,
+                      hipStream_t s) {
+  if (!st || !tokens || !hidden_out || n <= 0 || vocab_lo < 0) return fail(st, STAGE_E_INVALID, "bad embed arguments");
+  if (!(st->s.flags & STAGE_FIRST)) return fail(st, STAGE_E_ROLE, "embed on a non-first stage");
+  if (n > st->s.max_tokens) return fail(st, STAGE_E_INVALID, "n > max_tokens");
+  HIP_TRY(st, hipSetDevice(st->device));
+  Timed t(st, STAGE_KT_EMBED, s);
+  HIP_TRY(st, launch_embed_range(st->embed, st->m.vocab, st->m.d_model, vocab_lo, tokens, n, hidden_out, accumulate,
+                                 st->err, s));
+  return STAGE_OK;
+}
 
 int stage_greedy(int n, int V, const float* logits, int32_t* tokens_out, hipStream_t s) {
   if (n < 0 || V <= 0 || (n > 0 && (!logits || !tokens_out))) return STAGE_E_INVALID;

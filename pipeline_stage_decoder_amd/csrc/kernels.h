@@ -77,6 +77,8 @@ struct AttnPrefillArgs {
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s);
 hipError_t launch_embed(const uint16_t* table, int V, int d, const int32_t* tokens, int n, float* out,
                         uint32_t* err, hipStream_t s);
+hipError_t launch_embed_range(const uint16_t* table, int V, int d, int lo, const int32_t* tokens, int n, float* out,
+                              int accumulate, uint32_t* err, hipStream_t s);
 hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s);
 // k, v: [n][Hkv][Dh] in the cache's element type (bf16 bits or F32)
 hipError_t launch_kv_import(void* kc, void* vc, int kv_f32, int hkv, int dh, int ctx_cap, int slot, int pos0,

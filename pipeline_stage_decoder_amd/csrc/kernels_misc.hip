@@ -47,6 +47,29 @@ __global__ __launch_bounds__(256) void k_embed(const uint16_t* __restrict__ tabl
   }
 }
 
+// Embedding rows of a vocabulary slice: the table holds ids [lo, lo + V); other ids contribute a
+// zero row.  out = (accumulate ? out : 0) + row, one F32 add per element.  Negative ids are errors.
+__global__ __launch_bounds__(256) void k_embed_range(const uint16_t* __restrict__ table, int V, int d, int lo,
+                                                     const int32_t* __restrict__ tokens, float* __restrict__ out,
+                                                     int accumulate, uint32_t* err) {
+  const int i = blockIdx.x;
+  const int tok = tokens[i];
+  float* o = out + (size_t)i * d;
+  if (tok < 0 && threadIdx.x == 0) atomicAdd(err, 1u);
+  const bool inside = tok >= lo && tok - lo < V;
+  const uint16_t* e = table + (size_t)(inside ? tok - lo : 0) * d;
+  for (int j = threadIdx.x * 4; j < d; j += 1024) {
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (inside) {
+      const uint2 w = *(const uint2*)(e + j);
+      r = make_float4(bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y));
+    }
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (accumulate) a = *(const float4*)(o + j);
+    *(float4*)(o + j) = make_float4(a.x + r.x, a.y + r.y, a.z + r.z, a.w + r.w);
+  }
+}
+
 __global__ void k_bf16_to_f32(const uint16_t* __restrict__ src, float* __restrict__ dst, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) dst[i] = bf2f(src[i]);
@@ -133,6 +156,13 @@ hipError_t launch_embed(const uint16_t* table, int V, int d, const int32_t* toke
                         uint32_t* err, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   k_embed<<<n, 256, 0, s>>>(table, V, d, tokens, out, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_range(const uint16_t* table, int V, int d, int lo, const int32_t* tokens, int n, float* out,
+                              int accumulate, uint32_t* err, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_embed_range<<<n, 256, 0, s>>>(table, V, d, lo, tokens, out, accumulate, err);
   return hipGetLastError();
 }
 

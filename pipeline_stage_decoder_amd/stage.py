@@ -74,6 +74,8 @@ EXPORTS = {
     "stage_device_errors": [_vp, _i32, ctypes.POINTER(ctypes.c_uint32), _vp],
     "stage_timing": [_vp, ctypes.c_uint32],
     "stage_timing_read": [_vp, _i32, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_double)],
+    "stage_attn": [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp],
+    "stage_embed_range": [_vp, _i32, _vp, _i32, _vp, _i32, _vp],
     "stage_greedy": [_i32, _i32, _vp, _vp, _vp],
     "stage_describe": [_vp, ctypes.POINTER(ModelCfg), ctypes.POINTER(StageCfg), ctypes.POINTER(ctypes.c_int)],
     "stage_pipeline_workspace": [ctypes.POINTER(_vp), _i32, ctypes.POINTER(GenCfg), ctypes.POINTER(ctypes.c_uint64)],
@@ -264,6 +266,26 @@ class Stage:
             out = torch.empty_like(hidden_in)
         self._check(lib().stage_mlp(self._h, global_block, n, _ptr(hidden_in), _ptr(out), int(accumulate),
                                     _stream(stream)), "stage_mlp")
+        return out
+
+    def attn(self, global_block: int, hidden_in: torch.Tensor, slot: int, pos0: int, out: torch.Tensor | None = None,
+             accumulate: bool = False, stream=None) -> torch.Tensor:
+        """Attention sublayer of one block without its residual (stage_attn)."""
+        t = hidden_in.shape[0]
+        if out is None:
+            out = torch.empty_like(hidden_in)
+        self._check(lib().stage_attn(self._h, global_block, slot, pos0, t, _ptr(hidden_in), _ptr(out), int(accumulate),
+                                     _stream(stream)), "stage_attn")
+        return out
+
+    def embed_range(self, tokens: torch.Tensor, vocab_lo: int, out: torch.Tensor | None = None,
+                    accumulate: bool = False, stream=None) -> torch.Tensor:
+        """Rows of a vocabulary slice holding ids [vocab_lo, vocab_lo + V) (stage_embed_range)."""
+        n = tokens.shape[0]
+        if out is None:
+            out = torch.empty((n, self.shape.d_model), dtype=torch.float32, device=tokens.device)
+        self._check(lib().stage_embed_range(self._h, n, _ptr(tokens), vocab_lo, _ptr(out), int(accumulate),
+                                            _stream(stream)), "stage_embed_range")
         return out
 
     def kv_copy(self, src_slot: int, dst_slot: int, n_pos: int, stream=None):

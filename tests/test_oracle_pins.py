@@ -351,3 +351,85 @@ def test_kv_cache_holds_bf16_values():
     want = o.round_bf16(o.rope(k_raw, np.arange(4), c.rope_theta))
     np.testing.assert_array_equal(k[0, :4], want)
     assert not np.array_equal(k[0, 1:4], o.round_bf16(k_raw[1:]))   # RoPE was applied
+
+
+# ---------------------------------------------------------------------------------------------
+# tensor-parallel slices ("41. Many GPUs", Tensor parallelism)
+# ---------------------------------------------------------------------------------------------
+
+def tp_weights(d, hq, hkv, dh, seed=5):
+    g = fx.gain_bf16(seed, 1, d, 0.1)
+    wq = fx.normal_bf16(seed, 2, hq * dh * d, 0.1).reshape(hq * dh, d)
+    wk = fx.normal_bf16(seed, 3, hkv * dh * d, 0.1).reshape(hkv * dh, d)
+    wv = fx.normal_bf16(seed, 4, hkv * dh * d, 0.1).reshape(hkv * dh, d)
+    wo = fx.normal_bf16(seed, 5, d * hq * dh, 0.1).reshape(d, hq * dh)
+    return g, wq, wk, wv, wo
+
+
+def test_attn_sublayer_single_row_is_wo_times_v():
+    # one row attends only to itself: softmax over one key is 1, so the output is W_o applied to
+    # V of the KV head each query head reads (closed form; catches a wrong head map or operand)
+    d, hq, hkv, dh = 64, 4, 2, 16
+    g, wq, wk, wv, wo = tp_weights(d, hq, hkv, dh)
+    x = fx.normal_f32(5, 9, d).reshape(1, d)
+    got = o.attn_sublayer(x, g, wq, wk, wv, wo, dh, 1e-5, 1e4)
+    h = o.rms_norm(x, o.bf16_to_f32(g), 1e-5)
+    v = o.round_bf16(o.linear64(h, wv).reshape(1, hkv, dh))
+    want = o.linear64(o.gqa_expand(v, hq).reshape(1, hq * dh), wo)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_attn_sublayer_is_the_blocks_attention_half():
+    # a block whose MLP is zero (W_gate = 0 -> silu(0) = 0) outputs x + the attention delta
+    w = fx.draw_stage_weights(TINY, 0, 1, False, False, gain_sigma=0.1)
+    w[("wgate", 0)] = np.zeros_like(w[("wgate", 0)])
+    c = o.Dims.of(TINY)
+    x = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(3), 6 * TINY.d_model).reshape(6, TINY.d_model)
+    s = o.Stage(c, 0, 1, False, False, w, 16)
+    y = s.prefill(x, 0, 0)
+    delta = o.attn_sublayer(x, w[("attn_norm", 0)], w[("wq", 0)], w[("wk", 0)], w[("wv", 0)], w[("wo", 0)],
+                            c.head_dim, c.rms_eps, c.rope_theta)
+    np.testing.assert_array_equal(y, (x + delta).astype(np.float32))
+
+
+@pytest.mark.parametrize("hq,hkv,n", [(4, 2, 2), (4, 2, 4), (8, 8, 4), (8, 2, 8)])
+def test_attn_slices_sum_to_full_attention(hq, hkv, n):
+    d, dh = 64, 16
+    g, wq, wk, wv, wo = tp_weights(d, hq, hkv, dh)
+    x = fx.normal_f32(5, 11, 7 * d).reshape(7, d)
+    full = o.attn_sublayer(x, g, wq, wk, wv, wo, dh, 1e-5, 1e4)
+    # float64 invariant: the exact partials sum to the exact full sublayer
+    exact = []
+    for q0, q_n, kv0, k_n in o.head_slices(hq, hkv, n):
+        qr, kr = slice(q0 * dh, (q0 + q_n) * dh), slice(kv0 * dh, (kv0 + k_n) * dh)
+        exact.append(o.attn_sublayer(x, g, wq[qr], wk[kr], wv[kr], np.ascontiguousarray(wo[:, qr]), dh, 1e-5, 1e4))
+        # every query head of the slice reads the KV head the full model maps it to
+        for hh in range(q0, q0 + q_n):
+            assert kv0 <= hh // (hq // hkv) < kv0 + k_n
+    np.testing.assert_allclose(sum(exact), full, rtol=0, atol=1e-12)
+    parts, total = o.attn_slices(x, g, wq, wk, wv, wo, dh, 1e-5, 1e4, n)
+    np.testing.assert_allclose(total, full, rtol=1e-5, atol=1e-6)
+
+
+def test_head_slices_replicate_kv_heads_past_hkv():
+    # 32 query / 8 KV heads over 16 slices: 2 query heads each, KV head i shared by slices 2i, 2i+1
+    sl = o.head_slices(32, 8, 16)
+    assert [s[2] for s in sl] == [i // 2 for i in range(16)] and all(s[1] == 2 and s[3] == 1 for s in sl)
+    assert [s[2] for s in o.head_slices(32, 8, 4)] == [0, 2, 4, 6]
+    with pytest.raises(ValueError):
+        o.head_slices(32, 8, 3)
+
+
+@pytest.mark.parametrize("vocab,n", [(1024, 3), (1000, 8), (17, 4)])
+def test_vocab_slices_reassemble_embedding_and_logits(vocab, n):
+    d = 32
+    table = fx.normal_bf16(6, 1, vocab * d, 1.0).reshape(vocab, d)
+    per, lo, hi = o.vocab_range(vocab, n, n - 1)
+    assert per * n >= vocab and per * (n - 1) < vocab and hi == vocab
+    toks = np.array([0, vocab - 1, per - 1, per, min(2 * per, vocab - 1), vocab // 2], dtype=np.int64)
+    np.testing.assert_array_equal(o.embed_slices(table, toks, n), o.bf16_to_f32(table)[toks])
+    h = fx.normal_f32(6, 2, 3 * d).reshape(3, d)
+    full = o.linear(h, table)
+    np.testing.assert_allclose(o.readout_slices(h, table, n), full, rtol=1e-6, atol=1e-6)
+    # the padding rows are zero and never reach the logits
+    assert not o.vocab_slice(table, n, n - 1)[hi - lo:].any()
