@@ -305,15 +305,33 @@ PSD_DEV int k_swz(int key) {
   return RC >= 16 ? c * (RC / 16) : c >> 1;
 }
 
+// 4 F32 values -> their bf16 hi and lo planes (the same split as split_hi_lo, half as wide).
+PSD_DEV void split_hi_lo4(const uint4& v, uint2& hi, uint2& lo) {
+  const float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+  uint32_t h[2], l[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t a = f2bf(x[2 * i]), b = f2bf(x[2 * i + 1]);
+    h[i] = a | (b << 16);
+    l[i] = pack_bf2(x[2 * i] - bf2f(a), x[2 * i + 1] - bf2f(b));
+  }
+  hi = make_uint2(h[0], h[1]);
+  lo = make_uint2(l[0], l[1]);
+}
+
 template <int DH, bool KF32>
 __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
   constexpr int EB = KF32 ? 4 : 2;
-  constexpr int ROW_CHUNKS = DH * EB / 16;                 // 16-byte chunks per K row
-  constexpr int TILE_CHUNKS = kKeyTile * ROW_CHUNKS;       // per K tile (V tile the same)
+  constexpr int TILE_CHUNKS = kKeyTile * DH * EB / 16;     // 16-byte global chunks per K (and V) tile
   constexpr int PER_THREAD = TILE_CHUNKS / 256;
   static_assert(TILE_CHUNKS % 256 == 0, "tile chunks per thread");
-  __shared__ uint4 kt[2][TILE_CHUNKS];
-  __shared__ uint4 vt[2][TILE_CHUNKS];
+  // LDS holds bf16 planes: the cache's bf16 values, or an F32 cache's hi and lo planes split once
+  // when the tile is stored (every wave then reads ready MFMA operands in the bf16 layout)
+  constexpr int NPL = KF32 ? 2 : 1;
+  constexpr int RC = DH / 8;                               // 16-byte chunks per bf16 K row
+  constexpr int PLANE = kKeyTile * RC;                     // uint4 per plane tile
+  __shared__ uint4 kt[2][NPL][PLANE];
+  __shared__ uint4 vt[2][NPL][PLANE];
 
   const int G = a.hq / a.hkv;
   const int kvh = blockIdx.y;
@@ -353,9 +371,23 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       const int q = threadIdx.x + i * 256;
-      const int row = q / ROW_CHUNKS, ch = q - row * ROW_CHUNKS;
-      kt[buf][row * ROW_CHUNKS + (ch ^ k_swz<ROW_CHUNKS>(row))] = kr[i];
-      vt[buf][q] = vr[i];
+      if (KF32) {
+        // K: chunk q holds dims 4ch .. 4ch+3 of key `row` = half `hf` of bf16 chunk ch / 2
+        const int row = q / (DH / 4), ch = q - row * (DH / 4);
+        const int u2 = (row * RC + ((ch >> 1) ^ k_swz<RC>(row))) * 2 + (ch & 1);
+        uint2 hi, lo;
+        split_hi_lo4(kr[i], hi, lo);
+        reinterpret_cast<uint2*>(kt[buf][0])[u2] = hi;
+        reinterpret_cast<uint2*>(kt[buf][NPL - 1])[u2] = lo;
+        // V: chunk q holds keys 4(q&1) .. +4 of one (group, dim): half of its bf16 chunk, index q
+        split_hi_lo4(vr[i], hi, lo);
+        reinterpret_cast<uint2*>(vt[buf][0])[q] = hi;
+        reinterpret_cast<uint2*>(vt[buf][NPL - 1])[q] = lo;
+      } else {
+        const int row = q / RC, ch = q - row * RC;
+        kt[buf][0][row * RC + (ch ^ k_swz<RC>(row))] = kr[i];
+        vt[buf][0][q] = vr[i];
+      }
     }
   };
 
@@ -372,20 +404,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const int key = key_of_row(col, cc);
+        const int sw = k_swz<RC>(key);
 #pragma unroll
         for (int ks = 0; ks < DH / 32; ++ks) {
-          const int ch = (ks * 32 + grp * 8) * EB / 16;     // first chunk of the 8 elements
-          const uint4* row = &kt[cur][key * ROW_CHUNKS];
-          const int sw = k_swz<ROW_CHUNKS>(key);
-          if (KF32) {
-            const uint4 x = row[ch ^ sw], y = row[(ch + 1) ^ sw];
-            float f[8] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w),
-                          __uint_as_float(y.x), __uint_as_float(y.y), __uint_as_float(y.z), __uint_as_float(y.w)};
-            split_hi_lo(f, kh[cc][ks], kl[cc][ks]);
-          } else {
-            kh[cc][ks] = row[ch ^ sw];
-            kl[cc][ks] = make_uint4(0, 0, 0, 0);
-          }
+          const int at = key * RC + ((ks * 4 + grp) ^ sw);
+          kh[cc][ks] = kt[cur][0][at];
+          kl[cc][ks] = KF32 ? kt[cur][NPL - 1][at] : make_uint4(0, 0, 0, 0);
         }
       }
       f32x4_t sc[2];
@@ -432,17 +456,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
       const int nvalid = kend - (kb + grp * 8);
 #pragma unroll
       for (int dt = 0; dt < DH / 16; ++dt) {
-        const int q = (grp * DH + dt * 16 + col) * 8 * EB / 16;
-        uint4 vh, vl;
-        if (KF32) {
-          const uint4 x = vt[cur][q], y = vt[cur][q + 1];
-          float f[8] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w),
-                        __uint_as_float(y.x), __uint_as_float(y.y), __uint_as_float(y.z), __uint_as_float(y.w)};
-          split_hi_lo(f, vh, vl);
-        } else {
-          vh = vt[cur][q];
-          vl = make_uint4(0, 0, 0, 0);
-        }
+        const int q = grp * DH + dt * 16 + col;
+        uint4 vh = vt[cur][0][q];
+        uint4 vl = KF32 ? vt[cur][NPL - 1][q] : make_uint4(0, 0, 0, 0);
         if (nvalid < 8) {
           vh = mask_tail(vh, nvalid);
           vl = mask_tail(vl, nvalid);
