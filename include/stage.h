@@ -180,6 +180,18 @@ int stage_mlp(stage_t* st, int global_block, int n, const float* hidden_in, floa
 int stage_attn(stage_t* st, int global_block, int slot, int pos0, int T, const float* hidden_in, float* out,
                int accumulate, hipStream_t stream);
 
+/* Context-parallel (ring) form of stage_attn for a whole sequence of T rows at positions 0..T-1 of
+ * one slot ("41. Many GPUs", Ring attention for very long contexts): the sequence is cut into
+ * n_ranks chunks (zigzag != 0: 2 n_ranks chunks, rank r holding chunks r and 2 n_ranks - 1 - r);
+ * each rank attends its queries to the K/V chunks it holds at each hop h (those of rank
+ * (r - h) mod n_ranks), and the partial results merge in hop order by their log-sum-exp -- the
+ * split-KV merge.  On one device the ranks run one after another over the slot's cache; the result
+ * equals stage_attn's up to F32 rounding of the merges.  T must be a multiple of the chunk count.
+ * workspace: device memory of stage_attn_ring_workspace() bytes, 256-byte aligned. */
+int stage_attn_ring_workspace(const stage_t* st, int T, uint64_t* bytes /*host*/);
+int stage_attn_ring(stage_t* st, int global_block, int slot, int T, int n_ranks, int zigzag, const float* hidden_in,
+                    float* out, int accumulate, void* workspace, uint64_t workspace_bytes, hipStream_t stream);
+
 /* Embedding of a vocabulary slice on a first stage: the stage's table holds ids
  * [vocab_lo, vocab_lo + V) of a larger vocabulary.  hidden_out[i, :] = (accumulate ? hidden_out[i, :]
  * : 0) + (tokens[i] inside ? E[tokens[i] - vocab_lo, :] : 0), so slices called in order assemble

@@ -445,3 +445,54 @@ def readout_slices(h_final: np.ndarray, readout_bits: np.ndarray, n_slices: int)
     order and cut back to V (F32 logits)."""
     cols = [linear(h_final, vocab_slice(readout_bits, n_slices, i)) for i in range(n_slices)]
     return np.concatenate(cols, axis=1)[:, :readout_bits.shape[0]]
+
+
+# --------------------------------------------------------------------------------------------
+# context parallelism: ring attention ("41. Many GPUs", Ring attention for very long contexts)
+# --------------------------------------------------------------------------------------------
+
+def ring_chunks(T: int, n_ranks: int, zigzag: bool):
+    """Query/KV position ranges each rank holds: rank r gets [rT, (r+1)T) of n equal chunks, or
+    with zigzag the 2n chunks r and 2n - 1 - r (which evens out causal work)."""
+    if zigzag:
+        c = T // (2 * n_ranks)
+        return [[(r * c, (r + 1) * c), ((2 * n_ranks - 1 - r) * c, (2 * n_ranks - r) * c)] for r in range(n_ranks)]
+    c = T // n_ranks
+    return [[(r * c, (r + 1) * c)] for r in range(n_ranks)]
+
+
+def ring_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_ranks: int, zigzag: bool = False):
+    """Causal GQA attention of a whole sequence (positions 0..T-1; q [T, Hq, D], k / v [T, Hkv, D])
+    computed the ring way: rank r holds its chunks' queries and keys; at hop h it holds the K/V of
+    rank (r - h) mod n and attends its queries to it (attention_partial), merging the partials in
+    hop order by log-sum-exp (merge_partials).  Returns the f64 output [T, Hq, D]."""
+    t, hq, dd = q.shape
+    kx, vx = gqa_expand(k, hq), gqa_expand(v, hq)
+    chunks = ring_chunks(t, n_ranks, zigzag)
+    out = np.zeros((t, hq, dd))
+    for r in range(n_ranks):
+        for qa, qb in chunks[r]:
+            qp = np.arange(qa, qb)
+            acc, lse = np.zeros((qb - qa, hq, dd)), np.full((qb - qa, hq), -np.inf)
+            for hop in range(n_ranks):
+                owner = (r - hop) % n_ranks
+                for ka, kb in chunks[owner]:
+                    o, l = attention_partial(q[qa:qb], kx[ka:kb], vx[ka:kb], qp, np.arange(ka, kb), dd ** -0.5)
+                    acc, lse = merge_partials(acc, lse, o, l)
+            out[qa:qb] = acc
+    return out
+
+
+def attn_sublayer_ring(x: np.ndarray, g_attn, wq, wk, wv, wo, head_dim: int, eps: float, theta: float,
+                       n_ranks: int, zigzag: bool, kv_dtype: str = "bf16"):
+    """attn_sublayer with the attention taken by ring_attention (f64 delta [T, d])."""
+    t = x.shape[0]
+    hq, hkv = wq.shape[0] // head_dim, wk.shape[0] // head_dim
+    pos = np.arange(t)
+    h = rms_norm(x, bf16_to_f32(g_attn), eps)
+    q = rope(linear64(h, wq).reshape(t, hq, head_dim), pos, theta)
+    store = round_bf16 if kv_dtype == "bf16" else (lambda a: np.asarray(a, np.float32))
+    k = store(rope(linear64(h, wk).reshape(t, hkv, head_dim), pos, theta))
+    v = store(linear64(h, wv).reshape(t, hkv, head_dim))
+    o = ring_attention(q, k, v, n_ranks, zigzag)
+    return linear64(o.reshape(t, hq * head_dim), wo)

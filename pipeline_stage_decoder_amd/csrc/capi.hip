@@ -381,6 +381,8 @@ hipError_t attn_half(stage* st, int lb, int rows, const float* x_in, const float
     a.ctx_cap = st->L.ctx_cap;
     a.scale_log2 = scale_log2;
     a.out = st->attn;
+    a.k_lo = 0;
+    a.k_hi = INT32_MAX;
     Timed t(st, STAGE_KT_ATTN, s);
     err = launch_attn_prefill(a, s);
   }
@@ -457,6 +459,30 @@ hipError_t copy_rope_rows(uint16_t* dst_rows, const uint16_t* src_rows, int head
 
 }  // namespace
 
+namespace {
+
+// Ring workspace: per (row, head) partial output and log-sum-exp, and their running accumulators.
+uint64_t ring_ws_bytes(const stage* st, int T) {
+  const uint64_t rh = (uint64_t)T * st->m.n_q_heads;
+  return 2 * ((rh * st->m.head_dim * 4 + 255) / 256 * 256 + (rh * 4 + 255) / 256 * 256);
+}
+
+// Position ranges each of n ranks holds of a T-token sequence: one chunk each, or with zigzag the
+// 2n chunks r and 2n - 1 - r ("41. Many GPUs", Ring attention for very long contexts).
+std::vector<std::vector<std::pair<int, int>>> ring_chunks(int T, int n, bool zigzag) {
+  std::vector<std::vector<std::pair<int, int>>> c(n);
+  if (zigzag) {
+    const int w = T / (2 * n);
+    for (int r = 0; r < n; ++r) c[r] = {{r * w, (r + 1) * w}, {(2 * n - 1 - r) * w, (2 * n - r) * w}};
+  } else {
+    const int w = T / n;
+    for (int r = 0; r < n; ++r) c[r] = {{r * w, (r + 1) * w}};
+  }
+  return c;
+}
+
+}  // namespace
+
 extern "C" {
 
 int stage_attn(stage_t* st, int global_block, int slot, int pos0, int T, const float* hin, float* out,
@@ -482,6 +508,92 @@ int stage_embed_range(stage_t* st, int n, const int32_t* tokens, int vocab_lo, f
   Timed t(st, STAGE_KT_EMBED, s);
   HIP_TRY(st, launch_embed_range(st->embed, st->m.vocab, st->m.d_model, vocab_lo, tokens, n, hidden_out, accumulate,
                                  st->err, s));
+  return STAGE_OK;
+}
+
+int stage_attn_ring_workspace(const stage_t* st, int T, uint64_t* bytes) {
+  if (!st || T <= 0 || !bytes) return STAGE_E_INVALID;
+  *bytes = ring_ws_bytes(st, T);
+  return STAGE_OK;
+}
+
+int stage_attn_ring(stage_t* st, int global_block, int slot, int T, int n_ranks, int zigzag, const float* hin,
+                    float* out, int accumulate, void* workspace, uint64_t workspace_bytes, hipStream_t s) {
+  if (!st || !hin || !out || !workspace || T <= 0 || n_ranks <= 0) return fail(st, STAGE_E_INVALID, "bad ring arguments");
+  if (global_block < st->s.block_begin || global_block >= st->s.block_end)
+    return fail(st, STAGE_E_ROLE, "block outside the stage's range");
+  if (T > st->s.max_tokens) return fail(st, STAGE_E_INVALID, "T > max_tokens");
+  if (T % (n_ranks * (zigzag ? 2 : 1)) != 0) return fail(st, STAGE_E_INVALID, "T is not a multiple of the chunk count");
+  if (slot < 0 || slot >= st->s.max_slots || T > st->s.max_ctx) return fail(st, STAGE_E_RANGE, "slot or positions out of range");
+  if (workspace_bytes < ring_ws_bytes(st, T) || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(st, STAGE_E_DOES_NOT_FIT, "ring workspace too small or misaligned");
+  HIP_TRY(st, hipSetDevice(st->device));
+  const int lb = global_block - st->s.block_begin;
+  const BlockW& bw = st->blocks[lb];
+  const int d = st->m.d_model, hq = st->m.n_q_heads, hkv = st->m.n_kv_heads, dh = st->m.head_dim;
+  uint8_t* kc = st->kcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb;
+  uint8_t* vc = st->vcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb;
+  const uint64_t rh = (uint64_t)T * hq;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* part_o = reinterpret_cast<float*>(ws);
+  ws += (rh * dh * 4 + 255) / 256 * 256;
+  float* part_lse = reinterpret_cast<float*>(ws);
+  ws += (rh * 4 + 255) / 256 * 256;
+  float* acc_o = reinterpret_cast<float*>(ws);
+  ws += (rh * dh * 4 + 255) / 256 * 256;
+  float* acc_lse = reinterpret_cast<float*>(ws);
+
+  // q, K and V of the whole sequence (K/V into the slot's cache at positions 0 .. T-1)
+  EpiArgs e = epi_base(st, EPI_QKV);
+  e.kv_f32 = st->kv_f32;
+  e.q = st->q;
+  e.q_ps = ps_q(st);
+  e.kc = kc;
+  e.vc = vc;
+  e.rp = RowPos{nullptr, nullptr, slot, 0};
+  HIP_TRY(st, project(st, STAGE_KT_QKV, T, hin, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, 3));
+
+  // every rank attends its query chunks to the KV chunks it holds at each hop, merging in hop order
+  const auto chunks = ring_chunks(T, n_ranks, zigzag != 0);
+  AttnPrefillArgs a{};
+  a.q_ps = ps_q(st);
+  a.kc = kc;
+  a.vc = vc;
+  a.kv_f32 = st->kv_f32;
+  a.slot = slot;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.dh = dh;
+  a.ctx_cap = st->L.ctx_cap;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  for (int r = 0; r < n_ranks; ++r)
+    for (const auto& qc : chunks[r]) {
+      const int qa = qc.first, qn = qc.second - qc.first;
+      bool first = true;
+      for (int hop = 0; hop < n_ranks; ++hop) {
+        const int owner = ((r - hop) % n_ranks + n_ranks) % n_ranks;
+        for (const auto& kc2 : chunks[owner]) {
+          if (kc2.first >= qc.second) continue;   // keys after every query: an empty partial
+          a.q = st->q + (size_t)qa * hq * dh;
+          a.pos0 = qa;
+          a.T = qn;
+          a.k_lo = kc2.first;
+          a.k_hi = kc2.second;
+          a.part_o = part_o + (size_t)qa * hq * dh;
+          a.part_lse = part_lse + (size_t)qa * hq;
+          HIP_TRY(st, launch_attn_prefill(a, s));
+          HIP_TRY(st, launch_ring_merge(acc_o + (size_t)qa * hq * dh, acc_lse + (size_t)qa * hq, a.part_o,
+                                        a.part_lse, qn, hq, dh, first ? 1 : 0, s));
+          first = false;
+        }
+      }
+    }
+  HIP_TRY(st, launch_ring_store(acc_o, T, hq, dh, st->attn, ps_q(st), s));
+  EpiArgs eo = epi_base(st, accumulate ? EPI_RESID : EPI_F32);
+  eo.out = out;
+  eo.resid = accumulate ? out : nullptr;
+  eo.ldo = d;
+  HIP_TRY(st, project(st, STAGE_KT_O, T, nullptr, nullptr, st->attn, ps_q(st), bw.wo, d, hq * dh, eo, s));
   return STAGE_OK;
 }
 

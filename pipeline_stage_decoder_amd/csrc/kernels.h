@@ -71,7 +71,20 @@ struct AttnPrefillArgs {
   float scale_log2;
   uint16_t* out;            // pair buffer [T][Hq*Dh]
   size_t out_ps;
+  // keys attended: positions [k_lo, k_hi) that are also <= the query's position (0, INT_MAX: all)
+  int k_lo, k_hi;
+  // partial mode (non-null): per (row, head) the normalised partial output [T][Hq][Dh] F32 and its
+  // base-2 log-sum-exp [T][Hq] (-inf for a row that sees no key) instead of the pair buffer
+  float* part_o;
+  float* part_lse;
 };
+
+// Ring merge of one partial into running (out, lse) F32 accumulators [rows][Hq](*Dh): first != 0
+// copies, otherwise the log-sum-exp merge; store_pairs writes the accumulated output as pairs.
+hipError_t launch_ring_merge(float* acc_o, float* acc_lse, const float* part_o, const float* part_lse, int rows,
+                             int hq, int dh, int first, hipStream_t s);
+hipError_t launch_ring_store(const float* acc_o, int rows, int hq, int dh, uint16_t* out, size_t out_ps,
+                             hipStream_t s);
 
 // norm / misc
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s);

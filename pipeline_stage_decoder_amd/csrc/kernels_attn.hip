@@ -348,8 +348,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
   const int wlast = wave_live ? min(c0 + 15, ncols - 1) : 0;
   const int wave_kend = a.pos0 + wlast / G + 1;            // keys [0, wave_kend) matter to this wave
   const int blast = min(cblk * 64 + 63, ncols - 1);
-  const int kend = a.pos0 + blast / G + 1;                 // keys the work-group walks
-  const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
+  const int kend = min(a.pos0 + blast / G + 1, a.k_hi);   // keys the work-group walks: [k_lo, kend)
+  const int tile0 = a.k_lo / kKeyTile;
+  const int ntiles = kend > a.k_lo ? (kend + kKeyTile - 1) / kKeyTile : tile0;
 
   Col16<DH> st;
   load_q(st, cvalid ? a.q + ((size_t)t * a.hq + head) * DH : nullptr, a.q_ps);
@@ -391,14 +392,16 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
     }
   };
 
-  gload(0);
-  sstore(0);
+  if (tile0 < ntiles) {
+    gload(tile0);
+    sstore(tile0 & 1);
+  }
   __syncthreads();
-  for (int tile = 0; tile < ntiles; ++tile) {
+  for (int tile = tile0; tile < ntiles; ++tile) {
     const int cur = tile & 1;
     if (tile + 1 < ntiles) gload(tile + 1);
     const int kb = tile * kKeyTile;
-    if (wave_live && kb < wave_kend) {
+    if (wave_live && kb < wave_kend && kb < kend) {
       // K fragments: A row rho of chunk c is key key_of_row(rho, c); 8 elements at dim ks*32 + grp*8
       uint4 kh[2][DH / 32], kl[2][DH / 32];
 #pragma unroll
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int key = kb + grp * 8 + cc * 4 + j;
-          const float v = (key < kend && key <= my_pos) ? sc[cc][j] * a.scale_log2 : kNegInf;
+          const float v = (key >= a.k_lo && key < kend && key <= my_pos) ? sc[cc][j] * a.scale_log2 : kNegInf;
           sv[cc * 4 + j] = v;
           mx = fmaxf(mx, v);
         }
@@ -476,6 +479,17 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   if (!cvalid) return;
+  if (a.part_o) {
+    // partial of the key range: normalised output and base-2 log-sum-exp (no key: 0 and -inf)
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float* po = a.part_o + ((size_t)t * a.hq + head) * DH;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt)
+      *reinterpret_cast<float4*>(po + dt * 16 + grp * 4) =
+          make_float4(st.o[dt][0] * inv, st.o[dt][1] * inv, st.o[dt][2] * inv, st.o[dt][3] * inv);
+    if (grp == 0) a.part_lse[(size_t)t * a.hq + head] = l > 0.0f ? st.m + log2f(l) : kNegInf;
+    return;
+  }
   const float inv = 1.0f / l;
   uint16_t* out = a.out + (size_t)t * a.hq * DH + (size_t)head * DH;
 #pragma unroll
@@ -487,6 +501,39 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
     *reinterpret_cast<uint2*>(out + d) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
     *reinterpret_cast<uint2*>(out + a.out_ps + d) = make_uint2(ll[0] | (ll[1] << 16), ll[2] | (ll[3] << 16));
   }
+}
+
+// ------------------------------------------------------------------------------------------------
+// ring attention: merge a key range's partial into running accumulators, in hop order
+// ------------------------------------------------------------------------------------------------
+// One work-group per (row, head), one thread per dim.  All threads read the old log-sum-exp before
+// thread 0 replaces it.
+template <int DH>
+__global__ __launch_bounds__(DH) void k_ring_merge(float* __restrict__ acc_o, float* __restrict__ acc_lse,
+                                                   const float* __restrict__ part_o,
+                                                   const float* __restrict__ part_lse, int first) {
+  const size_t rh = blockIdx.x;
+  const int d = threadIdx.x;
+  const float pl = part_lse[rh], po = part_o[rh * DH + d];
+  if (first) {
+    acc_o[rh * DH + d] = po;
+    if (d == 0) acc_lse[rh] = pl;
+    return;
+  }
+  const float al = acc_lse[rh];
+  float top = fmaxf(al, pl);
+  if (top == kNegInf) top = 0.0f;
+  const float wa = exp2f(al - top), wb = exp2f(pl - top), tot = wa + wb;
+  acc_o[rh * DH + d] = tot > 0.0f ? (acc_o[rh * DH + d] * wa + po * wb) / tot : 0.0f;
+  __syncthreads();
+  if (d == 0) acc_lse[rh] = tot > 0.0f ? top + log2f(tot) : kNegInf;
+}
+
+template <int DH>
+__global__ __launch_bounds__(DH) void k_ring_store(const float* __restrict__ acc_o, uint16_t* __restrict__ out,
+                                                   size_t out_ps) {
+  const size_t i = (size_t)blockIdx.x * DH + threadIdx.x;
+  store_pair(out, out_ps, i, acc_o[i]);
 }
 
 }  // namespace
@@ -522,5 +569,23 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
     if (a.kv_f32) k_attn_prefill<64, true><<<grid, 256, 0, s>>>(a);
     else k_attn_prefill<64, false><<<grid, 256, 0, s>>>(a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_merge(float* acc_o, float* acc_lse, const float* part_o, const float* part_lse, int rows,
+                             int hq, int dh, int first, hipStream_t s) {
+  const unsigned n = (unsigned)rows * hq;
+  if (n == 0) return hipSuccess;
+  if (dh == 128) k_ring_merge<128><<<n, 128, 0, s>>>(acc_o, acc_lse, part_o, part_lse, first);
+  else k_ring_merge<64><<<n, 64, 0, s>>>(acc_o, acc_lse, part_o, part_lse, first);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_store(const float* acc_o, int rows, int hq, int dh, uint16_t* out, size_t out_ps,
+                             hipStream_t s) {
+  const unsigned n = (unsigned)rows * hq;
+  if (n == 0) return hipSuccess;
+  if (dh == 128) k_ring_store<128><<<n, 128, 0, s>>>(acc_o, out, out_ps);
+  else k_ring_store<64><<<n, 64, 0, s>>>(acc_o, out, out_ps);
   return hipGetLastError();
 }

@@ -76,6 +76,8 @@ EXPORTS = {
     "stage_timing_read": [_vp, _i32, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_double)],
     "stage_attn": [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp],
     "stage_embed_range": [_vp, _i32, _vp, _i32, _vp, _i32, _vp],
+    "stage_attn_ring_workspace": [_vp, _i32, ctypes.POINTER(ctypes.c_uint64)],
+    "stage_attn_ring": [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _u64, _vp],
     "stage_greedy": [_i32, _i32, _vp, _vp, _vp],
     "stage_describe": [_vp, ctypes.POINTER(ModelCfg), ctypes.POINTER(StageCfg), ctypes.POINTER(ctypes.c_int)],
     "stage_pipeline_workspace": [ctypes.POINTER(_vp), _i32, ctypes.POINTER(GenCfg), ctypes.POINTER(ctypes.c_uint64)],
@@ -276,6 +278,20 @@ class Stage:
             out = torch.empty_like(hidden_in)
         self._check(lib().stage_attn(self._h, global_block, slot, pos0, t, _ptr(hidden_in), _ptr(out), int(accumulate),
                                      _stream(stream)), "stage_attn")
+        return out
+
+    def attn_ring(self, global_block: int, hidden_in: torch.Tensor, slot: int, n_ranks: int, zigzag: bool,
+                  out: torch.Tensor | None = None, accumulate: bool = False, stream=None) -> torch.Tensor:
+        """stage_attn with the attention taken the ring way (stage_attn_ring), positions 0..T-1."""
+        t = hidden_in.shape[0]
+        if out is None:
+            out = torch.empty_like(hidden_in)
+        nbytes = ctypes.c_uint64(0)
+        self._check(lib().stage_attn_ring_workspace(self._h, t, ctypes.byref(nbytes)), "stage_attn_ring_workspace")
+        ws = torch.empty(int(nbytes.value), dtype=torch.uint8, device=hidden_in.device)
+        self._check(lib().stage_attn_ring(self._h, global_block, slot, t, n_ranks, int(zigzag), _ptr(hidden_in),
+                                          _ptr(out), int(accumulate), _ptr(ws), int(ws.numel()), _stream(stream)),
+                    "stage_attn_ring")
         return out
 
     def embed_range(self, tokens: torch.Tensor, vocab_lo: int, out: torch.Tensor | None = None,

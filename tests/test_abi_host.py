@@ -24,7 +24,7 @@ def test_header_declares_the_boundary():
     for n in ("stage_plan", "stage_create", "stage_load_weight", "stage_embed", "stage_prefill", "stage_decode",
               "stage_readout", "stage_mlp", "stage_kv_copy", "stage_kv_import", "stage_kv_export", "stage_destroy",
               "stage_status_str", "stage_last_error", "stage_greedy", "stage_describe", "stage_pipeline_workspace",
-              "stage_pipeline_generate", "stage_place", "stage_attn", "stage_embed_range"):
+              "stage_pipeline_generate", "stage_place", "stage_attn", "stage_embed_range", "stage_attn_ring", "stage_attn_ring_workspace"):
         assert n in names, n
 
 

@@ -129,3 +129,29 @@ def test_vocab_slices_embedding_and_readout(name, n):
         if rows <= 4:
             assert torch.equal(cat, lf)
         assert e <= 1e-6 and e_o <= 1e-3
+
+
+@pytest.mark.parametrize("name,T,n,zigzag", [("tiny", 24, 2, False), ("tiny", 24, 4, True), ("8b", 64, 2, False),
+                                             ("8b", 64, 4, True), ("8b", 96, 3, True)])
+def test_ring_attention_matches_the_plain_sublayer(name, T, n, zigzag):
+    # context parallelism ("41. Many GPUs", Ring attention): n ranks' query chunks attend the K/V
+    # chunks passed round the ring, partials merged in hop order; chunks of 3..48 keys straddle the
+    # kernel's 32-key tiles, exercising the key-range masking
+    s = fx.TINY if name == "tiny" else fx.LLAMA8B
+    w = attn_weights(s)
+    x = hidden_rows(53, T, s.d_model)
+    xt = torch.from_numpy(x).cuda()
+    st = Stage(slice_shape(s, s.n_q_heads, s.n_kv_heads), 0, 1, False, False, max_slots=2, max_ctx=128,
+               max_tokens=128)
+    for r, t in w.items():
+        st.load_weight(r, 0, t)
+    plain = st.attn(0, xt, 0, 0).cpu().numpy()
+    ring = st.attn_ring(0, xt, 1, n, zigzag).cpu().numpy()
+    c = o.Dims.of(s)
+    want = o.attn_sublayer_ring(x, w["attn_norm"], w["wq"], w["wk"], w["wv"], w["wo"], s.head_dim, c.rms_eps,
+                                c.rope_theta, n, zigzag)
+    e_gpu, e_o = rel_l2(ring, plain), rel_l2(ring, want)
+    say(f"{name} ring attention T={T}, {n} ranks, zigzag={zigzag}: vs plain (gpu) {e_gpu:.2e}, vs oracle {e_o:.2e}")
+    assert e_gpu <= 1e-5 and e_o <= 1e-3
+    # the ring call wrote the same K/V into its slot
+    assert torch.equal(st.kv_export(0, 0, 0, T)[0], st.kv_export(0, 1, 0, T)[0])

@@ -433,3 +433,41 @@ def test_vocab_slices_reassemble_embedding_and_logits(vocab, n):
     np.testing.assert_allclose(o.readout_slices(h, table, n), full, rtol=1e-6, atol=1e-6)
     # the padding rows are zero and never reach the logits
     assert not o.vocab_slice(table, n, n - 1)[hi - lo:].any()
+
+
+# ---------------------------------------------------------------------------------------------
+# ring attention ("41. Many GPUs", Ring attention for very long contexts)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,zigzag", [(1, False), (2, False), (4, False), (2, True), (4, True)])
+def test_ring_attention_equals_full_causal_attention(n, zigzag):
+    # the hop-ordered LSE merge of every (query chunk, KV chunk) partial is the full softmax
+    t, hq, hkv, dd = 24, 4, 2, 8
+    r = rng(7)
+    q, k, v = r.standard_normal((t, hq, dd)), r.standard_normal((t, hkv, dd)), r.standard_normal((t, hkv, dd))
+    pos = np.arange(t)
+    want = o.attention_gqa(q, k, v, pos, pos, dd ** -0.5)
+    np.testing.assert_allclose(o.ring_attention(q, k, v, n, zigzag), want, rtol=0, atol=1e-12)
+
+
+def test_ring_chunks_cover_the_sequence_and_zigzag_balances_work():
+    for n, zz in ((4, False), (4, True), (3, True)):
+        t = 2 * n * 5
+        cover = sorted(p for ch in o.ring_chunks(t, n, zz) for a, b in ch for p in range(a, b))
+        assert cover == list(range(t))
+    # causal work (visible keys) per rank: zigzag equal, plain chunking rising with the rank
+    def work(n, zz, t=48):
+        return [sum(p + 1 for a, b in ch for p in range(a, b)) for ch in o.ring_chunks(t, n, zz)]
+    assert len(set(work(4, True))) == 1
+    w = work(4, False)
+    assert w == sorted(w) and w[-1] > 3 * w[0]
+
+
+def test_attn_sublayer_ring_matches_attn_sublayer():
+    d, hq, hkv, dh = 64, 4, 2, 16
+    g, wq, wk, wv, wo = tp_weights(d, hq, hkv, dh)
+    x = fx.normal_f32(5, 13, 16 * d).reshape(16, d)
+    full = o.attn_sublayer(x, g, wq, wk, wv, wo, dh, 1e-5, 1e4)
+    for n, zz in ((2, False), (2, True), (4, True)):
+        np.testing.assert_allclose(o.attn_sublayer_ring(x, g, wq, wk, wv, wo, dh, 1e-5, 1e4, n, zz), full,
+                                   rtol=0, atol=1e-11)
