@@ -173,6 +173,149 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// One row (B = 1), K a multiple of 2048: the work-group's 4 waves split K into quarters.  Each lane
+// keeps its 8L input values (L = K / 2048) in registers -- no LDS copy of the input -- and every
+// wave walks all of the work-group's P row pairs over its quarter, weights of the next D pairs in
+// flight.  Per pair a wave reduces its lanes; the 4 quarter sums meet in LDS and are added in
+// quarter order ((q0 + q1) + q2) + q3 before the epilogue.  The RMS scale comes from the same
+// block_rms_scale as the row-norm kernel.
+// ------------------------------------------------------------------------------------------------
+template <int EPI, int L, int D>
+__global__ __launch_bounds__(kGemvThreads) void k_gemv1(GemvArgs a, int P) {
+  constexpr int kMaxP = 32;
+  __shared__ float part[4][kMaxP][2];
+  __shared__ double red[4];
+  const int K = a.K, N = a.N;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int npairs = ((N + 31) >> 5) << 4;
+  const int p0 = blockIdx.x * P;
+  const int k0 = wave * (K >> 2);                 // this wave's quarter of K
+  // weights of pair slot i (pair p0 + i): row r at k0 + (j * 64 + lane) * 8
+  auto load_pair = [&](int i, u32x4 (&w0)[L], u32x4 (&w1)[L]) {
+    const int pp = p0 + i;
+    const int r0 = ((pp >> 4) << 5) + (pp & 15), r1 = r0 + 16;
+    const bool ok0 = i < P && pp < npairs && r0 < N, ok1 = i < P && pp < npairs && r1 < N;
+    const u32x4* q0 = reinterpret_cast<const u32x4*>(a.w + (size_t)(ok0 ? r0 : 0) * K + k0);
+    const u32x4* q1 = reinterpret_cast<const u32x4*>(a.w + (size_t)(ok1 ? r1 : 0) * K + k0);
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      w0[j] = ok0 ? __builtin_nontemporal_load(q0 + j * 64 + lane) : u32x4{0, 0, 0, 0};
+      w1[j] = ok1 ? __builtin_nontemporal_load(q1 + j * 64 + lane) : u32x4{0, 0, 0, 0};
+    }
+  };
+  u32x4 wb0[D][L], wb1[D][L];
+#pragma unroll
+  for (int s = 0; s < D; ++s) load_pair(s, wb0[s], wb1[s]);
+
+  // ---- input quarter -> registers (normalised f32, or the pair buffer expanded) -----------------
+  float x[L][8];
+  if (a.x) {
+    const double r = block_rms_scale(a.x, K, a.eps, red);
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const int k = k0 + (j * 64 + lane) * 8;
+      const float4 v0 = *(const float4*)(a.x + k), v1 = *(const float4*)(a.x + k + 4);
+      const float4 g0 = *(const float4*)(a.gain + k), g1 = *(const float4*)(a.gain + k + 4);
+      x[j][0] = norm_mul(v0.x, r, g0.x); x[j][1] = norm_mul(v0.y, r, g0.y);
+      x[j][2] = norm_mul(v0.z, r, g0.z); x[j][3] = norm_mul(v0.w, r, g0.w);
+      x[j][4] = norm_mul(v1.x, r, g1.x); x[j][5] = norm_mul(v1.y, r, g1.y);
+      x[j][6] = norm_mul(v1.z, r, g1.z); x[j][7] = norm_mul(v1.w, r, g1.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const int k = k0 + (j * 64 + lane) * 8;
+      const uint4 h = *(const uint4*)(a.xb + k), l = *(const uint4*)(a.xb + a.xb_ps + k);
+      const uint32_t hh[4] = {h.x, h.y, h.z, h.w}, ll[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[j][2 * e] = bf_lo(hh[e]) + bf_lo(ll[e]);
+        x[j][2 * e + 1] = bf_hi(hh[e]) + bf_hi(ll[e]);
+      }
+    }
+  }
+
+  // ---- the work-group's pairs, D in flight --------------------------------------------------------
+  for (int i0 = 0; i0 < P; i0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int i = i0 + s;
+      if (i < P) {
+        float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+          const float4 xa = make_float4(x[j][0], x[j][1], x[j][2], x[j][3]);
+          const float4 xc = make_float4(x[j][4], x[j][5], x[j][6], x[j][7]);
+          const uint4 u0 = make_uint4(wb0[s][j].x, wb0[s][j].y, wb0[s][j].z, wb0[s][j].w);
+          const uint4 u1 = make_uint4(wb1[s][j].x, wb1[s][j].y, wb1[s][j].z, wb1[s][j].w);
+          dot8(u0, xa, xc, acc0);
+          dot8(u1, xa, xc, acc1);
+        }
+        load_pair(i + D, wb0[s], wb1[s]);
+        acc0 = wave_sum(acc0);
+        acc1 = wave_sum(acc1);
+        if (lane == 0) {
+          part[wave][i][0] = acc0;
+          part[wave][i][1] = acc1;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- quarter sums in order, epilogue: thread t < P owns pair p0 + t -------------------------------
+  const int t = threadIdx.x;
+  if (t >= P) return;
+  const int p = p0 + t;
+  if (p >= npairs) return;
+  const int r0 = ((p >> 4) << 5) + (p & 15), r1 = r0 + 16;
+  const bool v0 = r0 < N, v1 = r1 < N;
+  const float x0 = ((part[0][t][0] + part[1][t][0]) + part[2][t][0]) + part[3][t][0];
+  const float x1 = ((part[0][t][1] + part[1][t][1]) + part[2][t][1]) + part[3][t][1];
+  const EpiArgs& e = a.e;
+  switch (EPI) {
+    case EPI_F32:
+      if (v0) e.out[r0] = x0;
+      if (v1) e.out[r1] = x1;
+      break;
+    case EPI_RESID:
+      if (v0) e.out[r0] = e.resid[r0] + x0;
+      if (v1) e.out[r1] = e.resid[r1] + x1;
+      break;
+    case EPI_SWIGLU:
+      if (v1) store_pair(e.act, e.act_ps, (size_t)(p >> 4) * 16 + (p & 15), silu_mul(x0, x1));
+      break;
+    case EPI_QKV:
+      if (v1) {
+        int slot, pos;
+        if (!row_slot_pos(e, 0, slot, pos)) {
+          if (r0 == 0) atomicAdd(e.err, 1u);
+        } else {
+          qkv_epilogue_pair(e, 0, r0, x0, x1);
+        }
+      }
+      break;
+  }
+}
+
+template <int EPI, int L, int D>
+void launch_one(const GemvArgs& a, hipStream_t s) {
+  const int npairs = ((a.N + 31) >> 5) << 4;
+  const int P = (npairs + kGemvMaxGrid - 1) / kGemvMaxGrid;
+  const int grid = (npairs + P - 1) / P;
+  k_gemv1<EPI, L, D><<<grid, kGemvThreads, 0, s>>>(a, P);
+}
+
+template <int EPI>
+void launch_one_l(const GemvArgs& a, hipStream_t s) {
+  switch (a.K / 2048) {
+    case 2: launch_one<EPI, 2, 4>(a, s); break;
+    case 4: launch_one<EPI, 4, 2>(a, s); break;
+    default: launch_one<EPI, 7, 2>(a, s); break;
+  }
+}
+
 template <int EPI>
 void launch_nb(const GemvArgs& a, int nb, int grid, size_t lds, hipStream_t s) {
   switch (nb) {
@@ -189,7 +332,24 @@ bool gemv_fits(int B, int K) {
   return B >= 1 && B <= 4 && (size_t)nb * K * 4 <= (size_t)kGemvMaxLds && K % 8 == 0;
 }
 
+// the K-split single-row kernel's shapes: K = 4096, 8192 or 14336, at most 32 row pairs per
+// work-group at the maximum grid
+bool gemv1_fits(int B, int K, int N) {
+  const int L = K / 2048;
+  const int npairs = ((N + 31) >> 5) << 4;
+  return B == 1 && K % 2048 == 0 && (L == 2 || L == 4 || L == 7) && (npairs + kGemvMaxGrid - 1) / kGemvMaxGrid <= 32;
+}
+
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s) {
+  if (gemv1_fits(a.B, a.K, a.N)) {
+    switch (a.e.kind) {
+      case EPI_F32: launch_one_l<EPI_F32>(a, s); break;
+      case EPI_RESID: launch_one_l<EPI_RESID>(a, s); break;
+      case EPI_SWIGLU: launch_one_l<EPI_SWIGLU>(a, s); break;
+      default: launch_one_l<EPI_QKV>(a, s); break;
+    }
+    return hipGetLastError();
+  }
   const int npairs = ((a.N + 31) >> 5) << 4;
   int grid = (npairs + 3) / 4;
   if (grid > kGemvMaxGrid) grid = kGemvMaxGrid;
