@@ -183,6 +183,36 @@ def time_handoff(rows_prefill, row_decode, reps: int = 50) -> dict:
     return out
 
 
+def counter_pass(shape, blocks, T, dev, n_dec: int = 32):
+    """The workload's kernels for a hardware-counter run: one prefill of T tokens, then n_dec eager
+    B = 1 decode steps, no timing events; progress every 8 steps."""
+    import torch
+
+    import fixtures as fx
+    from pipeline_stage_decoder_amd.stage import Stage
+
+    st = Stage(shape, blocks[0], blocks[1], True, False, max_slots=1, max_ctx=T + n_dec, max_tokens=T, device=0,
+               kv_f32=True)
+    fill_weights(st, shape, blocks, True, False, fx.SEED_WEIGHTS)
+    prompt = fx.tokens_gpu(torch.empty(T, dtype=torch.int32, device=dev), fx.SEED_TOKENS, fx.token_stream(0),
+                           shape.vocab)
+    toks = fx.tokens_gpu(torch.empty(n_dec, dtype=torch.int32, device=dev), fx.SEED_TOKENS, fx.token_stream(1),
+                         shape.vocab)
+    pos = torch.arange(T, T + n_dec, dtype=torch.int32, device=dev)
+    slot0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    x = st.prefill(st.embed(prompt), 0, 0)
+    torch.cuda.synchronize()
+    log("[bench] counters: prefill done")
+    x1 = torch.empty((1, shape.d_model), dtype=torch.float32, device=dev)
+    for i in range(n_dec):
+        st.embed(toks[i:i + 1], out=x1)
+        st.decode(x1, slot0, pos[i:i + 1], out=x1)
+        if i % 8 == 7:
+            torch.cuda.synchronize()
+            log(f"[bench] counters: decode step {i + 1}/{n_dec}")
+    print(json.dumps({"phase": "counters", "prefill_tokens": T, "decode_steps": n_dec}), flush=True)
+
+
 def prefill_only(args, shape, blocks, T, dev, stream):
     """Time the prefill alone: stage sized for one T-token prompt, W warmups then K timed prefills."""
     import numpy as np
@@ -506,8 +536,9 @@ def main():
     ap.add_argument("--workload", choices=("first-8b", "last-8b", "mid-70b", "mlp-slices", "pipeline-8b"),
                     default="first-8b",
                     help="first-8b: the benchmark line; the others report the remaining workloads' rooflines")
-    ap.add_argument("--phase", choices=("both", "prefill"), default="both",
-                    help="prefill: only time the prefill (a short run for hardware-counter passes)")
+    ap.add_argument("--phase", choices=("both", "prefill", "counters"), default="both",
+                    help="prefill: only time the prefill; counters: prefill + 32 plain decode steps and nothing "
+                         "else (short runs for hardware-counter passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -556,6 +587,9 @@ def main():
 
     if args.phase == "prefill":
         prefill_only(args, shape, blocks, T, dev, stream)
+        return
+    if args.phase == "counters":
+        counter_pass(shape, blocks, T, dev)
         return
     if args.workload == "last-8b":
         print(json.dumps(batched_decode_line(
@@ -663,6 +697,7 @@ def main():
                 n, ms = st.timing_read(k)
                 kern[k][0] += n
                 kern[k][1] += ms
+            log(f"[bench] eager decode step {i + 1}/{n_dec}")
     st.timing([])
 
     # prefill per-kernel breakdown: one eager prefill of the same prompt with every kind timed

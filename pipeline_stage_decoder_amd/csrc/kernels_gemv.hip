@@ -19,6 +19,7 @@ constexpr int kGemvThreads = 256;
 constexpr int kGemvUnrollDefault = 4;   // 16-byte loads per row per chunk (swept: 4 ~ 8 > 16)
 constexpr int kGemvMaxGrid = 512;        // two work-groups per CU (swept: 512 beats 256 / 1024 / 2048)
 constexpr int kGemvMaxLds = 64 * 1024;
+constexpr int kGemv1Grid = 512;          // k_gemv1 work-groups at most (two per CU)
 
 PSD_DEV void dot8(const uint4& w, const float4& x0, const float4& x1, float& acc) {
   acc = fmaf(bf_lo(w.x), x0.x, acc);
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv1(GemvArgs a, int P) {
 template <int EPI, int L, int D>
 void launch_one(const GemvArgs& a, hipStream_t s) {
   const int npairs = ((a.N + 31) >> 5) << 4;
-  const int P = (npairs + kGemvMaxGrid - 1) / kGemvMaxGrid;
+  const int P = (npairs + kGemv1Grid - 1) / kGemv1Grid;
   const int grid = (npairs + P - 1) / P;
   k_gemv1<EPI, L, D><<<grid, kGemvThreads, 0, s>>>(a, P);
 }
@@ -310,7 +311,7 @@ void launch_one(const GemvArgs& a, hipStream_t s) {
 template <int EPI>
 void launch_one_l(const GemvArgs& a, hipStream_t s) {
   switch (a.K / 2048) {
-    case 2: launch_one<EPI, 2, 4>(a, s); break;
+    case 2: launch_one<EPI, 2, 2>(a, s); break;
     case 4: launch_one<EPI, 4, 2>(a, s); break;
     default: launch_one<EPI, 7, 2>(a, s); break;
   }
@@ -337,7 +338,7 @@ bool gemv_fits(int B, int K) {
 bool gemv1_fits(int B, int K, int N) {
   const int L = K / 2048;
   const int npairs = ((N + 31) >> 5) << 4;
-  return B == 1 && K % 2048 == 0 && (L == 2 || L == 4 || L == 7) && (npairs + kGemvMaxGrid - 1) / kGemvMaxGrid <= 32;
+  return B == 1 && K % 2048 == 0 && (L == 2 || L == 4 || L == 7) && (npairs + kGemv1Grid - 1) / kGemv1Grid <= 32;
 }
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s) {
