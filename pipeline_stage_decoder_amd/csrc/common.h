@@ -122,12 +122,20 @@ PSD_DEV bool row_slot_pos(const EpiArgs& e, int m, int& slot, int& pos) {
   return slot >= 0 && slot < e.max_slots && pos >= 0 && pos < e.ctx_cap;
 }
 
-// Apply the QKV epilogue to one RoPE pair / V pair of outputs of row m.
-// col0 is the stored row index of the first element (col0 % 32 < 16), x0/x1 the two sums of
-// stored rows col0 and col0 + 16.
-PSD_DEV void qkv_epilogue_pair(const EpiArgs& e, int m, int col0, float x0, float x1) {
-  int slot, pos;
-  if (!row_slot_pos(e, m, slot, pos)) return;
+// RoPE (cos, sin) of a stored QKV row pair at position pos: the table entry for q and k rows,
+// unused (1, 0) for V rows.  col0 is the stored row index of the pair's first element.
+PSD_DEV double2 qkv_rope_cs(const EpiArgs& e, int pos, int col0) {
+  const int dh = e.dh, qk = (e.hq + e.hkv) * dh;
+  if (col0 >= qk) return make_double2(1.0, 0.0);
+  const int c = col0 < e.hq * dh ? col0 : col0 - e.hq * dh;
+  const int s = c - (c / dh) * dh;
+  return e.rope[(size_t)pos * (dh >> 1) + rope_pair_dim(s)];
+}
+
+// Store one RoPE pair / V pair of outputs of row m (slot and position valid): x0/x1 are the sums
+// of stored rows col0 and col0 + 16 (col0 % 32 < 16), cs = qkv_rope_cs(e, pos, col0).
+PSD_DEV void qkv_store_pair(const EpiArgs& e, int m, int slot, int pos, int col0, float x0, float x1,
+                            double2 cs) {
   const int dh = e.dh, qw = e.hq * dh, kw = e.hkv * dh;
   if (col0 < qw + kw) {
     const bool is_q = col0 < qw;
@@ -135,7 +143,6 @@ PSD_DEV void qkv_epilogue_pair(const EpiArgs& e, int m, int col0, float x0, floa
     const int head = c / dh, s = c - head * dh;
     const int i = rope_pair_dim(s);
     // rotation in f64 from an f64 table, rounded once to f32 and then to bf16
-    const double2 cs = e.rope[(size_t)pos * (dh >> 1) + i];
     const float y0 = (float)((double)x0 * cs.x - (double)x1 * cs.y);
     const float y1 = (float)((double)x1 * cs.x + (double)x0 * cs.y);
     if (is_q) {
@@ -174,6 +181,14 @@ PSD_DEV void qkv_epilogue_pair(const EpiArgs& e, int m, int col0, float x0, floa
       base[i1] = (uint16_t)f2bf(x1);
     }
   }
+}
+
+// Apply the QKV epilogue to one RoPE pair / V pair of outputs of row m (nothing for a row whose
+// slot or position is out of range).
+PSD_DEV void qkv_epilogue_pair(const EpiArgs& e, int m, int col0, float x0, float x1) {
+  int slot, pos;
+  if (!row_slot_pos(e, m, slot, pos)) return;
+  qkv_store_pair(e, m, slot, pos, col0, x0, x1, qkv_rope_cs(e, pos, col0));
 }
 
 PSD_DEV float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }

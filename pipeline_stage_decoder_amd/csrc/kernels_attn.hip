@@ -227,7 +227,9 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
 // partials in split order.
 // A separate launch rather than a last-arriving work-group inside the partial kernel: making the
 // partials visible across work-groups inside one kernel takes a device-scope release/acquire,
-// which on gfx950 writes back and invalidates the L2 of every work-group's XCD.
+// which on gfx950 writes back and invalidates the L2 of each work-group's XCD.  Measured on the
+// 8B-shaped block at B = 1, ctx 1536: 8.4 + 4.7 us as two kernels; 19.0 us fused with
+// __threadfence, 15.8 us with agent-scope release / acquire fences.
 template <int DH>
 __global__ __launch_bounds__(DH) void k_attn_merge(AttnDecodeArgs a) {
   constexpr int R = 16;                       // splits per round of loads

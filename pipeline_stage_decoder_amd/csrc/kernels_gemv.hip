@@ -209,6 +209,28 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv1(GemvArgs a, int P) {
 #pragma unroll
   for (int s = 0; s < D; ++s) load_pair(s, wb0[s], wb1[s]);
 
+  // epilogue operands that do not depend on the sums (residual rows; the row's slot, position
+  // and RoPE entry) load now, with the weights, rather than after the reduction: thread t < P
+  // owns pair p0 + t
+  const EpiArgs& e = a.e;
+  const int t = threadIdx.x;
+  const int p = p0 + t;
+  const bool own = t < P && p < npairs;
+  const int r0 = ((p >> 4) << 5) + (p & 15), r1 = r0 + 16;
+  const bool v0 = own && r0 < N, v1 = own && r1 < N;
+  float res0 = 0.0f, res1 = 0.0f;
+  int slot = 0, pos = 0;
+  bool row_ok = false;
+  double2 cs = make_double2(1.0, 0.0);
+  if (EPI == EPI_RESID) {
+    if (v0) res0 = e.resid[r0];
+    if (v1) res1 = e.resid[r1];
+  }
+  if (EPI == EPI_QKV && v1) {
+    row_ok = row_slot_pos(e, 0, slot, pos);
+    if (row_ok) cs = qkv_rope_cs(e, pos, r0);
+  }
+
   // ---- input quarter -> registers (normalised f32, or the pair buffer expanded) -----------------
   float x[L][8];
   if (a.x) {
@@ -265,35 +287,28 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv1(GemvArgs a, int P) {
   }
   __syncthreads();
 
-  // ---- quarter sums in order, epilogue: thread t < P owns pair p0 + t -------------------------------
-  const int t = threadIdx.x;
-  if (t >= P) return;
-  const int p = p0 + t;
-  if (p >= npairs) return;
-  const int r0 = ((p >> 4) << 5) + (p & 15), r1 = r0 + 16;
-  const bool v0 = r0 < N, v1 = r1 < N;
+  // ---- quarter sums in order, epilogue -------------------------------------------------------------
+  if (!own) return;
   const float x0 = ((part[0][t][0] + part[1][t][0]) + part[2][t][0]) + part[3][t][0];
   const float x1 = ((part[0][t][1] + part[1][t][1]) + part[2][t][1]) + part[3][t][1];
-  const EpiArgs& e = a.e;
   switch (EPI) {
     case EPI_F32:
       if (v0) e.out[r0] = x0;
       if (v1) e.out[r1] = x1;
       break;
     case EPI_RESID:
-      if (v0) e.out[r0] = e.resid[r0] + x0;
-      if (v1) e.out[r1] = e.resid[r1] + x1;
+      if (v0) e.out[r0] = res0 + x0;
+      if (v1) e.out[r1] = res1 + x1;
       break;
     case EPI_SWIGLU:
       if (v1) store_pair(e.act, e.act_ps, (size_t)(p >> 4) * 16 + (p & 15), silu_mul(x0, x1));
       break;
     case EPI_QKV:
       if (v1) {
-        int slot, pos;
-        if (!row_slot_pos(e, 0, slot, pos)) {
+        if (!row_ok) {
           if (r0 == 0) atomicAdd(e.err, 1u);
         } else {
-          qkv_epilogue_pair(e, 0, r0, x0, x1);
+          qkv_store_pair(e, 0, slot, pos, r0, x0, x1, cs);
         }
       }
       break;
