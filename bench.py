@@ -722,7 +722,7 @@ def main():
     achieved = gu_bytes / gu_avg_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
-                "kernel": "k_gemv1<EPI_SWIGLU, 2, 4> (gate/up projection + SwiGLU, B=1, K split over the 4 waves)",
+                "kernel": "k_gemv1<EPI_SWIGLU, 2, 2> (gate/up projection + SwiGLU, B=1, K split over the 4 waves)",
                 "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 2), "launches": n_gu}
     kernel_avg_us = {k: round(v[1] * 1e3 / max(v[0], 1), 2) for k, v in kern.items()}
 

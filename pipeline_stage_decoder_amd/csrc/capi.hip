@@ -130,14 +130,15 @@ Layout make_layout(const stage_model_cfg& m, const stage_stage_cfg& s) {
   const int shapes[5][2] = {{L.qkv_n, (int)d}, {(int)d, (int)(hq * dh)}, {(int)(2 * F), (int)d},
                             {(int)d, (int)F}, {(int)V, (int)d}};
   for (int Mr = 1; Mr <= s.max_tokens; ++Mr)
-    for (int k = 0; k < 5; ++k) {
-      if (shapes[k][0] <= 0) continue;
-      const GemmPlan p = gemm_plan(Mr, shapes[k][0], shapes[k][1]);
-      if (p.splitk > 1) {
-        const uint64_t need = (uint64_t)p.splitk * Mr * shapes[k][0] * 4;
-        if (need > gpart) gpart = need;
+    for (int k = 0; k < 5; ++k)
+      for (int planes = 2; planes <= 3; ++planes) {
+        if (shapes[k][0] <= 0) continue;
+        const GemmPlan p = gemm_plan(Mr, shapes[k][0], shapes[k][1], planes);
+        if (p.splitk > 1) {
+          const uint64_t need = (uint64_t)p.splitk * Mr * shapes[k][0] * 4;
+          if (need > gpart) gpart = need;
+        }
       }
-    }
   L.gemm_part = take(gpart);
   L.err = take(4);
   L.staging = take(d * 2);
@@ -293,7 +294,7 @@ hipError_t project(stage* st, int kind, int rows, const float* x_f32, const floa
   g.M = rows;
   g.N = N;
   g.K = K;
-  const GemmPlan p = gemm_plan(rows, N, K);
+  const GemmPlan p = gemm_plan(rows, N, K, g.planes);
   g.splitk = p.splitk;
   g.part = st->gemm_part;
   g.e = e;

@@ -106,7 +106,8 @@ bool gemv_fits(int B, int K);
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
 
 // MFMA GEMM
-GemmPlan gemm_plan(int M, int N, int K);
+// planes: bf16 planes of the activation operand (2 or 3)
+GemmPlan gemm_plan(int M, int N, int K, int planes);
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s);
 
 // attention

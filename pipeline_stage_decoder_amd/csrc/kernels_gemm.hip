@@ -35,6 +35,66 @@ PSD_DEV void tile_coords(int block, int nblocks, int tiles_m, int tiles_n, int& 
   tn = in_group / gm;
 }
 
+// Store a wave's accumulators acc[i][j] (rows r0 + i*16 .., columns c0 + j*16 ..; MFMA C layout):
+// the split's f32 partial when K is split, else the epilogue.  Column pairs (c, c + 16) with
+// c % 32 < 16 meet in one lane for the SwiGLU and RoPE epilogues.
+template <int TM, int TN, int WTM, int WTN, int EPI>
+PSD_DEV void gemm_store(const GemmArgs& g, const f32x4_t (&acc)[TM][TN], int r0, int c0, int lane, int split) {
+  const int M = g.M, N = g.N;
+  // ---- split-K: write this split's partial; k_splitk_reduce sums them in split order ------------
+  if (g.splitk > 1) {
+    float* part = g.part + (size_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r = r0 + i * 16 + (lane >> 4) * 4 + jj;
+          const int c = c0 + j * 16 + (lane & 15);
+          if (r < M && c < N) part[(size_t)r * N + c] = acc[i][j][jj];
+        }
+    return;
+  }
+
+  // ---- epilogue ----------------------------------------------------------------------------------
+  const EpiArgs& e = g.e;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = r0 + i * 16 + (lane >> 4) * 4 + jj;
+      if (r >= M) continue;
+      if (EPI == EPI_F32 || EPI == EPI_RESID) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int c = c0 + j * 16 + (lane & 15);
+          if (c >= N) continue;
+          float v = acc[i][j][jj];
+          if (EPI == EPI_RESID) v += e.resid[(size_t)r * e.ldo + c];
+          e.out[(size_t)r * e.ldo + c] = v;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; j += 2) {
+          const int c = c0 + j * 16 + (lane & 15);   // c % 32 < 16, partner c + 16
+          if (c >= N) continue;
+          const float x0 = acc[i][j][jj], x1 = acc[i][j + 1][jj];
+          if (EPI == EPI_SWIGLU) {
+            store_pair(e.act, e.act_ps, (size_t)r * e.ldo + (c >> 5) * 16 + (c & 15), silu_mul(x0, x1));
+          } else {
+            int slot, pos;
+            if (!row_slot_pos(e, r, slot, pos)) {
+              if (c == 0) atomicAdd(e.err, 1u);
+            } else {
+              qkv_epilogue_pair(e, r, c, x0, x1);
+            }
+          }
+        }
+      }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int NP, int EPI, int STAGES, int DEPTH>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   static_assert(DEPTH == 1 || DEPTH == 2, "register staging sets");
@@ -180,58 +240,169 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   }
   }
 
-  // ---- split-K: write this split's partial; k_splitk_reduce sums them in split order ------------
-  if (g.splitk > 1) {
-    float* part = g.part + (size_t)split * M * N;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int r = m0 + wm * WTM + i * 16 + (lane >> 4) * 4 + jj;
-          const int c = n0 + wn * WTN + j * 16 + (lane & 15);
-          if (r < M && c < N) part[(size_t)r * N + c] = acc[i][j][jj];
-        }
-    return;
-  }
+  gemm_store<TM, TN, WTM, WTN, EPI>(g, acc, m0 + wm * WTM, n0 + wn * WTN, lane, split);
+}
 
-  // ---- epilogue ----------------------------------------------------------------------------------
-  const EpiArgs& e = g.e;
+// ------------------------------------------------------------------------------------------------
+// Large tiles for prefill-sized M (activation pair planes): 8 waves own a 256 x 256 tile, each wave
+// 64 x 128 (two waves per SIMD), K in 32-deep stages.  Tiles go from global memory straight into
+// LDS (global_load_lds_dwordx4), so no registers stage them and no ds_write is issued: the
+// accumulators, one stage's fragments and the addresses fit the 256 registers of two waves per
+// SIMD.  ST LDS buffers form a ring: while stage t feeds the MFMAs the loads of stages
+// t + 1 .. t + ST - 2 are in flight, and stage t + ST - 1 is issued into the buffer stage t - 1 has
+// just left.
+// A stage row is 32 k = 4 chunks of 16 bytes; chunk c of row r sits at position c ^ ((r >> 1) & 3),
+// so the 8 rows one ds_read_b128 phase reads land in distinct banks.  One load instruction writes
+// 64 consecutive chunks (16 rows) -- lane l's 16 bytes at position l -- so the swizzle is applied on
+// the global side: lane l fetches the chunk that belongs at position l.
+// The loads are issued from inline assembly and waited for by hand: each wave waits (vmcnt) for
+// its own loads of stage t before the barrier that hands the stage to the other waves.  (Through
+// the compiler builtin, every LDS read would also wait for the loads still in flight.)  The
+// kernel uses no other instruction that reads M0.
+// Per k step each accumulator takes the hi-plane product and then the lo-plane product, the same
+// sequence as k_gemm, so both kernels give identical sums.
+// ------------------------------------------------------------------------------------------------
+constexpr int kDmaBK = 32;
+
+// 16 bytes per lane from global memory (wave-uniform base + the lane's byte offset) into LDS at
+// lds_wave_base + 16 * lane (wave-uniform)
+PSD_DEV void dma16(const uint16_t* base, uint32_t lane_off, uint32_t lds_wave_base) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(lane_off), "s"(base), "s"(lds_wave_base)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8)
+template <int n>
+PSD_DEV void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
+// workgroup barrier that the compiler may not move memory accesses across
+PSD_DEV void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int NP, int EPI, int BM, int BN, int WM, int WN, int ST>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
+  constexpr int BK = kDmaBK, NT = WM * WN * 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 16, TN = WTN / 16;
+  static_assert(WTN % 32 == 0, "paired epilogues need 32-aligned wave columns");
+  constexpr int CH = BK / 8;                               // chunks per row
+  constexpr int A_DMA = BM * CH / NT, B_DMA = BN * CH / NT;     // load instructions per thread
+  static_assert(A_DMA * NT == BM * CH && B_DMA * NT == BN * CH, "whole load instructions");
+  constexpr int PER_STAGE = NP * A_DMA + B_DMA;
+  static_assert(ST >= 3 && ST <= 5, "ring depth");
+  __shared__ uint4 As[ST][NP][BM * CH];
+  __shared__ uint4 Bs[ST][BN * CH];
+
+  const int M = g.M, N = g.N, K = g.K;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int split = blockIdx.y;
+  const int kper = ((K + g.splitk - 1) / g.splitk + BK - 1) / BK * BK;
+  const int kbeg = split * kper;
+  const int kend = min(K, kbeg + kper);
+  const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;    // K and the split ranges are multiples of BK
+
+  // lane's source of load instruction i: row 16 * (wave * n + i) + lane / 4 (past M / N: the last
+  // row, never stored), logical chunk (lane % 4) ^ ((row >> 1) & 3); a byte offset from the
+  // operand's column kbeg (A and W are under 4 GiB)
+  auto src_off = [&](int row0, int rows_max, int i, int n) {
+    const int row = (wave * n + i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    return (uint32_t)(((size_t)min(row0 + row, rows_max - 1) * K + c * 8) * 2);
+  };
+  uint32_t a_off[A_DMA], b_off[B_DMA];
+#pragma unroll
+  for (int i = 0; i < A_DMA; ++i) a_off[i] = src_off(m0, M, i, A_DMA);
+#pragma unroll
+  for (int i = 0; i < B_DMA; ++i) b_off[i] = src_off(n0, N, i, B_DMA);
+  // LDS byte addresses of this wave's destination blocks in stage buffer 0 (wave-uniform)
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t a_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&As[0][0][0] +
+                         (uint32_t)(wave_s * A_DMA * 64 * 16);
+  const uint32_t b_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&Bs[0][0] +
+                         (uint32_t)(wave_s * B_DMA * 64 * 16);
+
+  auto issue = [&](int t) {   // stage t -> buffer t % ST
+    const int buf = t % ST;
+    const size_t k0 = (size_t)kbeg + (size_t)t * BK;
+#pragma unroll
+    for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+      for (int i = 0; i < A_DMA; ++i)
+        dma16(g.a + pl * g.a_ps + k0, a_off[i], a_lds + (uint32_t)((buf * NP + pl) * BM * CH * 16 + i * 64 * 16));
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i) dma16(g.w + k0, b_off[i], b_lds + (uint32_t)(buf * BN * CH * 16 + i * 64 * 16));
+  };
+
+  f32x4_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int r = m0 + wm * WTM + i * 16 + (lane >> 4) * 4 + jj;
-      if (r >= M) continue;
-      if (EPI == EPI_F32 || EPI == EPI_RESID) {
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int kc = lane >> 4;   // logical k chunk of this lane's MFMA operands
+  // s_waitcnt vmcnt(n * PER_STAGE) for n = 0 .. 3 later stages left in flight
+  auto wait_stages = [&](int n) {
+    if (n >= 3) wait_vmcnt<3 * PER_STAGE>();
+    else if (n == 2) wait_vmcnt<2 * PER_STAGE>();
+    else if (n == 1) wait_vmcnt<PER_STAGE>();
+    else wait_vmcnt<0>();
+  };
+
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int c = n0 + wn * WTN + j * 16 + (lane & 15);
-          if (c >= N) continue;
-          float v = acc[i][j][jj];
-          if (EPI == EPI_RESID) v += e.resid[(size_t)r * e.ldo + c];
-          e.out[(size_t)r * e.ldo + c] = v;
-        }
-      } else {
+  for (int t = 0; t < ST - 1; ++t)
+    if (t < nk) issue(t);
+  for (int t = 0; t < nk; ++t) {
+    // stage t's own loads done (later stages' may stay in flight); after the barrier every wave's
+    // loads of stage t are in LDS and no wave still reads stage t - 1's buffer
+    wait_stages(min(ST - 2, nk - 1 - t));
+    lds_barrier();
+    // all of this wave's fragment reads, then the hi-plane MFMAs, the loads of stage t + ST - 1
+    // into the freed buffer, and the MFMAs of the other planes
+    bf16x8_t af[NP][TM], bw[TN];
 #pragma unroll
-        for (int j = 0; j < TN; j += 2) {
-          const int c = n0 + wn * WTN + j * 16 + (lane & 15);   // c % 32 < 16, partner c + 16
-          if (c >= N) continue;
-          const float x0 = acc[i][j][jj], x1 = acc[i][j + 1][jj];
-          if (EPI == EPI_SWIGLU) {
-            store_pair(e.act, e.act_ps, (size_t)r * e.ldo + (c >> 5) * 16 + (c & 15), silu_mul(x0, x1));
-          } else {
-            int slot, pos;
-            if (!row_slot_pos(e, r, slot, pos)) {
-              if (c == 0) atomicAdd(e.err, 1u);
-            } else {
-              qkv_epilogue_pair(e, r, c, x0, x1);
-            }
-          }
-        }
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * WTM + i * 16 + (lane & 15);
+#pragma unroll
+      for (int pl = 0; pl < NP; ++pl)
+        af[pl][i] = as_bf16x8(As[t % ST][pl][row * CH + (kc ^ ((row >> 1) & 3))]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int row = wn * WTN + j * 16 + (lane & 15);
+      bw[j] = as_bf16x8(Bs[t % ST][row * CH + (kc ^ ((row >> 1) & 3))]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int pl = 0; pl < NP; ++pl) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[pl][i], bw[j], acc[i][j]);
+      if (pl == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + ST - 1 < nk) issue(t + ST - 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
+
+  gemm_store<TM, TN, WTM, WTN, EPI>(g, acc, m0 + wm * WTM, n0 + wn * WTN, lane, split);
 }
 
 // Sum the split-K partials of column pairs (c, c + 16), c % 32 < 16, in split order and apply the
@@ -275,18 +446,42 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
 struct Cfg {
   int bm, bn;
 };
-constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128}};
+constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128}, {256, 256}, {128, 256}};
 
 }  // namespace
 
-GemmPlan gemm_plan(int M, int N, int K) {
-  // Tile shapes from a sweep on MI355X over the prefill and batched-decode projections.  The big
-  // tiles keep one LDS buffer and one register staging set so that two work-groups fit a CU (the
-  // second hides the first's barrier, LDS and load waits) while each wave owns a 64 x 64 tile:
-  // 128 x 128 up to M = 512 and 64 x 256 above (its 4 MB weight panels kept the long-K 70B
-  // projections 1.5x faster than 128 x 128).  Skinny M uses 64 / 32 / 16 x 128 tiles.  Split K
-  // until the grid holds ~400 work-groups (256 for skinny tiles), each split >= 256 deep.
+GemmPlan gemm_plan(int M, int N, int K, int planes) {
+  // Tile shapes from sweeps on MI355X over the prefill and batched-decode projections.
+  //  * M >= 256: the LDS-direct kernels, K split until the grid holds ~200 work-groups (one per CU)
+  //    as long as each split keeps >= 1024 of K.  256 x 256 for the activation pair (gate/up and
+  //    the 70B projections 1.2-1.4x faster than the tiles below), else 128 x 256 (the QKV
+  //    projection's three planes; the 512-row O projection split 4 ways).
+  //  * otherwise 128 x 128 up to M = 512 and 64 x 256 above, one LDS buffer and one register
+  //    staging set so that two work-groups fit a CU (the second hides the first's barrier, LDS and
+  //    load waits), each wave owning a 64 x 64 tile; the 64 x 256 tile's 4 MB weight panels keep
+  //    the long-K projections 1.5x faster than 128 x 128.  Skinny M uses 64 / 32 / 16 x 128
+  //    tiles.  Split K until the grid holds ~400 work-groups (256 for skinny tiles), each split
+  //    >= 256 deep.
   GemmPlan p{};
+  if (M >= 256 && K % kDmaBK == 0 && (uint64_t)(M > N ? M : N) * K * 2 < (1ull << 32)) {
+    // cfg 5 (256 x 256, two planes) when it fills the chip, else cfg 6 (128 x 256)
+    for (int cfg = planes == 2 ? 5 : 6; cfg <= 6; ++cfg) {
+      const int bm = kCfgs[cfg].bm, bn = kCfgs[cfg].bn;
+      const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+      const int want = cfg == 5 ? 200 : 190, least = cfg == 5 ? 200 : 128;
+      int sk = 1;
+      while (tiles * sk < want && K / (sk * 2) >= 1024 && sk < 8) sk *= 2;
+      if (tiles * sk >= least) {
+        p.cfg = cfg;
+        p.bm = bm;
+        p.bn = bn;
+        p.tiles_m = (M + bm - 1) / bm;
+        p.tiles_n = (N + bn - 1) / bn;
+        p.splitk = sk;
+        return p;
+      }
+    }
+  }
   p.cfg = M > 512 ? 1 : (M > 64 ? 0 : (M > 32 ? 2 : (M > 16 ? 3 : 4)));
   p.bm = kCfgs[p.cfg].bm;
   p.bn = kCfgs[p.cfg].bn;
@@ -308,6 +503,12 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
     case 1: k_gemm<64, 256, 1, 4, NP, EPI, 1, 1><<<grid, 256, 0, s>>>(a); break;
     case 2: k_gemm<64, 128, 1, 4, NP, EPI, 2, 1><<<grid, 256, 0, s>>>(a); break;
     case 3: k_gemm<32, 128, 1, 4, NP, EPI, 2, 2><<<grid, 256, 0, s>>>(a); break;
+    case 5:   // the planner gives it two planes only
+      k_gemm_dma<2, EPI, 256, 256, 4, 2, 3><<<grid, 512, 0, s>>>(a);
+      break;
+    case 6:
+      k_gemm_dma<NP, EPI, 128, 256, 4, 2, 3><<<grid, 512, 0, s>>>(a);
+      break;
     default: k_gemm<16, 128, 1, 4, NP, EPI, 2, 2><<<grid, 256, 0, s>>>(a); break;
   }
 }
@@ -323,6 +524,9 @@ void launch_reduce(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+  // the LDS-direct tile takes two planes, K in whole 32-deep stages and operands under 4 GiB
+  if ((p.cfg == 5 && a.planes != 2) || (p.cfg >= 5 && ( a.K % kDmaBK != 0 || (uint64_t)(a.M > a.N ? a.M : a.N) * a.K * 2 >= (1ull << 32))))
+    return hipErrorInvalidValue;
   dim3 grid(p.tiles_m * p.tiles_n, p.splitk);
   switch (a.e.kind) {
     case EPI_QKV:

@@ -10,7 +10,9 @@ the stage's kernels at their real shapes on a slice the oracle can follow:
   8192 over a seeded KV cache;
 * sharded MLP: 8 column/row slices of a d 8192 / F 28672 MLP summed in slice order against the full
   MLP at T in {1, 64, 4096} (the T = 4096 oracle check on 64 sampled rows; MLP rows are
-  independent).
+  independent);
+* 8B MLP at T in {257, 300, 512}: the large-tile GEMM with a ragged last row tile, the oracle on
+  sampled rows and every row of the tail.
 Inputs: seeded bf16 N(0, 0.02) weights with norm gains 1 + N(0, 0.1^2), uniform tokens, F32 N(0,1)
 hidden rows, bf16 N(0,1) cached K/V.
 """
@@ -184,6 +186,26 @@ def test_mlp_slices_sum_to_full_mlp(mlp70b, T):
     say(f"  slices vs full (gpu) {e_gpu:.2e}; slices vs oracle {e_sum:.2e}; full vs oracle {e_full:.2e}")
     assert e_gpu <= 1e-5
     assert e_sum <= TOL and e_full <= TOL
+
+
+@pytest.mark.parametrize("T", [257, 300, 512])
+def test_8b_mlp_large_tiles_ragged_rows(w8b_first, T):
+    # T >= 256 rows take the 256 x 256 LDS-direct GEMM (gate/up whole-K, down split over K); rows
+    # past T in the last row tile are clamped reads that must never be stored.  MLP rows are
+    # independent: the oracle checks the first rows, a spread, and every row of the ragged tail.
+    s = fx.LLAMA8B
+    w = {(r, 0): w8b_first[(r, 0)] for r in ("mlp_norm", "wgate", "wup", "wdown")}
+    st = make_stage(s, 0, 1, False, False, w, max_slots=1, max_ctx=64, max_tokens=512)
+    x = hidden_rows(41, T, s.d_model)
+    got = st.mlp(0, torch.from_numpy(x).cuda()).cpu().numpy()
+    tail = np.arange((T - 1) // 256 * 256, T)
+    rows = np.unique(np.concatenate([np.arange(4), np.linspace(0, T - 1, 16).astype(int), tail[-24:]]))
+    say(f"8B MLP T={T}: oracle on {len(rows)} rows")
+    _, want = o.mlp_full(x[rows], w[("mlp_norm", 0)], w[("wgate", 0)], w[("wup", 0)], w[("wdown", 0)], s.rms_eps)
+    e = rel_l2(got[rows], want)
+    say(f"  rel L2 {e:.2e}")
+    assert e <= TOL
+    assert np.isfinite(got).all()
 
 
 def test_8b_first_stage_all_16_blocks_decode_kernels():
