@@ -251,6 +251,11 @@ size_t ps_xn(const stage* st) { return (size_t)st->s.max_tokens * st->m.d_model;
 size_t ps_q(const stage* st) { return (size_t)st->s.max_tokens * st->m.n_q_heads * st->m.head_dim; }
 size_t ps_act(const stage* st) { return (size_t)st->s.max_tokens * st->m.d_ffn; }
 
+// Planes of the QKV operand: three (~24 bits) when K/V are rounded into a bf16 cache, so that the
+// rounding sees f32-grade values; two with an F32 cache, whose values attention splits into two
+// bf16 planes anyway.
+int qkv_planes(const stage* st) { return st->kv_f32 ? 2 : 3; }
+
 // One projection y = x W^T with its epilogue.  x_f32 + gain: the input is RMS-normalised first
 // (fused in the GEMV prologue, or a row pass into the bf16 workspace before the GEMM).
 // planes: bf16 planes of the GEMM operand (2, or 3 for the QKV projection whose K/V outputs are
@@ -337,7 +342,7 @@ hipError_t attn_half(stage* st, int lb, int rows, const float* x_in, const float
   e.kc = kc;
   e.vc = vc;
   e.rp = rp;
-  hipError_t err = project(st, STAGE_KT_QKV, rows, x_in, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, 3);
+  hipError_t err = project(st, STAGE_KT_QKV, rows, x_in, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, qkv_planes(st));
   if (err != hipSuccess) return err;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   if (decode) {
@@ -552,7 +557,7 @@ int stage_attn_ring(stage_t* st, int global_block, int slot, int T, int n_ranks,
   e.kc = kc;
   e.vc = vc;
   e.rp = RowPos{nullptr, nullptr, slot, 0};
-  HIP_TRY(st, project(st, STAGE_KT_QKV, T, hin, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, 3));
+  HIP_TRY(st, project(st, STAGE_KT_QKV, T, hin, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, qkv_planes(st)));
 
   // every rank attends its query chunks to the KV chunks it holds at each hop, merging in hop order
   const auto chunks = ring_chunks(T, n_ranks, zigzag != 0);

@@ -55,14 +55,15 @@ def w8b_first():
     return fx.draw_stage_weights(fx.LLAMA8B, 0, 2, True, False, gain_sigma=0.1)
 
 
-@pytest.mark.parametrize("T", [512, 72])
-def test_8b_first_stage_prefill_and_decode(w8b_first, T):
+@pytest.mark.parametrize("T,kv_f32", [(512, False), (72, False), (512, True)])
+def test_8b_first_stage_prefill_and_decode(w8b_first, T, kv_f32):
+    # with an F32 cache the QKV projection takes two activation planes instead of three
     s = fx.LLAMA8B
     prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(0), T, s.vocab)
-    say(f"8B first stage: oracle prefill T={T}")
-    ost = o.Stage(o.Dims.of(s), 0, 2, True, False, w8b_first, T + 4)
+    say(f"8B first stage: oracle prefill T={T}, {'f32' if kv_f32 else 'bf16'} cache")
+    ost = o.Stage(o.Dims.of(s), 0, 2, True, False, w8b_first, T + 4, kv_dtype="f32" if kv_f32 else "bf16")
     want = ost.prefill(ost.embed(prompt), 0, 0)
-    st = make_stage(s, 0, 2, True, False, w8b_first, max_slots=1, max_ctx=2048, max_tokens=512)
+    st = make_stage(s, 0, 2, True, False, w8b_first, max_slots=1, max_ctx=2048, max_tokens=512, kv_f32=kv_f32)
     dev = torch.device("cuda")
     x = st.embed(torch.tensor(prompt, dtype=torch.int32, device=dev))
     got = st.prefill(x, 0, 0).cpu().numpy()
