@@ -290,10 +290,11 @@ __global__ __launch_bounds__(DH) void k_attn_merge(AttnDecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// prefill: 64 columns (queries x heads of one KV head) per work-group; the 4 waves share 32-key K/V
-// tiles staged in LDS, the next tile's global loads in flight while the current one is consumed
+// prefill: 64 columns (queries x heads of one KV head) per work-group; the 4 waves share 64-key K/V
+// tiles staged in LDS (consumed as two 32-key steps), the next tile's global loads in flight while
+// the current one is consumed
 // ------------------------------------------------------------------------------------------------
-constexpr int kKeyTile = 32;
+constexpr int kKeyTile = 64;   // keys per LDS tile; MFMA steps take 32
 
 // XOR applied to the 16-byte chunk index within K tile row `key` (0..31), RC chunks per row.  The
 // 16 keys one A-operand read touches (key_of_row(col, c), col 0..15) have distinct
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
       if (KF32) {
         // K: chunk q holds dims 4ch .. 4ch+3 of key `row` = half `hf` of bf16 chunk ch / 2
         const int row = q / (DH / 4), ch = q - row * (DH / 4);
-        const int u2 = (row * RC + ((ch >> 1) ^ k_swz<RC>(row))) * 2 + (ch & 1);
+        const int u2 = (row * RC + ((ch >> 1) ^ k_swz<RC>(row & 31))) * 2 + (ch & 1);
         uint2 hi, lo;
         split_hi_lo4(kr[i], hi, lo);
         reinterpret_cast<uint2*>(kt[buf][0])[u2] = hi;
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
         reinterpret_cast<uint2*>(vt[buf][NPL - 1])[q] = lo;
       } else {
         const int row = q / RC, ch = q - row * RC;
-        kt[buf][0][row * RC + (ch ^ k_swz<RC>(row))] = kr[i];
+        kt[buf][0][row * RC + (ch ^ k_swz<RC>(row & 31))] = kr[i];
         vt[buf][0][q] = vr[i];
       }
     }
@@ -402,7 +403,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
   for (int tile = tile0; tile < ntiles; ++tile) {
     const int cur = tile & 1;
     if (tile + 1 < ntiles) gload(tile + 1);
-    const int kb = tile * kKeyTile;
+#pragma unroll
+    for (int sub = 0; sub < kKeyTile / 32; ++sub) {
+    const int kb = tile * kKeyTile + sub * 32;
     if (wave_live && kb < wave_kend && kb < kend) {
       // K fragments: A row rho of chunk c is key key_of_row(rho, c); 8 elements at dim ks*32 + grp*8
       uint4 kh[2][DH / 32], kl[2][DH / 32];
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
         const int sw = k_swz<RC>(key);
 #pragma unroll
         for (int ks = 0; ks < DH / 32; ++ks) {
-          const int at = key * RC + ((ks * 4 + grp) ^ sw);
+          const int at = (sub * 32 + key) * RC + ((ks * 4 + grp) ^ sw);
           kh[cc][ks] = kt[cur][0][at];
           kl[cc][ks] = KF32 ? kt[cur][NPL - 1][at] : make_uint4(0, 0, 0, 0);
         }
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
       const int nvalid = kend - (kb + grp * 8);
 #pragma unroll
       for (int dt = 0; dt < DH / 16; ++dt) {
-        const int q = grp * DH + dt * 16 + col;
+        const int q = (sub * 4 + grp) * DH + dt * 16 + col;
         uint4 vh = vt[cur][0][q];
         uint4 vl = KF32 ? vt[cur][NPL - 1][q] : make_uint4(0, 0, 0, 0);
         if (nvalid < 8) {
@@ -472,6 +475,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
         st.o[dt] = mfma16(as_bf16x8(vh), as_bf16x8(plo), st.o[dt]);
         if (KF32) st.o[dt] = mfma16(as_bf16x8(vl), as_bf16x8(phi), st.o[dt]);
       }
+    }
     }
     if (tile + 1 < ntiles) sstore(cur ^ 1);
     __syncthreads();

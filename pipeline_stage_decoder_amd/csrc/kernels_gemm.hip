@@ -458,9 +458,10 @@ constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128},
 GemmPlan gemm_plan(int M, int N, int K, int planes) {
   // Tile shapes from sweeps on MI355X over the prefill and batched-decode projections.
   //  * M >= 256: the LDS-direct kernels, K split until the grid holds ~200 work-groups (one per CU)
-  //    as long as each split keeps >= 1024 of K.  256 x 256 for the activation pair (gate/up and
-  //    the 70B projections 1.2-1.4x faster than the tiles below), else 128 x 256 (the QKV
-  //    projection's three planes; the 512-row O projection split 4 ways).
+  //    as long as each split keeps >= 1024 of K.  256 x 256 for the activation pair when at most 4
+  //    splits fill the chip (gate/up and the 70B projections 1.2-1.4x faster than the tiles
+  //    below), else 128 x 256 (the QKV projection; the 512-row O and down projections split 4
+  //    ways, as fast as 256 x 256 split 8 with half the partials to reduce).
   //  * 64 < M <= 128 (batched decode): 128 x 256 with 8 waves of 64 x 64 and a deeper ring
   //    (70B-shaped projections at M = 128: 6-10% faster than 128 x 128).
   //  * otherwise 128 x 128 up to M = 512 and 64 x 256 above, one LDS buffer and one register
@@ -490,9 +491,9 @@ GemmPlan gemm_plan(int M, int N, int K, int planes) {
     for (int cfg = planes == 2 ? 5 : 6; cfg <= 6; ++cfg) {
       const int bm = kCfgs[cfg].bm, bn = kCfgs[cfg].bn;
       const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-      const int want = cfg == 5 ? 200 : 190, least = cfg == 5 ? 200 : 128;
+      const int want = cfg == 5 ? 200 : 190, least = cfg == 5 ? 200 : 128, most = cfg == 5 ? 4 : 8;
       int sk = 1;
-      while (tiles * sk < want && K / (sk * 2) >= 1024 && sk < 8) sk *= 2;
+      while (tiles * sk < want && K / (sk * 2) >= 1024 && sk < most) sk *= 2;
       if (tiles * sk >= least) {
         p.cfg = cfg;
         p.bm = bm;
@@ -534,6 +535,7 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
     case 7:
       k_gemm_dma<NP, EPI, 128, 256, 2, 4, NP == 2 ? 4 : 3><<<grid, 512, 0, s>>>(a);
       break;
+
     default: k_gemm<16, 128, 1, 4, NP, EPI, 2, 2><<<grid, 256, 0, s>>>(a); break;
   }
 }
