@@ -18,8 +18,8 @@
 // The softmax is online per column (max and rescale), in base 2 with the scale folded in.  O^T
 // puts a column's values in the same lane as its softmax state, so rescaling needs no shuffles.
 //
-// Decode: work-group = (split of `chunk` keys, KV head, batch row); its 4 waves take a quarter of
-// the chunk each and merge through LDS into one partial per split; a second kernel merges the
+// Decode: work-group = (split of `chunk` keys, KV head, batch row); its 4 waves take every fourth
+// 32-key step of the chunk and merge through LDS into one partial per split; a second kernel merges the
 // splits of each (row, query head) in split order.
 // Prefill: work-group = 64 columns (consecutive queries x the group's heads) of one KV head; the
 // 4 waves share 32-key K/V tiles staged in LDS (double-buffered), each wave skipping tiles past its
@@ -177,16 +177,16 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
   if (k0 >= ctx) return;
   const int k1 = min(k0 + a.chunk, ctx);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
-  const int sub = a.chunk >> 2;
-  const int w0 = k0 + wave * sub, w1 = min(w0 + sub, k1);
 
   Col16<DH> st;
   load_q(st, col < G ? a.q + ((size_t)b * a.hq + kvh * G + col) * DH : nullptr, a.q_ps);
   const size_t eb = KF32 ? 4 : 2;
   const char* kbase = static_cast<const char*>(a.kc) + ((size_t)slot * a.hkv + kvh) * a.ctx_cap * DH * eb;
   const char* vbase = static_cast<const char*>(a.vc) + ((size_t)slot * a.hkv + kvh) * (size_t)a.ctx_cap * DH * eb;
-  for (int kb = w0; kb < w1; kb += 32)
-    attn_step<DH, KF32>(st, kbase, vbase, kb, w1, a.scale_log2, [&](int key) { return key < w1; });
+  // the 4 waves take interleaved 32-key steps, so that the work-group reads one contiguous 128-key
+  // stretch of K and of V at a time (4% faster than a quarter of the chunk per wave at B = 128)
+  for (int kb = k0 + wave * 32; kb < k1; kb += 128)
+    attn_step<DH, KF32>(st, kbase, vbase, kb, k1, a.scale_log2, [&](int key) { return key < k1; });
 
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
