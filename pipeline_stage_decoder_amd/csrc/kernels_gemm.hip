@@ -244,23 +244,25 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Large tiles for prefill-sized M (activation pair planes): 8 waves own a 256 x 256 tile, each wave
-// 64 x 128 (two waves per SIMD), K in 32-deep stages.  Tiles go from global memory straight into
-// LDS (global_load_lds_dwordx4), so no registers stage them and no ds_write is issued: the
-// accumulators, one stage's fragments and the addresses fit the 256 registers of two waves per
-// SIMD.  ST LDS buffers form a ring: while stage t feeds the MFMAs the loads of stages
-// t + 1 .. t + ST - 2 are in flight, and stage t + ST - 1 is issued into the buffer stage t - 1 has
-// just left.
-// A stage row is 32 k = 4 chunks of 16 bytes; chunk c of row r sits at position c ^ ((r >> 1) & 3),
-// so the 8 rows one ds_read_b128 phase reads land in distinct banks.  One load instruction writes
-// 64 consecutive chunks (16 rows) -- lane l's 16 bytes at position l -- so the swizzle is applied on
-// the global side: lane l fetches the chunk that belongs at position l.
+// LDS-direct tiles.  For prefill-sized M (activation pair planes) 8 waves own a 256 x 256 tile,
+// each wave 64 x 128 (two waves per SIMD), K in 32-deep stages; the same kernel serves 128 x 256
+// (three planes, or too few 256 x 256 tiles) and the batched-decode shapes (64 x 256 / 64 x 128
+// with 64-deep stages, so every weight row segment a load instruction fetches is a whole 128-byte
+// line).  Tiles go from global memory straight into LDS (global_load_lds_dwordx4), so no
+// registers stage them and no ds_write is issued: the accumulators, one step's fragments and the
+// addresses fit the 256 registers of two waves per SIMD.  ST LDS buffers form a ring: while stage
+// t feeds the MFMAs the loads of stages t + 1 .. t + ST - 2 are in flight, and stage t + ST - 1 is
+// issued into the buffer stage t - 1 has just left.
+// Rows of a stage are BK / 8 chunks of 16 bytes, XOR-swizzled by row (dma_swz) so that the 8 rows
+// one ds_read_b128 phase reads land in distinct banks.  One load instruction writes 64 consecutive
+// chunks -- lane l's 16 bytes at position l -- so the swizzle is applied on the global side: lane
+// l fetches the chunk that belongs at position l.
 // The loads are issued from inline assembly and waited for by hand: each wave waits (vmcnt) for
 // its own loads of stage t before the barrier that hands the stage to the other waves.  (Through
 // the compiler builtin, every LDS read would also wait for the loads still in flight.)  The
 // kernel uses no other instruction that reads M0.
-// Per k step each accumulator takes the hi-plane product and then the lo-plane product, the same
-// sequence as k_gemm, so both kernels give identical sums.
+// Per 32-k step each accumulator takes the hi-plane product and then the lo-plane product(s), the
+// same sequence as k_gemm, so both kernels give identical sums.
 // ------------------------------------------------------------------------------------------------
 constexpr int kDmaBK = 32;
 
@@ -291,9 +293,18 @@ PSD_DEV void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int NP, int EPI, int BM, int BN, int WM, int WN, int ST>
+// Position of logical 16-byte chunk c of stage row r: rows of 4 chunks (BK = 32) XOR (r >> 1) & 3,
+// rows of 8 chunks (BK = 64) XOR r & 7 -- either way the 8 rows one ds_read_b128 phase reads land in
+// distinct banks.
+template <int CH>
+PSD_DEV int dma_swz(int r, int c) {
+  return CH == 4 ? c ^ ((r >> 1) & 3) : c ^ (r & 7);
+}
+
+template <int NP, int EPI, int BM, int BN, int WM, int WN, int ST, int BK = kDmaBK>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
-  constexpr int BK = kDmaBK, NT = WM * WN * 64;
+  constexpr int NT = WM * WN * 64;
+  static_assert(BK == 32 || BK == 64, "stage depth");
   constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 16, TN = WTN / 16;
   static_assert(WTN % 32 == 0, "paired epilogues need 32-aligned wave columns");
   constexpr int CH = BK / 8;                               // chunks per row
@@ -317,12 +328,12 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
   const int kend = min(K, kbeg + kper);
   const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;    // K and the split ranges are multiples of BK
 
-  // lane's source of load instruction i: row 16 * (wave * n + i) + lane / 4 (past M / N: the last
-  // row, never stored), logical chunk (lane % 4) ^ ((row >> 1) & 3); a byte offset from the
+  // lane's source of load instruction i: row (64 / CH) * (wave * n + i) + lane / CH (past M / N: the
+  // last row, never stored), the logical chunk stored at position lane % CH; a byte offset from the
   // operand's column kbeg (A and W are under 4 GiB)
   auto src_off = [&](int row0, int rows_max, int i, int n) {
-    const int row = (wave * n + i) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    const int row = (wave * n + i) * (64 / CH) + lane / CH;
+    const int c = dma_swz<CH>(row, lane % CH);
     return (uint32_t)(((size_t)min(row0 + row, rows_max - 1) * K + c * 8) * 2);
   };
   uint32_t a_off[A_DMA], b_off[B_DMA];
@@ -377,32 +388,35 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
     // loads of stage t are in LDS and no wave still reads stage t - 1's buffer
     wait_stages(min(ST - 2, nk - 1 - t));
     lds_barrier();
-    // all of this wave's fragment reads, then the hi-plane MFMAs, the loads of stage t + ST - 1
-    // into the freed buffer, and the MFMAs of the other planes
-    bf16x8_t af[NP][TM], bw[TN];
+    // per 32-k step: all of this wave's fragment reads, then the hi-plane MFMAs, (in the first
+    // step) the loads of stage t + ST - 1 into the freed buffer, and the MFMAs of the other planes
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * WTM + i * 16 + (lane & 15);
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int ch = ks * 4 + kc;
+      bf16x8_t af[NP][TM], bw[TN];
 #pragma unroll
-      for (int pl = 0; pl < NP; ++pl)
-        af[pl][i] = as_bf16x8(As[t % ST][pl][row * CH + (kc ^ ((row >> 1) & 3))]);
-    }
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * WTM + i * 16 + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row = wn * WTN + j * 16 + (lane & 15);
-      bw[j] = as_bf16x8(Bs[t % ST][row * CH + (kc ^ ((row >> 1) & 3))]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+        for (int pl = 0; pl < NP; ++pl) af[pl][i] = as_bf16x8(As[t % ST][pl][row * CH + dma_swz<CH>(row, ch)]);
+      }
 #pragma unroll
-    for (int pl = 0; pl < NP; ++pl) {
+      for (int j = 0; j < TN; ++j) {
+        const int row = wn * WTN + j * 16 + (lane & 15);
+        bw[j] = as_bf16x8(Bs[t % ST][row * CH + dma_swz<CH>(row, ch)]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int pl = 0; pl < NP; ++pl) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[pl][i], bw[j], acc[i][j]);
-      if (pl == 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (t + ST - 1 < nk) issue(t + ST - 1);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[pl][i], bw[j], acc[i][j]);
+        if (pl == 0 && ks == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (t + ST - 1 < nk) issue(t + ST - 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
@@ -451,7 +465,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
 struct Cfg {
   int bm, bn;
 };
-constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128}, {256, 256}, {128, 256}, {128, 256}};
+constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128}, {256, 256}, {128, 256}, {128, 256}, {64, 256}, {64, 128}};
 
 }  // namespace
 
@@ -462,6 +476,8 @@ GemmPlan gemm_plan(int M, int N, int K, int planes) {
   //    splits fill the chip (gate/up and the 70B projections 1.2-1.4x faster than the tiles
   //    below), else 128 x 256 (the QKV projection; the 512-row O and down projections split 4
   //    ways, as fast as 256 x 256 split 8 with half the partials to reduce).
+  //  * 32 < M <= 64 (batched decode): 64 x 256 or 64 x 128 LDS-direct tiles with 64-deep stages
+  //    (8B-shaped projections at M = 64: gate/up 55 -> 50 us, down 37 -> 31 us, O 17.5 -> 16 us).
   //  * 64 < M <= 128 (batched decode): 128 x 256 with 8 waves of 64 x 64 and a deeper ring
   //    (70B-shaped projections at M = 128: 6-10% faster than 128 x 128).
   //  * otherwise 128 x 128 up to M = 512 and 64 x 256 above, one LDS buffer and one register
@@ -472,6 +488,22 @@ GemmPlan gemm_plan(int M, int N, int K, int planes) {
   //    >= 256 deep.
   GemmPlan p{};
   const bool dma_ok = K % kDmaBK == 0 && (uint64_t)(M > N ? M : N) * K * 2 < (1ull << 32);
+  if (dma_ok && K % 64 == 0 && M > 32 && M <= 64) {
+    // batched decode rows: 64 x 256 (two planes, wide N) or 64 x 128 tiles with 64-deep stages,
+    // so that every weight row segment a load instruction touches is a whole 128-byte line; K split
+    // until the grid holds ~200 work-groups
+    const int cfg = (planes == 2 && (N + 255) / 256 >= 96) ? 8 : 9;
+    const int tiles = (N + kCfgs[cfg].bn - 1) / kCfgs[cfg].bn;
+    int sk = 1;
+    while (tiles * sk < 190 && K / (sk * 2) >= 512 && sk < 16) sk *= 2;
+    p.cfg = cfg;
+    p.bm = kCfgs[cfg].bm;
+    p.bn = kCfgs[cfg].bn;
+    p.tiles_m = 1;
+    p.tiles_n = tiles;
+    p.splitk = sk;
+    return p;
+  }
   if (dma_ok && M > 64 && M <= 128) {
     // batched decode rows: 128 x 256 with 64 x 64 wave tiles and a 4-stage ring (3 for three
     // planes), K split until the grid holds ~150 work-groups
@@ -535,6 +567,10 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
     case 7:
       k_gemm_dma<NP, EPI, 128, 256, 2, 4, NP == 2 ? 4 : 3><<<grid, 512, 0, s>>>(a);
       break;
+    case 8:   // the planner gives it two planes only
+      k_gemm_dma<2, EPI, 64, 256, 1, 4, 3, 64><<<grid, 256, 0, s>>>(a);
+      break;
+    case 9: k_gemm_dma<NP, EPI, 64, 128, 1, 4, NP == 2 ? 4 : 3, 64><<<grid, 256, 0, s>>>(a); break;
 
     default: k_gemm<16, 128, 1, 4, NP, EPI, 2, 2><<<grid, 256, 0, s>>>(a); break;
   }
@@ -552,8 +588,9 @@ void launch_reduce(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
   // the LDS-direct tile takes two planes, K in whole 32-deep stages and operands under 4 GiB
-  if ((p.cfg == 5 && a.planes != 2) || (p.cfg >= 5 && ( a.K % kDmaBK != 0 || (uint64_t)(a.M > a.N ? a.M : a.N) * a.K * 2 >= (1ull << 32))))
+  if (((p.cfg == 5 || p.cfg == 8) && a.planes != 2) || (p.cfg >= 5 && ( a.K % kDmaBK != 0 || (uint64_t)(a.M > a.N ? a.M : a.N) * a.K * 2 >= (1ull << 32))))
     return hipErrorInvalidValue;
+  if (p.cfg >= 8 && a.K % 64 != 0) return hipErrorInvalidValue;   // 64-deep stages
   dim3 grid(p.tiles_m * p.tiles_n, p.splitk);
   switch (a.e.kind) {
     case EPI_QKV:
