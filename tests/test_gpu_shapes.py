@@ -11,8 +11,8 @@ the stage's kernels at their real shapes on a slice the oracle can follow:
 * sharded MLP: 8 column/row slices of a d 8192 / F 28672 MLP summed in slice order against the full
   MLP at T in {1, 64, 4096} (the T = 4096 oracle check on 64 sampled rows; MLP rows are
   independent);
-* 8B MLP at T in {257, 300, 512}: the large-tile GEMM with a ragged last row tile, the oracle on
-  sampled rows and every row of the tail.
+* 8B MLP at T in {40, 100, 257, 300, 512}: every GEMM tiling with a ragged last row tile, the
+  oracle on sampled rows and the tail rows.
 Inputs: seeded bf16 N(0, 0.02) weights with norm gains 1 + N(0, 0.1^2), uniform tokens, F32 N(0,1)
 hidden rows, bf16 N(0,1) cached K/V.
 """
@@ -189,18 +189,20 @@ def test_mlp_slices_sum_to_full_mlp(mlp70b, T):
     assert e_sum <= TOL and e_full <= TOL
 
 
-@pytest.mark.parametrize("T", [257, 300, 512])
-def test_8b_mlp_large_tiles_ragged_rows(w8b_first, T):
-    # T >= 256 rows take the 256 x 256 LDS-direct GEMM (gate/up whole-K, down split over K); rows
-    # past T in the last row tile are clamped reads that must never be stored.  MLP rows are
-    # independent: the oracle checks the first rows, a spread, and every row of the ragged tail.
+@pytest.mark.parametrize("T", [40, 100, 257, 300, 512])
+def test_8b_mlp_gemm_tiles_ragged_rows(w8b_first, T):
+    # each row count takes another GEMM tiling: 40 the 64-row LDS-direct tiles with 64-deep stages,
+    # 100 the 128 x 256 tiles for 64 < M <= 128, 257 / 300 / 512 the 256 x 256 (gate/up) and
+    # 128 x 256 split-K (down) tiles; the last row tile is ragged in every case (clamped reads that
+    # must never be stored).  MLP rows are independent: the oracle checks the first rows, a spread,
+    # and the tail rows.
     s = fx.LLAMA8B
     w = {(r, 0): w8b_first[(r, 0)] for r in ("mlp_norm", "wgate", "wup", "wdown")}
     st = make_stage(s, 0, 1, False, False, w, max_slots=1, max_ctx=64, max_tokens=512)
     x = hidden_rows(41, T, s.d_model)
     got = st.mlp(0, torch.from_numpy(x).cuda()).cpu().numpy()
-    tail = np.arange((T - 1) // 256 * 256, T)
-    rows = np.unique(np.concatenate([np.arange(4), np.linspace(0, T - 1, 16).astype(int), tail[-24:]]))
+    tail = np.arange(max(0, T - 24), T)
+    rows = np.unique(np.concatenate([np.arange(4), np.linspace(0, T - 1, 16).astype(int), tail]))
     say(f"8B MLP T={T}: oracle on {len(rows)} rows")
     _, want = o.mlp_full(x[rows], w[("mlp_norm", 0)], w[("wgate", 0)], w[("wup", 0)], w[("wdown", 0)], s.rms_eps)
     e = rel_l2(got[rows], want)
