@@ -256,13 +256,22 @@ size_t ps_act(const stage* st) { return (size_t)st->s.max_tokens * st->m.d_ffn; 
 // bf16 planes anyway.
 int qkv_planes(const stage* st) { return st->kv_f32 ? 2 : 3; }
 
+// The RMSNorm a projection's output feeds next: `gain` (null: none requested).  `done` is set when
+// the projection's split-K sum wrote the normalised rows into the norm workspace (st->xn), so the
+// next projection can skip its own norm pass.
+struct NextNorm {
+  const float* gain = nullptr;
+  bool done = false;
+};
+
 // One projection y = x W^T with its epilogue.  x_f32 + gain: the input is RMS-normalised first
-// (fused in the GEMV prologue, or a row pass into the bf16 workspace before the GEMM).
-// planes: bf16 planes of the GEMM operand (2, or 3 for the QKV projection whose K/V outputs are
-// rounded to the bf16 cache).
+// (fused in the GEMV prologue, or a row pass into the bf16 workspace before the GEMM; x_normed: the
+// workspace already holds it).  planes: bf16 planes of the GEMM operand (2, or 3 for the QKV
+// projection whose K/V outputs are rounded to the bf16 cache).  next: see NextNorm.
 hipError_t project(stage* st, int kind, int rows, const float* x_f32, const float* gain, const uint16_t* x_pair,
                    size_t x_ps, const uint16_t* w, int N, int K, const EpiArgs& e, hipStream_t s,
-                   int planes = 2) {
+                   int planes = 2, NextNorm* next = nullptr, bool x_normed = false) {
+  if (next) next->done = false;
   if (gemv_fits(rows, K)) {
     Timed t(st, kind, s);
     GemvArgs a{};
@@ -281,13 +290,15 @@ hipError_t project(stage* st, int kind, int rows, const float* x_f32, const floa
   const uint16_t* A = x_pair;
   size_t a_ps = x_ps;
   if (x_f32) {
-    NormArgs n{x_f32, gain, st->m.rms_eps, rows, K, nullptr, st->xn, ps_xn(st)};
-    hipError_t err;
-    {
-      Timed t(st, STAGE_KT_NORM, s);
-      err = launch_rmsnorm(n, s);
+    if (!x_normed) {
+      NormArgs n{x_f32, gain, st->m.rms_eps, rows, K, nullptr, st->xn, ps_xn(st)};
+      hipError_t err;
+      {
+        Timed t(st, STAGE_KT_NORM, s);
+        err = launch_rmsnorm(n, s);
+      }
+      if (err != hipSuccess) return err;
     }
-    if (err != hipSuccess) return err;
     A = st->xn;
     a_ps = ps_xn(st);
   }
@@ -303,26 +314,29 @@ hipError_t project(stage* st, int kind, int rows, const float* x_f32, const floa
   g.splitk = p.splitk;
   g.part = st->gemm_part;
   g.e = e;
+  NormArgs then{nullptr, next ? next->gain : nullptr, st->m.rms_eps, rows, N, nullptr, st->xn, ps_xn(st)};
   Timed t(st, kind, s);
-  return launch_gemm(g, p, s);
+  return launch_gemm(g, p, s, next && next->gain ? &then : nullptr, next ? &next->done : nullptr);
 }
 
 // The MLP half of a block: out = resid + W_down(silu(W_gate h) * W_up h), h = norm(x).
+// x_normed: the norm workspace already holds norm(x); next: see NextNorm (after the down projection).
 hipError_t mlp_half(stage* st, int lb, int rows, const float* x, const float* resid, float* out,
-                    hipStream_t s) {
+                    hipStream_t s, bool x_normed = false, NextNorm* next = nullptr) {
   const BlockW& bw = st->blocks[lb];
   const int d = st->m.d_model, F = st->m.d_ffn;
   EpiArgs e1 = epi_base(st, EPI_SWIGLU);
   e1.act = st->act;
   e1.act_ps = ps_act(st);
   e1.ldo = F;
-  hipError_t err = project(st, STAGE_KT_GATEUP, rows, x, bw.mlp_norm, nullptr, 0, bw.wgu, 2 * F, d, e1, s);
+  hipError_t err = project(st, STAGE_KT_GATEUP, rows, x, bw.mlp_norm, nullptr, 0, bw.wgu, 2 * F, d, e1, s, 2,
+                           nullptr, x_normed);
   if (err != hipSuccess) return err;
   EpiArgs e2 = epi_base(st, resid ? EPI_RESID : EPI_F32);
   e2.out = out;
   e2.resid = resid;
   e2.ldo = d;
-  return project(st, STAGE_KT_DOWN, rows, nullptr, nullptr, st->act, ps_act(st), bw.wd, d, F, e2, s);
+  return project(st, STAGE_KT_DOWN, rows, nullptr, nullptr, st->act, ps_act(st), bw.wd, d, F, e2, s, 2, next);
 }
 
 // One block over `rows` rows.  Prefill: rp = (slot, pos0), attention over keys [0, pos];
@@ -330,7 +344,8 @@ hipError_t mlp_half(stage* st, int lb, int rows, const float* x, const float* re
 // The attention sublayer of owned block lb: x_out = (resid ? resid : 0) + W_o attention(QKV(norm(x_in))),
 // with K/V written at the rows' positions.
 hipError_t attn_half(stage* st, int lb, int rows, const float* x_in, const float* resid, float* x_out,
-                     const RowPos& rp, bool decode, hipStream_t s) {
+                     const RowPos& rp, bool decode, hipStream_t s, bool x_normed = false,
+                     NextNorm* next = nullptr) {
   const BlockW& bw = st->blocks[lb];
   const int d = st->m.d_model, hq = st->m.n_q_heads, hkv = st->m.n_kv_heads, dh = st->m.head_dim;
   uint8_t* kc = st->kcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb;
@@ -342,7 +357,8 @@ hipError_t attn_half(stage* st, int lb, int rows, const float* x_in, const float
   e.kc = kc;
   e.vc = vc;
   e.rp = rp;
-  hipError_t err = project(st, STAGE_KT_QKV, rows, x_in, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, qkv_planes(st));
+  hipError_t err = project(st, STAGE_KT_QKV, rows, x_in, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s,
+                           qkv_planes(st), nullptr, x_normed);
   if (err != hipSuccess) return err;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   if (decode) {
@@ -397,13 +413,21 @@ hipError_t attn_half(stage* st, int lb, int rows, const float* x_in, const float
   eo.out = x_out;
   eo.resid = resid;
   eo.ldo = d;
-  return project(st, STAGE_KT_O, rows, nullptr, nullptr, st->attn, ps_q(st), bw.wo, d, hq * dh, eo, s);
+  return project(st, STAGE_KT_O, rows, nullptr, nullptr, st->attn, ps_q(st), bw.wo, d, hq * dh, eo, s, 2, next);
 }
 
+// One block.  *normed: on entry, whether the norm workspace already holds norm(x_in) for this
+// block's QKV projection; on exit, whether it holds the next block's (the down projection's split-K
+// sum normalises with the next block's attention-norm gain when there is one).
 int run_block(stage* st, int lb, int rows, const float* x_in, float* x_out, const RowPos& rp, bool decode,
-              hipStream_t s) {
-  HIP_TRY(st, attn_half(st, lb, rows, x_in, x_in, x_out, rp, decode, s));
-  HIP_TRY(st, mlp_half(st, lb, rows, x_out, x_out, x_out, s));
+              hipStream_t s, bool* normed) {
+  NextNorm n1;
+  n1.gain = st->blocks[lb].mlp_norm;
+  HIP_TRY(st, attn_half(st, lb, rows, x_in, x_in, x_out, rp, decode, s, *normed, &n1));
+  NextNorm n2;
+  n2.gain = lb + 1 < st->nb ? st->blocks[lb + 1].attn_norm : nullptr;
+  HIP_TRY(st, mlp_half(st, lb, rows, x_out, x_out, x_out, s, n1.done, &n2));
+  *normed = n2.done;
   return STAGE_OK;
 }
 
@@ -414,8 +438,9 @@ int run_blocks(stage* st, int rows, const float* hin, float* hout, const RowPos&
                                                  hipMemcpyDeviceToDevice, s));
     return STAGE_OK;
   }
+  bool normed = false;
   for (int lb = 0; lb < st->nb; ++lb) {
-    const int rc = run_block(st, lb, rows, lb == 0 ? hin : hout, hout, rp, decode, s);
+    const int rc = run_block(st, lb, rows, lb == 0 ? hin : hout, hout, rp, decode, s, &normed);
     if (rc != STAGE_OK) return rc;
   }
   return STAGE_OK;

@@ -108,7 +108,11 @@ hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
 // MFMA GEMM
 // planes: bf16 planes of the activation operand (2 or 3)
 GemmPlan gemm_plan(int M, int N, int K, int planes);
-hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s);
+// then_norm (nullable): when the plan splits K, the epilogue is EPI_RESID and M >= 256, the split-K
+// sum also writes the RMSNorm of the result rows (then_norm->x is ignored: the rows are e.out) into
+// then_norm->out_pair, and *normed (nullable) is set; otherwise *normed is false.
+hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, const NormArgs* then_norm = nullptr,
+                       bool* normed = nullptr);
 
 // attention
 int attn_decode_chunk(int B);

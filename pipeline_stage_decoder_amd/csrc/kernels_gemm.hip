@@ -13,6 +13,7 @@
 // kernel sums them in split order -- a fixed order, so results never depend on timing -- and
 // applies the epilogue.
 #include "kernels.h"
+#include "norm.h"
 
 namespace {
 
@@ -462,6 +463,47 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
   }
 }
 
+// Split-K sum with the residual epilogue, fused with the RMSNorm of the result (the operand of
+// the next projection): one work-group per row.  x = ((0 + p0) + p1) + ..., out = resid + x, as
+// k_splitk_reduce; then the row's RMS scale and the normalised bf16 planes exactly as k_rmsnorm
+// computes them from out (same element order, same f64 reduction).  N % 4 == 0, N <= 8192.
+constexpr int kReduceNormMaxN = 8192;
+
+__global__ __launch_bounds__(256) void k_splitk_reduce_norm(GemmArgs g, NormArgs nrm) {
+  constexpr int PER = kReduceNormMaxN / 1024;   // float4 per thread
+  __shared__ double red[4];
+  const int r = blockIdx.x, N = g.N;
+  const size_t plane = (size_t)g.M * N;
+  const EpiArgs& e = g.e;
+  float4 v[PER];
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x * 4 + j * 1024;
+    if (i < N) {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int sp = 0; sp < g.splitk; ++sp) {
+        const float4 p = *(const float4*)(g.part + sp * plane + (size_t)r * N + i);
+        x.x += p.x;
+        x.y += p.y;
+        x.z += p.z;
+        x.w += p.w;
+      }
+      const float4 res = *(const float4*)(e.resid + (size_t)r * e.ldo + i);
+      v[j] = make_float4(res.x + x.x, res.y + x.y, res.z + x.z, res.w + x.w);
+      *(float4*)(e.out + (size_t)r * e.ldo + i) = v[j];
+      ss = sumsq4(v[j], ss);
+    }
+  }
+  const double rs = block_rms_finish(ss, N, nrm.eps, red);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x * 4 + j * 1024;
+    if (i < N)
+      store_norm_planes4(nrm.out_pair + (size_t)r * N + i, nrm.pair_ps, v[j], rs, *(const float4*)(nrm.gain + i));
+  }
+}
+
 struct Cfg {
   int bm, bn;
 };
@@ -586,7 +628,9 @@ void launch_reduce(const GemmArgs& a, hipStream_t s) {
   k_splitk_reduce<EPI><<<(unsigned)grid, 256, 0, s>>>(a);
 }
 
-hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, const NormArgs* then_norm,
+                       bool* normed) {
+  if (normed) *normed = false;
   // the LDS-direct tile takes two planes, K in whole 32-deep stages and operands under 4 GiB
   if (((p.cfg == 5 || p.cfg == 8) && a.planes != 2) || (p.cfg >= 5 && ( a.K % kDmaBK != 0 || (uint64_t)(a.M > a.N ? a.M : a.N) * a.K * 2 >= (1ull << 32))))
     return hipErrorInvalidValue;
@@ -604,7 +648,16 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
       break;
     case EPI_RESID:
       launch_cfg<2, EPI_RESID>(a, p, grid, s);
-      if (p.splitk > 1) launch_reduce<EPI_RESID>(a, s);
+      if (p.splitk > 1) {
+        // one work-group per row: only when there are rows enough to fill the chip (at M = 64 the
+        // fused pass was slower than the two kernels)
+        if (then_norm && a.M >= 256 && a.N % 4 == 0 && a.N <= kReduceNormMaxN && a.e.ldo == a.N) {
+          k_splitk_reduce_norm<<<a.M, 256, 0, s>>>(a, *then_norm);
+          if (normed) *normed = true;
+        } else {
+          launch_reduce<EPI_RESID>(a, s);
+        }
+      }
       break;
     default:
       launch_cfg<2, EPI_F32>(a, p, grid, s);

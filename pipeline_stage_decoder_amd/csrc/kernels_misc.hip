@@ -12,20 +12,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   for (int i = threadIdx.x * 4; i < a.K; i += 1024) {
     const float4 v = *(const float4*)(x + i);
     const float4 g = *(const float4*)(a.gain + i);
-    const float y0 = norm_mul(v.x, r, g.x), y1 = norm_mul(v.y, r, g.y), y2 = norm_mul(v.z, r, g.z),
-                y3 = norm_mul(v.w, r, g.w);
-    if (a.out_f32) *(float4*)(a.out_f32 + (size_t)m * a.K + i) = make_float4(y0, y1, y2, y3);
-    if (a.out_pair) {
-      uint32_t h[4], md[4], l[4];
-      split3(y0, h[0], md[0], l[0]);
-      split3(y1, h[1], md[1], l[1]);
-      split3(y2, h[2], md[2], l[2]);
-      split3(y3, h[3], md[3], l[3]);
-      uint16_t* p = a.out_pair + (size_t)m * a.K + i;
-      *(uint2*)p = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-      *(uint2*)(p + a.pair_ps) = make_uint2(md[0] | (md[1] << 16), md[2] | (md[3] << 16));
-      *(uint2*)(p + 2 * a.pair_ps) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
-    }
+    if (a.out_f32)
+      *(float4*)(a.out_f32 + (size_t)m * a.K + i) =
+          make_float4(norm_mul(v.x, r, g.x), norm_mul(v.y, r, g.y), norm_mul(v.z, r, g.z), norm_mul(v.w, r, g.w));
+    if (a.out_pair) store_norm_planes4(a.out_pair + (size_t)m * a.K + i, a.pair_ps, v, r, g);
   }
 }
 

@@ -16,17 +16,17 @@ PSD_DEV double wave_sum_f64(double v) {
   return v;
 }
 
-// r = 1 / sqrt(mean(x^2) + eps) of one row of K f32 values (K % 4 == 0), for a 256-thread block.
-// `red` is 4 doubles of LDS.  Every thread returns r.
-PSD_DEV double block_rms_scale(const float* __restrict__ x, int K, float eps, double* red) {
-  double ss = 0.0;
-  for (int i = threadIdx.x * 4; i < K; i += 1024) {
-    const float4 v = *(const float4*)(x + i);
-    ss = fma((double)v.x, (double)v.x, ss);
-    ss = fma((double)v.y, (double)v.y, ss);
-    ss = fma((double)v.z, (double)v.z, ss);
-    ss = fma((double)v.w, (double)v.w, ss);
-  }
+// Sum of squares of 4 values in f64, accumulated into ss in element order.
+PSD_DEV double sumsq4(const float4& v, double ss) {
+  ss = fma((double)v.x, (double)v.x, ss);
+  ss = fma((double)v.y, (double)v.y, ss);
+  ss = fma((double)v.z, (double)v.z, ss);
+  return fma((double)v.w, (double)v.w, ss);
+}
+
+// r = 1 / sqrt(t / K + eps) from each thread's partial sum of squares (thread t holding
+// x[4t .. 4t+4), x[4t+1024 ..) ...), for a 256-thread block.  `red` is 4 doubles of LDS.
+PSD_DEV double block_rms_finish(double ss, int K, float eps, double* red) {
   ss = wave_sum_f64(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
@@ -35,5 +35,28 @@ PSD_DEV double block_rms_scale(const float* __restrict__ x, int K, float eps, do
   return 1.0 / sqrt(t / (double)K + (double)eps);
 }
 
+// r = 1 / sqrt(mean(x^2) + eps) of one row of K f32 values (K % 4 == 0), for a 256-thread block.
+// `red` is 4 doubles of LDS.  Every thread returns r.
+PSD_DEV double block_rms_scale(const float* __restrict__ x, int K, float eps, double* red) {
+  double ss = 0.0;
+  for (int i = threadIdx.x * 4; i < K; i += 1024) ss = sumsq4(*(const float4*)(x + i), ss);
+  return block_rms_finish(ss, K, eps, red);
+}
+
 // (float)(x * r * g) with the product in f64
 PSD_DEV float norm_mul(float x, double r, float g) { return (float)((double)x * r * (double)g); }
+
+// Normalised values x * r * g of elements i .. i+3 of a row, as three bf16 planes (hi, mid, lo) at
+// p, p + ps, p + 2 ps (p points at element i of the row in the hi plane).
+PSD_DEV void store_norm_planes4(uint16_t* p, size_t ps, const float4& v, double r, const float4& g) {
+  const float y0 = norm_mul(v.x, r, g.x), y1 = norm_mul(v.y, r, g.y), y2 = norm_mul(v.z, r, g.z),
+              y3 = norm_mul(v.w, r, g.w);
+  uint32_t h[4], md[4], l[4];
+  split3(y0, h[0], md[0], l[0]);
+  split3(y1, h[1], md[1], l[1]);
+  split3(y2, h[2], md[2], l[2]);
+  split3(y3, h[3], md[3], l[3]);
+  *(uint2*)p = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  *(uint2*)(p + ps) = make_uint2(md[0] | (md[1] << 16), md[2] | (md[3] << 16));
+  *(uint2*)(p + 2 * ps) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
