@@ -79,8 +79,20 @@ def cpu_baseline_decode(shape, ctx: int, n_blocks: int, reps: int = 2):
     per_token = per_block * n_blocks
     return {"value": 1.0 / per_token, "unit": "tok/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} decode steps of 1 of {n_blocks} blocks at context {ctx} (B=1); "
-                      f"tok/s = 1 / ({n_blocks} x {per_block:.2f} s per block-step)",
-            "seconds_per_block_step": per_block}
+                      f"tok/s = 1 / ({n_blocks} x {per_block:.2f} s per block-step), extrapolated "
+                      f"linearly over blocks",
+            "seconds_per_block_step": per_block, "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo), or 'unknown'."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 GEMV_SOURCES = ("pipeline_stage_decoder_amd/csrc/kernels_gemv.hip", "pipeline_stage_decoder_amd/csrc/common.h",
