@@ -11,6 +11,8 @@ the stage's kernels at their real shapes on a slice the oracle can follow:
 * sharded MLP: 8 column/row slices of a d 8192 / F 28672 MLP summed in slice order against the full
   MLP at T in {1, 64, 4096} (the T = 4096 oracle check on 64 sampled rows; MLP rows are
   independent);
+* 8B blocks [0, 2) against [0, 1) + [1, 2): bit-identical hidden rows and KV after a 300-row
+  prefill and two decode steps, bf16 and F32 caches;
 * 8B MLP at T in {40, 100, 257, 300, 512}: every GEMM tiling with a ragged last row tile, the
   oracle on sampled rows and the tail rows.
 Inputs: seeded bf16 N(0, 0.02) weights with norm gains 1 + N(0, 0.1^2), uniform tokens, F32 N(0,1)
@@ -22,7 +24,7 @@ import torch
 
 import fixtures as fx
 from oracle import decoder as o
-from tests.gpu_util import hidden_rows, make_stage, rel_l2, say
+from tests.gpu_util import hidden_rows, kv_bits, make_stage, rel_l2, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -187,6 +189,37 @@ def test_mlp_slices_sum_to_full_mlp(mlp70b, T):
     say(f"  slices vs full (gpu) {e_gpu:.2e}; slices vs oracle {e_sum:.2e}; full vs oracle {e_full:.2e}")
     assert e_gpu <= 1e-5
     assert e_sum <= TOL and e_full <= TOL
+
+
+@pytest.mark.parametrize("kv_f32", [False, True])
+def test_8b_split_equals_unsplit_on_gpu(w8b_first, kv_f32):
+    # blocks [0, 2) in one stage against [0, 1) + [1, 2) with the F32 handoff, at the real 8B shape:
+    # a 300-row prefill (LDS-direct GEMMs, split-K sums; in one stage block 0's down projection
+    # also normalises for block 1, in two stages block 1 normalises its input itself) and two B = 1
+    # decode steps (GEMVs, split-KV attention); hidden rows and both blocks' KV bit for bit
+    s, T = fx.LLAMA8B, 300
+    dev = torch.device("cuda")
+    kw = dict(max_slots=1, max_ctx=512, max_tokens=512, kv_f32=kv_f32)
+    whole = make_stage(s, 0, 2, True, False, w8b_first, **kw)
+    a = make_stage(s, 0, 1, True, False, w8b_first, **kw)
+    b = make_stage(s, 1, 2, False, False, w8b_first, **kw)
+    prompt = torch.tensor(fx.tokens(fx.SEED_TOKENS, fx.token_stream(2), T, s.vocab), dtype=torch.int32, device=dev)
+    y1 = whole.prefill(whole.embed(prompt), 0, 0)
+    y2 = b.prefill(a.prefill(a.embed(prompt), 0, 0), 0, 0)
+    assert torch.equal(y1, y2)
+    toks = fx.tokens(fx.SEED_TOKENS, fx.token_stream(3), 2, s.vocab)
+    for i, tok in enumerate(toks):
+        t = torch.tensor([tok], dtype=torch.int32, device=dev)
+        sl, ps = torch.tensor([0], dtype=torch.int32, device=dev), torch.tensor([T + i], dtype=torch.int32, device=dev)
+        d1 = whole.decode(whole.embed(t), sl, ps)
+        d2 = b.decode(a.decode(a.embed(t), sl, ps), sl, ps)
+        assert torch.equal(d1, d2)
+    n = T + len(toks)
+    for blk, part in ((0, a), (1, b)):
+        kw_, vw_ = kv_bits(whole, blk, 0, n)
+        kp, vp = kv_bits(part, blk, 0, n)
+        assert np.array_equal(kw_, kp) and np.array_equal(vw_, vp)
+    say(f"8B split [0,1)+[1,2) == [0,2), {'f32' if kv_f32 else 'bf16'} cache: prefill {T} rows, 2 decode steps, KV")
 
 
 @pytest.mark.parametrize("T", [40, 100, 257, 300, 512])
