@@ -478,6 +478,129 @@ def mlp_slices_line(args) -> dict:
     }
 
 
+def attn_parallel_line(args) -> dict:
+    """The parallel attention and vocabulary layouts on one GPU, at the 8B shape ("41. Many GPUs":
+    Tensor parallelism, Ring attention): one block's attention sublayer over a 4096-token sequence
+    taken plainly and the ring way (n ranks' query chunks, the K/V chunks passed round the ring,
+    partials merged by log-sum-exp; zigzag chunks for causal balance); the sublayer over 8 head
+    slices summed in slice order against the full one (T = 512 and T = 1); the readout over 8
+    vocabulary slices against the full one (64 rows)."""
+    import numpy as np
+    import torch
+
+    import fixtures as fx
+    from pipeline_stage_decoder_amd.stage import Stage
+
+    s, T, n = fx.LLAMA8B, 4096, 8
+    d, hq, hkv, dh, V = s.d_model, s.n_q_heads, s.n_kv_heads, s.head_dim, s.vocab
+    reps = max(args.steps, 3)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    def gpu_weight(role, shape, sigma=0.02):
+        t = torch.empty(int(np.prod(shape)), dtype=torch.int16, device="cuda")
+        if role in fx.GAIN_ROLES:
+            fx.gain_bf16_gpu(t, fx.SEED_WEIGHTS, fx.weight_stream(role, 0), 0.1)
+        else:
+            fx.normal_bf16_gpu(t, fx.SEED_WEIGHTS, fx.weight_stream(role, 0), sigma)
+        return t.view(*shape)
+
+    w = {r: gpu_weight(r, fx.role_shape(s, r)) for r in ("attn_norm", "wq", "wk", "wv", "wo")}
+    st = Stage(s, 0, 1, False, False, max_slots=2, max_ctx=T, max_tokens=T, device=0)
+    for r, t in w.items():
+        st.load_weight(r, 0, t)
+    x = fx.normal_f32_gpu(torch.empty((T, d), dtype=torch.float32, device="cuda"), fx.SEED_HIDDEN,
+                          fx.hidden_stream(60), 0)
+    proj = 2 * d * ((hq + 2 * hkv) * dh + hq * dh)
+
+    def sub_flops(t):
+        return proj * t + 4 * hq * dh * t * (t + 1) // 2
+
+    log("[bench] attn-parallel: plain and ring attention over 4096 tokens")
+    res = {"T": T, "plain_ms": timed(lambda: st.attn(0, x, 0, 0))}
+    for ranks, zz in ((4, True), (8, False)):
+        res[f"ring_{ranks}{'_zigzag' if zz else ''}_ms"] = timed(lambda: st.attn_ring(0, x, 1, ranks, zz))
+    fl = sub_flops(T)
+    for k in [k for k in res if k.endswith("_ms")]:
+        res[k.replace("_ms", "_tflops")] = round(fl / (res[k] / 1e3) / 1e12, 1)
+        res[k] = round(res[k], 3)
+
+    log("[bench] attn-parallel: 8 head slices against the full sublayer")
+    hq_s, hk_s = hq // n, max(hkv // n, 1)
+    sh = fx.Shape(d, hq_s, hk_s, dh, 64, V, n)
+    sl = Stage(sh, 0, n, False, False, max_slots=1, max_ctx=512, max_tokens=512, device=0)
+    for i in range(n):
+        qr = slice(i * hq_s * dh, (i + 1) * hq_s * dh)
+        kr = slice((i * hkv // n) * dh, (i * hkv // n + hk_s) * dh)
+        sl.load_weight("attn_norm", i, w["attn_norm"])
+        sl.load_weight("wq", i, w["wq"][qr].contiguous())
+        sl.load_weight("wk", i, w["wk"][kr].contiguous())
+        sl.load_weight("wv", i, w["wv"][kr].contiguous())
+        sl.load_weight("wo", i, w["wo"][:, qr].contiguous())
+    heads = {}
+    for t in (512, 1):
+        xt = x[:t].contiguous()
+        acc_out = torch.empty_like(xt)
+
+        def slices():
+            for i in range(n):
+                sl.attn(i, xt, 0, 0, out=acc_out, accumulate=i > 0)
+
+        heads[str(t)] = {"full_us": round(timed(lambda: st.attn(0, xt, 0, 0)) * 1e3, 1),
+                         "slices_us": round(timed(slices) * 1e3, 1)}
+    res["head_slices"] = heads
+
+    log("[bench] attn-parallel: 8 vocabulary slices against the full readout")
+    per = (V + n - 1) // n
+    ro = gpu_weight("readout", (V, d))
+    fn_ = gpu_weight("final_norm", (d,))
+    full = Stage(s, 0, 0, False, True, max_slots=1, max_ctx=64, max_tokens=64, device=0)
+    full.load_weight("final_norm", -1, fn_)
+    full.load_weight("readout", -1, ro)
+    vs = []
+    for i in range(n):
+        lo, hi = i * per, min(V, (i + 1) * per)
+        part = torch.zeros((per, d), dtype=torch.int16, device="cuda")
+        part[:hi - lo] = ro[lo:hi]
+        stv = Stage(fx.Shape(d, hq, hkv, dh, 64, per, 0), 0, 0, False, True, max_slots=1, max_ctx=64,
+                    max_tokens=64, device=0)
+        stv.load_weight("final_norm", -1, fn_)
+        stv.load_weight("readout", -1, part)
+        vs.append(stv)
+    h = x[:64].contiguous()
+    full_ms = timed(lambda: full.readout(h, want_normed=False))
+    slice_ms = timed(lambda: [v.readout(h, want_normed=False) for v in vs])
+    by = V * d * 2
+    res["vocab_slices_64_rows"] = {"full_us": round(full_ms * 1e3, 1), "slices_us": round(slice_ms * 1e3, 1),
+                                   "full_hbm_gbs": round(by / (full_ms / 1e3) / 1e9, 1),
+                                   "slices_hbm_gbs": round(by / (slice_ms / 1e3) / 1e9, 1)}
+    log(f"[bench] attn-parallel: {res}")
+    ring = res["ring_4_zigzag_ms"]
+    return {
+        "metric": "stage decode tok/s & HBM GB/s %peak; prefill tok/s & MFMA util",
+        "value": round(T / (ring / 1e3), 1), "unit": "tok/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": ring, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,0.02) bf16 weights, F32 N(0,1) hidden rows",
+        "config": {"workload": "8B-shaped block 0, attention sublayer over 4096 tokens taken the ring way "
+                               "(4 ranks' zigzag chunks on one GPU) against the plain sublayer and 8 ranks' "
+                               "plain chunks; 8 head slices (T = 512, 1) and 8 vocabulary slices of the "
+                               "readout (64 rows) against the full ones; value = tokens/s through the "
+                               "4-rank zigzag ring"},
+        "results": res, "roofline": None, "cpu_baseline": None,
+    }
+
+
 def pipeline_line(args) -> dict:
     """The whole 8B-shaped model as two stages on this GPU ([0, 16) + embedding, [16, 32) + final
     norm + readout), greedy generation through stage_pipeline_generate: two micro-batches of one
@@ -545,7 +668,8 @@ def main():
     ap.add_argument("--graph", choices=("on", "off"), default="on", help="replay decode steps from a HIP graph")
     ap.add_argument("--kv", choices=("f32", "bf16"), default="f32",
                     help="KV cache element type (f32: the configuration validated against the oracle at full depth)")
-    ap.add_argument("--workload", choices=("first-8b", "last-8b", "mid-70b", "mlp-slices", "pipeline-8b"),
+    ap.add_argument("--workload", choices=("first-8b", "last-8b", "mid-70b", "mlp-slices", "pipeline-8b",
+                                           "attn-parallel"),
                     default="first-8b",
                     help="first-8b: the benchmark line; the others report the remaining workloads' rooflines")
     ap.add_argument("--phase", choices=("both", "prefill", "counters"), default="both",
@@ -620,6 +744,9 @@ def main():
         return
     if args.workload == "mlp-slices":
         print(json.dumps(mlp_slices_line(args)), flush=True)
+        return
+    if args.workload == "attn-parallel":
+        print(json.dumps(attn_parallel_line(args)), flush=True)
         return
 
     log(f"[bench] creating stage: blocks {blocks}, embedding, max_ctx {ctx}, max_tokens {T}")
