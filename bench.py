@@ -601,6 +601,38 @@ def attn_parallel_line(args) -> dict:
     }
 
 
+def placement_line(args) -> dict:
+    """The placement planner (include/placement.h) on representative budgets, host only: the
+    contiguous cuts, each device's requirement and the planner's time; a budget nothing fits in
+    reports the typed does-not-fit status."""
+    import fixtures as fx
+    from pipeline_stage_decoder_amd.stage import StageError, place
+
+    gib = 1 << 30
+    cases = [("8B (32 blocks), 2 x 24 GiB", fx.LLAMA8B, [24 * gib] * 2),
+             ("8B, 24 + 12 GiB", fx.LLAMA8B, [24 * gib, 12 * gib]),
+             ("8B, 2 x 4 GiB", fx.LLAMA8B, [4 * gib] * 2),
+             ("70B-shaped (80 blocks), 2 x 80 GiB", fx.LLAMA70B, [80 * gib] * 2),
+             ("70B-shaped, 8 x 288 GiB", fx.LLAMA70B, [288 * gib] * 8)]
+    out = []
+    for name, shp, budgets in cases:
+        t0 = time.perf_counter()
+        try:
+            cuts, req = place(shp, budgets, max_slots=1, max_ctx=4096, max_tokens=512)
+            r = {"cuts": cuts, "required_gib": [round(x / gib, 2) for x in req]}
+        except StageError as e:
+            r = {"status": str(e)}
+        r["plan_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        r["case"] = name
+        out.append(r)
+        log(f"[bench] placement {r}")
+    return {"metric": "placement plan", "value": None, "unit": None, "n_gpus": 0, "steps": 1, "warmup": 0,
+            "ms_per_step": round(sum(r["plan_ms"] for r in out), 2), "higher_is_better": False,
+            "scaling": "weak", "vs_baseline": None, "dtype": "none", "data": "model shapes only",
+            "config": {"workload": "placement planner: 1 slot, ctx 4096, 512 prefill tokens per stage"},
+            "plans": out, "roofline": None, "cpu_baseline": None}
+
+
 def pipeline_line(args) -> dict:
     """The whole 8B-shaped model as two stages on this GPU ([0, 16) + embedding, [16, 32) + final
     norm + readout), greedy generation through stage_pipeline_generate: two micro-batches of one
@@ -669,7 +701,7 @@ def main():
     ap.add_argument("--kv", choices=("f32", "bf16"), default="f32",
                     help="KV cache element type (f32: the configuration validated against the oracle at full depth)")
     ap.add_argument("--workload", choices=("first-8b", "last-8b", "mid-70b", "mlp-slices", "pipeline-8b",
-                                           "attn-parallel"),
+                                           "attn-parallel", "placement"),
                     default="first-8b",
                     help="first-8b: the benchmark line; the others report the remaining workloads' rooflines")
     ap.add_argument("--phase", choices=("both", "prefill", "counters"), default="both",
@@ -688,6 +720,9 @@ def main():
         return
     if args.source_hash:
         print(gemv_source_hash())
+        return
+    if args.workload == "placement":             # host only
+        print(json.dumps(placement_line(args)), flush=True)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
