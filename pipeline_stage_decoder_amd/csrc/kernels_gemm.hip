@@ -471,26 +471,46 @@ constexpr int kReduceNormMaxN = 8192;
 
 __global__ __launch_bounds__(256) void k_splitk_reduce_norm(GemmArgs g, NormArgs nrm) {
   constexpr int PER = kReduceNormMaxN / 1024;   // float4 per thread
+  constexpr int SB = 4;                          // splits whose loads are in flight together
   __shared__ double red[4];
   const int r = blockIdx.x, N = g.N;
   const size_t plane = (size_t)g.M * N;
   const EpiArgs& e = g.e;
+  // the row's split partials, SB splits per round trip (a few rows only fill few CUs, so each
+  // work-group needs its loads in flight at once); summed per element in split order
+  float4 x[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp0 = 0; sp0 < g.splitk; sp0 += SB) {
+    float4 p[SB][PER];
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = threadIdx.x * 4 + j * 1024;
+        p[u][j] = (sp0 + u < g.splitk && i < N) ? *(const float4*)(g.part + (sp0 + u) * plane + (size_t)r * N + i)
+                                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+      if (sp0 + u < g.splitk) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          x[j].x += p[u][j].x;
+          x[j].y += p[u][j].y;
+          x[j].z += p[u][j].z;
+          x[j].w += p[u][j].w;
+        }
+      }
+  }
   float4 v[PER];
   double ss = 0.0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = threadIdx.x * 4 + j * 1024;
     if (i < N) {
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int sp = 0; sp < g.splitk; ++sp) {
-        const float4 p = *(const float4*)(g.part + sp * plane + (size_t)r * N + i);
-        x.x += p.x;
-        x.y += p.y;
-        x.z += p.z;
-        x.w += p.w;
-      }
       const float4 res = *(const float4*)(e.resid + (size_t)r * e.ldo + i);
-      v[j] = make_float4(res.x + x.x, res.y + x.y, res.z + x.z, res.w + x.w);
+      v[j] = make_float4(res.x + x[j].x, res.y + x[j].y, res.z + x[j].z, res.w + x[j].w);
       *(float4*)(e.out + (size_t)r * e.ldo + i) = v[j];
       ss = sumsq4(v[j], ss);
     }
@@ -649,9 +669,8 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
     case EPI_RESID:
       launch_cfg<2, EPI_RESID>(a, p, grid, s);
       if (p.splitk > 1) {
-        // one work-group per row: only when there are rows enough to fill the chip (at M = 64 the
-        // fused pass was slower than the two kernels)
-        if (then_norm && a.M >= 256 && a.N % 4 == 0 && a.N <= kReduceNormMaxN && a.e.ldo == a.N) {
+        // one work-group per row, every split's loads of a row in flight together
+        if (then_norm && a.N % 4 == 0 && a.N <= kReduceNormMaxN && a.e.ldo == a.N) {
           k_splitk_reduce_norm<<<a.M, 256, 0, s>>>(a, *then_norm);
           if (normed) *normed = true;
         } else {
