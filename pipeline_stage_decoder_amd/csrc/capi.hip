@@ -229,6 +229,9 @@ struct Timed {
     if (a && b) {
       (void)hipEventRecord(b, s);
       st->recs[kind].push_back({a, b});
+    } else {   // an event could not be created: hand back the one that was
+      if (a) st->ev_pool.push_back(a);
+      if (b) st->ev_pool.push_back(b);
     }
   }
 };
