@@ -12,7 +12,7 @@ the stage's kernels at their real shapes on a slice the oracle can follow:
   MLP at T in {1, 64, 4096} (the T = 4096 oracle check on 64 sampled rows; MLP rows are
   independent);
 * 8B blocks [0, 2) against [0, 1) + [1, 2): bit-identical hidden rows and KV after a 300-row
-  prefill and two decode steps, bf16 and F32 caches;
+  prefill, two B = 1 decode steps and a B = 64 decode step, bf16 and F32 caches;
 * 8B MLP at T in {40, 100, 257, 300, 512}: every GEMM tiling with a ragged last row tile, the
   oracle on sampled rows and the tail rows.
 Inputs: seeded bf16 N(0, 0.02) weights with norm gains 1 + N(0, 0.1^2), uniform tokens, F32 N(0,1)
@@ -195,11 +195,13 @@ def test_mlp_slices_sum_to_full_mlp(mlp70b, T):
 def test_8b_split_equals_unsplit_on_gpu(w8b_first, kv_f32):
     # blocks [0, 2) in one stage against [0, 1) + [1, 2) with the F32 handoff, at the real 8B shape:
     # a 300-row prefill (LDS-direct GEMMs, split-K sums; in one stage block 0's down projection
-    # also normalises for block 1, in two stages block 1 normalises its input itself) and two B = 1
-    # decode steps (GEMVs, split-KV attention); hidden rows and both blocks' KV bit for bit
-    s, T = fx.LLAMA8B, 300
+    # also normalises for block 1, in two stages block 1 normalises its input itself), two B = 1
+    # decode steps (GEMVs, split-KV attention), then one B = 64 decode step over 64 slots holding
+    # copies of that context (64-row GEMM tiles, split-K sums fused with the next norm); hidden rows
+    # and both blocks' KV bit for bit
+    s, T, B = fx.LLAMA8B, 300, 64
     dev = torch.device("cuda")
-    kw = dict(max_slots=1, max_ctx=512, max_tokens=512, kv_f32=kv_f32)
+    kw = dict(max_slots=B, max_ctx=512, max_tokens=512, kv_f32=kv_f32)
     whole = make_stage(s, 0, 2, True, False, w8b_first, **kw)
     a = make_stage(s, 0, 1, True, False, w8b_first, **kw)
     b = make_stage(s, 1, 2, False, False, w8b_first, **kw)
@@ -215,11 +217,23 @@ def test_8b_split_equals_unsplit_on_gpu(w8b_first, kv_f32):
         d2 = b.decode(a.decode(a.embed(t), sl, ps), sl, ps)
         assert torch.equal(d1, d2)
     n = T + len(toks)
+    for st in (whole, a, b):
+        for slot in range(1, B):
+            st.kv_copy(0, slot, n)
+    tb = torch.tensor(fx.tokens(fx.SEED_TOKENS, fx.token_stream(4), B, s.vocab), dtype=torch.int32, device=dev)
+    sl = torch.arange(B, dtype=torch.int32, device=dev)
+    ps = torch.full((B,), n, dtype=torch.int32, device=dev)
+    d1 = whole.decode(whole.embed(tb), sl, ps)
+    d2 = b.decode(a.decode(a.embed(tb), sl, ps), sl, ps)
+    assert torch.equal(d1, d2)
+    assert whole.device_errors() == 0 and a.device_errors() == 0 and b.device_errors() == 0
     for blk, part in ((0, a), (1, b)):
-        kw_, vw_ = kv_bits(whole, blk, 0, n)
-        kp, vp = kv_bits(part, blk, 0, n)
-        assert np.array_equal(kw_, kp) and np.array_equal(vw_, vp)
-    say(f"8B split [0,1)+[1,2) == [0,2), {'f32' if kv_f32 else 'bf16'} cache: prefill {T} rows, 2 decode steps, KV")
+        for slot in (0, 1, B - 1):
+            kw_, vw_ = kv_bits(whole, blk, slot, n + 1)
+            kp, vp = kv_bits(part, blk, slot, n + 1)
+            assert np.array_equal(kw_, kp) and np.array_equal(vw_, vp)
+    say(f"8B split [0,1)+[1,2) == [0,2), {'f32' if kv_f32 else 'bf16'} cache: prefill {T} rows, 2 decode steps, "
+        f"B={B} decode step, KV")
 
 
 @pytest.mark.parametrize("T", [40, 100, 257, 300, 512])
