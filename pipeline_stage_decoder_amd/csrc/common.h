@@ -4,19 +4,24 @@
 #include <stdint.h>
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 #define PSD_DEV __device__ __forceinline__
 
-// bf16 <-> f32 on raw bits.  f32 -> bf16 rounds to nearest, ties to even; inputs are finite.
+// bf16 <-> f32 on raw bits.  f32 -> bf16 rounds to nearest, ties to even, on gfx950's packed
+// conversion (v_cvt_pk_bf16_f32, two values per instruction): for every finite f32 it gives the
+// bits (u + 0x7FFF + ((u >> 16) & 1)) >> 16 of the rounding written out on the integer bits
+// (checked over all 2^32 patterns on MI355X).  Inputs are finite.
 PSD_DEV float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 PSD_DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 PSD_DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-PSD_DEV uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+PSD_DEV uint32_t pack_bf2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
-PSD_DEV uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+PSD_DEV uint32_t f2bf(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f); }
 
 PSD_DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -55,17 +60,25 @@ PSD_DEV void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   mid = f2bf(r);
   lo = f2bf(r - bf2f(mid));
 }
+// the same three planes of two values, packed as bf16 pairs
+PSD_DEV void split3_pk(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = pack_bf2(x0, x1);
+  const float r0 = x0 - bf_lo(hi), r1 = x1 - bf_hi(hi);
+  mid = pack_bf2(r0, r1);
+  lo = pack_bf2(r0 - bf_lo(mid), r1 - bf_hi(mid));
+}
+
+// hi and lo planes of two values packed as bf16 pairs (the same split as split2, two at a time)
+PSD_DEV void split2_pk(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf2(x0, x1);
+  lo = pack_bf2(x0 - bf_lo(hi), x1 - bf_hi(hi));
+}
 
 // Split an f32 x8 vector into bf16 hi + bf16 lo (x ~= hi + lo to ~2^-16 relative).
 PSD_DEV void split_hi_lo(const float* x, uint4& hi, uint4& lo) {
   uint32_t h[4], l[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t a = f2bf(x[2 * i]), b = f2bf(x[2 * i + 1]);
-    h[i] = a | (b << 16);
-    float ra = x[2 * i] - bf2f(a), rb = x[2 * i + 1] - bf2f(b);
-    l[i] = pack_bf2(ra, rb);
-  }
+  for (int i = 0; i < 4; ++i) split2_pk(x[2 * i], x[2 * i + 1], h[i], l[i]);
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
@@ -147,13 +160,12 @@ PSD_DEV void qkv_store_pair(const EpiArgs& e, int m, int slot, int pos, int col0
     const float y1 = (float)((double)x1 * cs.x + (double)x0 * cs.y);
     if (is_q) {
       uint16_t* dst = e.q + (size_t)m * qw + head * dh;
-      uint32_t h0, l0, h1, l1;
-      split2(y0, h0, l0);
-      split2(y1, h1, l1);
-      dst[i] = (uint16_t)h0;
-      dst[i + (dh >> 1)] = (uint16_t)h1;
-      dst[e.q_ps + i] = (uint16_t)l0;
-      dst[e.q_ps + i + (dh >> 1)] = (uint16_t)l1;
+      uint32_t h, l;
+      split2_pk(y0, y1, h, l);
+      dst[i] = (uint16_t)h;
+      dst[i + (dh >> 1)] = (uint16_t)(h >> 16);
+      dst[e.q_ps + i] = (uint16_t)l;
+      dst[e.q_ps + i + (dh >> 1)] = (uint16_t)(l >> 16);
     } else {
       const size_t o = (((size_t)slot * e.hkv + head) * e.ctx_cap + pos) * dh;
       if (e.kv_f32) {
@@ -162,8 +174,9 @@ PSD_DEV void qkv_store_pair(const EpiArgs& e, int m, int slot, int pos, int col0
         dst[i + (dh >> 1)] = y1;
       } else {
         uint16_t* dst = static_cast<uint16_t*>(e.kc) + o;
-        dst[i] = (uint16_t)f2bf(y0);
-        dst[i + (dh >> 1)] = (uint16_t)f2bf(y1);
+        const uint32_t h = pack_bf2(y0, y1);
+        dst[i] = (uint16_t)h;
+        dst[i + (dh >> 1)] = (uint16_t)(h >> 16);
       }
     }
   } else {
@@ -177,8 +190,9 @@ PSD_DEV void qkv_store_pair(const EpiArgs& e, int m, int slot, int pos, int col0
       base[i1] = x1;
     } else {
       uint16_t* base = static_cast<uint16_t*>(e.vc) + o;
-      base[i0] = (uint16_t)f2bf(x0);
-      base[i1] = (uint16_t)f2bf(x1);
+      const uint32_t h = pack_bf2(x0, x1);
+      base[i0] = (uint16_t)h;
+      base[i1] = (uint16_t)(h >> 16);
     }
   }
 }

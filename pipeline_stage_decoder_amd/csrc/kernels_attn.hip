@@ -310,14 +310,9 @@ PSD_DEV int k_swz(int key) {
 
 // 4 F32 values -> their bf16 hi and lo planes (the same split as split_hi_lo, half as wide).
 PSD_DEV void split_hi_lo4(const uint4& v, uint2& hi, uint2& lo) {
-  const float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
   uint32_t h[2], l[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t a = f2bf(x[2 * i]), b = f2bf(x[2 * i + 1]);
-    h[i] = a | (b << 16);
-    l[i] = pack_bf2(x[2 * i] - bf2f(a), x[2 * i + 1] - bf2f(b));
-  }
+  split2_pk(__uint_as_float(v.x), __uint_as_float(v.y), h[0], l[0]);
+  split2_pk(__uint_as_float(v.z), __uint_as_float(v.w), h[1], l[1]);
   hi = make_uint2(h[0], h[1]);
   lo = make_uint2(l[0], l[1]);
 }

@@ -51,12 +51,10 @@ PSD_DEV float norm_mul(float x, double r, float g) { return (float)((double)x * 
 PSD_DEV void store_norm_planes4(uint16_t* p, size_t ps, const float4& v, double r, const float4& g) {
   const float y0 = norm_mul(v.x, r, g.x), y1 = norm_mul(v.y, r, g.y), y2 = norm_mul(v.z, r, g.z),
               y3 = norm_mul(v.w, r, g.w);
-  uint32_t h[4], md[4], l[4];
-  split3(y0, h[0], md[0], l[0]);
-  split3(y1, h[1], md[1], l[1]);
-  split3(y2, h[2], md[2], l[2]);
-  split3(y3, h[3], md[3], l[3]);
-  *(uint2*)p = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-  *(uint2*)(p + ps) = make_uint2(md[0] | (md[1] << 16), md[2] | (md[3] << 16));
-  *(uint2*)(p + 2 * ps) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+  uint32_t h[2], md[2], l[2];
+  split3_pk(y0, y1, h[0], md[0], l[0]);
+  split3_pk(y2, y3, h[1], md[1], l[1]);
+  *(uint2*)p = make_uint2(h[0], h[1]);
+  *(uint2*)(p + ps) = make_uint2(md[0], md[1]);
+  *(uint2*)(p + 2 * ps) = make_uint2(l[0], l[1]);
 }
