@@ -73,10 +73,12 @@ typedef struct {
 
 #define STAGE_FIRST 1u  /* owns the token embedding */
 #define STAGE_LAST 2u   /* owns the final RMSNorm and the readout */
-#define STAGE_KV_F32 4u /* KV cache elements are F32 instead of bf16 (twice the bytes).  With bf16,
+#define STAGE_KV_F32 4u /* F32-grade KV cache instead of bf16 (twice the bytes): each K/V value
+                           is kept as a bf16 hi + lo pair (~16 significant bits), the two planes
+                           attention multiplies, split once when the value is written.  With bf16,
                            a K/V value that a float64 reference and the GPU's f32 sums put on
                            different sides of a bf16 rounding boundary perturbs attention, which
-                           flips more roundings in later blocks; F32 storage keeps a deep stage
+                           flips more roundings in later blocks; the pair keeps a deep stage
                            within 1e-3 of a float64 reference. */
 
 typedef struct {
@@ -90,7 +92,7 @@ typedef struct {
 
 typedef struct {
   uint64_t weight_bytes;    /* bf16 matrices, F32 norm gains */
-  uint64_t kv_bytes;        /* K and V (bf16, or F32 with STAGE_KV_F32) for every owned block and slot */
+  uint64_t kv_bytes;        /* K and V (bf16, or 4 bytes per value with STAGE_KV_F32) for every owned block and slot */
   uint64_t table_bytes;     /* RoPE cos/sin table (float64) */
   uint64_t workspace_bytes; /* per-call activations, split-K and split-KV partials, error counter */
   uint64_t total_bytes;     /* arena size stage_create needs (sum of the above with alignment) */
@@ -205,8 +207,8 @@ int stage_embed_range(stage_t* st, int n, const int32_t* tokens, int vocab_lo, f
 int stage_kv_copy(stage_t* st, int src_slot, int dst_slot, int n_pos, hipStream_t stream);
 
 /* Write / read KV of one owned block and slot at positions [pos0, pos0+n): k, v are device
- * [n, Hkv, Dh] arrays in the cache's element type -- bf16 bits, or F32 with STAGE_KV_F32 -- with K
- * after RoPE, as attention reads it. */
+ * [n, Hkv, Dh] arrays -- bf16 bits, or F32 with STAGE_KV_F32 (imported values are split into the
+ * cache's hi + lo pair; exported values are hi + lo) -- with K after RoPE, as attention reads it. */
 int stage_kv_import(stage_t* st, int global_block, int slot, int pos0, int n, const void* k, const void* v,
                     hipStream_t stream);
 int stage_kv_export(stage_t* st, int global_block, int slot, int pos0, int n, void* k, void* v,

@@ -112,7 +112,8 @@ struct EpiArgs {
   size_t q_ps;
   void* kc;                    // K cache of this block: [slots][Hkv][ctx_cap][Dh]
   void* vc;                    // V cache of this block: [slots][Hkv][ctx_cap/8][Dh][8]
-  int kv_f32;                  // cache elements are F32 (else bf16)
+  int kv_f32;                  // F32-grade cache: each K row / V 8-key group holds a bf16 hi
+                               // plane and then a lo plane (4 bytes per element); else bf16
   const double2* rope;         // [ctx_cap][Dh/2] (cos, sin), f64
   RowPos rp;
   int hq, hkv, dh, ctx_cap, max_slots;
@@ -169,9 +170,14 @@ PSD_DEV void qkv_store_pair(const EpiArgs& e, int m, int slot, int pos, int col0
     } else {
       const size_t o = (((size_t)slot * e.hkv + head) * e.ctx_cap + pos) * dh;
       if (e.kv_f32) {
-        float* dst = static_cast<float*>(e.kc) + o;
-        dst[i] = y0;
-        dst[i + (dh >> 1)] = y1;
+        // F32-grade cache: the key row holds the bf16 hi plane [Dh], then the lo plane [Dh]
+        uint16_t* dst = static_cast<uint16_t*>(e.kc) + 2 * o;
+        uint32_t h, l;
+        split2_pk(y0, y1, h, l);
+        dst[i] = (uint16_t)h;
+        dst[i + (dh >> 1)] = (uint16_t)(h >> 16);
+        dst[dh + i] = (uint16_t)l;
+        dst[dh + i + (dh >> 1)] = (uint16_t)(l >> 16);
       } else {
         uint16_t* dst = static_cast<uint16_t*>(e.kc) + o;
         const uint32_t h = pack_bf2(y0, y1);
@@ -185,9 +191,14 @@ PSD_DEV void qkv_store_pair(const EpiArgs& e, int m, int slot, int pos, int col0
     const size_t o = (((size_t)slot * e.hkv + head) * (e.ctx_cap >> 3) + (pos >> 3)) * dh * 8;
     const size_t i0 = (size_t)d0 * 8 + (pos & 7), i1 = (size_t)(d0 + 16) * 8 + (pos & 7);
     if (e.kv_f32) {
-      float* base = static_cast<float*>(e.vc) + o;
-      base[i0] = x0;
-      base[i1] = x1;
+      // F32-grade cache: the 8-key group holds the hi plane [Dh][8], then the lo plane [Dh][8]
+      uint16_t* base = static_cast<uint16_t*>(e.vc) + 2 * o;
+      uint32_t h, l;
+      split2_pk(x0, x1, h, l);
+      base[i0] = (uint16_t)h;
+      base[i1] = (uint16_t)(h >> 16);
+      base[(size_t)dh * 8 + i0] = (uint16_t)l;
+      base[(size_t)dh * 8 + i1] = (uint16_t)(l >> 16);
     } else {
       uint16_t* base = static_cast<uint16_t*>(e.vc) + o;
       const uint32_t h = pack_bf2(x0, x1);

@@ -47,7 +47,7 @@ struct AttnDecodeArgs {
   size_t q_ps;
   const void* kc;           // K cache of the block
   const void* vc;           // V cache of the block
-  int kv_f32;               // cache elements are F32 (else bf16)
+  int kv_f32;               // F32-grade cache (bf16 hi + lo planes per K row / V group), else bf16
   const int32_t* slots;     // [B]
   const int32_t* pos;       // [B]; keys [0, pos] are attended
   int B, hq, hkv, dh, ctx_cap, max_slots;

@@ -28,26 +28,23 @@
 
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // Keys of the two S^T MFMAs that A row `rho` (0..15) of chunk c feeds: (rho/4)*8 + c*4 + rho%4.
 PSD_DEV int key_of_row(int rho, int c) { return ((rho >> 2) << 3) + (c << 2) + (rho & 3); }
 
-// 8 consecutive cache elements from element offset `off`: bf16 bits as they are (lo = 0), or F32
-// split into bf16 hi + lo.
+// 8 consecutive cache elements: a bf16 cache's bits at element offset `off` (lo = 0), or an F32-grade
+// cache's hi plane there and its lo plane `lo_off` elements further (both bf16, split when written).
+// (Written as a branch: as a select between the load and zero, the compiler split each 16-byte
+// load into four 4-byte loads behind branches.)
 template <bool KF32>
-PSD_DEV void load8(const void* base, size_t off, bool ok, uint4& hi, uint4& lo) {
-  if (KF32) {
-    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (ok) {
-      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off + 4);
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    }
-    split_hi_lo(x, hi, lo);
-  } else {
-    hi = ok ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off) : make_uint4(0, 0, 0, 0);
-    lo = make_uint4(0, 0, 0, 0);
+PSD_DEV void load8(const uint16_t* base, size_t off, size_t lo_off, bool ok, uint4& hi, uint4& lo) {
+  hi = make_uint4(0, 0, 0, 0);
+  lo = make_uint4(0, 0, 0, 0);
+  if (ok) {
+    hi = *reinterpret_cast<const uint4*>(base + off);
+    if (KF32) lo = *reinterpret_cast<const uint4*>(base + off + lo_off);
   }
 }
 
@@ -70,25 +67,28 @@ struct Col16 {
 // One 32-key step for a wave's 16 columns.  kb: first key (multiple of 8); visible(key) says
 // whether a key counts for the lane's column; keys >= kend are never read.
 template <int DH, bool KF32, typename Visible>
-PSD_DEV void attn_step(Col16<DH>& st, const void* __restrict__ kbase, const void* __restrict__ vbase, int kb,
+PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase, int kb,
                        int kend, float scale_log2, Visible visible) {
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   // issue every K and V load of the step first: one memory round trip per step
   uint4 kh[2][DH / 32], kl[2][DH / 32];
+  // K row `key` starts at element key * DH (bf16) or key * 2 DH (hi plane, then lo plane); V group
+  // g at g * DH * 8 or g * 2 DH * 8 (likewise)
+  constexpr int NPL = KF32 ? 2 : 1;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int key = kb + key_of_row(col, c);
     const bool ok = key < kend;
 #pragma unroll
     for (int ks = 0; ks < DH / 32; ++ks)
-      load8<KF32>(kbase, (size_t)key * DH + ks * 32 + grp * 8, ok, kh[c][ks], kl[c][ks]);
+      load8<KF32>(kbase, (size_t)key * NPL * DH + ks * 32 + grp * 8, DH, ok, kh[c][ks], kl[c][ks]);
   }
   const int kg = kb + grp * 8;              // this lane's 8 keys in the PV product
   const int nvalid = kend - kg;             // keys of the group below kend
   uint4 vh[DH / 16], vl[DH / 16];
 #pragma unroll
   for (int dt = 0; dt < DH / 16; ++dt)
-    load8<KF32>(vbase, ((size_t)(kg >> 3) * DH + dt * 16 + col) * 8, nvalid > 0, vh[dt], vl[dt]);
+    load8<KF32>(vbase, (size_t)(kg >> 3) * NPL * DH * 8 + (dt * 16 + col) * 8, DH * 8, nvalid > 0, vh[dt], vl[dt]);
   f32x4_t sc[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -181,8 +181,10 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
   Col16<DH> st;
   load_q(st, col < G ? a.q + ((size_t)b * a.hq + kvh * G + col) * DH : nullptr, a.q_ps);
   const size_t eb = KF32 ? 4 : 2;
-  const char* kbase = static_cast<const char*>(a.kc) + ((size_t)slot * a.hkv + kvh) * a.ctx_cap * DH * eb;
-  const char* vbase = static_cast<const char*>(a.vc) + ((size_t)slot * a.hkv + kvh) * (size_t)a.ctx_cap * DH * eb;
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.kc) +
+                                                            ((size_t)slot * a.hkv + kvh) * a.ctx_cap * DH * eb);
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.vc) +
+                                                            ((size_t)slot * a.hkv + kvh) * (size_t)a.ctx_cap * DH * eb);
   // the 4 waves take interleaved 32-key steps, so that the work-group reads one contiguous 128-key
   // stretch of K and of V at a time (4% faster than a quarter of the chunk per wave at B = 128)
   for (int kb = k0 + wave * 32; kb < k1; kb += 128)
@@ -308,23 +310,14 @@ PSD_DEV int k_swz(int key) {
   return RC >= 16 ? c * (RC / 16) : c >> 1;
 }
 
-// 4 F32 values -> their bf16 hi and lo planes (the same split as split_hi_lo, half as wide).
-PSD_DEV void split_hi_lo4(const uint4& v, uint2& hi, uint2& lo) {
-  uint32_t h[2], l[2];
-  split2_pk(__uint_as_float(v.x), __uint_as_float(v.y), h[0], l[0]);
-  split2_pk(__uint_as_float(v.z), __uint_as_float(v.w), h[1], l[1]);
-  hi = make_uint2(h[0], h[1]);
-  lo = make_uint2(l[0], l[1]);
-}
-
 template <int DH, bool KF32>
 __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
   constexpr int EB = KF32 ? 4 : 2;
   constexpr int TILE_CHUNKS = kKeyTile * DH * EB / 16;     // 16-byte global chunks per K (and V) tile
   constexpr int PER_THREAD = TILE_CHUNKS / 256;
   static_assert(TILE_CHUNKS % 256 == 0, "tile chunks per thread");
-  // LDS holds bf16 planes: the cache's bf16 values, or an F32 cache's hi and lo planes split once
-  // when the tile is stored (every wave then reads ready MFMA operands in the bf16 layout)
+  // LDS holds bf16 planes: the cache's bf16 values, or an F32-grade cache's hi and lo planes (split
+  // when the cache was written), so every wave reads ready MFMA operands in the bf16 layout
   constexpr int NPL = KF32 ? 2 : 1;
   constexpr int RC = DH / 8;                               // 16-byte chunks per bf16 K row
   constexpr int PLANE = kKeyTile * RC;                     // uint4 per plane tile
@@ -352,12 +345,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
 
   Col16<DH> st;
   load_q(st, cvalid ? a.q + ((size_t)t * a.hq + head) * DH : nullptr, a.q_ps);
-  const uint4* kg = reinterpret_cast<const uint4*>(static_cast<const char*>(a.kc) +
+  const u32x4* kg = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.kc) +
                                                   ((size_t)a.slot * a.hkv + kvh) * a.ctx_cap * DH * EB);
-  const uint4* vg = reinterpret_cast<const uint4*>(static_cast<const char*>(a.vc) +
+  const u32x4* vg = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.vc) +
                                                   ((size_t)a.slot * a.hkv + kvh) * (size_t)a.ctx_cap * DH * EB);
-  // a tile is one contiguous byte range of K (32 rows of [Dh]) and of V (4 packed 8-key groups)
-  uint4 kr[PER_THREAD], vr[PER_THREAD];
+  // a tile is one contiguous byte range of K (kKeyTile rows) and of V (kKeyTile / 8 packed groups)
+  u32x4 kr[PER_THREAD], vr[PER_THREAD];
   auto gload = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
@@ -371,21 +364,17 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
     for (int i = 0; i < PER_THREAD; ++i) {
       const int q = threadIdx.x + i * 256;
       if (KF32) {
-        // K: chunk q holds dims 4ch .. 4ch+3 of key `row` = half `hf` of bf16 chunk ch / 2
-        const int row = q / (DH / 4), ch = q - row * (DH / 4);
-        const int u2 = (row * RC + ((ch >> 1) ^ k_swz<RC>(row & 31))) * 2 + (ch & 1);
-        uint2 hi, lo;
-        split_hi_lo4(kr[i], hi, lo);
-        reinterpret_cast<uint2*>(kt[buf][0])[u2] = hi;
-        reinterpret_cast<uint2*>(kt[buf][NPL - 1])[u2] = lo;
-        // V: chunk q holds keys 4(q&1) .. +4 of one (group, dim): half of its bf16 chunk, index q
-        split_hi_lo4(vr[i], hi, lo);
-        reinterpret_cast<uint2*>(vt[buf][0])[q] = hi;
-        reinterpret_cast<uint2*>(vt[buf][NPL - 1])[q] = lo;
+        // K: a row is RC hi-plane chunks, then RC lo-plane chunks (planes PLANE chunks apart in LDS)
+        const int row = q / (2 * RC), cc = q - row * (2 * RC);
+        const int pl = cc / RC, ch = cc % RC;
+        reinterpret_cast<u32x4*>(&kt[buf][0][0])[pl * PLANE + row * RC + (ch ^ k_swz<RC>(row & 31))] = kr[i];
+        // V: an 8-key group is DH hi-plane chunks (one per dim), then DH lo-plane chunks
+        const int g = q / (2 * DH), cv = q - g * (2 * DH);
+        reinterpret_cast<u32x4*>(&vt[buf][0][0])[(cv / DH) * PLANE + g * DH + cv % DH] = vr[i];
       } else {
         const int row = q / RC, ch = q - row * RC;
-        kt[buf][0][row * RC + (ch ^ k_swz<RC>(row & 31))] = kr[i];
-        vt[buf][0][q] = vr[i];
+        reinterpret_cast<u32x4*>(kt[buf][0])[row * RC + (ch ^ k_swz<RC>(row & 31))] = kr[i];
+        reinterpret_cast<u32x4*>(vt[buf][0])[q] = vr[i];
       }
     }
   };

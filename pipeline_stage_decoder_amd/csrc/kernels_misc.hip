@@ -91,6 +91,35 @@ __global__ void k_kv_export(const T* kc, const T* vc, int hkv, int dh, int ctx_c
   v[dst] = vc[((((size_t)slot * hkv + h) * (ctx_cap >> 3) + (pos >> 3)) * dh + d) * 8 + (pos & 7)];
 }
 
+// The F32-grade cache: element d of a K row (V 8-key group) is hi + lo, the row's (group's) bf16 hi
+// plane followed by its lo plane.  Import splits F32 values the way the QKV epilogue does; export
+// returns hi + lo (exact in F32).
+__global__ void k_kv_import_pair(uint16_t* kc, uint16_t* vc, int hkv, int dh, int ctx_cap, int slot, int pos0,
+                                 const float* __restrict__ k, const float* __restrict__ v) {
+  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const int pos = pos0 + t;
+  const size_t src = ((size_t)t * hkv + h) * dh + d;
+  const size_t kr = (((size_t)slot * hkv + h) * ctx_cap + pos) * 2 * dh;
+  const size_t vg = (((size_t)slot * hkv + h) * (ctx_cap >> 3) + (pos >> 3)) * 2 * dh * 8 + (size_t)d * 8 + (pos & 7);
+  uint32_t hi, lo;
+  split2(k[src], hi, lo);
+  kc[kr + d] = (uint16_t)hi;
+  kc[kr + dh + d] = (uint16_t)lo;
+  split2(v[src], hi, lo);
+  vc[vg] = (uint16_t)hi;
+  vc[vg + (size_t)dh * 8] = (uint16_t)lo;
+}
+
+__global__ void k_kv_export_pair(const uint16_t* kc, const uint16_t* vc, int hkv, int dh, int ctx_cap, int slot,
+                                 int pos0, float* __restrict__ k, float* __restrict__ v) {
+  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const int pos = pos0 + t;
+  const size_t dst = ((size_t)t * hkv + h) * dh + d;
+  const size_t kr = (((size_t)slot * hkv + h) * ctx_cap + pos) * 2 * dh;
+  const size_t vg = (((size_t)slot * hkv + h) * (ctx_cap >> 3) + (pos >> 3)) * 2 * dh * 8 + (size_t)d * 8 + (pos & 7);
+  k[dst] = bf2f(kc[kr + d]) + bf2f(kc[kr + dh + d]);
+  v[dst] = bf2f(vc[vg]) + bf2f(vc[vg + (size_t)dh * 8]);
+}
 
 // Greedy choice per row: the largest logit, the lowest index among equal ones.  Each thread scans
 // a strided subset in ascending index order (a strict > keeps its first maximum), then the
@@ -174,9 +203,9 @@ hipError_t launch_kv_import(void* kc, void* vc, int kv_f32, int hkv, int dh, int
                             int n, const void* k, const void* v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (kv_f32)
-    k_kv_import<float><<<dim3(n, hkv), dh, 0, s>>>(static_cast<float*>(kc), static_cast<float*>(vc), hkv, dh,
-                                                   ctx_cap, slot, pos0, static_cast<const float*>(k),
-                                                   static_cast<const float*>(v));
+    k_kv_import_pair<<<dim3(n, hkv), dh, 0, s>>>(static_cast<uint16_t*>(kc), static_cast<uint16_t*>(vc), hkv, dh,
+                                                 ctx_cap, slot, pos0, static_cast<const float*>(k),
+                                                 static_cast<const float*>(v));
   else
     k_kv_import<uint16_t><<<dim3(n, hkv), dh, 0, s>>>(static_cast<uint16_t*>(kc), static_cast<uint16_t*>(vc), hkv,
                                                       dh, ctx_cap, slot, pos0, static_cast<const uint16_t*>(k),
@@ -188,9 +217,9 @@ hipError_t launch_kv_export(const void* kc, const void* vc, int kv_f32, int hkv,
                             int pos0, int n, void* k, void* v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (kv_f32)
-    k_kv_export<float><<<dim3(n, hkv), dh, 0, s>>>(static_cast<const float*>(kc), static_cast<const float*>(vc), hkv,
-                                                   dh, ctx_cap, slot, pos0, static_cast<float*>(k),
-                                                   static_cast<float*>(v));
+    k_kv_export_pair<<<dim3(n, hkv), dh, 0, s>>>(static_cast<const uint16_t*>(kc), static_cast<const uint16_t*>(vc),
+                                                 hkv, dh, ctx_cap, slot, pos0, static_cast<float*>(k),
+                                                 static_cast<float*>(v));
   else
     k_kv_export<uint16_t><<<dim3(n, hkv), dh, 0, s>>>(static_cast<const uint16_t*>(kc),
                                                       static_cast<const uint16_t*>(vc), hkv, dh, ctx_cap, slot, pos0,
