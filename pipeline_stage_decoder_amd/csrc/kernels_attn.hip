@@ -325,9 +325,13 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
   __shared__ uint4 vt[2][NPL][PLANE];
 
   const int G = a.hq / a.hkv;
-  const int kvh = blockIdx.y;
+  // Work-groups go to the 8 XCDs round-robin in linear block order, so block b takes KV head
+  // b % Hkv: with 8 KV heads each XCD's L2 holds one head's K/V, which all of that head's column
+  // blocks re-read.  Heavier (later) column blocks first.
+  const int b = blockIdx.y * gridDim.x + blockIdx.x;
+  const int kvh = b % a.hkv;
   const int ncols = a.T * G;
-  const int cblk = gridDim.x - 1 - blockIdx.x;               // heavier (later) column blocks first
+  const int cblk = gridDim.x - 1 - b / a.hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int c0 = cblk * 64 + wave * 16;
   const int c = c0 + col;
