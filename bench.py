@@ -883,11 +883,13 @@ def main():
     torch.cuda.synchronize()
     prefill_kernel_ms = {k: round(st.timing_read(k)[1], 4) for k in pkinds}
     st.timing([])
-    # MFMA work issued: activation operands enter as bf16 hi + lo planes (three for QKV), so the
-    # matrix cores execute planes x the algorithmic linear flops; attention issues 2 products per
-    # score / output term (3 with an F32 cache, whose lo plane adds one)
+    # MFMA work issued: activation operands enter as bf16 hi + lo planes (three for QKV with a bf16
+    # cache, two with the F32-grade one), so the matrix cores execute planes x the algorithmic
+    # linear flops; attention issues 2 products per score / output term (3 with the F32-grade
+    # cache, whose lo plane adds one)
     lin = acc.projection_shapes(shape)
-    issued_lin = 16 * 2 * T * sum(n * k * (3 if kind == "qkv" else 2) for kind, (n, k) in lin.items()
+    qkv_planes = 2 if kv_f32 else 3
+    issued_lin = 16 * 2 * T * sum(n * k * (qkv_planes if kind == "qkv" else 2) for kind, (n, k) in lin.items()
                                   if kind != "readout")
 
     n_gu, ms_gu = kern["gateup"]

@@ -255,8 +255,8 @@ size_t ps_q(const stage* st) { return (size_t)st->s.max_tokens * st->m.n_q_heads
 size_t ps_act(const stage* st) { return (size_t)st->s.max_tokens * st->m.d_ffn; }
 
 // Planes of the QKV operand: three (~24 bits) when K/V are rounded into a bf16 cache, so that the
-// rounding sees f32-grade values; two with an F32 cache, whose values attention splits into two
-// bf16 planes anyway.
+// rounding sees f32-grade values; two with the F32-grade cache, which keeps each value as a bf16
+// hi + lo pair (~16 bits) anyway.
 int qkv_planes(const stage* st) { return st->kv_f32 ? 2 : 3; }
 
 // The RMSNorm a projection's output feeds next: `gain` (null: none requested).  `done` is set when

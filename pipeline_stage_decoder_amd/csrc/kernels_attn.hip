@@ -14,7 +14,8 @@
 //   O^T[d, col] += V^T[d, key] P^T[key, col]   A = V^T read as 8 consecutive elements from the
 //       packed V cache [pos/8][Dh][8]; B = P^T straight from registers, split into bf16 hi + lo
 //       (two MFMAs) so the probabilities keep ~16 bits.
-//   An F32 cache is split into bf16 hi + lo on load and adds the K_lo.q_hi and V_lo.P_hi MFMAs.
+//   An F32-grade cache holds each value as bf16 hi + lo planes and adds the K_lo.q_hi and V_lo.P_hi
+//   MFMAs.
 // The softmax is online per column (max and rescale), in base 2 with the scale folded in.  O^T
 // puts a column's values in the same lane as its softmax state, so rescaling needs no shuffles.
 //
