@@ -83,3 +83,31 @@ def test_stage_refuses_small_arena_and_foreign_roles():
     rc = S.lib().stage_create(ctypes.byref(st._m), ctypes.byref(st._s), arena.data_ptr(), arena.numel(), 0,
                               ctypes.byref(h))
     assert rc == S.STAGE_E_DOES_NOT_FIT
+
+
+def test_kv_import_export_formats():
+    # STAGE_KV_F32 keeps each value as a bf16 hi + lo pair: import splits F32 values (hi = bf16(x),
+    # lo = bf16(x - hi), both rounded to nearest even), export returns hi + lo, so the round trip
+    # is that sum bit for bit and within 2^-16 of x.  A bf16 cache returns the imported bits.
+    from oracle import decoder as o
+    s = fx.TINY
+    dev = torch.device("cuda")
+    n, shp = 40, (40, s.n_kv_heads, s.head_dim)
+    per = int(np.prod(shp))
+    st = make_stage(s, 0, 1, False, False, {}, max_slots=2, max_ctx=64, max_tokens=16, kv_f32=True)
+    k = fx.normal_f32(9, 1, per).reshape(shp)
+    v = fx.normal_f32(9, 2, per).reshape(shp)
+    st.kv_import(0, 1, 3, torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev))
+    ke, ve = st.kv_export(0, 1, 3, n)
+    for x, got in ((k, ke.cpu().numpy()), (v, ve.cpu().numpy())):
+        hi = o.bf16_to_f32(o.f32_to_bf16_bits(x))
+        lo = o.bf16_to_f32(o.f32_to_bf16_bits((x - hi).astype(np.float32)))
+        assert np.array_equal(got, (hi + lo).astype(np.float32))
+        assert np.all(np.abs(got.astype(np.float64) - x) <= 2.0 ** -16 * np.abs(x))
+    st2 = make_stage(s, 0, 1, False, False, {}, max_slots=2, max_ctx=64, max_tokens=16)
+    kb = fx.normal_bf16(9, 3, per, 1.0).reshape(shp)
+    vb = fx.normal_bf16(9, 4, per, 1.0).reshape(shp)
+    st2.kv_import(0, 0, 0, torch.from_numpy(kb.view(np.int16)).to(dev), torch.from_numpy(vb.view(np.int16)).to(dev))
+    ke2, ve2 = st2.kv_export(0, 0, 0, n)
+    assert np.array_equal(ke2.cpu().numpy().view(np.uint16), kb)
+    assert np.array_equal(ve2.cpu().numpy().view(np.uint16), vb)
