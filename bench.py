@@ -52,9 +52,10 @@ def fill_weights(st, shape, blocks, first, last, seed, gain_sigma=0.0):
     del scratch
 
 
-def cpu_baseline_decode(shape, ctx: int, n_blocks: int, reps: int = 2):
-    """The oracle, as it stands, on this host: one block's decode step at context `ctx`,
-    `reps` times; per-token time = n_blocks x the per-block time."""
+def cpu_baseline_decode(shape, ctx: int, n_blocks: int, seconds: float = 10.0, ctx_lo: int = 512):
+    """The oracle, as it stands, on this host: one block's B = 1 decode step at contexts spread
+    over [ctx_lo, ctx] (the workload's decode range), repeated for about `seconds` of CPU work;
+    per-token time = n_blocks x the mean per-block time."""
     import numpy as np
 
     import fixtures as fx
@@ -71,16 +72,20 @@ def cpu_baseline_decode(shape, ctx: int, n_blocks: int, reps: int = 2):
     kv = o.round_bf16(fx.normal_f32(fx.SEED_HIDDEN, 0x7000, int(np.prod(kshape))).reshape(kshape))
     st.kv[0] = (kv.copy(), kv.copy())
     x = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(0), shape.d_model).reshape(1, shape.d_model)
+    positions = [ctx_lo + (ctx - ctx_lo) * i // 3 for i in range(4)]   # spread over the decode range
     st.forward(x, [0], [ctx])                     # warm caches
+    reps = 0
     t0 = time.perf_counter()
-    for _ in range(reps):
-        st.forward(x, [0], [ctx])
-    per_block = (time.perf_counter() - t0) / reps
+    while reps < 4 or time.perf_counter() - t0 < seconds:
+        st.forward(x, [0], [positions[reps % len(positions)]])
+        reps += 1
+    elapsed = time.perf_counter() - t0
+    per_block = elapsed / reps
     per_token = per_block * n_blocks
     return {"value": 1.0 / per_token, "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"{reps} decode steps of 1 of {n_blocks} blocks at context {ctx} (B=1); "
-                      f"tok/s = 1 / ({n_blocks} x {per_block:.2f} s per block-step), extrapolated "
-                      f"linearly over blocks",
+            "sample": f"{reps} decode steps ({elapsed:.1f} s) of 1 of {n_blocks} blocks at contexts "
+                      f"{positions} in turn (B=1); tok/s = 1 / ({n_blocks} x {per_block:.3f} s per "
+                      f"block-step), extrapolated linearly over blocks",
             "seconds_per_block_step": per_block, "cpu_model": cpu_model()}
 
 
