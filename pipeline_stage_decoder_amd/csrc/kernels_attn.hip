@@ -65,6 +65,17 @@ struct Col16 {
   float m, l;              // running max (base-2 scaled) and this lane's share of the sum
 };
 
+// o *= alpha for the wave's columns.  A column whose running max did not move has alpha exactly 1,
+// and one that has seen no visible key still has o exactly 0; the product changes no bit in either
+// case, so the wave skips the multiplies when one of the two holds for every lane.
+template <int DH>
+PSD_DEV void rescale_o(Col16<DH>& st, float m_old, float m_new, float alpha) {
+  if (__any(m_old != m_new && m_old != kNegInf)) {
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] *= alpha;
+  }
+}
+
 // One 32-key step for a wave's 16 columns.  kb: first key (multiple of 8); visible(key) says
 // whether a key counts for the lane's column; keys >= kend are never read.
 template <int DH, bool KF32, typename Visible>
@@ -114,10 +125,10 @@ PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const 
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float m_new = fmaxf(st.m, mx);
+  const float m_old = st.m, m_new = fmaxf(st.m, mx);
   // m_new is -inf only if this column has seen no visible key yet; keep everything at zero then.
   const float base = (m_new == kNegInf) ? 0.0f : m_new;
-  const float alpha = exp2f(st.m - base);
+  const float alpha = exp2f(m_old - base);
   float p[8], ps = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -126,8 +137,7 @@ PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const 
   }
   st.l = st.l * alpha + ps;
   st.m = m_new;
-#pragma unroll
-  for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] *= alpha;
+  rescale_o(st, m_old, m_new, alpha);
   uint4 phi, plo;
   split_hi_lo(p, phi, plo);
 #pragma unroll
@@ -433,9 +443,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(st.m, mx);
+      const float m_old = st.m, m_new = fmaxf(st.m, mx);
       const float base = (m_new == kNegInf) ? 0.0f : m_new;
-      const float alpha = exp2f(st.m - base);
+      const float alpha = exp2f(m_old - base);
       float p[8], ps = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -444,8 +454,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
       }
       st.l = st.l * alpha + ps;
       st.m = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] *= alpha;
+      rescale_o(st, m_old, m_new, alpha);
       uint4 phi, plo;
       split_hi_lo(p, phi, plo);
       // V fragments: 8 keys of group grp at dim dt*16 + col; keys at or past kend (p = 0) are
