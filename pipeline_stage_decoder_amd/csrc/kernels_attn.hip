@@ -27,6 +27,8 @@
 // last query.
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -76,11 +78,11 @@ PSD_DEV void rescale_o(Col16<DH>& st, float m_old, float m_new, float alpha) {
   }
 }
 
-// One 32-key step for a wave's 16 columns.  kb: first key (multiple of 8); visible(key) says
-// whether a key counts for the lane's column; keys >= kend are never read.
-template <int DH, bool KF32, typename Visible>
+// One 32-key step for a wave's 16 columns.  kb: first key (multiple of 8); the keys below kend count
+// for every column, keys >= kend are never read.
+template <int DH, bool KF32>
 PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase, int kb,
-                       int kend, float scale_log2, Visible visible) {
+                       int kend, float scale_log2) {
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   // issue every K and V load of the step first: one memory round trip per step
   uint4 kh[2][DH / 32], kl[2][DH / 32];
@@ -114,15 +116,21 @@ PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const 
   }
   float s[8];
   float mx = kNegInf;
+  auto scores = [&](auto masked_c) {
+    constexpr bool masked = decltype(masked_c)::value;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = kb + grp * 8 + c * 4 + j;
-      const float v = visible(key) ? sc[c][j] * scale_log2 : kNegInf;
-      s[c * 4 + j] = v;
-      mx = fmaxf(mx, v);
-    }
+      for (int j = 0; j < 4; ++j) {
+        const int key = kb + grp * 8 + c * 4 + j;
+        const float v = (!masked || key < kend) ? sc[c][j] * scale_log2 : kNegInf;
+        s[c * 4 + j] = v;
+        mx = fmaxf(mx, v);
+      }
+  };
+  // a whole step below kend: the same values without the per-key test
+  if (kb + 32 <= kend) scores(std::false_type{});
+  else scores(std::true_type{});
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   const float m_old = st.m, m_new = fmaxf(st.m, mx);
@@ -199,7 +207,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
   // the 4 waves take interleaved 32-key steps, so that the work-group reads one contiguous 128-key
   // stretch of K and of V at a time (4% faster than a quarter of the chunk per wave at B = 128)
   for (int kb = k0 + wave * 32; kb < k1; kb += 128)
-    attn_step<DH, KF32>(st, kbase, vbase, kb, k1, a.scale_log2, [&](int key) { return key < k1; });
+    attn_step<DH, KF32>(st, kbase, vbase, kb, k1, a.scale_log2);
 
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
@@ -432,15 +440,23 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
       }
       float sv[8];
       float mx = kNegInf;
+      auto scores = [&](auto masked_c) {
+        constexpr bool masked = decltype(masked_c)::value;
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
+        for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = kb + grp * 8 + cc * 4 + j;
-          const float v = (key >= a.k_lo && key < kend && key <= my_pos) ? sc[cc][j] * a.scale_log2 : kNegInf;
-          sv[cc * 4 + j] = v;
-          mx = fmaxf(mx, v);
-        }
+          for (int j = 0; j < 4; ++j) {
+            const int key = kb + grp * 8 + cc * 4 + j;
+            const bool vis = !masked || (key >= a.k_lo && key < kend && key <= my_pos);
+            const float v = vis ? sc[cc][j] * a.scale_log2 : kNegInf;
+            sv[cc * 4 + j] = v;
+            mx = fmaxf(mx, v);
+          }
+      };
+      // every key of the step visible to every live column of the wave (inside [k_lo, kend) and at
+      // or before the wave's first query): the same values without the per-key mask
+      if (kb >= a.k_lo && kb + 32 <= kend && kb + 31 <= a.pos0 + c0 / G) scores(std::false_type{});
+      else scores(std::true_type{});
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_old = st.m, m_new = fmaxf(st.m, mx);
