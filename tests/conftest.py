@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are only meaningful where a GPU exists; on a CPU-only host they are skipped
-    # (the driver selects them with -m gpu on the GPU machine).
+    # (select them with -m gpu on a machine with an MI355X).
     try:
         import torch
         has_gpu = torch.cuda.is_available()
