@@ -151,3 +151,29 @@ def test_device_side_range_checks(weights):
     st.decode(x, torch.tensor([0, 7], dtype=torch.int32, device=dev), torch.tensor([3, 1], dtype=torch.int32, device=dev))
     torch.cuda.synchronize()
     assert st.device_errors() >= 3
+
+
+@pytest.mark.parametrize("hq,hkv,dh", [(4, 4, 64), (16, 1, 128), (8, 2, 128)])
+def test_gqa_group_sizes_prefill_and_decode(hq, hkv, dh):
+    # query heads per KV head from 1 (every head its own K/V) to 16 (the largest group the kernels
+    # take: one wave's 16 columns are one query's heads); prefill, then B = 2 decode over two slots
+    d = hq * dh if hq * dh >= 256 else 256
+    s = fx.Shape(d, hq, hkv, dh, 128, 512, 1)
+    w = fx.draw_stage_weights(s, 0, 1, False, False, gain_sigma=0.1)
+    T = 40
+    ost = o.Stage(o.Dims.of(s), 0, 1, False, False, w, T + 4)
+    st = make_stage(s, 0, 1, False, False, w, max_slots=2, max_ctx=64, max_tokens=64)
+    dev = torch.device("cuda")
+    for slot in range(2):
+        x = hidden_rows(60 + slot, T - 8 * slot, d)
+        want = ost.prefill(x, slot, 0)
+        got = st.prefill(torch.from_numpy(x).to(dev), slot, 0).cpu().numpy()
+        assert rel_l2(got, want) <= TOL, (slot, "prefill")
+    for step in range(2):
+        pos = np.array([T + step, T - 8 + step])
+        x = np.vstack([hidden_rows(70 + b, 1, d, int(pos[b])) for b in range(2)])
+        want = ost.forward(x, [0, 1], pos)
+        got = st.decode(torch.from_numpy(x).to(dev), torch.tensor([0, 1], dtype=torch.int32, device=dev),
+                        torch.tensor(pos, dtype=torch.int32, device=dev)).cpu().numpy()
+        assert rel_l2(got, want) <= TOL, (step, "decode")
+    assert st.device_errors() == 0
