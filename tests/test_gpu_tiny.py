@@ -177,3 +177,32 @@ def test_gqa_group_sizes_prefill_and_decode(hq, hkv, dh):
                         torch.tensor(pos, dtype=torch.int32, device=dev)).cpu().numpy()
         assert rel_l2(got, want) <= TOL, (step, "decode")
     assert st.device_errors() == 0
+
+
+def test_context_end_and_ragged_capacity(weights):
+    # max_ctx 77, so the cache holds 128 positions per slot: a two-chunk prefill of positions
+    # 0 .. 75, a decode step at the last position 76, a prefill past max_ctx refused on the host, and
+    # a decode row past the cache counted by the device and not computed
+    from pipeline_stage_decoder_amd import stage as S
+    max_ctx, T = 77, 60
+    ost = oracle_stage(weights, 0, 2, False, False, max_ctx=max_ctx)
+    st = make_stage(TINY, 0, 2, False, False, weights, max_slots=1, max_ctx=max_ctx, max_tokens=64)
+    dev = torch.device("cuda")
+    x = hidden_rows(5, max_ctx - 1, TINY.d_model)
+    want = [ost.prefill(x[:T], 0, 0), ost.prefill(x[T:], 0, T)]
+    got = [st.prefill(torch.from_numpy(x[:T]).to(dev), 0, 0).cpu().numpy(),
+           st.prefill(torch.from_numpy(x[T:]).to(dev), 0, T).cpu().numpy()]
+    for g, wv in zip(got, want):
+        assert rel_l2(g, wv) <= TOL
+    xd = hidden_rows(6, 1, TINY.d_model, max_ctx - 1)
+    wd = ost.forward(xd, [0], [max_ctx - 1])
+    gd = st.decode(torch.from_numpy(xd).to(dev), torch.tensor([0], dtype=torch.int32, device=dev),
+                   torch.tensor([max_ctx - 1], dtype=torch.int32, device=dev)).cpu().numpy()
+    assert rel_l2(gd, wd) <= TOL
+    with pytest.raises(S.StageError) as e:
+        st.prefill(torch.from_numpy(x[:2]).to(dev), 0, max_ctx - 1)
+    assert e.value.code == S.STAGE_E_RANGE
+    assert st.device_errors(reset=True) == 0
+    st.decode(torch.from_numpy(xd).to(dev), torch.tensor([0], dtype=torch.int32, device=dev),
+              torch.tensor([128], dtype=torch.int32, device=dev))       # past the cache: refused per row
+    assert st.device_errors(reset=True) > 0
