@@ -264,6 +264,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 // kernel uses no other instruction that reads M0.
 // Per 32-k step each accumulator takes the hi-plane product and then the lo-plane product(s), the
 // same sequence as k_gemm, so both kernels give identical sums.
+// PP (ping-pong, 8 waves, 32-deep stages): the waves on one SIMD are split into two groups that
+// run half a step apart, with two barriers per step; while one group reads its fragments and
+// issues its loads, the other issues its MFMAs, so the matrix core takes both waves' products
+// back to back instead of both waves reading LDS at once after one barrier.  The same products
+// in the same order: identical sums.
 // ------------------------------------------------------------------------------------------------
 constexpr int kDmaBK = 32;
 
@@ -302,7 +307,7 @@ PSD_DEV int dma_swz(int r, int c) {
   return CH == 4 ? c ^ ((r >> 1) & 3) : c ^ (r & 7);
 }
 
-template <int NP, int EPI, int BM, int BN, int WM, int WN, int ST, int BK = kDmaBK>
+template <int NP, int EPI, int BM, int BN, int WM, int WN, int ST, int BK = kDmaBK, bool PP = false>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
   static_assert(BK == 32 || BK == 64, "stage depth");
@@ -384,6 +389,63 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
 #pragma unroll
   for (int t = 0; t < ST - 1; ++t)
     if (t < nk) issue(t);
+  if constexpr (PP) {
+    static_assert(BK == 32 && WM * WN == 8, "ping-pong: 32-deep stages, two waves per SIMD");
+    bf16x8_t af[NP][TM], bw[TN];
+    auto read_frags = [&](int t) {   // this wave's fragments of stage t, landed in registers
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * WTM + i * 16 + (lane & 15);
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl) af[pl][i] = as_bf16x8(As[t % ST][pl][row * CH + dma_swz<CH>(row, kc)]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int row = wn * WTN + j * 16 + (lane & 15);
+        bw[j] = as_bf16x8(Bs[t % ST][row * CH + dma_swz<CH>(row, kc)]);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto products = [&]() {   // at raised issue priority, so the other wave's reads do not delay them
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[pl][i], bw[j], acc[i][j]);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // Waves 0-3 and 4-7 (one of each per SIMD) run half a step apart: between two barriers one
+    // group reads its fragments from LDS while the other issues its MFMAs, so each SIMD's matrix
+    // core takes the two waves' products back to back.  Barrier 2t: every wave's loads of stage t
+    // have landed and every read of stage t - 1 has completed (its buffer takes stage t + ST - 1).
+    if (wave_s < 4) {   // wave-uniform branch: both sides take 2 nk + 1 barriers
+      for (int t = 0; t < nk; ++t) {
+        wait_stages(min(ST - 2, nk - 1 - t));
+        lds_barrier();
+        if (t + ST - 1 < nk) issue(t + ST - 1);
+        read_frags(t);
+        lds_barrier();
+        products();
+      }
+      lds_barrier();
+    } else {
+      for (int t = 0; t < nk; ++t) {
+        wait_stages(min(ST - 2, nk - 1 - t));
+        lds_barrier();
+        if (t + ST - 1 < nk) issue(t + ST - 1);
+        if (t > 0) products();
+        lds_barrier();
+        read_frags(t);
+      }
+      lds_barrier();
+      if (nk > 0) products();
+    }
+  } else
   for (int t = 0; t < nk; ++t) {
     // stage t's own loads done (later stages' may stay in flight); after the barrier every wave's
     // loads of stage t are in LDS and no wave still reads stage t - 1's buffer
@@ -613,18 +675,26 @@ GemmPlan gemm_plan(int M, int N, int K, int planes) {
 
 namespace {
 
+// Grids of at least kPingPongMinGroups work-groups (several per CU) run the 8-wave tiles with the
+// two wave groups half a step apart; on single-round grids and short split-K ranges the lock-step
+// schedule measured faster.  Both give identical sums.
+constexpr int kPingPongMinGroups = 512;
+
 template <int NP, int EPI>
 void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) {
+  const bool pp = (int)(grid.x * grid.y) >= kPingPongMinGroups;
   switch (p.cfg) {
     case 0: k_gemm<128, 128, 2, 2, NP, EPI, 1, 1><<<grid, 256, 0, s>>>(a); break;
     case 1: k_gemm<64, 256, 1, 4, NP, EPI, 1, 1><<<grid, 256, 0, s>>>(a); break;
     case 2: k_gemm<64, 128, 1, 4, NP, EPI, 2, 1><<<grid, 256, 0, s>>>(a); break;
     case 3: k_gemm<32, 128, 1, 4, NP, EPI, 2, 2><<<grid, 256, 0, s>>>(a); break;
     case 5:   // the planner gives it two planes only
-      k_gemm_dma<2, EPI, 256, 256, 4, 2, 3><<<grid, 512, 0, s>>>(a);
+      if (pp) k_gemm_dma<2, EPI, 256, 256, 4, 2, 3, kDmaBK, true><<<grid, 512, 0, s>>>(a);
+      else k_gemm_dma<2, EPI, 256, 256, 4, 2, 3><<<grid, 512, 0, s>>>(a);
       break;
     case 6:
-      k_gemm_dma<NP, EPI, 128, 256, 4, 2, 3><<<grid, 512, 0, s>>>(a);
+      if (pp) k_gemm_dma<NP, EPI, 128, 256, 4, 2, 3, kDmaBK, true><<<grid, 512, 0, s>>>(a);
+      else k_gemm_dma<NP, EPI, 128, 256, 4, 2, 3><<<grid, 512, 0, s>>>(a);
       break;
     case 7:
       k_gemm_dma<NP, EPI, 128, 256, 2, 4, NP == 2 ? 4 : 3><<<grid, 512, 0, s>>>(a);
