@@ -7,7 +7,8 @@ the stage's kernels at their real shapes on a slice the oracle can follow:
 * 8B-shaped last stage: block 16 + final norm + readout, B = 64 decode at context 4096 over a
   seeded KV cache imported into both sides;
 * 70B-shaped middle stage: block 20 at d 8192, T = 64 prefill, then B = 128 decode at context
-  8192 over a seeded KV cache;
+  8192 over a seeded KV cache; and a 4096-token chunk (the large-grid GEMM schedule for every
+  projection), its first 64 rows and their KV against the oracle's 64-token prefill;
 * sharded MLP: 8 column/row slices of a d 8192 / F 28672 MLP summed in slice order against the full
   MLP at T in {1, 64, 4096} (the T = 4096 oracle check on 64 sampled rows; MLP rows are
   independent);
@@ -108,9 +109,14 @@ def test_8b_last_stage_batched_decode_and_readout():
     assert st.device_errors() == 0
 
 
-def test_70b_mid_stage_prefill_and_batched_decode():
+@pytest.fixture(scope="module")
+def w70b_block():
+    return fx.draw_stage_weights(fx.LLAMA70B, 20, 21, False, False, gain_sigma=0.1)
+
+
+def test_70b_mid_stage_prefill_and_batched_decode(w70b_block):
     s, blk, B, ctx = fx.LLAMA70B, 20, 128, 8192
-    w = fx.draw_stage_weights(s, blk, blk + 1, False, False, gain_sigma=0.1)
+    w = w70b_block
     st = make_stage(s, blk, blk + 1, False, False, w, max_slots=B + 1, max_ctx=ctx + 1, max_tokens=B)
     # prefill T = 64 into the extra slot B
     ost = o.Stage(o.Dims.of(s), blk, blk + 1, False, False, w, ctx + 1)
@@ -134,6 +140,33 @@ def test_70b_mid_stage_prefill_and_batched_decode():
     e = rel_l2(got, want)
     say(f"  decode B=128 rel L2 {e:.2e}")
     assert e <= TOL
+    assert st.device_errors() == 0
+
+
+@pytest.mark.parametrize("kv_f32", [False, True])
+def test_70b_prefill_chunk_4096_first_rows(w70b_block, kv_f32):
+    # a 4096-token chunk runs every projection of the block on the large-grid GEMM schedule (QKV +
+    # RoPE + KV write, O + residual, gate/up + SwiGLU, down + residual); rows 0..63 of the chunk
+    # depend only on each other (causal), so the oracle's 64-token prefill is their exact value
+    s, blk, T, n = fx.LLAMA70B, 20, 4096, 64
+    kv = "f32" if kv_f32 else "bf16"
+    st = make_stage(s, blk, blk + 1, False, False, w70b_block, max_slots=1, max_ctx=T, max_tokens=T, kv_f32=kv_f32)
+    x = hidden_rows(9, T, s.d_model)
+    say(f"70B block, {kv} cache: gpu prefill T={T}")
+    got = st.prefill(torch.from_numpy(x).cuda(), 0, 0).cpu().numpy()
+    assert np.isfinite(got).all()
+    ost = o.Stage(o.Dims.of(s), blk, blk + 1, False, False, w70b_block, n, kv_dtype=kv)
+    want = ost.prefill(x[:n], 0, 0)
+    e = rel_l2(got[:n], want)
+    say(f"  rows 0..{n - 1} rel L2 {e:.2e}")
+    assert e <= TOL
+    kc, vc = ost._cache(0)                      # [blocks of the stage, positions, Hkv, Dh]
+    kg, vg = kv_bits(st, blk, 0, n)
+    for g_bits, want_kv in ((kg, kc[0, :n]), (vg, vc[0, :n])):
+        gv = g_bits.view(np.float32) if kv_f32 else o.bf16_to_f32(g_bits)
+        assert rel_l2(gv, want_kv) <= TOL
+        if not kv_f32:                             # bf16 rounding flips are rare
+            assert np.mean(g_bits == o.f32_to_bf16_bits(want_kv)) > 0.99
     assert st.device_errors() == 0
 
 
