@@ -247,9 +247,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 // ------------------------------------------------------------------------------------------------
 // LDS-direct tiles.  For prefill-sized M (activation pair planes) 8 waves own a 256 x 256 tile,
 // each wave 64 x 128 (two waves per SIMD), K in 32-deep stages; the same kernel serves 128 x 256
-// (three planes, or too few 256 x 256 tiles) and the batched-decode shapes (64 x 256 / 64 x 128
-// with 64-deep stages, so every weight row segment a load instruction fetches is a whole 128-byte
-// line).  Tiles go from global memory straight into LDS (global_load_lds_dwordx4), so no
+// (three planes, or too few 256 x 256 tiles) and the batched-decode shapes (128 x 256, 64 x 256 and
+// 64 x 128 with 64-deep stages, so every row segment a load instruction fetches is a whole
+// 128-byte line; 128 x 256 of two planes then fits two stage buffers, ST = 2).  Tiles go from global memory straight into LDS (global_load_lds_dwordx4), so no
 // registers stage them and no ds_write is issued: the accumulators, one step's fragments and the
 // addresses fit the 256 registers of two waves per SIMD.  ST LDS buffers form a ring: while stage
 // t feeds the MFMAs the loads of stages t + 1 .. t + ST - 2 are in flight, and stage t + ST - 1 is
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
   constexpr int A_DMA = BM * CH / NT, B_DMA = BN * CH / NT;     // load instructions per thread
   static_assert(A_DMA * NT == BM * CH && B_DMA * NT == BN * CH, "whole load instructions");
   constexpr int PER_STAGE = NP * A_DMA + B_DMA;
-  static_assert(ST >= 3 && ST <= 8 && (ST - 2) * PER_STAGE < 64, "ring depth within vmcnt");
+  static_assert(ST >= 2 && ST <= 8 && (ST - 2) * PER_STAGE < 64, "ring depth within vmcnt");
   __shared__ uint4 As[ST][NP][BM * CH];
   __shared__ uint4 Bs[ST][BN * CH];
 
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_norm(GemmArgs g, NormArgs
 struct Cfg {
   int bm, bn;
 };
-constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128}, {256, 256}, {128, 256}, {128, 256}, {64, 256}, {64, 128}};
+constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128}, {256, 256}, {128, 256}, {128, 256}, {64, 256}, {64, 128}, {128, 256}};
 
 }  // namespace
 
@@ -602,8 +602,12 @@ GemmPlan gemm_plan(int M, int N, int K, int planes) {
   //    ways, as fast as 256 x 256 split 8 with half the partials to reduce).
   //  * 32 < M <= 64 (batched decode): 64 x 256 or 64 x 128 LDS-direct tiles with 64-deep stages
   //    (8B-shaped projections at M = 64: gate/up 55 -> 50 us, down 37 -> 31 us, O 17.5 -> 16 us).
-  //  * 64 < M <= 128 (batched decode): 128 x 256 with 8 waves of 64 x 64 and a deeper ring
-  //    (70B-shaped projections at M = 128: 6-10% faster than 128 x 128).
+  //  * 64 < M <= 128 (batched decode): 128 x 256.  Two planes (K a multiple of 64): 64-deep stages
+  //    in two LDS buffers, so each row segment a load instruction fetches is a whole 128-byte line
+  //    of the activation or weight row (M = 128: 70B gate/up 324 -> 280 us, O 46.5 -> 41 us, 8B O
+  //    25.7 -> 23 us, readout 337 -> 309 us; bit-identical).  Three planes: 32-deep stages in a
+  //    3-deep ring, 8 waves of 64 x 64 (6-10% faster than 128 x 128; 64-deep stages of three
+  //    planes only fit 128 x 128 tiles, which were no faster).
   //  * otherwise 128 x 128 up to M = 512 and 64 x 256 above, one LDS buffer and one register
   //    staging set so that two work-groups fit a CU (the second hides the first's barrier, LDS and
   //    load waits), each wave owning a 64 x 64 tile; the 64 x 256 tile's 4 MB weight panels keep
@@ -629,14 +633,15 @@ GemmPlan gemm_plan(int M, int N, int K, int planes) {
     return p;
   }
   if (dma_ok && M > 64 && M <= 128) {
-    // batched decode rows: 128 x 256 with 64 x 64 wave tiles and a 4-stage ring (3 for three
-    // planes), K split until the grid holds ~150 work-groups
+    // batched decode rows: 128 x 256, two planes with 64-deep stages in two buffers (8 waves of
+    // 32 x 128), three planes with 64 x 64 wave tiles and a 3-deep ring of 32-deep stages; K split
+    // until the grid holds ~150 work-groups
     const int tiles = (N + 255) / 256;
     int sk = 1;
     while (tiles * sk < 150 && K / (sk * 2) >= 512 && sk < 16) sk *= 2;
-    p.cfg = 7;
-    p.bm = kCfgs[7].bm;
-    p.bn = kCfgs[7].bn;
+    p.cfg = (planes == 2 && K % 64 == 0) ? 10 : 7;
+    p.bm = kCfgs[p.cfg].bm;
+    p.bn = kCfgs[p.cfg].bn;
     p.tiles_m = 1;
     p.tiles_n = tiles;
     p.splitk = sk;
@@ -703,6 +708,9 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
       k_gemm_dma<2, EPI, 64, 256, 1, 4, 3, 64><<<grid, 256, 0, s>>>(a);
       break;
     case 9: k_gemm_dma<NP, EPI, 64, 128, 1, 4, NP == 2 ? 4 : 3, 64><<<grid, 256, 0, s>>>(a); break;
+    case 10:   // the planner gives it two planes only
+      k_gemm_dma<2, EPI, 128, 256, 4, 2, 2, 64><<<grid, 512, 0, s>>>(a);
+      break;
 
     default: k_gemm<16, 128, 1, 4, NP, EPI, 2, 2><<<grid, 256, 0, s>>>(a); break;
   }
@@ -722,7 +730,7 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
                        bool* normed) {
   if (normed) *normed = false;
   // the LDS-direct tile takes two planes, K in whole 32-deep stages and operands under 4 GiB
-  if (((p.cfg == 5 || p.cfg == 8) && a.planes != 2) || (p.cfg >= 5 && ( a.K % kDmaBK != 0 || (uint64_t)(a.M > a.N ? a.M : a.N) * a.K * 2 >= (1ull << 32))))
+  if (((p.cfg == 5 || p.cfg == 8 || p.cfg == 10) && a.planes != 2) || (p.cfg >= 5 && ( a.K % kDmaBK != 0 || (uint64_t)(a.M > a.N ? a.M : a.N) * a.K * 2 >= (1ull << 32))))
     return hipErrorInvalidValue;
   if (p.cfg >= 8 && a.K % 64 != 0) return hipErrorInvalidValue;   // 64-deep stages
   dim3 grid(p.tiles_m * p.tiles_n, p.splitk);
