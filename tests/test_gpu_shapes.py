@@ -269,16 +269,17 @@ def test_8b_split_equals_unsplit_on_gpu(w8b_first, kv_f32):
         f"B={B} decode step, KV")
 
 
-@pytest.mark.parametrize("T", [40, 100, 257, 300, 512])
+@pytest.mark.parametrize("T", [40, 100, 257, 300, 512, 2600])
 def test_8b_mlp_gemm_tiles_ragged_rows(w8b_first, T):
     # each row count takes another GEMM tiling: 40 the 64-row LDS-direct tiles with 64-deep stages,
-    # 100 the 128 x 256 tiles for 64 < M <= 128, 257 / 300 / 512 the 256 x 256 (gate/up) and
-    # 128 x 256 split-K (down) tiles; the last row tile is ragged in every case (clamped reads that
-    # must never be stored).  MLP rows are independent: the oracle checks the first rows, a spread,
-    # and the tail rows.
+    # 100 the 128 x 256 two-buffer tiles for 64 < M <= 128, 257 / 300 / 512 the 256 x 256 (gate/up)
+    # and 128 x 256 split-K (down) tiles, 2600 the ping-pong schedule for gate/up (1232
+    # work-groups); the last row tile is ragged in every case (clamped reads that must never be
+    # stored).  MLP rows are independent: the oracle checks the first rows, a spread, and the tail
+    # rows.
     s = fx.LLAMA8B
     w = {(r, 0): w8b_first[(r, 0)] for r in ("mlp_norm", "wgate", "wup", "wdown")}
-    st = make_stage(s, 0, 1, False, False, w, max_slots=1, max_ctx=64, max_tokens=512)
+    st = make_stage(s, 0, 1, False, False, w, max_slots=1, max_ctx=64, max_tokens=max(T, 512))
     x = hidden_rows(41, T, s.d_model)
     got = st.mlp(0, torch.from_numpy(x).cuda()).cpu().numpy()
     tail = np.arange(max(0, T - 24), T)
