@@ -249,9 +249,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 // each wave 64 x 128 (two waves per SIMD), K in 32-deep stages; the same kernel serves 128 x 256
 // (three planes, or too few 256 x 256 tiles) and the batched-decode shapes (128 x 256, 64 x 256 and
 // 64 x 128 with 64-deep stages, so every row segment a load instruction fetches is a whole
-// 128-byte line; 128 x 256 of two planes then fits two stage buffers, ST = 2).  Tiles go from global memory straight into LDS (global_load_lds_dwordx4), so no
-// registers stage them and no ds_write is issued: the accumulators, one step's fragments and the
-// addresses fit the 256 registers of two waves per SIMD.  ST LDS buffers form a ring: while stage
+// 128-byte line; 128 x 256 of two planes then fits two stage buffers, ST = 2).  Tiles go from
+// global memory straight into LDS (global_load_lds_dwordx4), so no registers stage them and no
+// ds_write is issued: the accumulators, one step's fragments and the addresses fit the 256
+// registers of two waves per SIMD.  ST LDS buffers form a ring: while stage
 // t feeds the MFMAs the loads of stages t + 1 .. t + ST - 2 are in flight, and stage t + ST - 1 is
 // issued into the buffer stage t - 1 has just left.
 // Rows of a stage are BK / 8 chunks of 16 bytes, XOR-swizzled by row (dma_swz) so that the 8 rows
@@ -634,8 +635,8 @@ GemmPlan gemm_plan(int M, int N, int K, int planes) {
   }
   if (dma_ok && M > 64 && M <= 128) {
     // batched decode rows: 128 x 256, two planes with 64-deep stages in two buffers (8 waves of
-    // 32 x 128), three planes with 64 x 64 wave tiles and a 3-deep ring of 32-deep stages; K split
-    // until the grid holds ~150 work-groups
+    // 32 x 128); three planes (or K not a multiple of 64) with 64 x 64 wave tiles and a 3-deep (two
+    // planes: 4-deep) ring of 32-deep stages; K split until the grid holds ~150 work-groups
     const int tiles = (N + 255) / 256;
     int sk = 1;
     while (tiles * sk < 150 && K / (sk * 2) >= 512 && sk < 16) sk *= 2;
