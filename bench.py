@@ -230,8 +230,9 @@ def counter_pass(shape, blocks, T, dev, n_dec: int = 32):
     print(json.dumps({"phase": "counters", "prefill_tokens": T, "decode_steps": n_dec}), flush=True)
 
 
-def prefill_only(args, shape, blocks, T, dev, stream):
-    """Time the prefill alone: stage sized for one T-token prompt, W warmups then K timed prefills."""
+def prefill_only(args, shape, blocks, T, dev, stream, first=True, kv_f32=None):
+    """Time the prefill alone: stage sized for one T-token prompt, W warmups then K timed prefills.
+    A first stage embeds seeded tokens; any other stage takes seeded F32 N(0,1) hidden rows."""
     import numpy as np
     import torch
 
@@ -239,31 +240,40 @@ def prefill_only(args, shape, blocks, T, dev, stream):
     from pipeline_stage_decoder_amd import accounting as acc
     from pipeline_stage_decoder_amd.stage import Stage
 
-    kv_f32 = args.kv == "f32"
-    st = Stage(shape, blocks[0], blocks[1], True, False, max_slots=1, max_ctx=T, max_tokens=T, device=0,
+    if kv_f32 is None:
+        kv_f32 = args.kv == "f32"
+    st = Stage(shape, blocks[0], blocks[1], first, False, max_slots=1, max_ctx=T, max_tokens=T, device=0,
                kv_f32=kv_f32)
-    fill_weights(st, shape, blocks, True, False, fx.SEED_WEIGHTS)
-    prompt = fx.tokens_gpu(torch.empty(T, dtype=torch.int32, device=dev), fx.SEED_TOKENS, fx.token_stream(0),
-                           shape.vocab)
+    fill_weights(st, shape, blocks, first, False, fx.SEED_WEIGHTS)
     xin = torch.empty((T, shape.d_model), dtype=torch.float32, device=dev)
     hout = torch.empty_like(xin)
-    for _ in range(max(args.warmup, 1)):
-        st.embed(prompt, out=xin)
+    if first:
+        prompt = fx.tokens_gpu(torch.empty(T, dtype=torch.int32, device=dev), fx.SEED_TOKENS,
+                               fx.token_stream(0), shape.vocab)
+    else:
+        fx.normal_f32_gpu(xin, fx.SEED_HIDDEN, fx.hidden_stream(0), 0)
+
+    def run():
+        if first:
+            st.embed(prompt, out=xin)
         st.prefill(xin, 0, 0, out=hout)
+
+    for _ in range(max(args.warmup, 1)):
+        run()
     torch.cuda.synchronize()
     ms = []
     for k in range(args.steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        st.embed(prompt, out=xin)
-        st.prefill(xin, 0, 0, out=hout)
+        run()
         e1.record(stream)
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
         log(f"[bench] prefill {k + 1}/{args.steps}: {ms[-1]:.3f} ms")
     pre_ms = float(np.median(ms))
     flops = acc.prefill_flops(shape, blocks[1] - blocks[0], T)
-    print(json.dumps({"phase": "prefill", "prefill_tokens": T, "kv_cache": args.kv, "prefill_ms": round(pre_ms, 3),
+    print(json.dumps({"phase": "prefill", "prefill_tokens": T, "blocks": list(blocks),
+                      "kv_cache": "f32" if kv_f32 else "bf16", "prefill_ms": round(pre_ms, 3),
                       "prefill_tok_s": round(T / (pre_ms / 1e3), 1),
                       "prefill_tflops": round(flops / (pre_ms / 1e3) / 1e12, 1),
                       "prefill_mfma_frac": round(flops / (pre_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}),
@@ -762,7 +772,10 @@ def main():
     stream = torch.cuda.current_stream()
 
     if args.phase == "prefill":
-        prefill_only(args, shape, blocks, T, dev, stream)
+        if args.workload == "mid-70b":     # one 4096-token chunk at position 0, bf16 KV cache
+            prefill_only(args, fx.LLAMA70B, (20, 40), 4096, dev, stream, first=False, kv_f32=False)
+        else:
+            prefill_only(args, shape, blocks, T, dev, stream)
         return
     if args.phase == "counters":
         counter_pass(shape, blocks, T, dev)
