@@ -532,13 +532,29 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
 // computes them from out (same element order, same f64 reduction).  N % 4 == 0, N <= 8192.
 constexpr int kReduceNormMaxN = 8192;
 
+// PER float4 per thread (rows of up to 1024 PER).  With PER = 4 the residual row and the gain are
+// loaded before the partials so that all loads are in flight together; at PER = 8 the extra
+// registers would leave one wave per SIMD, so they are loaded after the sum.
+template <int PER>
 __global__ __launch_bounds__(256) void k_splitk_reduce_norm(GemmArgs g, NormArgs nrm) {
-  constexpr int PER = kReduceNormMaxN / 1024;   // float4 per thread
+  constexpr bool kEarly = PER <= 4;
   constexpr int SB = 4;                          // splits whose loads are in flight together
   __shared__ double red[4];
   const int r = blockIdx.x, N = g.N;
   const size_t plane = (size_t)g.M * N;
   const EpiArgs& e = g.e;
+  // the residual row and the gain (first when kEarly, so that their loads are in flight with the
+  // partials'; out may be resid itself: each thread reads its own elements before it writes them)
+  float4 res[PER], gn[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x * 4 + j * 1024;
+    res[j] = gn[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (kEarly && i < N) {
+      res[j] = *(const float4*)(e.resid + (size_t)r * e.ldo + i);
+      gn[j] = *(const float4*)(nrm.gain + i);
+    }
+  }
   // the row's split partials, SB splits per round trip (a few rows only fill few CUs, so each
   // work-group needs its loads in flight at once); summed per element in split order
   float4 x[PER];
@@ -572,8 +588,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_norm(GemmArgs g, NormArgs
   for (int j = 0; j < PER; ++j) {
     const int i = threadIdx.x * 4 + j * 1024;
     if (i < N) {
-      const float4 res = *(const float4*)(e.resid + (size_t)r * e.ldo + i);
-      v[j] = make_float4(res.x + x[j].x, res.y + x[j].y, res.z + x[j].z, res.w + x[j].w);
+      if (!kEarly) res[j] = *(const float4*)(e.resid + (size_t)r * e.ldo + i);
+      v[j] = make_float4(res[j].x + x[j].x, res[j].y + x[j].y, res[j].z + x[j].z, res[j].w + x[j].w);
       *(float4*)(e.out + (size_t)r * e.ldo + i) = v[j];
       ss = sumsq4(v[j], ss);
     }
@@ -583,7 +599,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_norm(GemmArgs g, NormArgs
   for (int j = 0; j < PER; ++j) {
     const int i = threadIdx.x * 4 + j * 1024;
     if (i < N)
-      store_norm_planes4(nrm.out_pair + (size_t)r * N + i, nrm.pair_ps, v[j], rs, *(const float4*)(nrm.gain + i));
+      store_norm_planes4(nrm.out_pair + (size_t)r * N + i, nrm.pair_ps, v[j], rs,
+                         kEarly ? gn[j] : *(const float4*)(nrm.gain + i));
   }
 }
 
@@ -750,7 +767,8 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
       if (p.splitk > 1) {
         // one work-group per row, every split's loads of a row in flight together
         if (then_norm && a.N % 4 == 0 && a.N <= kReduceNormMaxN && a.e.ldo == a.N) {
-          k_splitk_reduce_norm<<<a.M, 256, 0, s>>>(a, *then_norm);
+          if (a.N <= 4096) k_splitk_reduce_norm<4><<<a.M, 256, 0, s>>>(a, *then_norm);
+          else k_splitk_reduce_norm<kReduceNormMaxN / 1024><<<a.M, 256, 0, s>>>(a, *then_norm);
           if (normed) *normed = true;
         } else {
           launch_reduce<EPI_RESID>(a, s);
