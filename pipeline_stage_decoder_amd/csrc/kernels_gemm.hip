@@ -494,6 +494,35 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
 template <int EPI>
 __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
   const int M = g.M, N = g.N;
+  if constexpr (EPI == EPI_QKV) {
+    // two adjacent pairs per thread, (c0, c0 + 16) and (c0 + 1, c0 + 17) with c0 even: 8-byte
+    // partial loads (the fused QKV width is a multiple of 32), each element summed in split order
+    const int quads_per_row = N >> 2;
+    const size_t total = (size_t)M * quads_per_row, plane = (size_t)M * N;
+    const EpiArgs& e = g.e;
+    for (size_t t = (size_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (size_t)gridDim.x * 256) {
+      const int r = (int)(t / quads_per_row), pp = 2 * (int)(t - (size_t)r * quads_per_row);
+      const int c0 = ((pp >> 4) << 5) + (pp & 15);
+      float2 x0 = make_float2(0.0f, 0.0f), x1 = make_float2(0.0f, 0.0f);
+      for (int sp = 0; sp < g.splitk; ++sp) {
+        const float* p = g.part + sp * plane + (size_t)r * N;
+        const float2 a = *reinterpret_cast<const float2*>(p + c0);
+        const float2 b = *reinterpret_cast<const float2*>(p + c0 + 16);
+        x0.x += a.x;
+        x0.y += a.y;
+        x1.x += b.x;
+        x1.y += b.y;
+      }
+      int slot, pos;
+      if (!row_slot_pos(e, r, slot, pos)) {
+        if (c0 == 0) atomicAdd(e.err, 1u);
+      } else {
+        qkv_store_pair(e, r, slot, pos, c0, x0.x, x1.x, qkv_rope_cs(e, pos, c0));
+        qkv_store_pair(e, r, slot, pos, c0 + 1, x0.y, x1.y, qkv_rope_cs(e, pos, c0 + 1));
+      }
+    }
+    return;
+  }
   const int pairs_per_row = ((N + 31) >> 5) << 4;
   const size_t total = (size_t)M * pairs_per_row;
   const size_t plane = (size_t)M * N;
@@ -739,7 +768,7 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
 template <int EPI>
 void launch_reduce(const GemmArgs& a, hipStream_t s) {
   const size_t pairs = (size_t)a.M * ((((size_t)a.N + 31) >> 5) << 4);
-  size_t grid = (pairs + 255) / 256;
+  size_t grid = ((EPI == EPI_QKV ? pairs / 2 : pairs) + 255) / 256;   // QKV: two pairs per thread
   if (grid > 2048) grid = 2048;
   k_splitk_reduce<EPI><<<(unsigned)grid, 256, 0, s>>>(a);
 }
@@ -754,6 +783,7 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
   dim3 grid(p.tiles_m * p.tiles_n, p.splitk);
   switch (a.e.kind) {
     case EPI_QKV:
+      if (a.N % 32 != 0) return hipErrorInvalidValue;   // whole head-dim groups (Dh 64 or 128)
       if (a.planes == 3) launch_cfg<3, EPI_QKV>(a, p, grid, s);
       else launch_cfg<2, EPI_QKV>(a, p, grid, s);
       if (p.splitk > 1) launch_reduce<EPI_QKV>(a, s);
