@@ -70,7 +70,7 @@ def cpu_baseline_decode(shape, ctx: int, n_blocks: int, seconds: float = 10.0, c
     st = o.Stage(o.Dims.of(shape), 0, 1, False, False, w, ctx + 1)
     kshape = (1, ctx + 1, shape.n_kv_heads, shape.head_dim)
     kv = o.round_bf16(fx.normal_f32(fx.SEED_HIDDEN, 0x7000, int(np.prod(kshape))).reshape(kshape))
-    st.kv[0] = (kv.copy(), kv.copy())
+    st.import_kv(0, 0, 0, kv[0], kv[0].copy())
     x = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(0), shape.d_model).reshape(1, shape.d_model)
     positions = [ctx_lo + (ctx - ctx_lo) * i // 3 for i in range(4)]   # spread over the decode range
     st.forward(x, [0], [ctx])                     # warm caches

@@ -15,11 +15,43 @@ def say(*a):
     sys.stdout.flush()
 
 
-def rel_l2(got, want) -> float:
+def rel_l2_whole(got, want) -> float:
+    """||got - want|| / ||want|| over the whole tensor."""
     g = np.asarray(got, dtype=np.float64)
     w = np.asarray(want, dtype=np.float64)
     den = np.linalg.norm(w)
     return float(np.linalg.norm(g - w) / (den if den > 0 else 1.0))
+
+
+def rel_l2_rows(got, want) -> float:
+    """The worst per-row relative L2, a row being the last axis (a hidden row, a logits row); a row
+    whose reference is zero counts its absolute error."""
+    g = np.asarray(got, dtype=np.float64)
+    w = np.asarray(want, dtype=np.float64)
+    assert g.shape == w.shape, (g.shape, w.shape)
+    if g.ndim == 0 or g.size == 0:
+        return rel_l2_whole(g, w)
+    g = g.reshape(-1, g.shape[-1])
+    w = w.reshape(-1, w.shape[-1])
+    num = np.linalg.norm(g - w, axis=1)
+    den = np.linalg.norm(w, axis=1)
+    return float(np.max(num / np.where(den > 0, den, 1.0)))
+
+
+def rel_l2(got, want) -> float:
+    """The error every parity assertion bounds: the larger of the whole-tensor relative L2 and
+    the worst single row's, so an error confined to one row (one slot, one ragged tile row)
+    cannot hide in a large tensor."""
+    return max(rel_l2_whole(got, want), rel_l2_rows(got, want))
+
+
+def rel_l2_kv(got, want) -> float:
+    """Relative L2 of cached K or V [n, Hkv, Dh], the worst of the whole tensor and of each KV
+    head's [n, Dh] block."""
+    g = np.asarray(got, dtype=np.float64)
+    w = np.asarray(want, dtype=np.float64)
+    heads = [rel_l2_whole(g[:, h], w[:, h]) for h in range(g.shape[1])]
+    return max([rel_l2_whole(g, w)] + heads)
 
 
 def make_stage(shape, begin, end, first, last, weights: dict, **kw) -> Stage:

@@ -25,7 +25,7 @@ import torch
 
 import fixtures as fx
 from oracle import decoder as o
-from tests.gpu_util import hidden_rows, kv_bits, make_stage, rel_l2, say
+from tests.gpu_util import hidden_rows, kv_bits, make_stage, rel_l2, rel_l2_kv, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -43,13 +43,10 @@ def seeded_kv(shape, slot: int, n: int):
 
 def import_kv(st, ost, block, slots, n):
     """Write the same seeded KV (positions 0..n-1) into the GPU stage and the oracle stage."""
-    lb = block - ost.begin
     for s in slots:
         k, v = seeded_kv(st.shape, s, n)
         st.kv_import(block, s, 0, torch.from_numpy(k.view(np.int16)).cuda(), torch.from_numpy(v.view(np.int16)).cuda())
-        kc, vc = ost._cache(s)
-        kc[lb, :n] = o.bf16_to_f32(k)
-        vc[lb, :n] = o.bf16_to_f32(v)
+        ost.import_kv(block, s, 0, o.bf16_to_f32(k), o.bf16_to_f32(v))
     torch.cuda.synchronize()
 
 
@@ -164,7 +161,7 @@ def test_70b_prefill_chunk_4096_first_rows(w70b_block, kv_f32):
     kg, vg = kv_bits(st, blk, 0, n)
     for g_bits, want_kv in ((kg, kc[0, :n]), (vg, vc[0, :n])):
         gv = g_bits.view(np.float32) if kv_f32 else o.bf16_to_f32(g_bits)
-        assert rel_l2(gv, want_kv) <= TOL
+        assert rel_l2_kv(gv, want_kv) <= TOL
         if not kv_f32:                             # bf16 rounding flips are rare
             assert np.mean(g_bits == o.f32_to_bf16_bits(want_kv)) > 0.99
     assert st.device_errors() == 0

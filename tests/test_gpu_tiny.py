@@ -11,7 +11,7 @@ import torch
 
 import fixtures as fx
 from oracle import decoder as o
-from tests.gpu_util import gpu_generate, hidden_rows, kv_bits, make_stage, rel_l2, say
+from tests.gpu_util import gpu_generate, hidden_rows, kv_bits, make_stage, rel_l2, rel_l2_kv, say
 
 pytestmark = pytest.mark.gpu
 
@@ -80,7 +80,7 @@ def test_tiny_kv_matches_oracle(weights):
         kg, vg = kv_bits(st, blk, 0, 16)
         for g_bits, w_bits in ((kg, kw[blk]), (vg, vw[blk])):
             gv, wv = o.bf16_to_f32(g_bits), o.bf16_to_f32(w_bits)
-            assert rel_l2(gv, wv) <= TOL
+            assert rel_l2_kv(gv, wv) <= TOL
             assert np.mean(g_bits == w_bits) > 0.99      # bf16 rounding flips are rare
 
 

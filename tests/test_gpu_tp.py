@@ -43,7 +43,7 @@ def test_attention_head_slices_sum_to_full(name, n, T, kv_f32):
     dh = s.head_dim
     x = hidden_rows(50, T, s.d_model)
     xt = torch.from_numpy(x).cuda()
-    sl = o.head_slices(s.n_q_heads, s.n_kv_heads, n)
+    sl = o.head_shards(s.n_q_heads, s.n_kv_heads, n)
     hq, hk = sl[0][1], sl[0][3]
     st = Stage(slice_shape(s, hq, hk, n_blocks=n), 0, n, False, False, max_slots=1, max_ctx=64, max_tokens=64,
                kv_f32=kv_f32)
@@ -96,7 +96,7 @@ def test_vocab_slices_embedding_and_readout(name, n):
     emb = fx.draw_weight(s, "embed")
     ro = fx.draw_weight(s, "readout")
     g = fx.draw_weight(s, "final_norm", gain_sigma=0.1)
-    per = o.vocab_range(V, n, 0)[0]
+    per, firsts = o.vocab_shards(V, n)
     toks = np.concatenate([fx.tokens(fx.SEED_TOKENS, fx.token_stream(40), 13, V),
                            [0, V - 1, per - 1, per, min(2 * per, V - 1)]]).astype(np.int32)
     tt = torch.from_numpy(toks).cuda()
@@ -111,19 +111,19 @@ def test_vocab_slices_embedding_and_readout(name, n):
     for i in range(n):
         sh = slice_shape(s, s.n_q_heads, s.n_kv_heads, vocab=per, n_blocks=1)
         st = Stage(sh, 0, 0, True, True, max_slots=1, max_ctx=64, max_tokens=32)
-        st.load_weight("embed", -1, o.vocab_slice(emb, n, i))
-        st.load_weight("readout", -1, o.vocab_slice(ro, n, i))
+        st.load_weight("embed", -1, o.vocab_shard(emb, n, i))
+        st.load_weight("readout", -1, o.vocab_shard(ro, n, i))
         st.load_weight("final_norm", -1, g)
-        st.embed_range(tt, o.vocab_range(V, n, i)[1], out=acc, accumulate=i > 0)
+        st.embed_range(tt, firsts[i], out=acc, accumulate=i > 0)
         slices.append(st)
     assert torch.equal(acc, want_rows)
-    np.testing.assert_array_equal(acc.cpu().numpy(), o.embed_slices(emb, toks.astype(np.int64), n))
+    np.testing.assert_array_equal(acc.cpu().numpy(), o.embed_shards(emb, toks.astype(np.int64), n))
     for rows in (2, 16):                                  # GEMV path, then the MFMA GEMM path
         h = torch.from_numpy(hidden_rows(52, rows, d)).cuda()
         lf, hn = full.readout(h)
         cat = torch.cat([st.readout(h)[0] for st in slices], dim=1)[:, :V]
         e = rel_l2(cat.cpu().numpy(), lf.cpu().numpy())
-        want = o.readout_slices(o.rms_norm(h.cpu().numpy(), o.bf16_to_f32(g), s.rms_eps), ro, n)
+        want = o.readout_shards(o.rms_norm(h.cpu().numpy(), o.bf16_to_f32(g), s.rms_eps), ro, n)
         e_o = rel_l2(cat.cpu().numpy(), want)
         say(f"{name} vocab over {n} slices, {rows} rows: concat vs full {e:.2e}, vs oracle {e_o:.2e}")
         if rows <= 4:

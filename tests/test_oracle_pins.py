@@ -4,7 +4,8 @@ No page prints activations or logits for a worked forward pass, so the oracle's 
 are pinned by brute force on tiny shapes (pure-Python loops with math.exp, no numpy matmul or
 einsum), closed forms, a worked RoPE example, and invariants the pages fix:
 * split vs unsplit bit-identity ("RFC: pipeline placement ...", Numerical correctness proof);
-* the split-KV merge identity ("41. Many GPUs", Ring attention: merge_partials);
+* the split-KV merge identity ("41. Many GPUs", Ring attention: partials over disjoint key sets
+  combine through their log-sum-exps);
 * Megatron slice sums ("41. Many GPUs", Tensor parallelism: take_rows / take_cols);
 * prefill/decode/chunked-prefill consistency (TensorSharp, Reproducible validation: full and
   chunked prefill, decode, refill and reset probes compared against an unsplit control).
@@ -183,7 +184,7 @@ def brute_attention(q, k, v, q_pos, k_pos, scale, group):
 
 
 @pytest.mark.parametrize("tq,tk,hq,hkv,dd", [(4, 4, 2, 1, 4), (5, 8, 4, 2, 4), (3, 6, 4, 4, 8),
-                                             (8, 8, 4, 1, 64)])
+                                             (8, 8, 4, 1, 64), (1, 7, 16, 2, 8), (5, 9, 8, 2, 8)])
 def test_attention_bruteforce(tq, tk, hq, hkv, dd):
     r = rng(tq * 100 + tk)
     q = r.standard_normal((tq, hq, dd))                 # N(0,1): not near-uniform attention
@@ -192,32 +193,41 @@ def test_attention_bruteforce(tq, tk, hq, hkv, dd):
     q_pos = np.arange(tk - tq, tk)
     k_pos = np.arange(tk)
     scale = dd ** -0.5
-    got, lse = o.attention_partial(q, o.gqa_expand(k, hq), o.gqa_expand(v, hq), q_pos, k_pos, scale)
+    got, lse = o.attend(q, k, v, q_pos, k_pos, scale)
     want = brute_attention(q, k, v, q_pos, k_pos, scale, hq // hkv)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
     assert lse.shape == (tq, hq) and np.all(np.isfinite(lse))
+    # the log-sum-exp, brute force
+    for t in range(tq):
+        for h in range(hq):
+            z = sum(math.exp(sum(float(q[t, h, e]) * float(k[j, h // (hq // hkv), e]) for e in range(dd)) * scale)
+                    for j in range(tk) if k_pos[j] <= q_pos[t])
+            assert abs(lse[t, h] - math.log(z)) < 1e-12 * max(1.0, abs(math.log(z)))
 
 
-@pytest.mark.parametrize("tq,tk,hq,hkv", [(4, 4, 2, 1), (5, 9, 8, 2), (3, 6, 4, 4), (1, 7, 16, 2)])
-def test_attention_gqa_equals_expanded_and_bruteforce(tq, tk, hq, hkv):
-    r = rng(tq * 7 + tk)
-    dd = 8
-    q, k, v = r.standard_normal((tq, hq, dd)), r.standard_normal((tk, hkv, dd)), r.standard_normal((tk, hkv, dd))
-    q_pos, k_pos = np.arange(tk - tq, tk), np.arange(tk)
-    got = o.attention_gqa(q, k, v, q_pos, k_pos, 0.3)
-    ref, _ = o.attention_partial(q, o.gqa_expand(k, hq), o.gqa_expand(v, hq), q_pos, k_pos, 0.3)
-    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-13)
-    np.testing.assert_allclose(got, brute_attention(q, k, v, q_pos, k_pos, 0.3, hq // hkv), rtol=0, atol=1e-12)
+def test_attention_key_order_and_unsorted_positions():
+    # visibility is by position, not by storage order: shuffled keys give the same result
+    r = rng(12)
+    q, k, v = r.standard_normal((3, 4, 8)), r.standard_normal((9, 2, 8)), r.standard_normal((9, 2, 8))
+    q_pos, k_pos = np.array([2, 5, 8]), np.arange(9)
+    perm = r.permutation(9)
+    a, la = o.attend(q, k, v, q_pos, k_pos, 0.4)
+    b, lb = o.attend(q, k[perm], v[perm], q_pos, k_pos[perm], 0.4)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(la, lb, rtol=1e-14)
+    np.testing.assert_allclose(a, brute_attention(q, k, v, q_pos, k_pos, 0.4, 2), rtol=0, atol=1e-12)
 
 
 def test_attention_gqa_map_pin_catches_modulo_mapping():
     r = rng(9)
     q, k, v = r.standard_normal((2, 4, 4)), r.standard_normal((3, 2, 4)), r.standard_normal((3, 2, 4))
     want = brute_attention(q, k, v, np.array([1, 2]), np.arange(3), 0.5, 2)
-    wrong = np.concatenate([k, k], axis=1)              # planted: head h -> KV head h % Hkv
-    got, _ = o.attention_partial(q, wrong, np.concatenate([v, v], axis=1), np.array([1, 2]),
-                                 np.arange(3), 0.5)
-    assert np.max(np.abs(got - want)) > 1e-3
+    got, _ = o.attend(q, k, v, np.array([1, 2]), np.arange(3), 0.5)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    # planted: head h -> KV head h % Hkv (expanding K/V by tiling instead of repeating)
+    wrong, _ = o.attend(q, np.concatenate([k, k], axis=1), np.concatenate([v, v], axis=1), np.array([1, 2]),
+                        np.arange(3), 0.5)
+    assert np.max(np.abs(wrong - want)) > 1e-3
 
 
 def test_attention_special_cases():
@@ -226,34 +236,56 @@ def test_attention_special_cases():
     k = np.zeros((5, 1, 4))
     q = r.standard_normal((1, 1, 4))
     # equal scores -> mean of the visible values
-    out, lse = o.attention_partial(q, k, v, np.array([2]), np.arange(5), 1.0)
+    out, lse = o.attend(q, k, v, np.array([2]), np.arange(5), 1.0)
     np.testing.assert_allclose(out[0, 0], v[:3, 0].mean(axis=0), rtol=1e-14)
     np.testing.assert_allclose(lse[0, 0], math.log(3.0), rtol=1e-14)
     # one visible key -> its value
-    out, _ = o.attention_partial(q, r.standard_normal((5, 1, 4)), v, np.array([0]), np.arange(5), 1.0)
+    out, _ = o.attend(q, r.standard_normal((5, 1, 4)), v, np.array([0]), np.arange(5), 1.0)
     np.testing.assert_allclose(out[0, 0], v[0, 0], rtol=1e-14)
     # no visible key -> zero output and lse -inf
-    out, lse = o.attention_partial(q, k, v, np.array([0]), np.arange(1, 6), 1.0)
+    out, lse = o.attend(q, k, v, np.array([0]), np.arange(1, 6), 1.0)
     assert np.all(out == 0) and np.isneginf(lse[0, 0])
+    # a very large score dominates completely (no overflow: the definition is shift-invariant)
+    kk = np.zeros((3, 1, 4))
+    kk[1, 0, 0] = 1e4
+    qq = np.array([[[1.0, 0, 0, 0]]])
+    out, lse = o.attend(qq, kk, v[:3], np.array([2]), np.arange(3), 1.0)
+    np.testing.assert_allclose(out[0, 0], v[1, 0], rtol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], 1e4, rtol=1e-15)
 
 
 def test_split_kv_merge_identity():
     r = rng(11)
     tq, tk, h, dd = 3, 37, 4, 16
-    q, k, v = r.standard_normal((tq, h, dd)), r.standard_normal((tk, h, dd)), r.standard_normal((tk, h, dd))
+    q, k, v = r.standard_normal((tq, h, dd)), r.standard_normal((tk, 2, dd)), r.standard_normal((tk, 2, dd))
     q_pos, k_pos = np.arange(tk - tq, tk), np.arange(tk)
-    full, full_lse = o.attention_partial(q, k, v, q_pos, k_pos, 0.25)
+    full, full_lse = o.attend(q, k, v, q_pos, k_pos, 0.25)
     for chunk in (1, 5, 16, 36):
-        out = np.zeros((tq, h, dd))
-        lse = np.full((tq, h), -np.inf)
-        for s in range(0, tk, chunk):
-            po, pl = o.attention_partial(q, k[s:s + chunk], v[s:s + chunk], q_pos, k_pos[s:s + chunk], 0.25)
-            out, lse = o.merge_partials(out, lse, po, pl)
+        parts = [o.attend(q, k[s:s + chunk], v[s:s + chunk], q_pos, k_pos[s:s + chunk], 0.25)
+                 for s in range(0, tk, chunk)]
+        out, lse = o.lse_combine(parts)
         np.testing.assert_allclose(out, full, rtol=0, atol=1e-12)
         np.testing.assert_allclose(lse, full_lse, rtol=1e-13)
-    # merging an empty partial (lse -inf) is the identity
-    e_out, e_lse = o.merge_partials(full, full_lse, np.zeros_like(full), np.full_like(full_lse, -np.inf))
+        # combining two at a time, in order, is the same combination
+        run = parts[0]
+        for p in parts[1:]:
+            run = o.lse_combine([run, p])
+        np.testing.assert_allclose(run[0], full, rtol=0, atol=1e-12)
+    # a partial with no visible key (lse -inf) weighs nothing; all-empty gives (0, -inf)
+    empty = (np.zeros_like(full), np.full_like(full_lse, -np.inf))
+    e_out, e_lse = o.lse_combine([(full, full_lse), empty])
     np.testing.assert_allclose(e_out, full, rtol=1e-15)
+    z_out, z_lse = o.lse_combine([empty, empty])
+    assert np.all(z_out == 0) and np.all(np.isneginf(z_lse))
+
+
+def test_lse_combine_closed_form_two_keys():
+    # two single-key partials: the combination is the softmax over the two keys
+    s1, s2, v1, v2 = 0.3, -1.7, np.array([1.0, 2.0]), np.array([-3.0, 0.5])
+    out, lse = o.lse_combine([(v1[None, None], np.array([[s1]])), (v2[None, None], np.array([[s2]]))])
+    p1 = math.exp(s1) / (math.exp(s1) + math.exp(s2))
+    np.testing.assert_allclose(out[0, 0], p1 * v1 + (1 - p1) * v2, rtol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], math.log(math.exp(s1) + math.exp(s2)), rtol=1e-14)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -337,24 +369,233 @@ def test_determinism_and_reset():
     assert all(a.tobytes() == b.tobytes() for a, b in zip(tr1["logits"], tr2["logits"]))
 
 
-def test_kv_cache_holds_bf16_values():
-    # the KV cache is the one bf16 storage point of activations: cached K and V are bf16 values,
-    # and K is cached after RoPE (the value attention reads)
+@pytest.mark.parametrize("fmt", ["bf16", "f16", "f32"])
+def test_kv_cache_holds_rotated_keys_in_the_cache_format(fmt):
+    # the KV cache is the one storage point of activations: cached K and V are values of the
+    # cache format, and K is cached after RoPE (the value attention reads)
     x = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(0), 4 * TINY.d_model).reshape(4, TINY.d_model)
-    s = tiny_stage(0, 1, False, False)
+    w = fx.draw_stage_weights(TINY, 0, 1, False, False, gain_sigma=0.1)
+    s = o.Stage(o.Dims.of(TINY), 0, 1, False, False, w, 64, kv_dtype=fmt)
     s.prefill(x, 0, 0)
     k, v = s.kv[0]
-    assert np.array_equal(o.round_bf16(k), k) and np.array_equal(o.round_bf16(v), v)
+    if fmt == "bf16":
+        assert np.array_equal(o.round_bf16(k), k) and np.array_equal(o.round_bf16(v), v)
+    if fmt == "f16":
+        assert np.array_equal(k.astype(np.float16).astype(np.float32), k)
+        assert np.array_equal(v.astype(np.float16).astype(np.float32), v)
     c = o.Dims.of(TINY)
-    h = o.rms_norm(x, o.bf16_to_f32(s.w[("attn_norm", 0)]), c.rms_eps)
-    k_raw = o.linear64(h, s.w[("wk", 0)]).reshape(4, c.n_kv_heads, c.head_dim)
-    want = o.round_bf16(o.rope(k_raw, np.arange(4), c.rope_theta))
+    h = o.rms_norm(x, o.bf16_to_f32(w[("attn_norm", 0)]), c.rms_eps)
+    k_raw = o.linear64(h, w[("wk", 0)]).reshape(4, c.n_kv_heads, c.head_dim)
+    want = o.KV_FORMATS[fmt](o.rope(k_raw, np.arange(4), c.rope_theta))
     np.testing.assert_array_equal(k[0, :4], want)
-    assert not np.array_equal(k[0, 1:4], o.round_bf16(k_raw[1:]))   # RoPE was applied
+    assert not np.allclose(k[0, 1:4], o.KV_FORMATS[fmt](k_raw[1:]))   # RoPE was applied
+    assert s.held[0][0, :4].all() and not s.held[0][0, 4:].any()
+
+
+def test_f16_rounding_is_round_to_nearest_even():
+    # binary16 has 11 significant bits: 1 + 2^-11 is a tie (rounds to 1), 1 + 3 * 2^-11 rounds up
+    vals = np.array([1.0, 1 + 2 ** -11, 1 + 3 * 2 ** -11, 1 + 2 ** -11 + 2 ** -20, 65504.0, 2 ** -24], np.float32)
+    want = [1.0, 1.0, 1 + 2 ** -9, 1 + 2 ** -10, 65504.0, 2 ** -24]
+    assert o.round_f16(vals).tolist() == want
 
 
 # ---------------------------------------------------------------------------------------------
-# tensor-parallel slices ("41. Many GPUs", Tensor parallelism)
+# how a block composes its parts ("41. Many GPUs", Pipeline parallelism: each block normalises
+# the residual, adds attention, normalises the new residual, adds the MLP)
+# ---------------------------------------------------------------------------------------------
+
+def brute_rms_norm(row, gain, eps):
+    ms = sum(float(t) * float(t) for t in row) / len(row)
+    r = 1.0 / math.sqrt(ms + eps)
+    return [float(t) * r * float(g) for t, g in zip(row, gain)]
+
+
+def brute_swiglu_mlp(x, g_mlp, w_gate, w_up, w_down, eps):
+    """Pure-Python SwiGLU MLP of rows x: y_j = sum_f W_down[j, f] silu(gate_f) up_f with
+    gate_f = sum_k h_k W_gate[f, k], up_f = sum_k h_k W_up[f, k], h = RMSNorm(x) g."""
+    wg, wu, wd = (o.bf16_to_f32(t).astype(np.float64) for t in (w_gate, w_up, w_down))
+    out = []
+    for row in x:
+        h = brute_rms_norm(row, o.bf16_to_f32(g_mlp), eps)
+        act = []
+        for f in range(wg.shape[0]):
+            gate = sum(h[k] * wg[f, k] for k in range(len(h)))
+            up = sum(h[k] * wu[f, k] for k in range(len(h)))
+            act.append(gate / (1.0 + math.exp(-gate)) * up)
+        out.append([sum(wd[j, f] * act[f] for f in range(len(act))) for j in range(wd.shape[0])])
+    return np.array(out)
+
+
+def small_mlp(d=6, f=4, seed=21):
+    g = fx.gain_bf16(seed, 1, d, 0.2)
+    wg = fx.normal_bf16(seed, 2, f * d, 0.5).reshape(f, d)
+    wu = fx.normal_bf16(seed, 3, f * d, 0.5).reshape(f, d)
+    wd = fx.normal_bf16(seed, 4, d * f, 0.5).reshape(d, f)
+    return g, wg, wu, wd
+
+
+def test_mlp_bruteforce_gate_and_up_named():
+    # W_gate and W_up differ, so silu(gate) * up and silu(up) * gate give different outputs
+    g, wg, wu, wd = small_mlp()
+    x = (2.0 * rng(22).standard_normal((3, 6))).astype(np.float32)
+    want = brute_swiglu_mlp(x, g, wg, wu, wd, 1e-5)
+    _, y = o.mlp_full(x, g, wg, wu, wd, 1e-5)
+    np.testing.assert_allclose(y, want, rtol=1e-6, atol=1e-7)
+    _, y64 = o.mlp_delta(x, g, wg, wu, wd, 1e-5)
+    np.testing.assert_allclose(y64, want, rtol=1e-12, atol=1e-13)
+    _, parts, total = o.mlp_slices(x, g, wg, wu, wd, 1e-5, 2)
+    np.testing.assert_allclose(total, want, rtol=1e-6, atol=1e-6)
+    swapped = brute_swiglu_mlp(x, g, wu, wg, wd, 1e-5)
+    assert np.max(np.abs(swapped - want)) > 1e-2          # the pin can tell gate from up
+
+
+def tiny_dims(d=6, hq=2, hkv=1, dh=2, f=4):
+    return o.Dims(d, hq, hkv, dh, f, 8, 1e-5, 1e4)
+
+
+def small_block_weights(dims, seed=23, wo_zero=False):
+    d, hq, hkv, dh, f = dims.d_model, dims.n_q_heads, dims.n_kv_heads, dims.head_dim, dims.d_ffn
+    g, wg, wu, wd = small_mlp(d, f, seed)
+    w = {("attn_norm", 0): fx.gain_bf16(seed, 5, d, 0.2), ("mlp_norm", 0): g,
+         ("wq", 0): fx.normal_bf16(seed, 6, hq * dh * d, 0.7).reshape(hq * dh, d),
+         ("wk", 0): fx.normal_bf16(seed, 7, hkv * dh * d, 0.7).reshape(hkv * dh, d),
+         ("wv", 0): fx.normal_bf16(seed, 8, hkv * dh * d, 0.7).reshape(hkv * dh, d),
+         ("wo", 0): fx.normal_bf16(seed, 9, d * hq * dh, 0.7).reshape(d, hq * dh),
+         ("wgate", 0): wg, ("wup", 0): wu, ("wdown", 0): wd}
+    if wo_zero:
+        w[("wo", 0)] = np.zeros_like(w[("wo", 0)])
+    return w
+
+
+def test_block_with_zero_attention_output_is_x_plus_mlp_of_x():
+    # W_o = 0: the attention adds nothing, so the block is x + MLP(x) (brute force, named gate/up)
+    dims = tiny_dims()
+    w = small_block_weights(dims, wo_zero=True)
+    x = (1.5 * rng(24).standard_normal((3, 6))).astype(np.float32)
+    st = o.Stage(dims, 0, 1, False, False, w, 8, kv_dtype="f32")
+    y = st.prefill(x, 0, 0)
+    want = x.astype(np.float64) + brute_swiglu_mlp(x, w[("mlp_norm", 0)], w[("wgate", 0)], w[("wup", 0)],
+                                                   w[("wdown", 0)], 1e-5)
+    np.testing.assert_allclose(y, want, rtol=1e-6, atol=1e-6)
+
+
+def rot(vec, delta, theta):
+    """Pure-Python rotate-half rotation of one head vector by the angles delta * theta^(-2i/D)."""
+    dd = len(vec)
+    half = dd // 2
+    out = list(vec)
+    for i in range(half):
+        a = delta * theta ** (-2.0 * i / dd)
+        c, s_ = math.cos(a), math.sin(a)
+        out[i] = vec[i] * c - vec[i + half] * s_
+        out[i + half] = vec[i + half] * c + vec[i] * s_
+    return out
+
+
+def brute_attn_sublayer(x, w, dims, positions):
+    """Pure-Python attention sublayer over one sequence at `positions`: scores are computed as
+    <q_p, R(j - p) k_j> (rotating the key by the RELATIVE position only), which equals
+    <R(p) q_p, R(j) k_j> exactly when RoPE rotates both q and k at their absolute positions."""
+    d, hq, hkv, dh = dims.d_model, dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    grp = hq // hkv
+    wq, wk, wv, wo = (o.bf16_to_f32(w[(r, 0)]).astype(np.float64) for r in ("wq", "wk", "wv", "wo"))
+    hs = [brute_rms_norm(row, o.bf16_to_f32(w[("attn_norm", 0)]), dims.rms_eps) for row in x]
+
+    def proj(wm, h):
+        return [sum(wm[r, c] * h[c] for c in range(d)) for r in range(wm.shape[0])]
+
+    qs, ks, vs = [proj(wq, h) for h in hs], [proj(wk, h) for h in hs], [proj(wv, h) for h in hs]
+    out = []
+    for t, p in enumerate(positions):
+        o_row = []
+        for h in range(hq):
+            g = h // grp
+            qh = qs[t][h * dh:(h + 1) * dh]
+            sc = []
+            for j, pj in enumerate(positions):
+                if pj <= p:
+                    kj = rot(ks[j][g * dh:(g + 1) * dh], pj - p, dims.rope_theta)
+                    sc.append((j, sum(a * b for a, b in zip(qh, kj)) * dh ** -0.5))
+            mx = max(s_ for _, s_ in sc)
+            z = sum(math.exp(s_ - mx) for _, s_ in sc)
+            o_row += [sum(math.exp(s_ - mx) / z * vs[j][g * dh + e] for j, s_ in sc) for e in range(dh)]
+        out.append([sum(wo[r, c] * o_row[c] for c in range(hq * dh)) for r in range(d)])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("pos0", [0, 5, 1000])
+def test_attention_sublayer_bruteforce_relative_rotation(pos0):
+    # pins RoPE on BOTH q and k (dropping either, or both, changes the scores), the scale, the
+    # causal mask, the GQA map and W_o, at absolute positions pos0 .. pos0 + 3
+    dims = tiny_dims(d=6, hq=4, hkv=2, dh=4)
+    w = small_block_weights(dims)
+    x = (1.5 * rng(25).standard_normal((4, 6))).astype(np.float32)
+    positions = list(range(pos0, pos0 + 4))
+    want = brute_attn_sublayer(x, w, dims, positions)
+    got = o.attn_sublayer(x, w[("attn_norm", 0)], w[("wq", 0)], w[("wk", 0)], w[("wv", 0)], w[("wo", 0)],
+                          dims.head_dim, dims.rms_eps, dims.rope_theta, "f32", pos0=pos0)
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-6)      # K, V stored as float32
+    st = o.Stage(dims, 0, 1, False, False, w, pos0 + 4, kv_dtype="f32")
+    delta = st.attention(0, x, np.zeros(4, np.int64), np.array(positions))
+    np.testing.assert_allclose(delta, want, rtol=1e-6, atol=1e-6)
+
+
+def test_prefill_is_invariant_to_a_shift_of_all_positions():
+    # RoPE makes attention depend on relative positions only: the same rows prefilled as a fresh
+    # sequence at positions 0.. and at s.. give the same block outputs (to the float32 rounding
+    # of the cached K and V, which differs with the absolute rotation)
+    w = fx.draw_stage_weights(TINY, 0, 2, False, False, gain_sigma=0.1)
+    x = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(5), 9 * TINY.d_model).reshape(9, TINY.d_model)
+    st = o.Stage(o.Dims.of(TINY), 0, 2, False, False, w, 300, kv_dtype="f32")
+    y0 = st.prefill(x, 0, 0)
+    for s_ in (1, 37, 290):
+        ys = st.prefill(x, s_ % 7 + 1, s_)                  # fresh slots
+        np.testing.assert_allclose(ys, y0, rtol=2e-6, atol=2e-6)
+
+
+def test_block_composes_attention_then_mlp_of_the_new_residual():
+    # x1 = x + attention(x); y = x1 + MLP(x1): the MLP norm reads x1 (not x), both residuals are
+    # added, in that order (nonzero attention, so x1 != x)
+    w = fx.draw_stage_weights(TINY, 0, 1, False, False, gain_sigma=0.1)
+    c = o.Dims.of(TINY)
+    x = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(6), 5 * TINY.d_model).reshape(5, TINY.d_model)
+    st = o.Stage(c, 0, 1, False, False, w, 8, kv_dtype="f32")
+    y = st.prefill(x, 0, 0)
+    att = o.attn_sublayer(x, w[("attn_norm", 0)], w[("wq", 0)], w[("wk", 0)], w[("wv", 0)], w[("wo", 0)],
+                          c.head_dim, c.rms_eps, c.rope_theta, "f32")
+    x1 = (x + att).astype(np.float32)
+    assert rel(x1, x) > 1e-2
+    _, m = o.mlp_full(x1, w[("mlp_norm", 0)], w[("wgate", 0)], w[("wup", 0)], w[("wdown", 0)], c.rms_eps)
+    np.testing.assert_allclose(y, x1.astype(np.float64) + m, rtol=1e-6, atol=1e-6)
+    _, m_wrong = o.mlp_full(x, w[("mlp_norm", 0)], w[("wgate", 0)], w[("wup", 0)], w[("wdown", 0)], c.rms_eps)
+    assert rel(x1 + m_wrong, y) > 1e-4                     # the MLP of x would be visible
+
+
+def rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def test_readout_bruteforce_with_gains():
+    # h_N = RMSNorm(x) g_final, logits = h_N W_readout^T; the gains are far from 1
+    d, V = 8, 5
+    g = fx.gain_bf16(31, 1, d, 0.3)
+    wr = fx.normal_bf16(31, 2, V * d, 0.5).reshape(V, d)
+    dims = o.Dims(d, 2, 1, 4, 4, V, 1e-5, 1e4)
+    st = o.Stage(dims, 0, 0, False, True, {("final_norm", -1): g, ("readout", -1): wr}, 4)
+    x = (3.0 * rng(32).standard_normal((3, d))).astype(np.float32)
+    logits, hn = st.readout(x)
+    wrf = o.bf16_to_f32(wr).astype(np.float64)
+    for m in range(3):
+        h = brute_rms_norm(x[m], o.bf16_to_f32(g), 1e-5)
+        np.testing.assert_allclose(hn[m], h, rtol=1e-6)
+        for j in range(V):
+            assert abs(logits[m, j] - sum(h[i] * wrf[j, i] for i in range(d))) <= 1e-6 * (1 + abs(logits[m, j]))
+    assert rel(o.rms_norm(x, np.ones(d), 1e-5), hn) > 1e-2       # the gains matter here
+
+
+# ---------------------------------------------------------------------------------------------
+# tensor-parallel shards ("41. Many GPUs", Tensor parallelism)
 # ---------------------------------------------------------------------------------------------
 
 def tp_weights(d, hq, hkv, dh, seed=5):
@@ -375,7 +616,7 @@ def test_attn_sublayer_single_row_is_wo_times_v():
     got = o.attn_sublayer(x, g, wq, wk, wv, wo, dh, 1e-5, 1e4)
     h = o.rms_norm(x, o.bf16_to_f32(g), 1e-5)
     v = o.round_bf16(o.linear64(h, wv).reshape(1, hkv, dh))
-    want = o.linear64(o.gqa_expand(v, hq).reshape(1, hq * dh), wo)
+    want = o.linear64(np.repeat(v, hq // hkv, axis=1).reshape(1, hq * dh), wo)
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
@@ -400,10 +641,10 @@ def test_attn_slices_sum_to_full_attention(hq, hkv, n):
     full = o.attn_sublayer(x, g, wq, wk, wv, wo, dh, 1e-5, 1e4)
     # float64 invariant: the exact partials sum to the exact full sublayer
     exact = []
-    for q0, q_n, kv0, k_n in o.head_slices(hq, hkv, n):
+    for q0, q_n, kv0, k_n in o.head_shards(hq, hkv, n):
         qr, kr = slice(q0 * dh, (q0 + q_n) * dh), slice(kv0 * dh, (kv0 + k_n) * dh)
         exact.append(o.attn_sublayer(x, g, wq[qr], wk[kr], wv[kr], np.ascontiguousarray(wo[:, qr]), dh, 1e-5, 1e4))
-        # every query head of the slice reads the KV head the full model maps it to
+        # every query head of the shard reads the KV head the full model maps it to
         for hh in range(q0, q0 + q_n):
             assert kv0 <= hh // (hq // hkv) < kv0 + k_n
     np.testing.assert_allclose(sum(exact), full, rtol=0, atol=1e-12)
@@ -411,28 +652,49 @@ def test_attn_slices_sum_to_full_attention(hq, hkv, n):
     np.testing.assert_allclose(total, full, rtol=1e-5, atol=1e-6)
 
 
-def test_head_slices_replicate_kv_heads_past_hkv():
-    # 32 query / 8 KV heads over 16 slices: 2 query heads each, KV head i shared by slices 2i, 2i+1
-    sl = o.head_slices(32, 8, 16)
+def test_head_shards_exhaustive():
+    # every (Hq, Hkv, n) up to 16: a split is accepted exactly when query heads divide evenly and
+    # KV heads either divide evenly too or are replicated a whole number of times (n a multiple of
+    # Hkv); an accepted split covers every query head once, keeps every KV head its query heads
+    # read, and splits or replicates the KV heads evenly
+    for hq in range(1, 17):
+        for hkv in (k for k in range(1, hq + 1) if hq % k == 0):
+            for n in range(1, 17):
+                ok = hq % n == 0 and (hkv % n == 0 or n % hkv == 0)
+                if not ok:
+                    with pytest.raises(ValueError):
+                        o.head_shards(hq, hkv, n)
+                    continue
+                sh = o.head_shards(hq, hkv, n)
+                assert sorted(h for q0, k, _, _ in sh for h in range(q0, q0 + k)) == list(range(hq))
+                for q0, k, kv0, hk in sh:
+                    assert {h // (hq // hkv) for h in range(q0, q0 + k)} == set(range(kv0, kv0 + hk))
+                use = [sum(kv0 <= g < kv0 + hk for _, _, kv0, hk in sh) for g in range(hkv)]
+                assert len(set(use)) == 1 and use[0] == max(1, n // hkv)
+    sl = o.head_shards(32, 8, 16)
     assert [s[2] for s in sl] == [i // 2 for i in range(16)] and all(s[1] == 2 and s[3] == 1 for s in sl)
-    assert [s[2] for s in o.head_slices(32, 8, 4)] == [0, 2, 4, 6]
-    with pytest.raises(ValueError):
-        o.head_slices(32, 8, 3)
+    assert [s[2] for s in o.head_shards(32, 8, 4)] == [0, 2, 4, 6]
 
 
-@pytest.mark.parametrize("vocab,n", [(1024, 3), (1000, 8), (17, 4)])
-def test_vocab_slices_reassemble_embedding_and_logits(vocab, n):
+@pytest.mark.parametrize("vocab,n", [(1024, 3), (1000, 8), (17, 4), (16, 4)])
+def test_vocab_shards_reassemble_embedding_and_logits(vocab, n):
     d = 32
     table = fx.normal_bf16(6, 1, vocab * d, 1.0).reshape(vocab, d)
-    per, lo, hi = o.vocab_range(vocab, n, n - 1)
-    assert per * n >= vocab and per * (n - 1) < vocab and hi == vocab
-    toks = np.array([0, vocab - 1, per - 1, per, min(2 * per, vocab - 1), vocab // 2], dtype=np.int64)
-    np.testing.assert_array_equal(o.embed_slices(table, toks, n), o.bf16_to_f32(table)[toks])
+    rows, firsts = o.vocab_shards(vocab, n)
+    assert rows * n >= vocab and rows * (n - 1) < vocab and rows == math.ceil(vocab / n)
+    # every id lands in exactly one shard, at row id - first
+    for t in range(vocab):
+        owners = [i for i in range(n) if firsts[i] <= t < firsts[i] + rows]
+        assert len(owners) == 1
+        assert np.array_equal(o.vocab_shard(table, n, owners[0])[t - firsts[owners[0]]], table[t])
+    toks = np.array([0, vocab - 1, rows - 1, min(rows, vocab - 1), min(2 * rows, vocab - 1), vocab // 2],
+                    dtype=np.int64)
+    np.testing.assert_array_equal(o.embed_shards(table, toks, n), o.bf16_to_f32(table)[toks])
     h = fx.normal_f32(6, 2, 3 * d).reshape(3, d)
     full = o.linear(h, table)
-    np.testing.assert_allclose(o.readout_slices(h, table, n), full, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(o.readout_shards(h, table, n), full, rtol=1e-6, atol=1e-6)
     # the padding rows are zero and never reach the logits
-    assert not o.vocab_slice(table, n, n - 1)[hi - lo:].any()
+    assert not o.vocab_shard(table, n, n - 1)[vocab - firsts[n - 1]:].any()
 
 
 # ---------------------------------------------------------------------------------------------
@@ -441,12 +703,12 @@ def test_vocab_slices_reassemble_embedding_and_logits(vocab, n):
 
 @pytest.mark.parametrize("n,zigzag", [(1, False), (2, False), (4, False), (2, True), (4, True)])
 def test_ring_attention_equals_full_causal_attention(n, zigzag):
-    # the hop-ordered LSE merge of every (query chunk, KV chunk) partial is the full softmax
+    # the combination of every (query chunk, KV chunk) partial is the full softmax
     t, hq, hkv, dd = 24, 4, 2, 8
     r = rng(7)
     q, k, v = r.standard_normal((t, hq, dd)), r.standard_normal((t, hkv, dd)), r.standard_normal((t, hkv, dd))
     pos = np.arange(t)
-    want = o.attention_gqa(q, k, v, pos, pos, dd ** -0.5)
+    want = brute_attention(q, k, v, pos, pos, dd ** -0.5, hq // hkv)
     np.testing.assert_allclose(o.ring_attention(q, k, v, n, zigzag), want, rtol=0, atol=1e-12)
 
 
