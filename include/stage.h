@@ -33,8 +33,15 @@
  *    positions, and "reset"/"truncate" are rewinds of the caller's positions.
  *  - One host thread per handle; calls that overlap on one handle are not supported.
  *  - Values that only the device sees (token ids, decode slots and positions) are checked on the
- *    device: rows with an out-of-range value are not computed (their outputs are zero) and the
- *    device error counter (stage_device_errors) is incremented; nothing is written out of bounds.
+ *    device and nothing is ever written out of bounds.  An out-of-range token id gives a zero
+ *    embedding row and counts one device error (stage_device_errors).  A decode row whose slot or
+ *    position is out of range writes no K/V and attends to no key: its attention output is zero,
+ *    so each block passes it on as x + MLP(x); it counts one device error per block.  Its output
+ *    is therefore defined but meaningless, and the other rows of the call are unaffected.
+ *  - Activations enter the matrix products as a bf16 "hi" plane and a bf16 "lo" plane
+ *    (hi = bf16(v), lo = bf16(v - hi): about 16 significant bits), weights as their bf16 values,
+ *    with F32 accumulation; norms and RoPE are evaluated in float64.  The decode projections for
+ *    up to 4 rows take the F32 activation directly.  No activation is rounded to bf16 alone.
  */
 #ifndef PIPELINE_STAGE_DECODER_STAGE_H
 #define PIPELINE_STAGE_DECODER_STAGE_H
@@ -80,11 +87,19 @@ typedef struct {
                            different sides of a bf16 rounding boundary perturbs attention, which
                            flips more roundings in later blocks; the pair keeps a deep stage
                            within 1e-3 of a float64 reference. */
+#define STAGE_KV_F16 8u /* IEEE binary16 KV cache (2 bytes per value, the cache precision of the
+                           TensorSharp runs, "Measured on two SSH-connected nodes": F16 KV).
+                           Eleven significant bits instead of bf16's eight make the rounding
+                           flips above eight times rarer and smaller: a 16- or 20-block stage stays
+                           within 1e-3 of a float64 reference at bf16's byte cost.  Attention
+                           multiplies it on binary16 MFMAs with q and the probabilities carried as
+                           binary16 hi + lo planes.  Values must lie in binary16's range (|v| <=
+                           65504).  Exclusive with STAGE_KV_F32. */
 
 typedef struct {
   int32_t block_begin; /* first GLOBAL block id (inclusive) */
   int32_t block_end;   /* one past the last GLOBAL block id; block_begin <= block_end */
-  uint32_t flags;      /* STAGE_FIRST | STAGE_LAST | STAGE_KV_F32 */
+  uint32_t flags;      /* STAGE_FIRST | STAGE_LAST | at most one of STAGE_KV_F32, STAGE_KV_F16 */
   int32_t max_slots;   /* KV slots (sequences) */
   int32_t max_ctx;     /* positions per slot: every position used is < max_ctx */
   int32_t max_tokens;  /* rows per call: prefill T and decode B are <= max_tokens */
@@ -92,7 +107,7 @@ typedef struct {
 
 typedef struct {
   uint64_t weight_bytes;    /* bf16 matrices, F32 norm gains */
-  uint64_t kv_bytes;        /* K and V (bf16, or 4 bytes per value with STAGE_KV_F32) for every owned block and slot */
+  uint64_t kv_bytes;        /* K and V (2 bytes per value; 4 with STAGE_KV_F32) for every owned block and slot */
   uint64_t table_bytes;     /* RoPE cos/sin table (float64) */
   uint64_t workspace_bytes; /* per-call activations, split-K and split-KV partials, error counter */
   uint64_t total_bytes;     /* arena size stage_create needs (sum of the above with alignment) */
@@ -119,20 +134,27 @@ enum {
 
 /* ---- entry points ------------------------------------------------------------------------------ */
 
-/* Byte plan of a stage (host only, no GPU call).  The arena of stage_create must hold
- * out->total_bytes.  STAGE_E_UNSUPPORTED for a configuration the kernels do not cover
+/* Byte plan of a stage (host only, no GPU call): its resource plan -- weights, KV state, tables
+ * and workspace -- as one allocation domain ("RFC: pipeline placement ...", What I found: a fit is
+ * assessed against one allocation domain including state and workspace; Proposed architecture:
+ * a stage placement carries a state plan and a resource plan).  The arena of stage_create must
+ * hold out->total_bytes.  STAGE_E_UNSUPPORTED for a configuration the kernels do not cover
  * (checked before anything is allocated), STAGE_E_INVALID for a malformed one. */
 int stage_plan(const stage_model_cfg* model, const stage_stage_cfg* stage, stage_plan_t* out /*host*/);
 
 /* Create a stage inside a caller-allocated device arena (e.g. a torch uint8 tensor) on device
- * `device`.  The stage sub-allocates weights, KV cache, tables and workspace inside the arena and
+ * `device` ("RFC: pipeline placement ...", What I found: each stage owns its resident weights, KV
+ * state, heap and workspace, with no allocator shared between stages; TensorSharp, Supported
+ * stage executors: an unsupported configuration is refused before any GPU allocation).  The stage sub-allocates weights, KV cache, tables and workspace inside the arena and
  * never allocates device memory itself.  The arena must stay allocated until stage_destroy.
  * Zero-fills the KV cache and uploads the RoPE table synchronously.  *out receives a host handle.
  * STAGE_E_DOES_NOT_FIT if arena_bytes < plan.total_bytes. */
 int stage_create(const stage_model_cfg* model, const stage_stage_cfg* stage, void* arena,
                  uint64_t arena_bytes, int device, stage_t** out);
 
-/* Copy one weight tensor into the stage.  src: bf16 bits in the role's [out, in] layout, host or
+/* Copy one weight tensor into the stage (TensorSharp, Supported stage executors: each stage loads
+ * only its own layers' weights; "RFC: pipeline placement ...", Proposed architecture: weight roles
+ * over a global block range).  src: bf16 bits in the role's [out, in] layout, host or
  * device memory; n_elems must equal the role's element count.  global_block is the GLOBAL block
  * id for per-block roles (inside [block_begin, block_end)) and -1 for EMBED/FINAL_NORM/READOUT.
  * The stage stores its own layout (fused QKV, interleaved gate/up, F32 gains).  Host sources are
@@ -140,30 +162,46 @@ int stage_create(const stage_model_cfg* model, const stage_stage_cfg* stage, voi
 int stage_load_weight(stage_t* st, int role, int global_block, const uint16_t* src, uint64_t n_elems,
                       hipStream_t stream);
 
-/* First stage: hidden_out[i, :] = f32(E[tokens[i], :]) for i < n (exact bf16 -> f32). */
+/* First stage: hidden_out[i, :] = f32(E[tokens[i], :]) for i < n (exact bf16 -> f32)
+ * ("41. Many GPUs", Pipeline parallelism: the first stage embeds the tokens; TensorSharp,
+ * Supported stage executors: the first stage embeds).  STAGE_E_ROLE off the first stage. */
 int stage_embed(stage_t* st, int n, const int32_t* tokens, float* hidden_out, hipStream_t stream);
 
 /* Prefill (or a prefill chunk) of T rows of one slot at positions pos0 .. pos0+T-1: runs every
  * owned block over hidden_in [T, d] (F32), writes K/V at those positions, attends causally over
- * positions [0, pos0 + t] for row t, and writes the stage output residual to hidden_out [T, d].
- * hidden_out may equal hidden_in.  Positions below pos0 must hold KV written earlier. */
+ * positions [0, pos0 + t] for row t, and writes the stage output residual to hidden_out [T, d]
+ * ("41. Many GPUs", Pipeline parallelism: each block adds attention and then the MLP to the
+ * residual stream, which alone crosses to the next stage; Ring attention for very long contexts:
+ * a key is visible to a query unless its position is later; TensorSharp, Supported stage
+ * executors: F32 hidden activations at the boundary; Reproducible validation: full and chunked
+ * prefill).  hidden_out may equal hidden_in.  Positions below pos0 must hold KV written earlier.
+ * STAGE_E_RANGE if slot >= max_slots or pos0 + T > max_ctx; STAGE_E_INVALID if T > max_tokens. */
 int stage_prefill(stage_t* st, int slot, int pos0, int T, const float* hidden_in, float* hidden_out,
                   hipStream_t stream);
 
 /* One decode step for B rows: row b is slot slots[b] at position positions[b] (device int32
  * arrays; slots distinct), attending over positions [0, positions[b]].  hidden_in/out [B, d] F32;
- * hidden_out may equal hidden_in.  The kernel schedule depends only on B, the shapes and
- * max_ctx, so the call can be captured in a HIP graph and replayed with new slots/positions. */
+ * hidden_out may equal hidden_in ("41. Many GPUs", Pipeline parallelism: one token per sequence
+ * through the blocks; "RFC: pipeline placement ...", What I found: a decode step is accepted only
+ * after every stage has completed it, so the caller owns positions and retries a failed step at
+ * the same ones).  The kernel schedule depends only on B, the shapes and max_ctx, so the call can
+ * be captured in a HIP graph and replayed with new slots/positions.  Out-of-range slots or
+ * positions are handled per row on the device (see the conventions above). */
 int stage_decode(stage_t* st, int B, const int32_t* slots, const int32_t* positions,
                  const float* hidden_in, float* hidden_out, hipStream_t stream);
 
-/* Last stage: normed_out = RMSNorm(hidden_in) * g_final (F32 "final hidden", nullable) and
- * logits_out [n, V] (F32) = bf16(normed) W_readout^T. */
+/* Last stage: h = RMSNorm(hidden_in) * g_final, written to normed_out as the F32 "final hidden"
+ * (nullable), and logits_out [n, V] (F32) = h W_readout^T, h entering the product as its bf16 hi
+ * and lo planes ("41. Many GPUs", Pipeline parallelism: the final norm follows the last block;
+ * TensorSharp, Supported stage executors: the last stage computes logits; "RFC: pipeline
+ * placement ...", Numerical correctness proof: full logits and final features are the outputs
+ * compared).  STAGE_E_ROLE off the last stage. */
 int stage_readout(stage_t* st, int n, const float* hidden_in, float* logits_out, float* normed_out,
                   hipStream_t stream);
 
 /* SwiGLU MLP of one owned block without its residual: out [n, d] (F32) = W_down a with
- * a = bf16(silu(W_gate h) * (W_up h)), h = bf16(RMSNorm(hidden_in) * g_mlp).  With accumulate != 0
+ * a = silu(W_gate h) * (W_up h) and h = RMSNorm(hidden_in) * g_mlp, each entering its product as
+ * bf16 hi and lo planes.  With accumulate != 0
  * the result is added to out (out = out + W_down a, one F32 add per element), so calling it over
  * column/row slices of one MLP in slice order sums the partials as ((p0 + p1) + p2) + ...
  * ("41. Many GPUs", Tensor parallelism: take_rows / take_cols and the one all-reduce per MLP;
@@ -203,7 +241,9 @@ int stage_attn_ring(stage_t* st, int global_block, int slot, int T, int n_ranks,
 int stage_embed_range(stage_t* st, int n, const int32_t* tokens, int vocab_lo, float* hidden_out, int accumulate,
                       hipStream_t stream);
 
-/* Copy KV positions [0, n_pos) of every owned block from src_slot to dst_slot. */
+/* Copy KV positions [0, n_pos) of every owned block from src_slot to dst_slot, e.g. to give many
+ * sequences one shared context ("RFC: pipeline placement ...", What I found: the KV state is the
+ * stage's own and never crosses the boundary).  STAGE_E_RANGE for a slot or n_pos out of range. */
 int stage_kv_copy(stage_t* st, int src_slot, int dst_slot, int n_pos, hipStream_t stream);
 
 /* Write / read KV of one owned block and slot at positions [pos0, pos0+n): k, v are device
@@ -250,7 +290,9 @@ int stage_timing(stage_t* st, uint32_t kind_mask);
  * waits for the recorded events, then forgets them. */
 int stage_timing_read(stage_t* st, int kind, uint64_t* launches /*host*/, double* total_ms /*host*/);
 
-/* Release the handle (the arena stays the caller's). */
+/* Release the handle; the arena, which holds the stage's weights and KV state, stays the
+ * caller's ("RFC: pipeline placement ...", What I found: each stage owns its heap and memory
+ * accounting, with no allocator shared between stages). */
 int stage_destroy(stage_t* st);
 
 const char* stage_status_str(int status);

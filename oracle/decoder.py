@@ -153,9 +153,11 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos, k_pos, scale: flo
     q, k, v = f64(q), f64(k), f64(v)
     q_pos, k_pos = np.asarray(q_pos), np.asarray(k_pos)
     order = np.argsort(k_pos, kind="stable")
-    k, v, k_pos = k[order], v[order], k_pos[order]
+    k_pos = k_pos[order]
+    k = np.ascontiguousarray(k[order].transpose(1, 0, 2))                # [Hkv, Tk, D]
+    v = np.ascontiguousarray(v[order].transpose(1, 0, 2))
     n_q, hq, dd = q.shape
-    hkv = k.shape[1]
+    hkv = k.shape[0]
     group = hq // hkv
     out = np.zeros((n_q, hq, dd))
     lse = np.full((n_q, hq), -np.inf)
@@ -165,11 +167,11 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos, k_pos, scale: flo
             continue
         for g in range(hkv):
             heads = slice(g * group, (g + 1) * group)                   # query heads reading KV head g
-            s = (k[:n_vis, g] @ q[t, heads].T) * scale                 # [|J|, group]
+            s = (k[g, :n_vis] @ q[t, heads].T) * scale                 # [|J|, group]
             m = s.max(axis=0)
             l = m + np.log(np.sum(np.exp(s - m), axis=0))
             lse[t, heads] = l
-            out[t, heads] = np.exp(s - l).T @ v[:n_vis, g]
+            out[t, heads] = np.exp(s - l).T @ v[g, :n_vis]
     return out, lse
 
 

@@ -57,7 +57,8 @@ int validate(const stage_model_cfg* m, const stage_stage_cfg* s) {
   if (s->block_begin < 0 || s->block_end < s->block_begin || s->block_end > m->n_blocks_total)
     return STAGE_E_INVALID;
   if (s->max_slots <= 0 || s->max_ctx <= 0 || s->max_tokens <= 0) return STAGE_E_INVALID;
-  if ((s->flags & ~(STAGE_FIRST | STAGE_LAST | STAGE_KV_F32)) != 0) return STAGE_E_INVALID;
+  if ((s->flags & ~(STAGE_FIRST | STAGE_LAST | STAGE_KV_F32 | STAGE_KV_F16)) != 0) return STAGE_E_INVALID;
+  if ((s->flags & STAGE_KV_F32) && (s->flags & STAGE_KV_F16)) return STAGE_E_INVALID;
   if ((s->flags & (STAGE_FIRST | STAGE_LAST)) && m->vocab <= 0) return STAGE_E_INVALID;
   // what the kernels cover (refused before anything is allocated)
   if (m->head_dim != 64 && m->head_dim != 128) return STAGE_E_UNSUPPORTED;
@@ -133,7 +134,7 @@ Layout make_layout(const stage_model_cfg& m, const stage_stage_cfg& s) {
     for (int k = 0; k < 5; ++k)
       for (int planes = 2; planes <= 3; ++planes) {
         if (shapes[k][0] <= 0) continue;
-        const GemmPlan p = gemm_plan(Mr, shapes[k][0], shapes[k][1], planes);
+        const GemmPlan p = gemm_plan(Mr, shapes[k][0], shapes[k][1], planes, k == 0);
         if (p.splitk > 1) {
           const uint64_t need = (uint64_t)p.splitk * Mr * shapes[k][0] * 4;
           if (need > gpart) gpart = need;
@@ -162,7 +163,7 @@ struct stage {
   uint16_t* readout;
   float* final_norm;
   uint8_t *kcache, *vcache;
-  int kv_f32;
+  int kv_fmt;  // KvFmt of the cache
   size_t kvb;  // bytes per KV element
   double2* rope;
   uint16_t *xn, *q, *attn, *act;
@@ -254,10 +255,10 @@ size_t ps_xn(const stage* st) { return (size_t)st->s.max_tokens * st->m.d_model;
 size_t ps_q(const stage* st) { return (size_t)st->s.max_tokens * st->m.n_q_heads * st->m.head_dim; }
 size_t ps_act(const stage* st) { return (size_t)st->s.max_tokens * st->m.d_ffn; }
 
-// Planes of the QKV operand: three (~24 bits) when K/V are rounded into a bf16 cache, so that the
-// rounding sees f32-grade values; two with the F32-grade cache, which keeps each value as a bf16
-// hi + lo pair (~16 bits) anyway.
-int qkv_planes(const stage* st) { return st->kv_f32 ? 2 : 3; }
+// Planes of the QKV operand: three (~24 bits) when K/V are rounded into a bf16 or binary16 cache,
+// so that the rounding sees f32-grade values; two with the F32-grade cache, which keeps each value
+// as a bf16 hi + lo pair (~16 bits) anyway.
+int qkv_planes(const stage* st) { return st->kv_fmt == KV_F32 ? 2 : 3; }
 
 // The RMSNorm a projection's output feeds next: `gain` (null: none requested).  `done` is set when
 // the projection's split-K sum wrote the normalised rows into the norm workspace (st->xn), so the
@@ -313,7 +314,7 @@ hipError_t project(stage* st, int kind, int rows, const float* x_f32, const floa
   g.M = rows;
   g.N = N;
   g.K = K;
-  const GemmPlan p = gemm_plan(rows, N, K, g.planes);
+  const GemmPlan p = gemm_plan(rows, N, K, g.planes, e.kind == EPI_QKV);
   g.splitk = p.splitk;
   g.part = st->gemm_part;
   g.e = e;
@@ -354,7 +355,7 @@ hipError_t attn_half(stage* st, int lb, int rows, const float* x_in, const float
   uint8_t* kc = st->kcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb;
   uint8_t* vc = st->vcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb;
   EpiArgs e = epi_base(st, EPI_QKV);
-  e.kv_f32 = st->kv_f32;
+  e.kv_fmt = st->kv_fmt;
   e.q = st->q;
   e.q_ps = ps_q(st);
   e.kc = kc;
@@ -371,7 +372,7 @@ hipError_t attn_half(stage* st, int lb, int rows, const float* x_in, const float
     a.out_ps = ps_q(st);
     a.kc = kc;
     a.vc = vc;
-    a.kv_f32 = st->kv_f32;
+    a.kv_fmt = st->kv_fmt;
     a.slots = rp.slots;
     a.pos = rp.pos;
     a.B = rows;
@@ -396,7 +397,7 @@ hipError_t attn_half(stage* st, int lb, int rows, const float* x_in, const float
     a.out_ps = ps_q(st);
     a.kc = kc;
     a.vc = vc;
-    a.kv_f32 = st->kv_f32;
+    a.kv_fmt = st->kv_fmt;
     a.slot = rp.slot;
     a.pos0 = rp.pos0;
     a.T = rows;
@@ -579,7 +580,7 @@ int stage_attn_ring(stage_t* st, int global_block, int slot, int T, int n_ranks,
 
   // q, K and V of the whole sequence (K/V into the slot's cache at positions 0 .. T-1)
   EpiArgs e = epi_base(st, EPI_QKV);
-  e.kv_f32 = st->kv_f32;
+  e.kv_fmt = st->kv_fmt;
   e.q = st->q;
   e.q_ps = ps_q(st);
   e.kc = kc;
@@ -593,7 +594,7 @@ int stage_attn_ring(stage_t* st, int global_block, int slot, int T, int n_ranks,
   a.q_ps = ps_q(st);
   a.kc = kc;
   a.vc = vc;
-  a.kv_f32 = st->kv_f32;
+  a.kv_fmt = st->kv_fmt;
   a.slot = slot;
   a.hq = hq;
   a.hkv = hkv;
@@ -694,8 +695,8 @@ int stage_create(const stage_model_cfg* model, const stage_stage_cfg* stg, void*
   st->final_norm = (stg->flags & STAGE_LAST) ? at<float>(st, L.final_norm) : nullptr;
   st->kcache = at<uint8_t>(st, L.kcache);
   st->vcache = at<uint8_t>(st, L.vcache);
-  st->kv_f32 = (stg->flags & STAGE_KV_F32) ? 1 : 0;
-  st->kvb = st->kv_f32 ? 4 : 2;
+  st->kv_fmt = (stg->flags & STAGE_KV_F32) ? KV_F32 : (stg->flags & STAGE_KV_F16) ? KV_F16 : KV_BF16;
+  st->kvb = st->kv_fmt == KV_F32 ? 4 : 2;
   st->rope = at<double2>(st, L.rope);
   st->xn = at<uint16_t>(st, L.xn);
   st->q = at<uint16_t>(st, L.q);
@@ -927,7 +928,7 @@ int stage_kv_import(stage_t* st, int global_block, int slot, int pos0, int n, co
   HIP_TRY(st, hipSetDevice(st->device));
   const int lb = global_block - st->s.block_begin;
   HIP_TRY(st, launch_kv_import(st->kcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb,
-                               st->vcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb, st->kv_f32, st->m.n_kv_heads,
+                               st->vcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb, st->kv_fmt == KV_F32, st->m.n_kv_heads,
                                st->m.head_dim, st->L.ctx_cap, slot, pos0, n, k, v, s));
   return STAGE_OK;
 }
@@ -939,7 +940,7 @@ int stage_kv_export(stage_t* st, int global_block, int slot, int pos0, int n, vo
   HIP_TRY(st, hipSetDevice(st->device));
   const int lb = global_block - st->s.block_begin;
   HIP_TRY(st, launch_kv_export(st->kcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb,
-                               st->vcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb, st->kv_f32, st->m.n_kv_heads,
+                               st->vcache + (uint64_t)lb * st->L.kv_block_elems * st->kvb, st->kv_fmt == KV_F32, st->m.n_kv_heads,
                                st->m.head_dim, st->L.ctx_cap, slot, pos0, n, k, v, s));
   return STAGE_OK;
 }

@@ -5,6 +5,8 @@
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
@@ -25,6 +27,16 @@ PSD_DEV uint32_t f2bf(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (
 
 PSD_DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// IEEE binary16 on raw bits: f32 -> f16 rounds to nearest, ties to even (the hardware conversion
+// in the default rounding mode); f16 -> f32 is exact.
+PSD_DEV uint32_t pack_f16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+PSD_DEV float h_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+PSD_DEV float h_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+PSD_DEV f16x8_t as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8_t, v); }
+
 PSD_DEV float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -40,6 +52,10 @@ PSD_DEV float wave_max(float v) {
 // B[k (l/16)*8 .. +8][col l%16]; C: lane l holds C[rows (l/16)*4 .. +4][col l%16].
 PSD_DEV f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// The same shape on binary16 operands (the F16 KV cache's attention products).
+PSD_DEV f32x4_t mfma16(f16x8_t a, f16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Activations are carried as a pair of bf16 planes, hi = bf16(x) and lo = bf16(x - hi), so the
@@ -74,6 +90,22 @@ PSD_DEV void split2_pk(float x0, float x1, uint32_t& hi, uint32_t& lo) {
   lo = pack_bf2(x0 - bf_lo(hi), x1 - bf_hi(hi));
 }
 
+// hi and lo binary16 planes of two values packed as f16 pairs: hi = f16(x), lo = f16(x - hi), so
+// hi + lo keeps ~22 significant bits for values in binary16's normal range.
+PSD_DEV void split2_pk_f16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_f16x2(x0, x1);
+  lo = pack_f16x2(x0 - h_lo(hi), x1 - h_hi(hi));
+}
+
+// Split an f32 x8 vector into binary16 hi + lo planes.
+PSD_DEV void split_hi_lo_f16(const float* x, uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) split2_pk_f16(x[2 * i], x[2 * i + 1], h[i], l[i]);
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
 // Split an f32 x8 vector into bf16 hi + bf16 lo (x ~= hi + lo to ~2^-16 relative).
 PSD_DEV void split_hi_lo(const float* x, uint4& hi, uint4& lo) {
   uint32_t h[4], l[4];
@@ -90,8 +122,14 @@ enum EpiKind {
   EPI_F32 = 0,      // out[m, n] = acc                          (readout logits, MLP partial)
   EPI_RESID = 1,    // out[m, n] = resid[m, n] + acc            (O-proj, down-proj)
   EPI_SWIGLU = 2,   // act[m, f] = bf16(silu(gate) * up)        (rows interleaved by 16)
-  EPI_QKV = 3       // RoPE on q/k, q -> bf16 buffer, k/v -> bf16 KV cache
+  EPI_QKV = 3       // RoPE on q/k, q -> plane buffer, k/v -> KV cache
 };
+
+// KV cache element formats.  KV_BF16: one bf16 per value.  KV_F32: an F32-grade pair, each value
+// kept as a bf16 hi plane and a bf16 lo plane (4 bytes).  KV_F16: one IEEE binary16 per value;
+// its attention runs on f16 MFMAs, so q and the softmax probabilities are carried as binary16
+// hi + lo planes there (the other formats carry them as bf16 planes).
+enum KvFmt { KV_BF16 = 0, KV_F32 = 1, KV_F16 = 2 };
 
 // Where each output row's token sits: slot and absolute position.
 struct RowPos {
@@ -112,8 +150,9 @@ struct EpiArgs {
   size_t q_ps;
   void* kc;                    // K cache of this block: [slots][Hkv][ctx_cap][Dh]
   void* vc;                    // V cache of this block: [slots][Hkv][ctx_cap/8][Dh][8]
-  int kv_f32;                  // F32-grade cache: each K row / V 8-key group holds a bf16 hi
-                               // plane and then a lo plane (4 bytes per element); else bf16
+  int kv_fmt;                  // KvFmt.  KV_F32: each K row / V 8-key group holds a bf16 hi plane
+                               // and then a lo plane (4 bytes per element); KV_F16 also stores
+                               // q as binary16 planes
   const double2* rope;         // [ctx_cap][Dh/2] (cos, sin), f64
   RowPos rp;
   int hq, hkv, dh, ctx_cap, max_slots;
@@ -156,20 +195,21 @@ PSD_DEV void qkv_store_pair(const EpiArgs& e, int m, int slot, int pos, int col0
     const int c = is_q ? col0 : col0 - qw;
     const int head = c / dh, s = c - head * dh;
     const int i = rope_pair_dim(s);
-    // rotation in f64 from an f64 table, rounded once to f32 and then to bf16
+    // rotation in f64 from an f64 table, rounded once to f32 and then to the stored format
     const float y0 = (float)((double)x0 * cs.x - (double)x1 * cs.y);
     const float y1 = (float)((double)x1 * cs.x + (double)x0 * cs.y);
     if (is_q) {
       uint16_t* dst = e.q + (size_t)m * qw + head * dh;
       uint32_t h, l;
-      split2_pk(y0, y1, h, l);
+      if (e.kv_fmt == KV_F16) split2_pk_f16(y0, y1, h, l);
+      else split2_pk(y0, y1, h, l);
       dst[i] = (uint16_t)h;
       dst[i + (dh >> 1)] = (uint16_t)(h >> 16);
       dst[e.q_ps + i] = (uint16_t)l;
       dst[e.q_ps + i + (dh >> 1)] = (uint16_t)(l >> 16);
     } else {
       const size_t o = (((size_t)slot * e.hkv + head) * e.ctx_cap + pos) * dh;
-      if (e.kv_f32) {
+      if (e.kv_fmt == KV_F32) {
         // F32-grade cache: the key row holds the bf16 hi plane [Dh], then the lo plane [Dh]
         uint16_t* dst = static_cast<uint16_t*>(e.kc) + 2 * o;
         uint32_t h, l;
@@ -180,7 +220,7 @@ PSD_DEV void qkv_store_pair(const EpiArgs& e, int m, int slot, int pos, int col0
         dst[dh + i + (dh >> 1)] = (uint16_t)(l >> 16);
       } else {
         uint16_t* dst = static_cast<uint16_t*>(e.kc) + o;
-        const uint32_t h = pack_bf2(y0, y1);
+        const uint32_t h = e.kv_fmt == KV_F16 ? pack_f16x2(y0, y1) : pack_bf2(y0, y1);
         dst[i] = (uint16_t)h;
         dst[i + (dh >> 1)] = (uint16_t)(h >> 16);
       }
@@ -190,7 +230,7 @@ PSD_DEV void qkv_store_pair(const EpiArgs& e, int m, int slot, int pos, int col0
     const int head = c / dh, d0 = c - head * dh;
     const size_t o = (((size_t)slot * e.hkv + head) * (e.ctx_cap >> 3) + (pos >> 3)) * dh * 8;
     const size_t i0 = (size_t)d0 * 8 + (pos & 7), i1 = (size_t)(d0 + 16) * 8 + (pos & 7);
-    if (e.kv_f32) {
+    if (e.kv_fmt == KV_F32) {
       // F32-grade cache: the 8-key group holds the hi plane [Dh][8], then the lo plane [Dh][8]
       uint16_t* base = static_cast<uint16_t*>(e.vc) + 2 * o;
       uint32_t h, l;
@@ -201,7 +241,7 @@ PSD_DEV void qkv_store_pair(const EpiArgs& e, int m, int slot, int pos, int col0
       base[(size_t)dh * 8 + i1] = (uint16_t)(l >> 16);
     } else {
       uint16_t* base = static_cast<uint16_t*>(e.vc) + o;
-      const uint32_t h = pack_bf2(x0, x1);
+      const uint32_t h = e.kv_fmt == KV_F16 ? pack_f16x2(x0, x1) : pack_bf2(x0, x1);
       base[i0] = (uint16_t)h;
       base[i1] = (uint16_t)(h >> 16);
     }

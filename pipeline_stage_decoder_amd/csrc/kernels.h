@@ -43,11 +43,11 @@ struct GemmPlan {
 };
 
 struct AttnDecodeArgs {
-  const uint16_t* q;        // pair buffer [B][Hq][Dh]
+  const uint16_t* q;        // pair buffer [B][Hq][Dh] (binary16 planes with KV_F16, else bf16)
   size_t q_ps;
   const void* kc;           // K cache of the block
   const void* vc;           // V cache of the block
-  int kv_f32;               // F32-grade cache (bf16 hi + lo planes per K row / V group), else bf16
+  int kv_fmt;               // KvFmt: KV_BF16, KV_F32 (bf16 hi + lo planes per K row / V group) or KV_F16
   const int32_t* slots;     // [B]
   const int32_t* pos;       // [B]; keys [0, pos] are attended
   int B, hq, hkv, dh, ctx_cap, max_slots;
@@ -66,7 +66,7 @@ struct AttnPrefillArgs {
   size_t q_ps;
   const void* kc;
   const void* vc;
-  int kv_f32;
+  int kv_fmt;               // KvFmt
   int slot, pos0, T, hq, hkv, dh, ctx_cap;
   float scale_log2;
   uint16_t* out;            // pair buffer [T][Hq*Dh]
@@ -93,7 +93,8 @@ hipError_t launch_embed(const uint16_t* table, int V, int d, const int32_t* toke
 hipError_t launch_embed_range(const uint16_t* table, int V, int d, int lo, const int32_t* tokens, int n, float* out,
                               int accumulate, uint32_t* err, hipStream_t s);
 hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s);
-// k, v: [n][Hkv][Dh] in the cache's element type (bf16 bits or F32)
+// k, v: [n][Hkv][Dh] in the cache's element type (bf16 or binary16 bits, copied as they are; or F32,
+// split into the F32-grade cache's hi + lo pair when kv_f32 is set)
 hipError_t launch_kv_import(void* kc, void* vc, int kv_f32, int hkv, int dh, int ctx_cap, int slot, int pos0,
                             int n, const void* k, const void* v, hipStream_t s);
 hipError_t launch_kv_export(const void* kc, const void* vc, int kv_f32, int hkv, int dh, int ctx_cap, int slot,
@@ -106,8 +107,8 @@ bool gemv_fits(int B, int K);
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s);
 
 // MFMA GEMM
-// planes: bf16 planes of the activation operand (2 or 3)
-GemmPlan gemm_plan(int M, int N, int K, int planes);
+// planes: bf16 planes of the activation operand (2 or 3); qkv: the QKV epilogue (RoPE + cache stores)
+GemmPlan gemm_plan(int M, int N, int K, int planes, bool qkv);
 // then_norm (nullable): when the plan splits K, the epilogue is EPI_RESID and M >= 256, the split-K
 // sum also writes the RMSNorm of the result rows (then_norm->x is ignored: the rows are e.out) into
 // then_norm->out_pair, and *normed (nullable) is set; otherwise *normed is false.

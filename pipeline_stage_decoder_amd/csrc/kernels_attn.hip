@@ -15,7 +15,8 @@
 //       packed V cache [pos/8][Dh][8]; B = P^T straight from registers, split into bf16 hi + lo
 //       (two MFMAs) so the probabilities keep ~16 bits.
 //   An F32-grade cache holds each value as bf16 hi + lo planes and adds the K_lo.q_hi and V_lo.P_hi
-//   MFMAs.
+//   MFMAs.  An F16 cache holds binary16 values, multiplied on f16 MFMAs with q and P split into
+//   binary16 hi + lo planes instead (~22 significant bits each); otherwise identical to bf16.
 // The softmax is online per column (max and rescale), in base 2 with the scale folded in.  O^T
 // puts a column's values in the same lane as its softmax state, so rescaling needs no shuffles.
 //
@@ -37,10 +38,26 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // Keys of the two S^T MFMAs that A row `rho` (0..15) of chunk c feeds: (rho/4)*8 + c*4 + rho%4.
 PSD_DEV int key_of_row(int rho, int c) { return ((rho >> 2) << 3) + (c << 2) + (rho & 3); }
 
-// 8 consecutive cache elements: a bf16 cache's bits at element offset `off` (lo = 0), or an F32-grade
-// cache's hi plane there and its lo plane `lo_off` elements further (both bf16, split when written).
-// (Written as a branch: as a select between the load and zero, the compiler split each 16-byte
-// load into four 4-byte loads behind branches.)
+// Cache format traits: the MFMA operand type (binary16 for the F16 cache, bf16 otherwise), whether
+// each value is a hi + lo pair of planes (F32-grade cache), and bytes per value.
+template <int FMT>
+struct Kv {
+  static constexpr bool pair = FMT == KV_F32;
+  static constexpr bool f16 = FMT == KV_F16;
+  static constexpr int bytes = pair ? 4 : 2;
+  typedef typename std::conditional<f16, f16x8_t, bf16x8_t>::type op;
+  static PSD_DEV op as_op(uint4 v) { return __builtin_bit_cast(op, v); }
+  // hi + lo planes of 8 probabilities in the operand format
+  static PSD_DEV void split(const float* x, uint4& hi, uint4& lo) {
+    if (f16) split_hi_lo_f16(x, hi, lo);
+    else split_hi_lo(x, hi, lo);
+  }
+};
+
+// 8 consecutive cache elements: a bf16 / binary16 cache's bits at element offset `off` (lo = 0), or
+// an F32-grade cache's hi plane there and its lo plane `lo_off` elements further (both bf16, split
+// when written).  (Written as a branch: as a select between the load and zero, the compiler split
+// each 16-byte load into four 4-byte loads behind branches.)
 template <bool KF32>
 PSD_DEV void load8(const uint16_t* base, size_t off, size_t lo_off, bool ok, uint4& hi, uint4& lo) {
   hi = make_uint4(0, 0, 0, 0);
@@ -59,10 +76,10 @@ PSD_DEV uint4 mask_tail(uint4 v, int nvalid) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <int DH>
+template <int DH, int FMT>
 struct Col16 {
-  bf16x8_t qh[DH / 32];    // B operand of S^T: q[col][ks*32 + grp*8 .. +8], hi plane
-  bf16x8_t ql[DH / 32];    // lo plane
+  typename Kv<FMT>::op qh[DH / 32];    // B operand of S^T: q[col][ks*32 + grp*8 .. +8], hi plane
+  typename Kv<FMT>::op ql[DH / 32];    // lo plane
   f32x4_t o[DH / 16];      // O^T[dt*16 + grp*4 + j][col]
   float m, l;              // running max (base-2 scaled) and this lane's share of the sum
 };
@@ -70,8 +87,8 @@ struct Col16 {
 // o *= alpha for the wave's columns.  A column whose running max did not move has alpha exactly 1,
 // and one that has seen no visible key still has o exactly 0; the product changes no bit in either
 // case, so the wave skips the multiplies when one of the two holds for every lane.
-template <int DH>
-PSD_DEV void rescale_o(Col16<DH>& st, float m_old, float m_new, float alpha) {
+template <int DH, int FMT>
+PSD_DEV void rescale_o(Col16<DH, FMT>& st, float m_old, float m_new, float alpha) {
   if (__any(m_old != m_new && m_old != kNegInf)) {
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] *= alpha;
@@ -80,9 +97,11 @@ PSD_DEV void rescale_o(Col16<DH>& st, float m_old, float m_new, float alpha) {
 
 // One 32-key step for a wave's 16 columns.  kb: first key (multiple of 8); the keys below kend count
 // for every column, keys >= kend are never read.
-template <int DH, bool KF32>
-PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase, int kb,
-                       int kend, float scale_log2) {
+template <int DH, int FMT>
+PSD_DEV void attn_step(Col16<DH, FMT>& st, const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
+                       int kb, int kend, float scale_log2) {
+  typedef Kv<FMT> F;
+  constexpr bool KF32 = F::pair;
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   // issue every K and V load of the step first: one memory round trip per step
   uint4 kh[2][DH / 32], kl[2][DH / 32];
@@ -109,9 +128,9 @@ PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const 
     sc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DH / 32; ++ks) {
-      sc[c] = mfma16(as_bf16x8(kh[c][ks]), st.qh[ks], sc[c]);
-      sc[c] = mfma16(as_bf16x8(kh[c][ks]), st.ql[ks], sc[c]);
-      if (KF32) sc[c] = mfma16(as_bf16x8(kl[c][ks]), st.qh[ks], sc[c]);
+      sc[c] = mfma16(F::as_op(kh[c][ks]), st.qh[ks], sc[c]);
+      sc[c] = mfma16(F::as_op(kh[c][ks]), st.ql[ks], sc[c]);
+      if (KF32) sc[c] = mfma16(F::as_op(kl[c][ks]), st.qh[ks], sc[c]);
     }
   }
   float s[8];
@@ -147,7 +166,7 @@ PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const 
   st.m = m_new;
   rescale_o(st, m_old, m_new, alpha);
   uint4 phi, plo;
-  split_hi_lo(p, phi, plo);
+  F::split(p, phi, plo);
 #pragma unroll
   for (int dt = 0; dt < DH / 16; ++dt) {
     uint4 a = vh[dt], b = vl[dt];
@@ -155,14 +174,14 @@ PSD_DEV void attn_step(Col16<DH>& st, const uint16_t* __restrict__ kbase, const 
       a = mask_tail(a, nvalid);
       b = mask_tail(b, nvalid);
     }
-    st.o[dt] = mfma16(as_bf16x8(a), as_bf16x8(phi), st.o[dt]);
-    st.o[dt] = mfma16(as_bf16x8(a), as_bf16x8(plo), st.o[dt]);
-    if (KF32) st.o[dt] = mfma16(as_bf16x8(b), as_bf16x8(phi), st.o[dt]);
+    st.o[dt] = mfma16(F::as_op(a), F::as_op(phi), st.o[dt]);
+    st.o[dt] = mfma16(F::as_op(a), F::as_op(plo), st.o[dt]);
+    if (KF32) st.o[dt] = mfma16(F::as_op(b), F::as_op(phi), st.o[dt]);
   }
 }
 
-template <int DH>
-PSD_DEV void load_q(Col16<DH>& st, const uint16_t* __restrict__ qrow /* null = padded column */, size_t q_ps) {
+template <int DH, int FMT>
+PSD_DEV void load_q(Col16<DH, FMT>& st, const uint16_t* __restrict__ qrow /* null = padded column */, size_t q_ps) {
   const int grp = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int ks = 0; ks < DH / 32; ++ks) {
@@ -171,8 +190,8 @@ PSD_DEV void load_q(Col16<DH>& st, const uint16_t* __restrict__ qrow /* null = p
       h = *reinterpret_cast<const uint4*>(qrow + ks * 32 + grp * 8);
       l = *reinterpret_cast<const uint4*>(qrow + q_ps + ks * 32 + grp * 8);
     }
-    st.qh[ks] = as_bf16x8(h);
-    st.ql[ks] = as_bf16x8(l);
+    st.qh[ks] = Kv<FMT>::as_op(h);
+    st.ql[ks] = Kv<FMT>::as_op(l);
   }
 #pragma unroll
   for (int dt = 0; dt < DH / 16; ++dt) st.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -183,7 +202,7 @@ PSD_DEV void load_q(Col16<DH>& st, const uint16_t* __restrict__ qrow /* null = p
 // ------------------------------------------------------------------------------------------------
 // decode: partial attention per (split, KV head, row)
 // ------------------------------------------------------------------------------------------------
-template <int DH, bool KF32>
+template <int DH, int FMT>
 __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
   __shared__ float sm[4][16], sl[4][16];
   __shared__ float so[4][DH][17];
@@ -197,9 +216,9 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
   const int k1 = min(k0 + a.chunk, ctx);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
 
-  Col16<DH> st;
+  Col16<DH, FMT> st;
   load_q(st, col < G ? a.q + ((size_t)b * a.hq + kvh * G + col) * DH : nullptr, a.q_ps);
-  const size_t eb = KF32 ? 4 : 2;
+  const size_t eb = Kv<FMT>::bytes;
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.kc) +
                                                             ((size_t)slot * a.hkv + kvh) * a.ctx_cap * DH * eb);
   const uint16_t* vbase = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.vc) +
@@ -207,7 +226,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
   // the 4 waves take interleaved 32-key steps, so that the work-group reads one contiguous 128-key
   // stretch of K and of V at a time (4% faster than a quarter of the chunk per wave at B = 128)
   for (int kb = k0 + wave * 32; kb < k1; kb += 128)
-    attn_step<DH, KF32>(st, kbase, vbase, kb, k1, a.scale_log2);
+    attn_step<DH, FMT>(st, kbase, vbase, kb, k1, a.scale_log2);
 
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
@@ -329,9 +348,11 @@ PSD_DEV int k_swz(int key) {
   return RC >= 16 ? c * (RC / 16) : c >> 1;
 }
 
-template <int DH, bool KF32>
+template <int DH, int FMT>
 __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
-  constexpr int EB = KF32 ? 4 : 2;
+  typedef Kv<FMT> F;
+  constexpr bool KF32 = F::pair;
+  constexpr int EB = F::bytes;
   constexpr int TILE_CHUNKS = kKeyTile * DH * EB / 16;     // 16-byte global chunks per K (and V) tile
   constexpr int PER_THREAD = TILE_CHUNKS / 256;
   static_assert(TILE_CHUNKS % 256 == 0, "tile chunks per thread");
@@ -366,7 +387,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
   const int tile0 = a.k_lo / kKeyTile;
   const int ntiles = kend > a.k_lo ? (kend + kKeyTile - 1) / kKeyTile : tile0;
 
-  Col16<DH> st;
+  Col16<DH, FMT> st;
   load_q(st, cvalid ? a.q + ((size_t)t * a.hq + head) * DH : nullptr, a.q_ps);
   const u32x4* kg = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.kc) +
                                                   ((size_t)a.slot * a.hkv + kvh) * a.ctx_cap * DH * EB);
@@ -433,9 +454,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
         sc[cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < DH / 32; ++ks) {
-          sc[cc] = mfma16(as_bf16x8(kh[cc][ks]), st.qh[ks], sc[cc]);
-          sc[cc] = mfma16(as_bf16x8(kh[cc][ks]), st.ql[ks], sc[cc]);
-          if (KF32) sc[cc] = mfma16(as_bf16x8(kl[cc][ks]), st.qh[ks], sc[cc]);
+          sc[cc] = mfma16(F::as_op(kh[cc][ks]), st.qh[ks], sc[cc]);
+          sc[cc] = mfma16(F::as_op(kh[cc][ks]), st.ql[ks], sc[cc]);
+          if (KF32) sc[cc] = mfma16(F::as_op(kl[cc][ks]), st.qh[ks], sc[cc]);
         }
       }
       float sv[8];
@@ -472,7 +493,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
       st.m = m_new;
       rescale_o(st, m_old, m_new, alpha);
       uint4 phi, plo;
-      split_hi_lo(p, phi, plo);
+      F::split(p, phi, plo);
       // V fragments: 8 keys of group grp at dim dt*16 + col; keys at or past kend (p = 0) are
       // zeroed so that whatever the cache holds there cannot reach the sum
       const int nvalid = kend - (kb + grp * 8);
@@ -485,9 +506,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
           vh = mask_tail(vh, nvalid);
           vl = mask_tail(vl, nvalid);
         }
-        st.o[dt] = mfma16(as_bf16x8(vh), as_bf16x8(phi), st.o[dt]);
-        st.o[dt] = mfma16(as_bf16x8(vh), as_bf16x8(plo), st.o[dt]);
-        if (KF32) st.o[dt] = mfma16(as_bf16x8(vl), as_bf16x8(phi), st.o[dt]);
+        st.o[dt] = mfma16(F::as_op(vh), F::as_op(phi), st.o[dt]);
+        st.o[dt] = mfma16(F::as_op(vh), F::as_op(plo), st.o[dt]);
+        if (KF32) st.o[dt] = mfma16(F::as_op(vl), F::as_op(phi), st.o[dt]);
       }
     }
     }
@@ -565,30 +586,37 @@ int attn_decode_chunk(int B) {
   return 512;
 }
 
+template <int DH>
+void attn_decode_fmt(const AttnDecodeArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.kv_fmt) {
+    case KV_F32: k_attn_decode<DH, KV_F32><<<grid, 256, 0, s>>>(a); break;
+    case KV_F16: k_attn_decode<DH, KV_F16><<<grid, 256, 0, s>>>(a); break;
+    default: k_attn_decode<DH, KV_BF16><<<grid, 256, 0, s>>>(a); break;
+  }
+  k_attn_merge<DH><<<dim3(a.hq, a.B), DH, 0, s>>>(a);
+}
+
+template <int DH>
+void attn_prefill_fmt(const AttnPrefillArgs& a, dim3 grid, hipStream_t s) {
+  switch (a.kv_fmt) {
+    case KV_F32: k_attn_prefill<DH, KV_F32><<<grid, 256, 0, s>>>(a); break;
+    case KV_F16: k_attn_prefill<DH, KV_F16><<<grid, 256, 0, s>>>(a); break;
+    default: k_attn_prefill<DH, KV_BF16><<<grid, 256, 0, s>>>(a); break;
+  }
+}
+
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
   dim3 grid(a.nsplit, a.hkv, a.B);
-  if (a.dh == 128) {
-    if (a.kv_f32) k_attn_decode<128, true><<<grid, 256, 0, s>>>(a);
-    else k_attn_decode<128, false><<<grid, 256, 0, s>>>(a);
-    k_attn_merge<128><<<dim3(a.hq, a.B), 128, 0, s>>>(a);
-  } else {
-    if (a.kv_f32) k_attn_decode<64, true><<<grid, 256, 0, s>>>(a);
-    else k_attn_decode<64, false><<<grid, 256, 0, s>>>(a);
-    k_attn_merge<64><<<dim3(a.hq, a.B), 64, 0, s>>>(a);
-  }
+  if (a.dh == 128) attn_decode_fmt<128>(a, grid, s);
+  else attn_decode_fmt<64>(a, grid, s);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
   const int G = a.hq / a.hkv;
   dim3 grid((a.T * G + 63) / 64, a.hkv);
-  if (a.dh == 128) {
-    if (a.kv_f32) k_attn_prefill<128, true><<<grid, 256, 0, s>>>(a);
-    else k_attn_prefill<128, false><<<grid, 256, 0, s>>>(a);
-  } else {
-    if (a.kv_f32) k_attn_prefill<64, true><<<grid, 256, 0, s>>>(a);
-    else k_attn_prefill<64, false><<<grid, 256, 0, s>>>(a);
-  }
+  if (a.dh == 128) attn_prefill_fmt<128>(a, grid, s);
+  else attn_prefill_fmt<64>(a, grid, s);
   return hipGetLastError();
 }
 

@@ -640,13 +640,15 @@ constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128},
 
 }  // namespace
 
-GemmPlan gemm_plan(int M, int N, int K, int planes) {
+GemmPlan gemm_plan(int M, int N, int K, int planes, bool qkv) {
   // Tile shapes from sweeps on MI355X over the prefill and batched-decode projections.
   //  * M >= 256: the LDS-direct kernels, K split until the grid holds ~200 work-groups (one per CU)
   //    as long as each split keeps >= 1024 of K.  256 x 256 for the activation pair when at most 4
   //    splits fill the chip (gate/up and the 70B projections 1.2-1.4x faster than the tiles
   //    below), else 128 x 256 (the QKV projection; the 512-row O and down projections split 4
-  //    ways, as fast as 256 x 256 split 8 with half the partials to reduce).
+  //    ways, as fast as 256 x 256 split 8 with half the partials to reduce).  The QKV epilogue
+  //    (RoPE in f64 and the cache stores) never takes 256 x 256: on that tile it needed more
+  //    registers than two waves per SIMD leave and spilled 528 bytes per lane.
   //  * 32 < M <= 64 (batched decode): 64 x 256 or 64 x 128 LDS-direct tiles with 64-deep stages
   //    (8B-shaped projections at M = 64: gate/up 55 -> 50 us, down 37 -> 31 us, O 17.5 -> 16 us).
   //  * 64 < M <= 128 (batched decode): 128 x 256.  Two planes (K a multiple of 64): 64-deep stages
@@ -696,7 +698,7 @@ GemmPlan gemm_plan(int M, int N, int K, int planes) {
   }
   if (dma_ok && M >= 256) {
     // cfg 5 (256 x 256, two planes) when it fills the chip, else cfg 6 (128 x 256)
-    for (int cfg = planes == 2 ? 5 : 6; cfg <= 6; ++cfg) {
+    for (int cfg = planes == 2 && !qkv ? 5 : 6; cfg <= 6; ++cfg) {
       const int bm = kCfgs[cfg].bm, bn = kCfgs[cfg].bn;
       const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
       const int want = cfg == 5 ? 200 : 190, least = cfg == 5 ? 200 : 128, most = cfg == 5 ? 4 : 8;
@@ -740,9 +742,11 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
     case 1: k_gemm<64, 256, 1, 4, NP, EPI, 1, 1><<<grid, 256, 0, s>>>(a); break;
     case 2: k_gemm<64, 128, 1, 4, NP, EPI, 2, 1><<<grid, 256, 0, s>>>(a); break;
     case 3: k_gemm<32, 128, 1, 4, NP, EPI, 2, 2><<<grid, 256, 0, s>>>(a); break;
-    case 5:   // the planner gives it two planes only
-      if (pp) k_gemm_dma<2, EPI, 256, 256, 4, 2, 3, kDmaBK, true><<<grid, 512, 0, s>>>(a);
-      else k_gemm_dma<2, EPI, 256, 256, 4, 2, 3><<<grid, 512, 0, s>>>(a);
+    case 5:   // the planner gives it two planes and no QKV epilogue only
+      if constexpr (EPI != EPI_QKV) {
+        if (pp) k_gemm_dma<2, EPI, 256, 256, 4, 2, 3, kDmaBK, true><<<grid, 512, 0, s>>>(a);
+        else k_gemm_dma<2, EPI, 256, 256, 4, 2, 3><<<grid, 512, 0, s>>>(a);
+      }
       break;
     case 6:
       if (pp) k_gemm_dma<NP, EPI, 128, 256, 4, 2, 3, kDmaBK, true><<<grid, 512, 0, s>>>(a);
@@ -779,6 +783,7 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
   // the LDS-direct tile takes two planes, K in whole 32-deep stages and operands under 4 GiB
   if (((p.cfg == 5 || p.cfg == 8 || p.cfg == 10) && a.planes != 2) || (p.cfg >= 5 && ( a.K % kDmaBK != 0 || (uint64_t)(a.M > a.N ? a.M : a.N) * a.K * 2 >= (1ull << 32))))
     return hipErrorInvalidValue;
+  if (p.cfg == 5 && a.e.kind == EPI_QKV) return hipErrorInvalidValue;   // not instantiated (see gemm_plan)
   if (p.cfg >= 8 && a.K % 64 != 0) return hipErrorInvalidValue;   // 64-deep stages
   dim3 grid(p.tiles_m * p.tiles_n, p.splitk);
   switch (a.e.kind) {

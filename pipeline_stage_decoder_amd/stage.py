@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpsd_stag
 
 STAGE_OK, STAGE_E_INVALID, STAGE_E_UNSUPPORTED, STAGE_E_DOES_NOT_FIT, STAGE_E_ROLE, STAGE_E_RANGE, \
     STAGE_E_HIP = range(7)
-STAGE_FIRST, STAGE_LAST, STAGE_KV_F32 = 1, 2, 4
+STAGE_FIRST, STAGE_LAST, STAGE_KV_F32, STAGE_KV_F16 = 1, 2, 4, 8
+KV_FLAGS = {"bf16": 0, "f32": STAGE_KV_F32, "f16": STAGE_KV_F16}
 
 KERNEL_KINDS = {"embed": 0, "norm": 1, "qkv": 2, "attn": 3, "o": 4, "gateup": 5, "down": 6, "readout": 7}
 
@@ -112,13 +113,21 @@ def model_cfg(shape) -> ModelCfg:
                     shape.n_blocks_total, shape.rms_eps, shape.rope_theta)
 
 
+def kv_format(kv, kv_f32: bool) -> str:
+    """The cache format name: `kv` ("bf16", "f16" or "f32") if given, else "f32" when kv_f32."""
+    fmt = kv if kv is not None else ("f32" if kv_f32 else "bf16")
+    if fmt not in KV_FLAGS:
+        raise ValueError(f"unknown KV cache format {fmt!r}")
+    return fmt
+
+
 def place(shape, budgets, *, max_slots: int = 1, max_ctx: int = 2048, max_tokens: int = 512,
-          kv_f32: bool = False):
+          kv_f32: bool = False, kv: str | None = None):
     """Contiguous byte-balanced placement over len(budgets) devices (include/placement.h), host only.
     Returns (cuts, required): device i gets blocks [cuts[i], cuts[i+1])."""
     n = len(budgets)
     m = model_cfg(shape)
-    s = StageCfg(0, 0, STAGE_KV_F32 if kv_f32 else 0, max_slots, max_ctx, max_tokens)
+    s = StageCfg(0, 0, KV_FLAGS[kv_format(kv, kv_f32)], max_slots, max_ctx, max_tokens)
     b = (ctypes.c_uint64 * n)(*[int(x) for x in budgets])
     cuts = (ctypes.c_int32 * (n + 1))()
     req = (ctypes.c_uint64 * n)()
@@ -128,10 +137,10 @@ def place(shape, budgets, *, max_slots: int = 1, max_ctx: int = 2048, max_tokens
     return list(cuts), list(req)
 
 
-def plan(shape, block_begin, block_end, first, last, max_slots, max_ctx, max_tokens) -> Plan:
+def plan(shape, block_begin, block_end, first, last, max_slots, max_ctx, max_tokens, kv: str = "bf16") -> Plan:
     m = model_cfg(shape)
-    s = StageCfg(block_begin, block_end, (STAGE_FIRST if first else 0) | (STAGE_LAST if last else 0),
-                 max_slots, max_ctx, max_tokens)
+    s = StageCfg(block_begin, block_end, (STAGE_FIRST if first else 0) | (STAGE_LAST if last else 0)
+                 | KV_FLAGS[kv_format(kv, False)], max_slots, max_ctx, max_tokens)
     p = Plan()
     rc = lib().stage_plan(ctypes.byref(m), ctypes.byref(s), ctypes.byref(p))
     if rc != STAGE_OK:
@@ -163,16 +172,18 @@ class Stage:
     """One pipeline stage on one GPU: weights, KV cache and workspace in one torch-owned arena."""
 
     def __init__(self, shape, block_begin: int, block_end: int, first: bool, last: bool, *, max_slots: int = 1,
-                 max_ctx: int = 2048, max_tokens: int = 512, device: int = 0, kv_f32: bool = False):
+                 max_ctx: int = 2048, max_tokens: int = 512, device: int = 0, kv_f32: bool = False,
+                 kv: str | None = None):
         if not torch.cuda.is_available():
             raise RuntimeError("Stage needs a ROCm GPU; none is visible")
         self.shape = shape
         self.spec = StageSpec(block_begin, block_end, first, last, max_slots, max_ctx, max_tokens)
         self.device = device
         self._m = model_cfg(shape)
-        self.kv_f32 = kv_f32
+        self.kv = kv_format(kv, kv_f32)          # KV cache format: "bf16", "f16" or "f32"
+        self.kv_f32 = self.kv == "f32"
         self._s = StageCfg(block_begin, block_end, (STAGE_FIRST if first else 0) | (STAGE_LAST if last else 0)
-                           | (STAGE_KV_F32 if kv_f32 else 0), max_slots, max_ctx, max_tokens)
+                           | KV_FLAGS[self.kv], max_slots, max_ctx, max_tokens)
         self.plan = Plan()
         self._check(lib().stage_plan(ctypes.byref(self._m), ctypes.byref(self._s), ctypes.byref(self.plan)),
                     "stage_plan")
@@ -308,7 +319,8 @@ class Stage:
         self._check(lib().stage_kv_copy(self._h, src_slot, dst_slot, n_pos, _stream(stream)), "stage_kv_copy")
 
     def kv_import(self, global_block: int, slot: int, pos0: int, k: torch.Tensor, v: torch.Tensor, stream=None):
-        """k, v: [n, Hkv, Dh] device tensors in the cache's element type (bf16 bits as int16, or float32)."""
+        """k, v: [n, Hkv, Dh] device tensors in the cache's element type (bf16 or binary16 bits as int16,
+        or float32 for the F32-grade cache)."""
         want = torch.float32 if self.kv_f32 else torch.int16
         if k.dtype != want or v.dtype != want:
             raise TypeError(f"kv_import expects {want} tensors for this stage")
@@ -317,7 +329,7 @@ class Stage:
                                           _ptr(v.contiguous()), _stream(stream)), "stage_kv_import")
 
     def kv_export(self, global_block: int, slot: int, pos0: int, n: int, stream=None):
-        """K and V [n, Hkv, Dh] in the cache's element type (int16 bf16 bits, or float32)."""
+        """K and V [n, Hkv, Dh] in the cache's element type (int16 bf16 or binary16 bits, or float32)."""
         shp = (n, self.shape.n_kv_heads, self.shape.head_dim)
         dev = self.arena.device
         dt = torch.float32 if self.kv_f32 else torch.int16

@@ -100,11 +100,31 @@ def gpu_generate(stages: list, prompt: np.ndarray, n_new: int, slot: int = 0):
 
 
 def kv_bits(st: Stage, block: int, slot: int, n: int):
-    """The cache's K and V of one block and slot as raw bits (uint16 for bf16, uint32 for F32)."""
+    """The cache's K and V of one block and slot as raw bits (uint16 for bf16 and binary16, uint32
+    for F32)."""
     k, v = st.kv_export(block, slot, 0, n)
     torch.cuda.synchronize()
     view = np.uint32 if st.kv_f32 else np.uint16
     return k.cpu().numpy().view(view), v.cpu().numpy().view(view)
+
+
+def kv_values(kv: str, bits: np.ndarray) -> np.ndarray:
+    """float32 values of cache bits in format kv ("bf16", "f16" or "f32")."""
+    if kv == "f32":
+        return bits.view(np.float32)
+    if kv == "f16":
+        return bits.view(np.float16).astype(np.float32)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def kv_bits_of(kv: str, values: np.ndarray) -> np.ndarray:
+    """Cache bits of float32 values already representable in format kv."""
+    values = np.asarray(values, np.float32)
+    if kv == "f32":
+        return values.view(np.uint32)
+    if kv == "f16":
+        return values.astype(np.float16).view(np.uint16)
+    return (values.view(np.uint32) >> 16).astype(np.uint16)
 
 
 def hidden_rows(seed_slot: int, n: int, d: int, offset_pos: int = 0) -> np.ndarray:

@@ -86,7 +86,8 @@ def test_plan_refuses_unsupported_models(change, code):
     (dict(block_end=3), S.STAGE_E_INVALID),
     (dict(max_slots=0), S.STAGE_E_INVALID),
     (dict(max_tokens=0), S.STAGE_E_INVALID),
-    (dict(flags=8), S.STAGE_E_INVALID),
+    (dict(flags=16), S.STAGE_E_INVALID),
+    (dict(flags=S.STAGE_KV_F32 | S.STAGE_KV_F16), S.STAGE_E_INVALID),
     (dict(max_ctx=1 << 25), S.STAGE_E_UNSUPPORTED),
 ])
 def test_plan_refuses_malformed_stages(kw, code):
@@ -129,3 +130,14 @@ def test_pipeline_and_greedy_refuse_bad_arguments_on_the_host():
     assert L.stage_greedy(2, 0, None, None, None) == S.STAGE_E_INVALID
     assert L.stage_greedy(0, 10, None, None, None) == S.STAGE_OK          # nothing to do, no GPU call
     assert L.stage_describe(None, None, None, None) == S.STAGE_E_INVALID
+
+
+def test_plan_kv_bytes_per_format():
+    # bf16 and binary16 caches take 2 bytes per value, the F32-grade pair 4; nothing else changes
+    def kv_bytes(flags):
+        rc, p = plan_rc(fx.TINY, flags=flags)
+        assert rc == S.STAGE_OK
+        return p
+    b16, f16, f32 = kv_bytes(0), kv_bytes(S.STAGE_KV_F16), kv_bytes(S.STAGE_KV_F32)
+    assert f16.kv_bytes == b16.kv_bytes and f16.weight_bytes == b16.weight_bytes
+    assert f32.kv_bytes >= 2 * b16.kv_bytes - 512

@@ -25,7 +25,9 @@ import torch
 
 import fixtures as fx
 from oracle import decoder as o
-from tests.gpu_util import hidden_rows, kv_bits, make_stage, rel_l2, rel_l2_kv, say
+from pipeline_stage_decoder_amd.stage import Stage
+from tests.gpu_util import (hidden_rows, kv_bits, kv_bits_of, kv_values, make_stage, rel_l2, rel_l2_kv, rel_l2_rows,
+                            rel_l2_whole, say)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -33,20 +35,26 @@ TOL = 1e-3
 SEED_KV = 0x5EED0004
 
 
-def seeded_kv(shape, slot: int, n: int):
-    """bf16 bits of K and V [n, Hkv, Dh] for one slot (K stands for post-RoPE keys)."""
+def seeded_kv(shape, slot: int, n: int, kv: str = "bf16"):
+    """Seeded N(0,1) K and V [n, Hkv, Dh] of one slot (K stands for post-RoPE keys) as values of
+    the cache format kv (bf16 draws, rounded to binary16 for an F16 cache)."""
     per = shape.n_kv_heads * shape.head_dim
     k = fx.normal_bf16(SEED_KV, 2 * slot, n * per, 1.0).reshape(n, shape.n_kv_heads, shape.head_dim)
     v = fx.normal_bf16(SEED_KV, 2 * slot + 1, n * per, 1.0).reshape(n, shape.n_kv_heads, shape.head_dim)
+    k, v = o.bf16_to_f32(k), o.bf16_to_f32(v)
+    if kv == "f16":
+        k, v = k.astype(np.float16).astype(np.float32), v.astype(np.float16).astype(np.float32)
     return k, v
 
 
 def import_kv(st, ost, block, slots, n):
     """Write the same seeded KV (positions 0..n-1) into the GPU stage and the oracle stage."""
+    dt = torch.float32 if st.kv == "f32" else torch.int16
     for s in slots:
-        k, v = seeded_kv(st.shape, s, n)
-        st.kv_import(block, s, 0, torch.from_numpy(k.view(np.int16)).cuda(), torch.from_numpy(v.view(np.int16)).cuda())
-        ost.import_kv(block, s, 0, o.bf16_to_f32(k), o.bf16_to_f32(v))
+        k, v = seeded_kv(st.shape, s, n, st.kv)
+        kb, vb = kv_bits_of(st.kv, k), kv_bits_of(st.kv, v)
+        st.kv_import(block, s, 0, torch.from_numpy(kb).view(dt).cuda(), torch.from_numpy(vb).view(dt).cuda())
+        ost.import_kv(block, s, 0, k, v)
     torch.cuda.synchronize()
 
 
@@ -55,15 +63,15 @@ def w8b_first():
     return fx.draw_stage_weights(fx.LLAMA8B, 0, 2, True, False, gain_sigma=0.1)
 
 
-@pytest.mark.parametrize("T,kv_f32", [(512, False), (72, False), (512, True)])
-def test_8b_first_stage_prefill_and_decode(w8b_first, T, kv_f32):
+@pytest.mark.parametrize("T,kv", [(72, "bf16"), (512, "f32"), (72, "f32"), (512, "f16"), (72, "f16")])
+def test_8b_first_stage_prefill_and_decode(w8b_first, T, kv):
     # with an F32 cache the QKV projection takes two activation planes instead of three
     s = fx.LLAMA8B
     prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(0), T, s.vocab)
-    say(f"8B first stage: oracle prefill T={T}, {'f32' if kv_f32 else 'bf16'} cache")
-    ost = o.Stage(o.Dims.of(s), 0, 2, True, False, w8b_first, T + 4, kv_dtype="f32" if kv_f32 else "bf16")
+    say(f"8B first stage: oracle prefill T={T}, {kv} cache")
+    ost = o.Stage(o.Dims.of(s), 0, 2, True, False, w8b_first, T + 4, kv_dtype=kv)
     want = ost.prefill(ost.embed(prompt), 0, 0)
-    st = make_stage(s, 0, 2, True, False, w8b_first, max_slots=1, max_ctx=2048, max_tokens=512, kv_f32=kv_f32)
+    st = make_stage(s, 0, 2, True, False, w8b_first, max_slots=1, max_ctx=2048, max_tokens=512, kv=kv)
     dev = torch.device("cuda")
     x = st.embed(torch.tensor(prompt, dtype=torch.int32, device=dev))
     got = st.prefill(x, 0, 0).cpu().numpy()
@@ -81,11 +89,36 @@ def test_8b_first_stage_prefill_and_decode(w8b_first, T, kv_f32):
         assert e <= TOL
 
 
-def test_8b_last_stage_batched_decode_and_readout():
+def test_8b_bf16_cache_outside_the_row_bound(w8b_first):
+    # bf16 KV storage is offered but is not inside the parity envelope.  A K/V value that the GPU's
+    # f32 sums and the float64 oracle put on different sides of a bf16 rounding boundary is stored
+    # 2^-8 apart, and over a 512-token prompt of the 8B-shaped first stage (two blocks) that moves
+    # single rows past 1e-3 (measured 1.18e-3 on MI355X) although the whole tensor stays well below
+    # it; the F16 and F32-grade caches hold the row bound at full depth.  What this checks of the
+    # bf16 format itself: the rounding (bits equal to the oracle's bf16 rounding for > 99% of the
+    # cached values), the whole-tensor bound, and a worst row under 2e-3 as a regression guard.
+    s, T = fx.LLAMA8B, 512
+    prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(0), T, s.vocab)
+    ost = o.Stage(o.Dims.of(s), 0, 2, True, False, w8b_first, T, kv_dtype="bf16")
+    want = ost.prefill(ost.embed(prompt), 0, 0)
+    st = make_stage(s, 0, 2, True, False, w8b_first, max_slots=1, max_ctx=T, max_tokens=T, kv="bf16")
+    got = st.prefill(st.embed(torch.tensor(prompt, dtype=torch.int32, device="cuda")), 0, 0).cpu().numpy()
+    e_whole, e_row = rel_l2_whole(got, want), rel_l2_rows(got, want)
+    say(f"8B first stage, bf16 cache, T={T}: whole {e_whole:.2e}, worst row {e_row:.2e}")
+    assert e_whole <= TOL and e_row <= 2e-3
+    for blk in range(2):
+        kg, vg = kv_bits(st, blk, 0, T)
+        kc, vc = ost.kv[0]
+        for g_bits, w_vals in ((kg, kc[blk, :T]), (vg, vc[blk, :T])):
+            assert np.mean(g_bits == kv_bits_of("bf16", w_vals)) > 0.99
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f16"])
+def test_8b_last_stage_batched_decode_and_readout(kv):
     s, blk, B, ctx = fx.LLAMA8B, 16, 64, 4096
     w = fx.draw_stage_weights(s, blk, blk + 1, False, True, gain_sigma=0.1)
-    ost = o.Stage(o.Dims.of(s), blk, blk + 1, False, True, w, ctx + 1)
-    st = make_stage(s, blk, blk + 1, False, True, w, max_slots=B, max_ctx=ctx + 1, max_tokens=B)
+    ost = o.Stage(o.Dims.of(s), blk, blk + 1, False, True, w, ctx + 1, kv_dtype=kv)
+    st = make_stage(s, blk, blk + 1, False, True, w, max_slots=B, max_ctx=ctx + 1, max_tokens=B, kv=kv)
     say("8B last stage: importing KV")
     import_kv(st, ost, blk, range(B), ctx)
     slots = np.arange(B)[::-1].copy()
@@ -111,12 +144,13 @@ def w70b_block():
     return fx.draw_stage_weights(fx.LLAMA70B, 20, 21, False, False, gain_sigma=0.1)
 
 
-def test_70b_mid_stage_prefill_and_batched_decode(w70b_block):
+@pytest.mark.parametrize("kv", ["bf16", "f16"])
+def test_70b_mid_stage_prefill_and_batched_decode(w70b_block, kv):
     s, blk, B, ctx = fx.LLAMA70B, 20, 128, 8192
     w = w70b_block
-    st = make_stage(s, blk, blk + 1, False, False, w, max_slots=B + 1, max_ctx=ctx + 1, max_tokens=B)
+    st = make_stage(s, blk, blk + 1, False, False, w, max_slots=B + 1, max_ctx=ctx + 1, max_tokens=B, kv=kv)
     # prefill T = 64 into the extra slot B
-    ost = o.Stage(o.Dims.of(s), blk, blk + 1, False, False, w, ctx + 1)
+    ost = o.Stage(o.Dims.of(s), blk, blk + 1, False, False, w, ctx + 1, kv_dtype=kv)
     xp = hidden_rows(7, 64, s.d_model)
     say("70B block: oracle prefill")
     want = ost.prefill(xp, B, 0)
@@ -140,30 +174,38 @@ def test_70b_mid_stage_prefill_and_batched_decode(w70b_block):
     assert st.device_errors() == 0
 
 
-@pytest.mark.parametrize("kv_f32", [False, True])
-def test_70b_prefill_chunk_4096_first_rows(w70b_block, kv_f32):
+@pytest.mark.parametrize("kv", ["bf16", "f32", "f16"])
+def test_70b_prefill_chunk_4096_all_kv_rows_and_late_rows(w70b_block, kv):
     # a 4096-token chunk runs every projection of the block on the large-grid GEMM schedule (QKV +
-    # RoPE + KV write, O + residual, gate/up + SwiGLU, down + residual); rows 0..63 of the chunk
-    # depend only on each other (causal), so the oracle's 64-token prefill is their exact value
-    s, blk, T, n = fx.LLAMA70B, 20, 4096, 64
-    kv = "f32" if kv_f32 else "bf16"
-    st = make_stage(s, blk, blk + 1, False, False, w70b_block, max_slots=1, max_ctx=T, max_tokens=T, kv_f32=kv_f32)
+    # RoPE + KV write, O + residual, gate/up + SwiGLU, down + residual).  Every row's K and V
+    # depend only on that row's input, so the oracle's K/V of all 4096 rows are compared with the
+    # exported cache, per KV head; then the oracle's attention (over its own K/V of every earlier
+    # row), O projection and MLP give the exact outputs of rows spread over the chunk -- the first
+    # GEMM row tile, middle tiles and the last 64 rows, which attend to up to 4096 keys.
+    s, blk, T = fx.LLAMA70B, 20, 4096
+    st = make_stage(s, blk, blk + 1, False, False, w70b_block, max_slots=1, max_ctx=T, max_tokens=T, kv=kv)
     x = hidden_rows(9, T, s.d_model)
     say(f"70B block, {kv} cache: gpu prefill T={T}")
     got = st.prefill(torch.from_numpy(x).cuda(), 0, 0).cpu().numpy()
     assert np.isfinite(got).all()
-    ost = o.Stage(o.Dims.of(s), blk, blk + 1, False, False, w70b_block, n, kv_dtype=kv)
-    want = ost.prefill(x[:n], 0, 0)
-    e = rel_l2(got[:n], want)
-    say(f"  rows 0..{n - 1} rel L2 {e:.2e}")
+    kg, vg = kv_bits(st, blk, 0, T)
+    say("  oracle K/V of all rows")
+    ost = o.Stage(o.Dims.of(s), blk, blk + 1, False, False, w70b_block, T, kv_dtype=kv)
+    pos = np.arange(T)
+    _, k_all, v_all = ost.qkv(blk, x, pos)
+    for name, g_bits, want_kv in (("K", kg, k_all), ("V", vg, v_all)):
+        e = rel_l2_kv(kv_values(kv, g_bits), want_kv)
+        say(f"  {name} of rows 0..{T - 1}: rel L2 (worst head) {e:.2e}")
+        assert e <= TOL
+        if kv != "f32":                            # rounding flips are rare
+            assert np.mean(g_bits == kv_bits_of(kv, want_kv)) > 0.99
+    ost.import_kv(blk, 0, 0, k_all, v_all)        # the oracle's own cache, every row held
+    rows = np.concatenate([np.arange(0, 64), np.arange(1000, 1032), np.arange(2500, 2532), np.arange(T - 64, T)])
+    say(f"  oracle block output of {len(rows)} rows")
+    want = ost.forward(x[rows], np.zeros(len(rows), np.int64), rows)
+    e = rel_l2(got[rows], want)
+    say(f"  rows 0..63, 1000..1031, 2500..2531, {T - 64}..{T - 1}: rel L2 (worst row) {e:.2e}")
     assert e <= TOL
-    kc, vc = ost._cache(0)                      # [blocks of the stage, positions, Hkv, Dh]
-    kg, vg = kv_bits(st, blk, 0, n)
-    for g_bits, want_kv in ((kg, kc[0, :n]), (vg, vc[0, :n])):
-        gv = g_bits.view(np.float32) if kv_f32 else o.bf16_to_f32(g_bits)
-        assert rel_l2_kv(gv, want_kv) <= TOL
-        if not kv_f32:                             # bf16 rounding flips are rare
-            assert np.mean(g_bits == o.f32_to_bf16_bits(want_kv)) > 0.99
     assert st.device_errors() == 0
 
 
@@ -221,8 +263,8 @@ def test_mlp_slices_sum_to_full_mlp(mlp70b, T):
     assert e_sum <= TOL and e_full <= TOL
 
 
-@pytest.mark.parametrize("kv_f32", [False, True])
-def test_8b_split_equals_unsplit_on_gpu(w8b_first, kv_f32):
+@pytest.mark.parametrize("kv", ["bf16", "f32", "f16"])
+def test_8b_split_equals_unsplit_on_gpu(w8b_first, kv):
     # blocks [0, 2) in one stage against [0, 1) + [1, 2) with the F32 handoff, at the real 8B shape:
     # a 300-row prefill (LDS-direct GEMMs, split-K sums; in one stage block 0's down projection
     # also normalises for block 1, in two stages block 1 normalises its input itself), two B = 1
@@ -231,7 +273,7 @@ def test_8b_split_equals_unsplit_on_gpu(w8b_first, kv_f32):
     # and both blocks' KV bit for bit
     s, T, B = fx.LLAMA8B, 300, 64
     dev = torch.device("cuda")
-    kw = dict(max_slots=B, max_ctx=512, max_tokens=512, kv_f32=kv_f32)
+    kw = dict(max_slots=B, max_ctx=512, max_tokens=512, kv=kv)
     whole = make_stage(s, 0, 2, True, False, w8b_first, **kw)
     a = make_stage(s, 0, 1, True, False, w8b_first, **kw)
     b = make_stage(s, 1, 2, False, False, w8b_first, **kw)
@@ -262,7 +304,7 @@ def test_8b_split_equals_unsplit_on_gpu(w8b_first, kv_f32):
             kw_, vw_ = kv_bits(whole, blk, slot, n + 1)
             kp, vp = kv_bits(part, blk, slot, n + 1)
             assert np.array_equal(kw_, kp) and np.array_equal(vw_, vp)
-    say(f"8B split [0,1)+[1,2) == [0,2), {'f32' if kv_f32 else 'bf16'} cache: prefill {T} rows, 2 decode steps, "
+    say(f"8B split [0,1)+[1,2) == [0,2), {kv} cache: prefill {T} rows, 2 decode steps, "
         f"B={B} decode step, KV")
 
 
@@ -289,30 +331,89 @@ def test_8b_mlp_gemm_tiles_ragged_rows(w8b_first, T):
     assert np.isfinite(got).all()
 
 
-def test_8b_first_stage_all_16_blocks_decode_kernels():
+def oracle_layer_major(shape, begin, end, kv, x_rows, draw_block):
+    """Oracle output of blocks [begin, end) for one sequence whose rows x_rows sit at positions
+    0, 1, ...: a prefill of the first rows followed by decode steps of the rest gives, row for row,
+    the values of one prefill of every row (each row attends the keys at or before its position,
+    and every row's K/V is written first), so the oracle runs block by block over all rows at once
+    and holds one block's weights at a time (draw_block(b) -> that block's weights)."""
+    c = o.Dims.of(shape)
+    x = np.asarray(x_rows, np.float32)
+    for b in range(begin, end):
+        st = o.Stage(c, b, b + 1, False, False, draw_block(b), x.shape[0], kv_dtype=kv)
+        x = st.prefill(x, 0, 0)
+        say(f"    oracle block {b} done")
+    return x
+
+
+def fill_weights_on_gpu(st, shape, blocks, first, last, gain_sigma):
+    """Draw a stage's weights with the device generator (bit-identical to the host draws of
+    fixtures.draw_weight) and load them; no host copy of the whole stage."""
+    roles = fx.stage_roles(blocks[0], blocks[1], first, last)
+    biggest = max(int(np.prod(fx.role_shape(shape, r))) for r, _ in roles)
+    scratch = torch.empty(biggest, dtype=torch.int16, device="cuda")
+    for role, b in roles:
+        t = scratch[:int(np.prod(fx.role_shape(shape, role)))]
+        if role in fx.GAIN_ROLES:
+            fx.gain_bf16_gpu(t, fx.SEED_WEIGHTS, fx.weight_stream(role, b), gain_sigma)
+        else:
+            fx.normal_bf16_gpu(t, fx.SEED_WEIGHTS, fx.weight_stream(role, b), 0.02)
+        st.load_weight(role, b, t)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("kv", ["f32", "f16"])
+def test_8b_first_stage_all_16_blocks_decode_kernels(kv):
     # the whole first stage (embedding + 16 blocks) with a short prompt, then B = 1 decode steps:
-    # the decode launches are the benchmark's (GEMV kernels, split-KV attention over max_ctx 2048)
+    # the decode launches are the benchmark's (GEMV kernels, split-KV attention over max_ctx 2048).
+    # F32-grade and binary16 caches hold 1e-3 at this depth; bf16 storage does not (its rounding
+    # flips cascade through the blocks) and is covered block by block above.
     s = fx.LLAMA8B
-    w = fx.draw_stage_weights(s, 0, 16, True, False, gain_sigma=0.1)
-    T = 24
+    T, n_dec = 24, 2
     prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(2), T, s.vocab)
-    # an F32 KV cache: with bf16 storage, rounding decisions that the f32 GPU sums and the float64
-    # oracle take differently cascade through 16 blocks past 1e-3 (the bf16 case is covered
-    # block by block above)
-    ost = o.Stage(o.Dims.of(s), 0, 16, True, False, w, T + 4, kv_dtype="f32")
-    say("8B first stage, 16 blocks: oracle")
-    want = [ost.prefill(ost.embed(prompt), 0, 0)]
-    toks = fx.tokens(fx.SEED_TOKENS, fx.token_stream(3), 2, s.vocab)
-    for i, tok in enumerate(toks):
-        want.append(ost.forward(ost.embed(np.array([tok])), [0], [T + i]))
-    st = make_stage(s, 0, 16, True, False, w, max_slots=1, max_ctx=2048, max_tokens=512, kv_f32=True)
+    toks = fx.tokens(fx.SEED_TOKENS, fx.token_stream(3), n_dec, s.vocab)
+    emb = fx.draw_weight(s, "embed")
+    x_rows = o.bf16_to_f32(emb[np.concatenate([prompt, toks])])
+    say(f"8B first stage, 16 blocks, {kv} cache: oracle")
+    want = oracle_layer_major(s, 0, 16, kv, x_rows,
+                              lambda b: {(r, b): fx.draw_weight(s, r, b, gain_sigma=0.1) for r in fx.BLOCK_ROLES})
+    st = Stage(s, 0, 16, True, False, max_slots=1, max_ctx=2048, max_tokens=512, kv=kv)
+    fill_weights_on_gpu(st, s, (0, 16), True, False, 0.1)
     dev = torch.device("cuda")
     got = [st.prefill(st.embed(torch.tensor(prompt, dtype=torch.int32, device=dev)), 0, 0).cpu().numpy()]
     for i, tok in enumerate(toks):
         xg = st.embed(torch.tensor([tok], dtype=torch.int32, device=dev))
         got.append(st.decode(xg, torch.tensor([0], dtype=torch.int32, device=dev),
                              torch.tensor([T + i], dtype=torch.int32, device=dev)).cpu().numpy())
-    for i, (g, wv) in enumerate(zip(got, want)):
+    wants = [want[:T]] + [want[T + i:T + i + 1] for i in range(n_dec)]
+    for i, (g, wv) in enumerate(zip(got, wants)):
         e = rel_l2(g, wv)
-        say(f"  step {i} rel L2 {e:.2e}")
+        say(f"  step {i} rel L2 (worst row) {e:.2e}")
         assert e <= TOL
+    assert st.device_errors() == 0
+
+
+def test_70b_stage_all_20_blocks_f16_cache():
+    # the 70B-shaped middle stage at full depth (blocks 20..39, d 8192, 64 q / 8 KV heads, SwiGLU
+    # 28672) on the binary16 cache its benchmark runs: a 16-row prefill (GEMM path) and two B = 1
+    # decode steps (GEMV path), against the oracle through all 20 blocks
+    s = fx.LLAMA70B
+    T, n_dec, kv = 16, 2, "f16"
+    x_rows = hidden_rows(11, T + n_dec, s.d_model)
+    say("70B-shaped stage, 20 blocks, f16 cache: oracle")
+    want = oracle_layer_major(s, 20, 40, kv, x_rows,
+                              lambda b: {(r, b): fx.draw_weight(s, r, b, gain_sigma=0.1) for r in fx.BLOCK_ROLES})
+    st = Stage(s, 20, 40, False, False, max_slots=1, max_ctx=64, max_tokens=64, kv=kv)
+    fill_weights_on_gpu(st, s, (20, 40), False, False, 0.1)
+    dev = torch.device("cuda")
+    got = [st.prefill(torch.from_numpy(x_rows[:T]).to(dev), 0, 0).cpu().numpy()]
+    for i in range(n_dec):
+        got.append(st.decode(torch.from_numpy(x_rows[T + i:T + i + 1]).to(dev),
+                             torch.tensor([0], dtype=torch.int32, device=dev),
+                             torch.tensor([T + i], dtype=torch.int32, device=dev)).cpu().numpy())
+    wants = [want[:T]] + [want[T + i:T + i + 1] for i in range(n_dec)]
+    for i, (g, wv) in enumerate(zip(got, wants)):
+        e = rel_l2(g, wv)
+        say(f"  step {i} rel L2 (worst row) {e:.2e}")
+        assert e <= TOL
+    assert st.device_errors() == 0

@@ -28,14 +28,14 @@ def oracle_stage(w, begin, end, first, last, max_ctx=64, kv_dtype="bf16"):
     return o.Stage(o.Dims.of(TINY), begin, end, first, last, w, max_ctx, kv_dtype=kv_dtype)
 
 
-@pytest.mark.parametrize("kv_f32", [False, True])
-def test_tiny_greedy_parity(weights, kv_f32):
+@pytest.mark.parametrize("kv", ["bf16", "f32", "f16"])
+def test_tiny_greedy_parity(weights, kv):
     prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(0), 16, TINY.vocab)
     say("tiny greedy: oracle")
-    want_toks, want = o.generate([oracle_stage(weights, 0, 2, True, True, kv_dtype="f32" if kv_f32 else "bf16")],
+    want_toks, want = o.generate([oracle_stage(weights, 0, 2, True, True, kv_dtype=kv)],
                                  prompt, 8)
     say("tiny greedy: gpu")
-    st = make_stage(TINY, 0, 2, True, True, weights, max_slots=2, max_ctx=64, max_tokens=16, kv_f32=kv_f32)
+    st = make_stage(TINY, 0, 2, True, True, weights, max_slots=2, max_ctx=64, max_tokens=16, kv=kv)
     got_toks, got = gpu_generate([st], prompt, 8)
     for step in range(8):
         for key in ("logits", "final_hidden", "residual"):
@@ -47,10 +47,10 @@ def test_tiny_greedy_parity(weights, kv_f32):
     assert st.device_errors() == 0
 
 
-@pytest.mark.parametrize("kv_f32", [False, True])
-def test_tiny_split_equals_unsplit_on_gpu(weights, kv_f32):
+@pytest.mark.parametrize("kv", ["bf16", "f32", "f16"])
+def test_tiny_split_equals_unsplit_on_gpu(weights, kv):
     prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(1), 16, TINY.vocab)
-    kw = dict(max_slots=1, max_ctx=64, max_tokens=16, kv_f32=kv_f32)
+    kw = dict(max_slots=1, max_ctx=64, max_tokens=16, kv=kv)
     whole = make_stage(TINY, 0, 2, True, True, weights, **kw)
     t1, tr1 = gpu_generate([whole], prompt, 8)
     a = make_stage(TINY, 0, 1, True, False, weights, **kw)
@@ -111,11 +111,12 @@ def test_tiny_chunked_prefill_and_decode(weights):
         assert rel_l2(g, w) <= TOL
 
 
-@pytest.mark.parametrize("B,kv_f32", [(2, False), (4, False), (6, False), (9, False), (3, True), (9, True)])
-def test_tiny_batched_decode(weights, B, kv_f32):
+@pytest.mark.parametrize("B,kv", [(2, "bf16"), (4, "bf16"), (6, "bf16"), (9, "bf16"), (3, "f32"), (9, "f32"),
+                                  (1, "f16"), (3, "f16"), (9, "f16")])
+def test_tiny_batched_decode(weights, B, kv):
     # slots prefilled to different lengths, then one decode step for all rows at once
-    ost = oracle_stage(weights, 0, 2, False, False, kv_dtype="f32" if kv_f32 else "bf16")
-    st = make_stage(TINY, 0, 2, False, False, weights, max_slots=B, max_ctx=64, max_tokens=64, kv_f32=kv_f32)
+    ost = oracle_stage(weights, 0, 2, False, False, kv_dtype=kv)
+    st = make_stage(TINY, 0, 2, False, False, weights, max_slots=B, max_ctx=64, max_tokens=64, kv=kv)
     lens = [3 + 5 * b for b in range(B)]
     for b, n in enumerate(lens):
         x = hidden_rows(10 + b, n, TINY.d_model)
@@ -142,15 +143,40 @@ def test_tiny_determinism(weights):
     assert all(a.tobytes() == b.tobytes() for a, b in zip(tr1["logits"], tr2["logits"]))
 
 
-def test_device_side_range_checks(weights):
-    st = make_stage(TINY, 0, 2, True, False, weights, max_slots=2, max_ctx=64, max_tokens=4)
+@pytest.mark.parametrize("bad", ["slot", "position"])
+def test_device_side_range_checks(weights, bad):
+    # the documented per-row contract: an out-of-range token id embeds a zero row (one error); a
+    # decode row with an out-of-range slot or position writes no K/V and gets a zero attention
+    # output, so each block passes it on as x + MLP(x) (one error per block); the other rows are
+    # exactly what they are in a call where every row is valid
     dev = torch.device("cuda")
+    kw = dict(max_slots=2, max_ctx=64, max_tokens=4)
+    st = make_stage(TINY, 0, 2, True, False, weights, **kw)
+    ref = make_stage(TINY, 0, 2, True, False, weights, **kw)
     st.device_errors(reset=True)
-    st.embed(torch.tensor([5, TINY.vocab, -1], dtype=torch.int32, device=dev))
-    x = torch.zeros((2, TINY.d_model), dtype=torch.float32, device=dev)
-    st.decode(x, torch.tensor([0, 7], dtype=torch.int32, device=dev), torch.tensor([3, 1], dtype=torch.int32, device=dev))
-    torch.cuda.synchronize()
-    assert st.device_errors() >= 3
+    rows = st.embed(torch.tensor([5, TINY.vocab, -1], dtype=torch.int32, device=dev)).cpu().numpy()
+    assert st.device_errors(reset=True) == 2
+    assert not rows[1:].any()
+    np.testing.assert_array_equal(rows[0], o.bf16_to_f32(weights[("embed", -1)][5]))
+    x = hidden_rows(7, 2, TINY.d_model)
+    xt = torch.from_numpy(x).to(dev)
+    good = ref.decode(xt, torch.tensor([0, 1], dtype=torch.int32, device=dev),
+                      torch.tensor([3, 1], dtype=torch.int32, device=dev)).cpu().numpy()
+    slots, pos = ([0, 7], [3, 1]) if bad == "slot" else ([0, 1], [3, 128])   # 128: past the cache
+    got = st.decode(xt, torch.tensor(slots, dtype=torch.int32, device=dev),
+                    torch.tensor(pos, dtype=torch.int32, device=dev)).cpu().numpy()
+    assert st.device_errors(reset=True) == 2                  # one per block
+    assert ref.device_errors() == 0
+    assert got[0].tobytes() == good[0].tobytes()
+    ost = oracle_stage(weights, 0, 2, True, False)
+    want = x[1:2]
+    for b in range(2):                                        # x <- x + MLP_b(x), block by block
+        want = (want + ost.mlp(b, want)).astype(np.float32)
+    assert rel_l2(got[1:2], want) <= TOL
+    # the bad row wrote nothing: slot 1's cache is still empty where the row would have gone
+    if bad == "position":
+        k, v = kv_bits(st, 0, 1, 2)
+        assert not k.any() and not v.any()
 
 
 @pytest.mark.parametrize("hq,hkv,dh", [(4, 4, 64), (16, 1, 128), (8, 2, 128)])

@@ -6,7 +6,8 @@
   sublayer (rel L2 <= 1e-3).  With an F32 cache the slice sum must also equal the GPU's full
   sublayer up to F32 reassociation (rel L2 <= 1e-5).  With a bf16 cache it need not: the slice and
   full projections sum in different orders, so a few K/V values round to neighbouring bf16 values
-  (measured up to 2.7e-4 on one 8B slice), the cache-rounding effect the oracle bound covers.
+  (measured up to 2.7e-4 on one 8B slice), the cache-rounding effect the oracle bound covers; the
+  same holds for a binary16 cache.
   The sublayer itself plus stage_mlp reproduces stage_prefill's block bit for bit.
 * Vocabulary: slices of the embedding (zero-padded to a multiple of the slice count) summed by
   stage_embed_range reproduce the full embedding bit for bit; readout slices concatenated and cut
@@ -35,9 +36,9 @@ def attn_weights(s, block=0):
     return w
 
 
-@pytest.mark.parametrize("kv_f32", [False, True])
+@pytest.mark.parametrize("kv", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("name,n,T", [("tiny", 2, 24), ("tiny", 4, 24), ("8b", 8, 64), ("8b", 16, 20)])
-def test_attention_head_slices_sum_to_full(name, n, T, kv_f32):
+def test_attention_head_slices_sum_to_full(name, n, T, kv):
     s = fx.TINY if name == "tiny" else fx.LLAMA8B
     w = attn_weights(s)
     dh = s.head_dim
@@ -46,7 +47,7 @@ def test_attention_head_slices_sum_to_full(name, n, T, kv_f32):
     sl = o.head_shards(s.n_q_heads, s.n_kv_heads, n)
     hq, hk = sl[0][1], sl[0][3]
     st = Stage(slice_shape(s, hq, hk, n_blocks=n), 0, n, False, False, max_slots=1, max_ctx=64, max_tokens=64,
-               kv_f32=kv_f32)
+               kv=kv)
     for i, (q0, _, kv0, _) in enumerate(sl):
         qr, kr = slice(q0 * dh, (q0 + hq) * dh), slice(kv0 * dh, (kv0 + hk) * dh)
         st.load_weight("attn_norm", i, w["attn_norm"])
@@ -58,13 +59,13 @@ def test_attention_head_slices_sum_to_full(name, n, T, kv_f32):
     for i in range(n):                                   # ((p0 + p1) + p2) + ... in slice order
         st.attn(i, xt, 0, 0, out=acc, accumulate=i > 0)
     full_st = Stage(slice_shape(s, s.n_q_heads, s.n_kv_heads), 0, 1, False, False, max_slots=1, max_ctx=64,
-                    max_tokens=64, kv_f32=kv_f32)
+                    max_tokens=64, kv=kv)
     for r, t in w.items():
         full_st.load_weight(r, 0, t)
     full = full_st.attn(0, xt, 0, 0).cpu().numpy()
     got = acc.cpu().numpy()
     c = o.Dims.of(s)
-    kvd = "f32" if kv_f32 else "bf16"
+    kvd = kv
     want = o.attn_sublayer(x, w["attn_norm"], w["wq"], w["wk"], w["wv"], w["wo"], dh, c.rms_eps, c.rope_theta, kvd)
     _, want_sum = o.attn_slices(x, w["attn_norm"], w["wq"], w["wk"], w["wv"], w["wo"], dh, c.rms_eps,
                                 c.rope_theta, n, kvd)
@@ -72,7 +73,7 @@ def test_attention_head_slices_sum_to_full(name, n, T, kv_f32):
     say(f"{name} attention over {n} head slices, T={T}, {kvd} cache: slices vs full (gpu) {e_gpu:.2e}; "
         f"full vs oracle {e_full:.2e}; slices vs oracle {e_sum:.2e}")
     assert e_full <= 1e-3 and e_sum <= 1e-3
-    if kv_f32:
+    if kv == "f32":
         assert e_gpu <= 1e-5
 
 
