@@ -1,15 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark of one pipeline stage's decoder forward on one MI355X.
 
-Workload (default): the 8B-shaped first stage -- token embedding + blocks 0..15 of a 32-block
-decoder (d 4096, 32 q / 8 KV heads, head dim 128, SwiGLU 14336, vocabulary 128256), seeded
-synthetic bf16 weights N(0, 0.02) and uniform tokens, batch 1: prefill of a 512-token prompt, then
-teacher-forced decode one token at a time up to context 2048.  One step = that whole request.
+Workload (default): the 70B-shaped middle stage -- blocks 20..39 of an 80-block decoder (d 8192,
+64 q / 8 KV heads, head dim 128, SwiGLU 28672), seeded synthetic bf16 weights N(0, 0.02), binary16
+KV cache.  One step = one 4096-token prefill chunk (a fresh sequence) plus one batched decode step of
+128 rows at context 8192 (slots filled by two 4096-token prefill chunks and copies).
 
 Prints ONE JSON line.  `value` is the decode throughput (tokens/s, inputs resident in HBM); the
-line also carries the prefill throughput, the dominant decode kernel's roofline (HBM bytes per
-launch / its average duration, timed live with HIP events on the launch stream) and the CPU
-oracle timed on this host's cores over a bounded sample.
+line also carries the prefill throughput, the dominant kernel's roofline (the prefill gate/up GEMM:
+algorithmic flops per launch / its average duration, timed live with HIP events on the launch stream
+over the timed region), the decode attention kernel's HBM roofline, the CPU oracle timed on this
+host's cores over a bounded sample, and the 8B-shaped first stage's figures (prefill 512, decode to
+2048, batch 1) under "first_8b".
 """
 from __future__ import annotations
 
@@ -52,43 +54,6 @@ def fill_weights(st, shape, blocks, first, last, seed, gain_sigma=0.0):
     del scratch
 
 
-def cpu_baseline_decode(shape, ctx: int, n_blocks: int, seconds: float = 10.0, ctx_lo: int = 512):
-    """The oracle, as it stands, on this host: one block's B = 1 decode step at contexts spread
-    over [ctx_lo, ctx] (the workload's decode range), repeated for about `seconds` of CPU work;
-    per-token time = n_blocks x the mean per-block time."""
-    import numpy as np
-
-    import fixtures as fx
-    from oracle import decoder as o
-
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    w = fx.draw_stage_weights(shape, 0, 1, False, False)
-    st = o.Stage(o.Dims.of(shape), 0, 1, False, False, w, ctx + 1)
-    kshape = (1, ctx + 1, shape.n_kv_heads, shape.head_dim)
-    kv = o.round_bf16(fx.normal_f32(fx.SEED_HIDDEN, 0x7000, int(np.prod(kshape))).reshape(kshape))
-    st.import_kv(0, 0, 0, kv[0], kv[0].copy())
-    x = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(0), shape.d_model).reshape(1, shape.d_model)
-    positions = [ctx_lo + (ctx - ctx_lo) * i // 3 for i in range(4)]   # spread over the decode range
-    st.forward(x, [0], [ctx])                     # warm caches
-    reps = 0
-    t0 = time.perf_counter()
-    while reps < 4 or time.perf_counter() - t0 < seconds:
-        st.forward(x, [0], [positions[reps % len(positions)]])
-        reps += 1
-    elapsed = time.perf_counter() - t0
-    per_block = elapsed / reps
-    per_token = per_block * n_blocks
-    return {"value": 1.0 / per_token, "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"{reps} decode steps ({elapsed:.1f} s) of 1 of {n_blocks} blocks at contexts "
-                      f"{positions} in turn (B=1); tok/s = 1 / ({n_blocks} x {per_block:.3f} s per "
-                      f"block-step), extrapolated linearly over blocks",
-            "seconds_per_block_step": per_block, "cpu_model": cpu_model()}
-
-
 def cpu_model() -> str:
     """The host CPU's model name (first 'model name' line of /proc/cpuinfo), or 'unknown'."""
     try:
@@ -102,28 +67,31 @@ def cpu_model() -> str:
 
 GEMV_SOURCES = ("pipeline_stage_decoder_amd/csrc/kernels_gemv.hip", "pipeline_stage_decoder_amd/csrc/common.h",
                 "pipeline_stage_decoder_amd/csrc/norm.h")
+GEMM_SOURCES = ("pipeline_stage_decoder_amd/csrc/kernels_gemm.hip", "pipeline_stage_decoder_amd/csrc/common.h",
+                "pipeline_stage_decoder_amd/csrc/norm.h")
 COUNTER_FILE = os.path.join(ROOT, "profiles", "decode_gemv_gateup_8b_counters.txt")
+GEMM_COUNTER_FILE = os.path.join(ROOT, "profiles", "prefill_gemm_gateup_70b_traffic_counters.txt")
 
 
-def gemv_source_hash() -> str:
+def source_hash(sources) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in GEMV_SOURCES:
+    for f in sources:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def counter_traffic():
-    """HBM bytes per launch of the gate/up GEMV from the committed counter summary: FETCH_SIZE and
+def counter_traffic(path: str, kernel: str, sources):
+    """HBM bytes per launch of a kernel from a committed counter summary: its FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch) scaled by what the same counters read for a plain 1 GiB copy.
-    None when the summary is missing or was taken on another version of the kernel source."""
+    None when the summary is missing or was taken on another version of the kernel's sources."""
     try:
-        kv = dict(line.split(":", 1) for line in open(COUNTER_FILE) if ":" in line and not line.startswith("#"))
+        kv = dict(line.split(":", 1) for line in open(path) if ":" in line and not line.startswith("#"))
         kv = {k.strip(): v.strip() for k, v in kv.items()}
-        if kv.get("kernel_source_sha256_16") != gemv_source_hash():
+        if kv.get("kernel_source_sha256_16") != source_hash(sources):
             return None
-        fetch = float(kv["gateup_fetch_kib"]) * 1048576.0 / float(kv["copy_fetch_kib"])
-        write = float(kv["gateup_write_kib"]) * 1048576.0 / float(kv["copy_write_kib"])
+        fetch = float(kv[f"{kernel}_fetch_kib"]) * 1048576.0 / float(kv["copy_fetch_kib"])
+        write = float(kv[f"{kernel}_write_kib"]) * 1048576.0 / float(kv["copy_write_kib"])
         return round((fetch + write) * 1024.0)
     except (OSError, KeyError, ValueError):
         return None
@@ -200,7 +168,7 @@ def time_handoff(rows_prefill, row_decode, reps: int = 50) -> dict:
     return out
 
 
-def counter_pass(shape, blocks, T, dev, n_dec: int = 32):
+def counter_pass(shape, blocks, T, dev, n_dec: int = 32, kv: str = "f16"):
     """The workload's kernels for a hardware-counter run: one prefill of T tokens, then n_dec eager
     B = 1 decode steps, no timing events; progress every 8 steps."""
     import torch
@@ -209,7 +177,7 @@ def counter_pass(shape, blocks, T, dev, n_dec: int = 32):
     from pipeline_stage_decoder_amd.stage import Stage
 
     st = Stage(shape, blocks[0], blocks[1], True, False, max_slots=1, max_ctx=T + n_dec, max_tokens=T, device=0,
-               kv_f32=True)
+               kv=kv)
     fill_weights(st, shape, blocks, True, False, fx.SEED_WEIGHTS)
     prompt = fx.tokens_gpu(torch.empty(T, dtype=torch.int32, device=dev), fx.SEED_TOKENS, fx.token_stream(0),
                            shape.vocab)
@@ -230,7 +198,7 @@ def counter_pass(shape, blocks, T, dev, n_dec: int = 32):
     print(json.dumps({"phase": "counters", "prefill_tokens": T, "decode_steps": n_dec}), flush=True)
 
 
-def prefill_only(args, shape, blocks, T, dev, stream, first=True, kv_f32=None):
+def prefill_only(args, shape, blocks, T, dev, stream, first=True):
     """Time the prefill alone: stage sized for one T-token prompt, W warmups then K timed prefills.
     A first stage embeds seeded tokens; any other stage takes seeded F32 N(0,1) hidden rows."""
     import numpy as np
@@ -240,10 +208,8 @@ def prefill_only(args, shape, blocks, T, dev, stream, first=True, kv_f32=None):
     from pipeline_stage_decoder_amd import accounting as acc
     from pipeline_stage_decoder_amd.stage import Stage
 
-    if kv_f32 is None:
-        kv_f32 = args.kv == "f32"
     st = Stage(shape, blocks[0], blocks[1], first, False, max_slots=1, max_ctx=T, max_tokens=T, device=0,
-               kv_f32=kv_f32)
+               kv=args.kv)
     fill_weights(st, shape, blocks, first, False, fx.SEED_WEIGHTS)
     xin = torch.empty((T, shape.d_model), dtype=torch.float32, device=dev)
     hout = torch.empty_like(xin)
@@ -273,7 +239,7 @@ def prefill_only(args, shape, blocks, T, dev, stream, first=True, kv_f32=None):
     pre_ms = float(np.median(ms))
     flops = acc.prefill_flops(shape, blocks[1] - blocks[0], T)
     print(json.dumps({"phase": "prefill", "prefill_tokens": T, "blocks": list(blocks),
-                      "kv_cache": "f32" if kv_f32 else "bf16", "prefill_ms": round(pre_ms, 3),
+                      "kv_cache": args.kv, "prefill_ms": round(pre_ms, 3),
                       "prefill_tok_s": round(T / (pre_ms / 1e3), 1),
                       "prefill_tflops": round(flops / (pre_ms / 1e3) / 1e12, 1),
                       "prefill_mfma_frac": round(flops / (pre_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}),
@@ -359,7 +325,8 @@ def batched_decode_line(args, workload: str, shape, blocks, first: bool, last: b
     d = shape.d_model
     log(f"[bench] {workload}: creating stage {blocks}, {B} slots, ctx {ctx}")
     st = Stage(shape, blocks[0], blocks[1], first, last, max_slots=B, max_ctx=ctx + 1,
-               max_tokens=max(B, prefill_chunk), device=0)
+               max_tokens=max(B, prefill_chunk), device=0, kv=args.kv)
+    kvb = 4 if args.kv == "f32" else 2
     fill_weights(st, shape, blocks, first, last, fx.SEED_WEIGHTS)
     pre = {}
     if time_prefill:
@@ -415,10 +382,10 @@ def batched_decode_line(args, workload: str, shape, blocks, first: bool, last: b
     step()
     torch.cuda.synchronize()
     kt = stage_kernel_ms(st, kinds)
-    step_bytes = acc.decode_step_bytes(shape, nb, [ctx] * B, first=first, last=last)
-    kv_launch = B * (ctx + 1) * acc.kv_bytes_per_token_block(shape)
+    step_bytes = acc.decode_step_bytes(shape, nb, [ctx] * B, first=first, last=last, kv_elem_bytes=kvb)
+    kv_launch = B * (ctx + 1) * acc.kv_bytes_per_token_block(shape, kvb)
     roof = kernel_roofline(kv_launch, kt["attn"][0], kt["attn"][1],
-                           "k_attn_decode + k_attn_merge (split-KV GQA decode over the slots' bf16 caches)")
+                           f"k_attn_decode + k_attn_merge (split-KV GQA decode over the slots' {args.kv} caches)")
     gbs = step_bytes / (ms / 1e3) / 1e9
     return {
         "metric": "stage decode tok/s & HBM GB/s %peak; prefill tok/s & MFMA util",
@@ -427,7 +394,7 @@ def batched_decode_line(args, workload: str, shape, blocks, first: bool, last: b
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: seeded N(0,0.02) bf16 weights, F32 N(0,1) hidden rows",
         "config": {"workload": workload, "batch": B, "decode_ctx": ctx, "blocks": list(blocks),
-                   "kv_cache": "bf16", "decode_graph": True},
+                   "kv_cache": args.kv, "decode_graph": True},
         "decode_step_bytes": step_bytes, "decode_hbm_gbs": round(gbs, 1),
         "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "kernel_ms_per_step": {k: round(v[1], 3) for k, v in kt.items()},
@@ -532,7 +499,7 @@ def attn_parallel_line(args) -> dict:
         return t.view(*shape)
 
     w = {r: gpu_weight(r, fx.role_shape(s, r)) for r in ("attn_norm", "wq", "wk", "wv", "wo")}
-    st = Stage(s, 0, 1, False, False, max_slots=2, max_ctx=T, max_tokens=T, device=0)
+    st = Stage(s, 0, 1, False, False, max_slots=2, max_ctx=T, max_tokens=T, device=0, kv=args.kv)
     for r, t in w.items():
         st.load_weight(r, 0, t)
     x = fx.normal_f32_gpu(torch.empty((T, d), dtype=torch.float32, device="cuda"), fx.SEED_HIDDEN,
@@ -554,7 +521,7 @@ def attn_parallel_line(args) -> dict:
     log("[bench] attn-parallel: 8 head slices against the full sublayer")
     hq_s, hk_s = hq // n, max(hkv // n, 1)
     sh = fx.Shape(d, hq_s, hk_s, dh, 64, V, n)
-    sl = Stage(sh, 0, n, False, False, max_slots=1, max_ctx=512, max_tokens=512, device=0)
+    sl = Stage(sh, 0, n, False, False, max_slots=1, max_ctx=512, max_tokens=512, device=0, kv=args.kv)
     for i in range(n):
         qr = slice(i * hq_s * dh, (i + 1) * hq_s * dh)
         kr = slice((i * hkv // n) * dh, (i * hkv // n + hk_s) * dh)
@@ -661,8 +628,10 @@ def pipeline_line(args) -> dict:
 
     shape = fx.LLAMA8B
     plen, n_new = 128, 128
-    stages = [S.Stage(shape, 0, 16, True, False, max_slots=2, max_ctx=plen + n_new, max_tokens=plen, device=0),
-              S.Stage(shape, 16, 32, False, True, max_slots=2, max_ctx=plen + n_new, max_tokens=plen, device=0)]
+    stages = [S.Stage(shape, 0, 16, True, False, max_slots=2, max_ctx=plen + n_new, max_tokens=plen, device=0,
+                      kv=args.kv),
+              S.Stage(shape, 16, 32, False, True, max_slots=2, max_ctx=plen + n_new, max_tokens=plen, device=0,
+                      kv=args.kv)]
     fill_weights(stages[0], shape, (0, 16), True, False, fx.SEED_WEIGHTS)
     fill_weights(stages[1], shape, (16, 32), False, True, fx.SEED_WEIGHTS)
     prompts = torch.stack([fx.tokens_gpu(torch.empty(plen, dtype=torch.int32, device="cuda"), fx.SEED_TOKENS,
@@ -705,36 +674,324 @@ def pipeline_line(args) -> dict:
     }
 
 
+PREFILL_KINDS = ("norm", "qkv", "attn", "o", "gateup", "down")
+DECODE_KINDS = ("qkv", "attn", "o", "gateup", "down")
+
+
+def issued_mfma_flops(shape, n_blocks: int, T: int, kv: str, pos0: int = 0) -> int:
+    """MFMA work a prefill issues: activation operands enter as bf16 planes -- three for QKV over a
+    2-byte cache, two otherwise -- so each projection executes planes x its algorithmic flops;
+    attention takes 2 products per score / output term (3 over the F32-grade cache's pairs)."""
+    from pipeline_stage_decoder_amd import accounting as acc
+    lin = 0
+    for kind, (n, k) in acc.projection_shapes(shape).items():
+        if kind == "readout":
+            continue
+        planes = (2 if kv == "f32" else 3) if kind == "qkv" else 2
+        lin += 2 * T * n * k * planes
+    attn = acc.prefill_flops(shape, 1, T, pos0=pos0) - acc.prefill_flops(shape, 1, T, pos0=pos0, attn=False)
+    return n_blocks * (lin + attn * (3 if kv == "f32" else 2))
+
+
+def cpu_baseline_70b(shape, kv: str, n_blocks: int, T: int, B: int, ctx: int, seconds: float = 4.0) -> dict:
+    """The oracle, as it stands, on this host, on one real-shape block of the stage: a 64-row
+    prefill (positions 0..63 of a fresh sequence) and a B = 2 decode step at position ctx over a
+    seeded cache of ctx positions per slot, each repeated for about `seconds`; tok/s of the whole
+    stage extrapolated linearly over blocks (and, for the prefill, over tokens: the timed chunk's
+    rows attend up to T keys, the sample's up to 64, so attention -- about 4% of the chunk's
+    flops -- is under-counted)."""
+    import numpy as np
+
+    import fixtures as fx
+    from oracle import decoder as o
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    blk = 20
+    w = {(r, blk): fx.draw_weight(shape, r, blk) for r in fx.BLOCK_ROLES}
+    st = o.Stage(o.Dims.of(shape), blk, blk + 1, False, False, w, ctx + 1, kv_dtype=kv)
+    n_s, b_s = 64, 2
+    shp = (ctx, shape.n_kv_heads, shape.head_dim)
+    for slot in range(b_s):
+        k = o.KV_FORMATS[kv](fx.normal_f32(fx.SEED_HIDDEN, 0x7000 + 2 * slot, int(np.prod(shp))).reshape(shp))
+        v = o.KV_FORMATS[kv](fx.normal_f32(fx.SEED_HIDDEN, 0x7001 + 2 * slot, int(np.prod(shp))).reshape(shp))
+        st.import_kv(blk, slot, 0, k, v)
+    xp = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(B), n_s * shape.d_model).reshape(n_s, shape.d_model)
+    xd = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(1000), b_s * shape.d_model).reshape(b_s, shape.d_model)
+
+    def timed(fn):
+        fn()
+        reps, t0 = 0, time.perf_counter()
+        while reps < 1 or time.perf_counter() - t0 < seconds:
+            fn()
+            reps += 1
+        return (time.perf_counter() - t0) / reps, reps
+
+    t_pre, r_pre = timed(lambda: st.prefill(xp, b_s, 0))
+    t_dec, r_dec = timed(lambda: st.forward(xd, np.arange(b_s), np.full(b_s, ctx)))
+    return {"value": b_s / (t_dec * n_blocks), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"decode: {r_dec} B={b_s} steps at position {ctx} of 1 of {n_blocks} blocks "
+                      f"({t_dec:.2f} s per block-step); prefill: {r_pre} {n_s}-row prefills of 1 block "
+                      f"({t_pre:.2f} s each); tok/s extrapolated linearly over the stage's {n_blocks} blocks "
+                      f"(and the prefill over tokens, to a {T}-token chunk)",
+            "prefill_value": n_s / (t_pre * n_blocks), "prefill_unit": "tok/s",
+            "seconds_per_block_decode_step": t_dec, "seconds_per_block_prefill_64": t_pre,
+            "cpu_model": cpu_model()}
+
+
+def stage70b_line(args) -> dict:
+    """The 70B-shaped middle stage (blocks 20..39 of 80): one step = a 4096-token prefill chunk (a
+    fresh sequence, positions 0..4095) plus one batched decode step, B = 128 rows at position 8192
+    of slots holding 8192 cached positions each."""
+    import numpy as np
+    import torch
+
+    import fixtures as fx
+    from pipeline_stage_decoder_amd import accounting as acc
+    from pipeline_stage_decoder_amd.stage import Stage
+
+    shape, blocks, B, ctx, T = fx.LLAMA70B, (20, 40), 128, 8192, 4096
+    nb, d, kv = blocks[1] - blocks[0], fx.LLAMA70B.d_model, args.kv
+    kvb = 4 if kv == "f32" else 2
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    log(f"[bench] 70B-shaped stage {blocks}, {kv} cache: creating ({B + 1} slots, ctx {ctx + 1})")
+    st = Stage(shape, blocks[0], blocks[1], False, False, max_slots=B + 1, max_ctx=ctx + 1, max_tokens=T,
+               device=0, kv=kv)
+    fill_weights(st, shape, blocks, False, False, fx.SEED_WEIGHTS)
+    log("[bench] filling slot 0 with two 4096-token chunks, then copying it into the other decode slots")
+    fill_kv_by_prefill(st, 0, ctx, T, range(1, B), d)
+    xp = fx.normal_f32_gpu(torch.empty((T, d), dtype=torch.float32, device=dev), fx.SEED_HIDDEN,
+                           fx.hidden_stream(B), 0)
+    yp = torch.empty_like(xp)
+    xd = fx.normal_f32_gpu(torch.empty((B, d), dtype=torch.float32, device=dev), fx.SEED_HIDDEN,
+                           fx.hidden_stream(1000), 0)
+    yd = torch.empty_like(xd)
+    slots = torch.arange(B, dtype=torch.int32, device=dev)
+    pos = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    g = graph_of(lambda: st.decode(xd, slots, pos, out=yd), 1)
+    log("[bench] decode step captured as a HIP graph")
+
+    def run_step(ev):
+        ev[0].record(stream)
+        st.prefill(xp, B, 0, out=yp)              # slot B: a fresh sequence's first chunk
+        ev[1].record(stream)
+        g.replay()                                # B rows of slots 0..B-1 at position ctx
+        ev[2].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]  # noqa: E731
+    for w in range(args.warmup):
+        run_step(mk())
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {w + 1}/{args.warmup}")
+    # the roofline kernel (gate/up GEMM + SwiGLU of the prefill chunk) is timed live with HIP events
+    # on the launch stream, over the timed region itself
+    st.timing(["gateup"])
+    evs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev = mk()
+        run_step(ev)
+        evs.append(ev)
+        if k % 5 == 4 or k == args.steps - 1:
+            log(f"[bench] timed step {k + 1}/{args.steps} enqueued")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n_gu, ms_gu = st.timing_read("gateup")
+    st.timing([])
+    pre_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    step_ms = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
+
+    # per-kind kernel time of one step: one eager prefill and one eager decode step, every kind timed
+    log("[bench] per-kind kernel times over one eager step")
+    st.timing(list(PREFILL_KINDS))
+    st.prefill(xp, B, 0, out=yp)
+    torch.cuda.synchronize()
+    pre_kinds = {k: st.timing_read(k) for k in PREFILL_KINDS}
+    st.timing(list(DECODE_KINDS))
+    st.decode(xd, slots, pos, out=yd)
+    torch.cuda.synchronize()
+    dec_kinds = {k: st.timing_read(k) for k in DECODE_KINDS}
+    st.timing([])
+
+    pre_flops = acc.prefill_flops(shape, nb, T)
+    dec_bytes = acc.decode_step_bytes(shape, nb, [ctx] * B, kv_elem_bytes=kvb)
+    gu_flops = acc.projection_flops(shape, "gateup", T)
+    gu_avg_s = ms_gu / 1e3 / max(n_gu, 1)
+    gu_tf = gu_flops / gu_avg_s / 1e12
+    roofline = {"bound": "mfma", "achieved": round(gu_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": counter_traffic(GEMM_COUNTER_FILE, "gateup", GEMM_SOURCES),
+                "kernel": "k_gemm_dma (gate/up projection + SwiGLU of the 4096-token chunk, 256 x 256 tiles, "
+                          "ping-pong schedule)",
+                "flops_per_launch": gu_flops, "algorithmic_bytes_per_launch": acc.projection_gemm_bytes(shape, "gateup", T),
+                "avg_launch_us": round(gu_avg_s * 1e6, 2), "launches": n_gu,
+                "issued_frac": round(2 * gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                "share_of_step": round(pre_kinds["gateup"][1] / step_ms, 4)}
+    n_at, ms_at = dec_kinds["attn"]
+    at_bytes = B * (ctx + 1) * acc.kv_bytes_per_token_block(shape, kvb)
+    roof_dec = kernel_roofline(at_bytes, n_at, ms_at,
+                               f"k_attn_decode + k_attn_merge (split-KV GQA decode, B={B} at ctx {ctx}, {kv} cache)")
+    dec_gbs = dec_bytes / (dec_ms / 1e3) / 1e9
+    pre_tf = pre_flops / (pre_ms / 1e3) / 1e12
+    return {
+        "metric": "stage decode tok/s & HBM GB/s %peak; prefill tok/s & MFMA util",
+        "value": round(B / (dec_ms / 1e3), 1), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,0.02) bf16 weights, F32 N(0,1) hidden rows (random-init weights, no dataset)",
+        "config": {"workload": "70B-shaped middle stage: blocks 20..39 of 80, d 8192, 64 q / 8 KV heads, head dim 128, "
+                               "SwiGLU 28672, bf16 weights; step = one 4096-token prefill chunk + one batched decode "
+                               "step B=128 at ctx 8192, F32 hidden in and out",
+                   "prefill_chunk": T, "decode_batch": B, "decode_ctx": ctx, "blocks": list(blocks), "kv_cache": kv,
+                   "decode_graph": True},
+        "decode_ms": round(dec_ms, 3), "decode_step_bytes": dec_bytes, "decode_hbm_gbs": round(dec_gbs, 1),
+        "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "prefill_tok_s": round(T / (pre_ms / 1e3), 1), "prefill_ms": round(pre_ms, 3),
+        "prefill_tflops": round(pre_tf, 1), "prefill_mfma_frac": round(pre_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "prefill_mfma_issued_frac": round(issued_mfma_flops(shape, nb, T, kv) / (pre_ms / 1e3) / 1e12
+                                          / MFMA_BF16_PEAK_TFLOPS, 4),
+        "prefill_kernel_ms": {k: round(v[1], 3) for k, v in pre_kinds.items()},
+        "decode_kernel_ms": {k: round(v[1], 3) for k, v in dec_kinds.items()},
+        "wall_s_timed": round(wall, 3), "roofline": roofline, "roofline_decode": roof_dec,
+    }
+
+
+def first8b_figures(args, reps: int = 3) -> dict:
+    """The 8B-shaped first stage (embedding + blocks 0..15 of 32), batch 1: a 512-token prefill, then
+    teacher-forced decode to ctx 2048 replayed from HIP graphs of 128 steps; `reps` timed requests."""
+    import numpy as np
+    import torch
+
+    import fixtures as fx
+    from pipeline_stage_decoder_amd import accounting as acc
+    from pipeline_stage_decoder_amd.stage import Stage
+
+    shape, blocks, T, ctx, kv = fx.LLAMA8B, (0, 16), 512, 2048, args.kv
+    n_dec = ctx - T
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    log(f"[bench] 8B-shaped first stage, {kv} cache")
+    st = Stage(shape, blocks[0], blocks[1], True, False, max_slots=1, max_ctx=ctx, max_tokens=T, device=0, kv=kv)
+    fill_weights(st, shape, blocks, True, False, fx.SEED_WEIGHTS)
+    prompt = fx.tokens_gpu(torch.empty(T, dtype=torch.int32, device=dev), fx.SEED_TOKENS, fx.token_stream(0),
+                           shape.vocab)
+    dec_tok = fx.tokens_gpu(torch.empty(n_dec, dtype=torch.int32, device=dev), fx.SEED_TOKENS,
+                            fx.token_stream(1), shape.vocab)
+    positions = torch.arange(T, ctx, dtype=torch.int32, device=dev)
+    slot0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    xin = torch.empty((T, shape.d_model), dtype=torch.float32, device=dev)
+    hout = torch.empty_like(xin)
+    x1 = torch.empty((1, shape.d_model), dtype=torch.float32, device=dev)
+    h1 = torch.empty_like(x1)
+    st.embed(dec_tok[:1], out=x1)
+    st.decode(x1, slot0, positions[:1], out=h1)
+    torch.cuda.synchronize()
+    graph_steps, graphs = 128, []
+    cs = torch.cuda.Stream()
+    for g0 in range(0, n_dec, graph_steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cs):
+            for i in range(g0, g0 + graph_steps):
+                st.embed(dec_tok[i:i + 1], out=x1)
+                st.decode(x1, slot0, positions[i:i + 1], out=h1)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    def run(ev):
+        ev[0].record(stream)
+        st.embed(prompt, out=xin)
+        st.prefill(xin, 0, 0, out=hout)
+        ev[1].record(stream)
+        for g in graphs:
+            g.replay()
+        ev[2].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]  # noqa: E731
+    run(mk())
+    torch.cuda.synchronize()
+    evs = []
+    for r in range(reps):
+        ev = mk()
+        run(ev)
+        torch.cuda.synchronize()
+        evs.append(ev)
+        log(f"[bench] 8B request {r + 1}/{reps}")
+    pre_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    dec_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    # the dominant decode kernel (gate/up GEMV + SwiGLU), timed live with HIP events over one eager
+    # decode pass of the request
+    st.embed(prompt, out=xin)
+    st.prefill(xin, 0, 0, out=hout)
+    st.timing(list(DECODE_KINDS))
+    kern = {k: [0, 0.0] for k in DECODE_KINDS}
+    for i in range(n_dec):
+        st.embed(dec_tok[i:i + 1], out=x1)
+        st.decode(x1, slot0, positions[i:i + 1], out=h1)
+        if i % 256 == 255 or i == n_dec - 1:
+            for k in DECODE_KINDS:
+                n, ms = st.timing_read(k)
+                kern[k][0] += n
+                kern[k][1] += ms
+    st.timing([])
+    kvb = 4 if kv == "f32" else 2
+    dec_bytes = sum(acc.decode_step_bytes(shape, 16, [c], first=True, kv_elem_bytes=kvb) for c in range(T, ctx))
+    dec_gbs = dec_bytes / (dec_ms / 1e3) / 1e9
+    pre_tf = acc.prefill_flops(shape, 16, T) / (pre_ms / 1e3) / 1e12
+    gu = kern["gateup"]
+    gu_bytes = acc.projection_bytes(shape, "gateup", 1)
+    out = {"workload": "8B-shaped first stage: embedding + blocks 0..15 of 32, d 4096, 32q/8kv heads, head dim 128, "
+                       "SwiGLU 14336, vocab 128256; batch 1, prefill 512 then decode to ctx 2048",
+           "kv_cache": kv, "requests_timed": reps,
+           "decode_tok_s": round(n_dec / (dec_ms / 1e3), 2), "decode_ms_per_token": round(dec_ms / n_dec, 4),
+           "decode_hbm_gbs": round(dec_gbs, 1), "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+           "prefill_tok_s": round(T / (pre_ms / 1e3), 1), "prefill_ms": round(pre_ms, 3),
+           "prefill_tflops": round(pre_tf, 1), "prefill_mfma_frac": round(pre_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+           "prefill_mfma_issued_frac": round(issued_mfma_flops(shape, 16, T, kv) / (pre_ms / 1e3) / 1e12
+                                             / MFMA_BF16_PEAK_TFLOPS, 4),
+           "decode_kernel_avg_us": {k: round(v[1] * 1e3 / max(v[0], 1), 2) for k, v in kern.items()},
+           "roofline_decode_gateup": kernel_roofline(gu_bytes, gu[0], gu[1],
+                                                     "k_gemv1 (gate/up projection + SwiGLU, B=1)")}
+    out["roofline_decode_gateup"]["traffic"] = counter_traffic(COUNTER_FILE, "gateup", GEMV_SOURCES)
+    del graphs
+    st.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2)
-    ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--prefill", type=int, default=512, help="prompt tokens")
-    ap.add_argument("--ctx", type=int, default=2048, help="decode up to this context")
-    ap.add_argument("--graph", choices=("on", "off"), default="on", help="replay decode steps from a HIP graph")
-    ap.add_argument("--kv", choices=("f32", "bf16"), default="f32",
-                    help="KV cache element type (f32: the configuration validated against the oracle at full depth)")
-    ap.add_argument("--workload", choices=("first-8b", "last-8b", "mid-70b", "mlp-slices", "pipeline-8b",
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--kv", choices=("f16", "f32", "bf16"), default="f16",
+                    help="KV cache format (f16 and f32 are validated against the oracle at full stage depth)")
+    ap.add_argument("--workload", choices=("mid-70b", "first-8b", "last-8b", "mlp-slices", "pipeline-8b",
                                            "attn-parallel", "placement"),
-                    default="first-8b",
-                    help="first-8b: the benchmark line; the others report the remaining workloads' rooflines")
+                    default="mid-70b",
+                    help="mid-70b: the benchmark line (70B-shaped stage; also reports the 8B first stage); "
+                         "the others report the remaining workloads")
     ap.add_argument("--phase", choices=("both", "prefill", "counters"), default="both",
                     help="prefill: only time the prefill; counters: prefill + 32 plain decode steps and nothing "
                          "else (short runs for hardware-counter passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-first-8b", action="store_true", help="skip the 8B first-stage figures of the default line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="only summarise the rocprofv3 CSV output under DIR")
-    ap.add_argument("--source-hash", action="store_true",
-                    help="only print the hash of the decode GEMV sources the counter summary was taken on")
+    ap.add_argument("--source-hash", choices=("gemv", "gemm"),
+                    help="only print the hash of the kernel sources a counter summary was taken on")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof)
         return
     if args.source_hash:
-        print(gemv_source_hash())
+        print(source_hash(GEMV_SOURCES if args.source_hash == "gemv" else GEMM_SOURCES))
         return
     if args.workload == "placement":             # host only
         print(json.dumps(placement_line(args)), flush=True)
@@ -746,7 +1003,6 @@ def main():
                                    "--gpus above 1 is not supported (the stage has no cross-GPU path)"}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     if args.copy_calibration:
@@ -760,37 +1016,23 @@ def main():
         return
 
     import fixtures as fx
-    from pipeline_stage_decoder_amd import accounting as acc
-    from pipeline_stage_decoder_amd.stage import Stage
 
-    shape = fx.LLAMA8B
-    blocks = (0, 16)
-    T, ctx = args.prefill, args.ctx
-    n_dec = ctx - T
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
-
+    torch.cuda.set_device(0)
     if args.phase == "prefill":
-        if args.workload == "mid-70b":     # one 4096-token chunk at position 0, bf16 KV cache
-            prefill_only(args, fx.LLAMA70B, (20, 40), 4096, dev, stream, first=False, kv_f32=False)
+        if args.workload == "mid-70b":     # one 4096-token chunk at position 0
+            prefill_only(args, fx.LLAMA70B, (20, 40), 4096, torch.device("cuda:0"), torch.cuda.current_stream(),
+                         first=False)
         else:
-            prefill_only(args, shape, blocks, T, dev, stream)
+            prefill_only(args, fx.LLAMA8B, (0, 16), 512, torch.device("cuda:0"), torch.cuda.current_stream())
         return
     if args.phase == "counters":
-        counter_pass(shape, blocks, T, dev)
+        counter_pass(fx.LLAMA8B, (0, 16), 512, torch.device("cuda:0"), kv=args.kv)
         return
     if args.workload == "last-8b":
         print(json.dumps(batched_decode_line(
             args, "8B-shaped last stage: blocks 16..31 of 32 + final norm + readout (vocab 128256); "
                   "batched decode B=64 at context 4096, F32 hidden in, F32 logits out",
-            shape, (16, 32), False, True, 64, 4096, 1024, False)), flush=True)
-        return
-    if args.workload == "mid-70b":
-        print(json.dumps(batched_decode_line(
-            args, "70B-shaped middle stage: blocks 20..39 of 80, d 8192, 64q/8kv, SwiGLU 28672; "
-                  "prefill in 4096-token chunks to context 8192, then batched decode B=128 at context 8192",
-            fx.LLAMA70B, (20, 40), False, False, 128, 8192, 4096, True)), flush=True)
+            fx.LLAMA8B, (16, 32), False, True, 64, 4096, 1024, False)), flush=True)
         return
     if args.workload == "pipeline-8b":
         print(json.dumps(pipeline_line(args)), flush=True)
@@ -801,174 +1043,19 @@ def main():
     if args.workload == "attn-parallel":
         print(json.dumps(attn_parallel_line(args)), flush=True)
         return
+    if args.workload == "first-8b":
+        print(json.dumps(first8b_figures(args, reps=max(args.steps, 1))), flush=True)
+        return
 
-    log(f"[bench] creating stage: blocks {blocks}, embedding, max_ctx {ctx}, max_tokens {T}")
-    kv_f32 = args.kv == "f32"
-    st = Stage(shape, blocks[0], blocks[1], True, False, max_slots=1, max_ctx=ctx, max_tokens=T, device=0,
-               kv_f32=kv_f32)
-    fill_weights(st, shape, blocks, True, False, fx.SEED_WEIGHTS)
-    prompt = fx.tokens_gpu(torch.empty(T, dtype=torch.int32, device=dev), fx.SEED_TOKENS, fx.token_stream(0),
-                           shape.vocab)
-    dec_tok = fx.tokens_gpu(torch.empty(n_dec, dtype=torch.int32, device=dev), fx.SEED_TOKENS,
-                            fx.token_stream(1), shape.vocab)
-    positions = torch.arange(T, ctx, dtype=torch.int32, device=dev)
-    slot0 = torch.zeros(1, dtype=torch.int32, device=dev)
-    xin = torch.empty((T, shape.d_model), dtype=torch.float32, device=dev)
-    hout = torch.empty_like(xin)
-    x1 = torch.empty((1, shape.d_model), dtype=torch.float32, device=dev)
-    h1 = torch.empty_like(x1)
-    torch.cuda.synchronize()
-
-    # decode steps as HIP graphs: each graph replays GRAPH_STEPS consecutive decode steps with their
-    # token and position pointers baked in, so a replay launches only the stage's own kernels
-    use_graph = args.graph == "on"
-    graph_steps = 128
-    graphs = []
-    if use_graph:
-        st.embed(dec_tok[:1], out=x1)                # warm every kernel once outside capture
-        st.decode(x1, slot0, positions[:1], out=h1)
-        torch.cuda.synchronize()
-        cs = torch.cuda.Stream()
-        for g0 in range(0, n_dec - n_dec % graph_steps, graph_steps):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cs):
-                for i in range(g0, g0 + graph_steps):
-                    st.embed(dec_tok[i:i + 1], out=x1)
-                    st.decode(x1, slot0, positions[i:i + 1], out=h1)
-            graphs.append(g)
-        torch.cuda.synchronize()
-        log(f"[bench] captured {len(graphs)} decode graphs of {graph_steps} steps")
-
-    def run_step(ev):
-        ev[0].record(stream)
-        st.embed(prompt, out=xin)
-        st.prefill(xin, 0, 0, out=hout)
-        ev[1].record(stream)
-        done = 0
-        for g in graphs:
-            g.replay()
-            done += graph_steps
-        for i in range(done, n_dec):
-            st.embed(dec_tok[i:i + 1], out=x1)
-            st.decode(x1, slot0, positions[i:i + 1], out=h1)
-        ev[2].record(stream)
-
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]  # noqa: E731
-    for w in range(args.warmup):
-        log(f"[bench] warmup step {w + 1}/{args.warmup}")
-        run_step(mk())
-    torch.cuda.synchronize()
-
-    evs = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev = mk()
-        run_step(ev)
-        evs.append(ev)
-        log(f"[bench] timed step {k + 1}/{args.steps} enqueued")
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    prefill_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
-
-    # dominant decode kernel (gate/up GEMV + SwiGLU, ~54% of the bytes), timed live with HIP events
-    # on the launch stream over one eager decode pass of the request
-    log("[bench] timing the decode kernels over one eager decode pass")
-    kinds = ("gateup", "qkv", "o", "down", "attn")
-    st.embed(prompt, out=xin)
-    st.prefill(xin, 0, 0, out=hout)
-    st.timing(list(kinds))
-    kern = {k: [0, 0.0] for k in kinds}
-    for i in range(n_dec):
-        st.embed(dec_tok[i:i + 1], out=x1)
-        st.decode(x1, slot0, positions[i:i + 1], out=h1)
-        if i % 64 == 63 or i == n_dec - 1:
-            for k in kinds:
-                n, ms = st.timing_read(k)
-                kern[k][0] += n
-                kern[k][1] += ms
-            log(f"[bench] eager decode step {i + 1}/{n_dec}")
-    st.timing([])
-
-    # prefill per-kernel breakdown: one eager prefill of the same prompt with every kind timed
-    log("[bench] timing the prefill kernels over one eager prefill")
-    pkinds = ("norm", "qkv", "attn", "o", "gateup", "down")
-    st.timing(list(pkinds))
-    st.embed(prompt, out=xin)
-    st.prefill(xin, 0, 0, out=hout)
-    torch.cuda.synchronize()
-    prefill_kernel_ms = {k: round(st.timing_read(k)[1], 4) for k in pkinds}
-    st.timing([])
-    # MFMA work issued: activation operands enter as bf16 hi + lo planes (three for QKV with a bf16
-    # cache, two with the F32-grade one), so the matrix cores execute planes x the algorithmic
-    # linear flops; attention issues 2 products per score / output term (3 with the F32-grade
-    # cache, whose lo plane adds one)
-    lin = acc.projection_shapes(shape)
-    qkv_planes = 2 if kv_f32 else 3
-    issued_lin = 16 * 2 * T * sum(n * k * (qkv_planes if kind == "qkv" else 2) for kind, (n, k) in lin.items()
-                                  if kind != "readout")
-
-    n_gu, ms_gu = kern["gateup"]
-    gu_bytes = acc.projection_bytes(shape, "gateup", 1)
-    gu_avg_s = ms_gu / 1e3 / max(n_gu, 1)
-    achieved = gu_bytes / gu_avg_s / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
-                "kernel": "k_gemv1<EPI_SWIGLU, 2, 2> (gate/up projection + SwiGLU, B=1, K split over the 4 waves)",
-                "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 2), "launches": n_gu}
-    kernel_avg_us = {k: round(v[1] * 1e3 / max(v[0], 1), 2) for k, v in kern.items()}
-
-    dec_ms = float(np.median(decode_ms))
-    pre_ms = float(np.median(prefill_ms))
-    dec_tok_s = n_dec / (dec_ms / 1e3)
-    dec_bytes = sum(acc.decode_step_bytes(shape, 16, [c], first=True, kv_elem_bytes=4 if kv_f32 else 2)
-                    for c in range(T, ctx))
-    dec_gbs = dec_bytes / (dec_ms / 1e3) / 1e9
-    pre_flops = acc.prefill_flops(shape, 16, T)
-    pre_tflops = pre_flops / (pre_ms / 1e3) / 1e12
-
-    handoff = time_handoff(hout, x1)
-
+    out = stage70b_line(args)
+    torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline_decode(shape, ctx - 1, 16)
-
-    out = {
-        "metric": "stage decode tok/s & HBM GB/s %peak; prefill tok/s & MFMA util",
-        "value": round(dec_tok_s, 2),
-        "unit": "tok/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(float(np.median(step_ms)), 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: seeded N(0,0.02) bf16 weights, uniform tokens",
-        "config": {"workload": "8B-shaped first stage: embedding + blocks 0..15 of 32, d 4096, 32q/8kv heads, "
-                               "head dim 128, SwiGLU 14336, vocab 128256; batch 1, prefill 512 then decode to ctx 2048",
-                   "prefill_tokens": T, "decode_ctx": ctx, "batch": 1, "decode_graph": use_graph,
-                   "kv_cache": args.kv},
-        "decode_ms_per_token": round(dec_ms / n_dec, 4),
-        "decode_hbm_gbs": round(dec_gbs, 1),
-        "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-        "prefill_tok_s": round(T / (pre_ms / 1e3), 1),
-        "prefill_ms": round(pre_ms, 3),
-        "prefill_tflops": round(pre_tflops, 1),
-        "prefill_mfma_frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-        "prefill_mfma_issued_frac": round((issued_lin + (pre_flops - acc.prefill_flops(shape, 16, T, attn=False)) * (3 if kv_f32 else 2))
-                                          / (pre_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "prefill_kernel_ms": prefill_kernel_ms,
-        "handoff_us": handoff,
-        "kernel_avg_us": kernel_avg_us,
-        "wall_s_timed": round(wall, 3),
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-    }
+        log("[bench] timing the CPU oracle on a bounded sample (one 70B-shaped block)")
+        cpu = cpu_baseline_70b(fx.LLAMA70B, args.kv, 20, 4096, 128, 8192)
+    out["cpu_baseline"] = cpu
+    if not args.no_first_8b:
+        out["first_8b"] = first8b_figures(args)
     print(json.dumps(out), flush=True)
 
 

@@ -65,6 +65,30 @@ def projection_bytes(s, kind: str, rows: int) -> int:
     return w + rows * (k * 4 + 2 * n * F32)
 
 
+def projection_flops(s, kind: str, rows: int) -> int:
+    """Algorithmic flops of one launch of a projection over `rows` rows: 2 * rows * N * K."""
+    n, k = projection_shapes(s)[kind]
+    return 2 * rows * n * k
+
+
+def projection_gemm_bytes(s, kind: str, rows: int, kv_elem_bytes: int = BF16) -> int:
+    """Bytes a prefill projection launch must move at least once: the bf16 weight, its activation
+    operand as the planes the GEMM multiplies (2 planes of bf16, 3 for QKV over a 2-byte cache),
+    and its outputs (F32 residual read + write for O/down, a 4-byte pair per SwiGLU output, pair q
+    and the K/V rows for QKV)."""
+    n, k = projection_shapes(s)[kind]
+    w = n * k * BF16
+    if kind == "qkv":
+        planes = 2 if kv_elem_bytes == F32 else 3
+        qw, kvw = s.n_q_heads * s.head_dim, 2 * s.n_kv_heads * s.head_dim
+        return w + rows * (planes * k * BF16 + qw * 4 + kvw * kv_elem_bytes)
+    if kind == "gateup":
+        return w + rows * (2 * k * BF16 + s.d_ffn * 4)
+    if kind == "readout":
+        return w + rows * (2 * k * BF16 + n * F32)
+    return w + rows * (2 * k * BF16 + 2 * n * F32)
+
+
 # ---------------------------------------------------------------------------------------------
 # whole steps
 # ---------------------------------------------------------------------------------------------

@@ -96,7 +96,8 @@ def test_8b_bf16_cache_outside_the_row_bound(w8b_first):
     # single rows past 1e-3 (measured 1.18e-3 on MI355X) although the whole tensor stays well below
     # it; the F16 and F32-grade caches hold the row bound at full depth.  What this checks of the
     # bf16 format itself: the rounding (bits equal to the oracle's bf16 rounding for > 99% of the
-    # cached values), the whole-tensor bound, and a worst row under 2e-3 as a regression guard.
+    # cached values of the first block), the whole-tensor bound, and a worst row under 2e-3 as a
+    # regression guard.
     s, T = fx.LLAMA8B, 512
     prompt = fx.tokens(fx.SEED_TOKENS, fx.token_stream(0), T, s.vocab)
     ost = o.Stage(o.Dims.of(s), 0, 2, True, False, w8b_first, T, kv_dtype="bf16")
@@ -106,11 +107,12 @@ def test_8b_bf16_cache_outside_the_row_bound(w8b_first):
     e_whole, e_row = rel_l2_whole(got, want), rel_l2_rows(got, want)
     say(f"8B first stage, bf16 cache, T={T}: whole {e_whole:.2e}, worst row {e_row:.2e}")
     assert e_whole <= TOL and e_row <= 2e-3
-    for blk in range(2):
-        kg, vg = kv_bits(st, blk, 0, T)
-        kc, vc = ost.kv[0]
-        for g_bits, w_vals in ((kg, kc[blk, :T]), (vg, vc[blk, :T])):
-            assert np.mean(g_bits == kv_bits_of("bf16", w_vals)) > 0.99
+    # block 0's K/V come from exact inputs (embedding rows), so they show the rounding itself;
+    # block 1's inputs already carry block 0's differences
+    kg, vg = kv_bits(st, 0, 0, T)
+    kc, vc = ost.kv[0]
+    for g_bits, w_vals in ((kg, kc[0, :T]), (vg, vc[0, :T])):
+        assert np.mean(g_bits == kv_bits_of("bf16", w_vals)) > 0.99
 
 
 @pytest.mark.parametrize("kv", ["bf16", "f16"])
