@@ -232,6 +232,19 @@ int stage_attn_ring_workspace(const stage_t* st, int T, uint64_t* bytes /*host*/
 int stage_attn_ring(stage_t* st, int global_block, int slot, int T, int n_ranks, int zigzag, const float* hidden_in,
                     float* out, int accumulate, void* workspace, uint64_t workspace_bytes, hipStream_t stream);
 
+/* stage_attn_ring without the workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the hops'
+ * partials and their running merge live in a device array inside the library, 32 MiB per GPU, held
+ * from the first stage_create on that GPU until the process ends.  It allocates nothing and is
+ * otherwise stage_attn_ring (the same kernels, bit-identical results).  Calls whose workspace
+ * (stage_attn_ring_workspace) would exceed 32 MiB -- 8 (Dh + 1) bytes per (row, query head), so
+ * about 1000 rows for 32 query heads of dim 128 -- are refused with STAGE_E_DOES_NOT_FIT before
+ * anything is enqueued.  Every call on one GPU shares that array: calls that overlap on one GPU
+ * (other streams, other handles, other threads) race and must be serialised by the caller.
+ * Nothing in the array needs to start at zero, and each call overwrites what it uses. */
+int stage_attn_ring_noalloc(stage_t* st, int global_block, int slot, int T, int n_ranks, int zigzag,
+                            const float* hidden_in, float* out, int accumulate, hipStream_t stream);
+
 /* Embedding of a vocabulary slice on a first stage: the stage's table holds ids
  * [vocab_lo, vocab_lo + V) of a larger vocabulary.  hidden_out[i, :] = (accumulate ? hidden_out[i, :]
  * : 0) + (tokens[i] inside ? E[tokens[i] - vocab_lo, :] : 0), so slices called in order assemble

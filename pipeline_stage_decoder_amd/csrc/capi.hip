@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -21,9 +22,36 @@
 #include "kernels.h"
 #include "stage.h"
 
+// Device scratch of the no-allocation ring entry point (stage_attn_ring_noalloc): the partial
+// outputs and log-sum-exps of its hops and their running merge.  Each GPU that loads the library
+// holds one copy at its own address until the process ends.  In host code `scratch` only names the
+// symbol: its device address is looked up once per device (scratch_ptr) and only that is used.
+constexpr uint64_t kScratchBytes = 32ull << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 constexpr uint64_t kAlign = 256;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The calling thread's current device must be `device`.  Looks the scratch array's address on that
+// device up on first use and keeps it; nullptr if the lookup fails or the device id is out of range.
+void* scratch_ptr(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[device] = p;
+  }
+  return g_scratch_ptr[device];
+}
 
 uint64_t align_up(uint64_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
@@ -552,17 +580,23 @@ int stage_attn_ring_workspace(const stage_t* st, int T, uint64_t* bytes) {
   return STAGE_OK;
 }
 
-int stage_attn_ring(stage_t* st, int global_block, int slot, int T, int n_ranks, int zigzag, const float* hin,
-                    float* out, int accumulate, void* workspace, uint64_t workspace_bytes, hipStream_t s) {
-  if (!st || !hin || !out || !workspace || T <= 0 || n_ranks <= 0) return fail(st, STAGE_E_INVALID, "bad ring arguments");
+namespace {
+
+// Arguments of a ring call, checked on the host before anything is enqueued.
+int ring_check(stage_t* st, int global_block, int slot, int T, int n_ranks, int zigzag, const float* hin, float* out) {
+  if (!st || !hin || !out || T <= 0 || n_ranks <= 0) return fail(st, STAGE_E_INVALID, "bad ring arguments");
   if (global_block < st->s.block_begin || global_block >= st->s.block_end)
     return fail(st, STAGE_E_ROLE, "block outside the stage's range");
   if (T > st->s.max_tokens) return fail(st, STAGE_E_INVALID, "T > max_tokens");
   if (T % (n_ranks * (zigzag ? 2 : 1)) != 0) return fail(st, STAGE_E_INVALID, "T is not a multiple of the chunk count");
   if (slot < 0 || slot >= st->s.max_slots || T > st->s.max_ctx) return fail(st, STAGE_E_RANGE, "slot or positions out of range");
-  if (workspace_bytes < ring_ws_bytes(st, T) || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(st, STAGE_E_DOES_NOT_FIT, "ring workspace too small or misaligned");
-  HIP_TRY(st, hipSetDevice(st->device));
+  return STAGE_OK;
+}
+
+// The ring sublayer over a checked call, its partials and accumulators in `workspace` (256-byte
+// aligned, ring_ws_bytes(st, T) bytes; nothing in it needs to start at zero).
+int ring_run(stage_t* st, int global_block, int slot, int T, int n_ranks, int zigzag, const float* hin, float* out,
+             int accumulate, void* workspace, hipStream_t s) {
   const int lb = global_block - st->s.block_begin;
   const BlockW& bw = st->blocks[lb];
   const int d = st->m.d_model, hq = st->m.n_q_heads, hkv = st->m.n_kv_heads, dh = st->m.head_dim;
@@ -630,6 +664,31 @@ int stage_attn_ring(stage_t* st, int global_block, int slot, int T, int n_ranks,
   eo.ldo = d;
   HIP_TRY(st, project(st, STAGE_KT_O, T, nullptr, nullptr, st->attn, ps_q(st), bw.wo, d, hq * dh, eo, s));
   return STAGE_OK;
+}
+
+}  // namespace
+
+int stage_attn_ring(stage_t* st, int global_block, int slot, int T, int n_ranks, int zigzag, const float* hin,
+                    float* out, int accumulate, void* workspace, uint64_t workspace_bytes, hipStream_t s) {
+  const int rc = ring_check(st, global_block, slot, T, n_ranks, zigzag, hin, out);
+  if (rc != STAGE_OK) return rc;
+  if (!workspace) return fail(st, STAGE_E_INVALID, "bad ring arguments");
+  if (workspace_bytes < ring_ws_bytes(st, T) || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(st, STAGE_E_DOES_NOT_FIT, "ring workspace too small or misaligned");
+  HIP_TRY(st, hipSetDevice(st->device));
+  return ring_run(st, global_block, slot, T, n_ranks, zigzag, hin, out, accumulate, workspace, s);
+}
+
+int stage_attn_ring_noalloc(stage_t* st, int global_block, int slot, int T, int n_ranks, int zigzag,
+                            const float* hin, float* out, int accumulate, hipStream_t s) {
+  const int rc = ring_check(st, global_block, slot, T, n_ranks, zigzag, hin, out);
+  if (rc != STAGE_OK) return rc;
+  if (ring_ws_bytes(st, T) > kScratchBytes)
+    return fail(st, STAGE_E_DOES_NOT_FIT, "ring scratch needs more than the library's 32 MiB for this T; use stage_attn_ring");
+  HIP_TRY(st, hipSetDevice(st->device));
+  void* ws = scratch_ptr(st->device);
+  if (!ws) return fail(st, STAGE_E_HIP, "hipGetSymbolAddress of the ring scratch failed");
+  return ring_run(st, global_block, slot, T, n_ranks, zigzag, hin, out, accumulate, ws, s);
 }
 
 int stage_greedy(int n, int V, const float* logits, int32_t* tokens_out, hipStream_t s) {
@@ -728,6 +787,7 @@ int stage_create(const stage_model_cfg* model, const stage_stage_cfg* stg, void*
     delete st;
     return STAGE_E_HIP;
   }
+  (void)scratch_ptr(device);   // the device's scratch address, looked up once with the device current
   *out = st;
   return STAGE_OK;
 }

@@ -79,6 +79,7 @@ EXPORTS = {
     "stage_embed_range": [_vp, _i32, _vp, _i32, _vp, _i32, _vp],
     "stage_attn_ring_workspace": [_vp, _i32, ctypes.POINTER(ctypes.c_uint64)],
     "stage_attn_ring": [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _u64, _vp],
+    "stage_attn_ring_noalloc": [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp],
     "stage_greedy": [_i32, _i32, _vp, _vp, _vp],
     "stage_describe": [_vp, ctypes.POINTER(ModelCfg), ctypes.POINTER(StageCfg), ctypes.POINTER(ctypes.c_int)],
     "stage_pipeline_workspace": [ctypes.POINTER(_vp), _i32, ctypes.POINTER(GenCfg), ctypes.POINTER(ctypes.c_uint64)],
@@ -303,6 +304,16 @@ class Stage:
         self._check(lib().stage_attn_ring(self._h, global_block, slot, t, n_ranks, int(zigzag), _ptr(hidden_in),
                                           _ptr(out), int(accumulate), _ptr(ws), int(ws.numel()), _stream(stream)),
                     "stage_attn_ring")
+        return out
+
+    def attn_ring_noalloc(self, global_block: int, hidden_in: torch.Tensor, slot: int, n_ranks: int, zigzag: bool,
+                          out: torch.Tensor, accumulate: bool = False, stream=None) -> torch.Tensor:
+        """stage_attn_ring_noalloc: attn_ring with the library's own scratch (the caller passes `out`;
+        nothing is allocated)."""
+        t = hidden_in.shape[0]
+        self._check(lib().stage_attn_ring_noalloc(self._h, global_block, slot, t, n_ranks, int(zigzag),
+                                                  _ptr(hidden_in), _ptr(out), int(accumulate), _stream(stream)),
+                    "stage_attn_ring_noalloc")
         return out
 
     def embed_range(self, tokens: torch.Tensor, vocab_lo: int, out: torch.Tensor | None = None,
