@@ -138,22 +138,27 @@ def summarize_rocprof(path: str, top: int = 12) -> None:
                 print(f"{k} | {n} | {100 * u:.1f}% | {fl:.4g}")
 
 
-def time_handoff(rows_prefill, row_decode, reps: int = 50) -> dict:
+def time_handoff(rows_prefill, rows_decode, reps: int = 20, cold_bytes: int = 768 << 20) -> dict:
     """The stage boundary's cost: the F32 hidden rows a stage hands to the next, copied device to
-    device (the one-GPU handoff), and as a pinned device->host->device round trip (the host-staged
-    transfer of two stages on two PCIe-attached GPUs)."""
+    device (the one-GPU handoff) from sources rotated through more than `cold_bytes` of memory --
+    past the 256 MB memory-side cache, so every copy reads HBM -- and as a pinned device->host->
+    device round trip (the host-staged transfer of two stages on two PCIe-attached GPUs)."""
     import torch
     out = {}
-    for name, src in (("prefill_rows", rows_prefill), ("decode_row", row_decode)):
+    for name, src in (("prefill_rows", rows_prefill), ("decode_rows", rows_decode)):
+        nbytes = src.numel() * 4
+        srcs = [src.clone() for _ in range(max(2, -(-cold_bytes // nbytes)))]
         dst = torch.empty_like(src)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        dst.copy_(src)
+        dst.copy_(srcs[0])
+        torch.cuda.synchronize()
         e0.record()
-        for _ in range(reps):
-            dst.copy_(src)
+        for i in range(reps):
+            dst.copy_(srcs[i % len(srcs)])
         e1.record()
         torch.cuda.synchronize()
         out[f"d2d_{name}"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+        del srcs
         host = torch.empty(src.shape, dtype=src.dtype, pin_memory=True)
         host.copy_(src)
         dst.copy_(host)
@@ -164,7 +169,7 @@ def time_handoff(rows_prefill, row_decode, reps: int = 50) -> dict:
             dst.copy_(host)
             torch.cuda.synchronize()
         out[f"pinned_round_trip_{name}"] = round((time.perf_counter() - t0) * 1e6 / reps, 2)
-        out[f"bytes_{name}"] = src.numel() * 4
+        out[f"bytes_{name}"] = nbytes
     return out
 
 
@@ -859,6 +864,7 @@ def stage70b_line(args) -> dict:
         "prefill_kernel_ms": {k: round(v[1], 3) for k, v in pre_kinds.items()},
         "decode_kernel_ms": {k: round(v[1], 3) for k, v in dec_kinds.items()},
         "wall_s_timed": round(wall, 3), "roofline": roofline, "roofline_decode": roof_dec,
+        "handoff_us": time_handoff(yp, yd),
     }
 
 
