@@ -636,19 +636,24 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_norm(GemmArgs g, NormArgs
 struct Cfg {
   int bm, bn;
 };
-constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128}, {256, 256}, {128, 256}, {128, 256}, {64, 256}, {64, 128}, {128, 256}};
+constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128}, {256, 256}, {128, 256}, {128, 256}, {64, 256}, {64, 128}, {128, 256}, {128, 256}};
 
 }  // namespace
 
 GemmPlan gemm_plan(int M, int N, int K, int planes, bool qkv) {
   // Tile shapes from sweeps on MI355X over the prefill and batched-decode projections.
-  //  * M >= 256: the LDS-direct kernels, K split until the grid holds ~200 work-groups (one per CU)
-  //    as long as each split keeps >= 1024 of K.  256 x 256 for the activation pair when at most 4
-  //    splits fill the chip (gate/up and the 70B projections 1.2-1.4x faster than the tiles
-  //    below), else 128 x 256 (the QKV projection; the 512-row O and down projections split 4
-  //    ways, as fast as 256 x 256 split 8 with half the partials to reduce).  The QKV epilogue
-  //    (RoPE in f64 and the cache stores) never takes 256 x 256: on that tile it needed more
-  //    registers than two waves per SIMD leave and spilled 528 bytes per lane.
+  //  * M >= 256 with K a multiple of 64: 128 x 256 LDS-direct tiles with 64-deep stages in two
+  //    LDS buffers (two or three activation planes; three planes fill exactly 160 KB), K split
+  //    until the grid holds ~190 work-groups as long as each split keeps >= 1024 of K.  Every row
+  //    segment a load instruction fetches is then a whole 128-byte line, which measured faster
+  //    than the 32-deep rings of 256 x 256 and 128 x 256 tiles at every prefill projection (70B
+  //    shape at M = 4096: gate/up 6.27 -> 5.91 ms, down 3.16 -> 3.04, O 0.96 -> 0.90, three-plane
+  //    QKV 1.78 -> 1.52; 8B shape at M = 512: down 113 -> 98 us, O 48 -> 42, QKV 85 -> 75, gate/up
+  //    equal).
+  //  * M >= 256 otherwise: 256 x 256 (two planes) when at most 4 splits fill the chip, else
+  //    128 x 256, both in 32-deep stages.  The QKV epilogue (RoPE in f64 and the cache stores)
+  //    never takes 256 x 256: on that tile it needed more registers than two waves per SIMD leave
+  //    and spilled 528 bytes per lane.
   //  * 32 < M <= 64 (batched decode): 64 x 256 or 64 x 128 LDS-direct tiles with 64-deep stages
   //    (8B-shaped projections at M = 64: gate/up 55 -> 50 us, down 37 -> 31 us, O 17.5 -> 16 us).
   //  * 64 < M <= 128 (batched decode): 128 x 256.  Two planes (K a multiple of 64): 64-deep stages
@@ -693,6 +698,20 @@ GemmPlan gemm_plan(int M, int N, int K, int planes, bool qkv) {
     p.bn = kCfgs[p.cfg].bn;
     p.tiles_m = 1;
     p.tiles_n = tiles;
+    p.splitk = sk;
+    return p;
+  }
+  if (dma_ok && M >= 256 && K % 64 == 0) {
+    // cfg 10 (two planes) / 11 (three planes): 128 x 256 with 64-deep stages in two buffers
+    const int cfg = planes == 2 ? 10 : 11;
+    const int tiles = ((M + 127) / 128) * ((N + 255) / 256);
+    int sk = 1;
+    while (tiles * sk < 190 && K / (sk * 2) >= 1024 && sk < 8) sk *= 2;
+    p.cfg = cfg;
+    p.bm = kCfgs[cfg].bm;
+    p.bn = kCfgs[cfg].bn;
+    p.tiles_m = (M + 127) / 128;
+    p.tiles_n = (N + 255) / 256;
     p.splitk = sk;
     return p;
   }
@@ -762,6 +781,9 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
     case 10:   // the planner gives it two planes only
       k_gemm_dma<2, EPI, 128, 256, 4, 2, 2, 64><<<grid, 512, 0, s>>>(a);
       break;
+    case 11:   // three planes only: 2 x (3 x 32 KB + 32 KB) = 160 KB of LDS
+      if constexpr (NP == 3) k_gemm_dma<3, EPI, 128, 256, 4, 2, 2, 64><<<grid, 512, 0, s>>>(a);
+      break;
 
     default: k_gemm<16, 128, 1, 4, NP, EPI, 2, 2><<<grid, 256, 0, s>>>(a); break;
   }
@@ -781,7 +803,8 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
                        bool* normed) {
   if (normed) *normed = false;
   // the LDS-direct tile takes two planes, K in whole 32-deep stages and operands under 4 GiB
-  if (((p.cfg == 5 || p.cfg == 8 || p.cfg == 10) && a.planes != 2) || (p.cfg >= 5 && ( a.K % kDmaBK != 0 || (uint64_t)(a.M > a.N ? a.M : a.N) * a.K * 2 >= (1ull << 32))))
+  if (((p.cfg == 5 || p.cfg == 8 || p.cfg == 10) && a.planes != 2) || (p.cfg == 11 && a.planes != 3) ||
+      (p.cfg >= 5 && (a.K % kDmaBK != 0 || (uint64_t)(a.M > a.N ? a.M : a.N) * a.K * 2 >= (1ull << 32))))
     return hipErrorInvalidValue;
   if (p.cfg == 5 && a.e.kind == EPI_QKV) return hipErrorInvalidValue;   // not instantiated (see gemm_plan)
   if (p.cfg >= 8 && a.K % 64 != 0) return hipErrorInvalidValue;   // 64-deep stages
