@@ -655,13 +655,15 @@ GemmPlan gemm_plan(int M, int N, int K, int planes, bool qkv) {
   //    never takes 256 x 256: on that tile it needed more registers than two waves per SIMD leave
   //    and spilled 528 bytes per lane.
   //  * 32 < M <= 64 (batched decode): 64 x 256 or 64 x 128 LDS-direct tiles with 64-deep stages
-  //    (8B-shaped projections at M = 64: gate/up 55 -> 50 us, down 37 -> 31 us, O 17.5 -> 16 us).
-  //  * 64 < M <= 128 (batched decode): 128 x 256.  Two planes (K a multiple of 64): 64-deep stages
-  //    in two LDS buffers, so each row segment a load instruction fetches is a whole 128-byte line
+  //    (8B-shaped projections at M = 64: gate/up 55 -> 50 us, down 37 -> 31 us, O 17.5 -> 16 us);
+  //    the wide-N 64 x 256 tile runs 8 waves of 32 x 64 (two per SIMD; four waves of 64 x 64: gate/up
+  //    50.1 -> 43.5 us, readout 292 -> 270 us).
+  //  * 64 < M <= 128 (batched decode): 128 x 256 with 64-deep stages in two LDS buffers (K a
+  //    multiple of 64), so each row segment a load instruction fetches is a whole 128-byte line
   //    of the activation or weight row (M = 128: 70B gate/up 324 -> 280 us, O 46.5 -> 41 us, 8B O
-  //    25.7 -> 23 us, readout 337 -> 309 us; bit-identical).  Three planes: 32-deep stages in a
-  //    3-deep ring, 8 waves of 64 x 64 (6-10% faster than 128 x 128; 64-deep stages of three
-  //    planes only fit 128 x 128 tiles, which were no faster).
+  //    25.7 -> 23 us, readout 337 -> 309 us; bit-identical); three planes fill exactly 160 KB
+  //    (70B QKV 74.6 -> 67.9 us against 32-deep stages in a 3-deep ring).  Otherwise 32-deep
+  //    stages in a ring, 8 waves of 64 x 64.
   //  * otherwise 128 x 128 up to M = 512 and 64 x 256 above, one LDS buffer and one register
   //    staging set so that two work-groups fit a CU (the second hides the first's barrier, LDS and
   //    load waits), each wave owning a 64 x 64 tile; the 64 x 256 tile's 4 MB weight panels keep
@@ -687,13 +689,13 @@ GemmPlan gemm_plan(int M, int N, int K, int planes, bool qkv) {
     return p;
   }
   if (dma_ok && M > 64 && M <= 128) {
-    // batched decode rows: 128 x 256, two planes with 64-deep stages in two buffers (8 waves of
-    // 32 x 128); three planes (or K not a multiple of 64) with 64 x 64 wave tiles and a 3-deep (two
-    // planes: 4-deep) ring of 32-deep stages; K split until the grid holds ~150 work-groups
+    // batched decode rows: 128 x 256 with 64-deep stages in two buffers (8 waves of 32 x 128),
+    // two or three planes; K not a multiple of 64: 64 x 64 wave tiles and a 3-deep (two planes:
+    // 4-deep) ring of 32-deep stages; K split until the grid holds ~150 work-groups
     const int tiles = (N + 255) / 256;
     int sk = 1;
     while (tiles * sk < 150 && K / (sk * 2) >= 512 && sk < 16) sk *= 2;
-    p.cfg = (planes == 2 && K % 64 == 0) ? 10 : 7;
+    p.cfg = K % 64 == 0 ? (planes == 2 ? 10 : 11) : 7;
     p.bm = kCfgs[p.cfg].bm;
     p.bn = kCfgs[p.cfg].bn;
     p.tiles_m = 1;
@@ -775,7 +777,7 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
       k_gemm_dma<NP, EPI, 128, 256, 2, 4, NP == 2 ? 4 : 3><<<grid, 512, 0, s>>>(a);
       break;
     case 8:   // the planner gives it two planes only
-      k_gemm_dma<2, EPI, 64, 256, 1, 4, 3, 64><<<grid, 256, 0, s>>>(a);
+      k_gemm_dma<2, EPI, 64, 256, 2, 4, 3, 64><<<grid, 512, 0, s>>>(a);
       break;
     case 9: k_gemm_dma<NP, EPI, 64, 128, 1, 4, NP == 2 ? 4 : 3, 64><<<grid, 256, 0, s>>>(a); break;
     case 10:   // the planner gives it two planes only
