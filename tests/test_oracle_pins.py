@@ -733,3 +733,26 @@ def test_attn_sublayer_ring_matches_attn_sublayer():
     for n, zz in ((2, False), (2, True), (4, True)):
         np.testing.assert_allclose(o.attn_sublayer_ring(x, g, wq, wk, wv, wo, dh, 1e-5, 1e4, n, zz), full,
                                    rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------------------------
+# node-order sums and greedy ties
+# ---------------------------------------------------------------------------------------------
+
+def test_f32_sum_in_order_is_left_to_right_in_float32():
+    # ((p0 + p1) + p2) with every partial rounded to float32: 1e8 + (-1e8) + 1 = 1, while
+    # 1 + 1e8 + (-1e8) = 0 in float32 (1 is below half an ulp of 1e8)
+    big = np.float32(1e8)
+    assert o.f32_sum_in_order([np.array([big]), np.array([-big]), np.array([np.float32(1)])])[0] == 1.0
+    assert o.f32_sum_in_order([np.array([np.float32(1)]), np.array([big]), np.array([-big])])[0] == 0.0
+    r = rng(33).standard_normal((5, 7)).astype(np.float32)
+    want = r[0].copy()
+    for row in r[1:]:
+        want = (want + row).astype(np.float32)
+    np.testing.assert_array_equal(o.f32_sum_in_order(list(r)), want)
+
+
+def test_greedy_lowest_index_on_ties():
+    logits = np.array([[0.5, 2.0, 2.0, -1.0], [3.0, 3.0, 3.0, 3.0], [-np.inf, -5.0, -5.0, -np.inf]])
+    assert o.greedy(logits).tolist() == [1, 0, 1]
+    np.testing.assert_allclose(o.top2_margin(np.array([[1.0, 4.0, 2.5]])), [1.5])
