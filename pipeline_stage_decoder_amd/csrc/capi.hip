@@ -97,8 +97,7 @@ int validate(const stage_model_cfg* m, const stage_stage_cfg* s) {
 }
 
 int nsplit_for(int B, int ctx_cap) {
-  const int ch = attn_decode_chunk(B);
-  return (ctx_cap + ch - 1) / ch;
+  return attn_decode_splits(ctx_cap, attn_decode_chunk(B));
 }
 
 Layout make_layout(const stage_model_cfg& m, const stage_stage_cfg& s) {

@@ -51,8 +51,8 @@ struct AttnDecodeArgs {
   const int32_t* slots;     // [B]
   const int32_t* pos;       // [B]; keys [0, pos] are attended
   int B, hq, hkv, dh, ctx_cap, max_slots;
-  int chunk;                // keys per work-group, multiple of 128
-  int nsplit;               // splits allocated per row
+  int chunk;                // keys per split (the last split of a row takes the remainder)
+  int nsplit;               // splits allocated per row (>= attn_decode_splits of every row)
   float scale_log2;         // Dh^-1/2 * log2(e)
   float* part_o;            // [B][Hq][nsplit][Dh]
   float* part_lse;          // [B][Hq][nsplit]  (base-2 log-sum-exp)
@@ -117,5 +117,13 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
 
 // attention
 int attn_decode_chunk(int B);
+// Splits of a row that attends n keys in chunks of `chunk`: n / chunk rounded to nearest, at least
+// one; split s covers keys [s * chunk, (s + 1) * chunk) except the last, which runs to n.  Every
+// split of a multi-split row holds between chunk / 2 and 1.5 chunk keys, so a row of 8193 keys is
+// 16 splits of 512 (the last with 513), not 17 with one key in the last.
+__host__ __device__ inline int attn_decode_splits(int n, int chunk) {
+  const int s = (n + chunk / 2) / chunk;
+  return s > 0 ? s : 1;
+}
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);

@@ -20,7 +20,7 @@
 // The softmax is online per column (max and rescale), in base 2 with the scale folded in.  O^T
 // puts a column's values in the same lane as its softmax state, so rescaling needs no shuffles.
 //
-// Decode: work-group = (split of `chunk` keys, KV head, batch row); its 4 waves take every fourth
+// Decode: work-group = (split of about `chunk` keys, KV head, batch row); its 4 waves take every fourth
 // 32-key step of the chunk and merge through LDS into one partial per split; a second kernel merges the
 // splits of each (row, query head) in split order.
 // Prefill: work-group = 64 columns (consecutive queries x the group's heads) of one KV head; the
@@ -211,9 +211,10 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnDecodeArgs a) {
   const int G = a.hq / a.hkv;
   if (slot < 0 || slot >= a.max_slots || pos < 0 || pos >= a.ctx_cap) return;
   const int ctx = pos + 1;
+  const int ns = attn_decode_splits(ctx, a.chunk);
+  if (split >= ns) return;
   const int k0 = split * a.chunk;
-  if (k0 >= ctx) return;
-  const int k1 = min(k0 + a.chunk, ctx);
+  const int k1 = split == ns - 1 ? ctx : k0 + a.chunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
 
   Col16<DH, FMT> st;
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(DH) void k_attn_merge(AttnDecodeArgs a) {
     a.out[a.out_ps + o] = 0;
     return;
   }
-  const int ns = (pos + a.chunk) / a.chunk;  // ceil((pos + 1) / chunk); every split holds a key
+  const int ns = attn_decode_splits(pos + 1, a.chunk);
   const size_t row0 = ((size_t)b * a.hq + head) * a.nsplit;
   const float* lse = a.part_lse + row0;
   const float* po = a.part_o + row0 * DH + d;
