@@ -308,9 +308,13 @@ PSD_DEV int dma_swz(int r, int c) {
   return CH == 4 ? c ^ ((r >> 1) & 3) : c ^ (r & 7);
 }
 
-template <int NP, int EPI, int BM, int BN, int WM, int WN, int ST, int BK = kDmaBK, bool PP = false>
+template <int NP, int EPI, int BM, int BN, int WM, int WN, int ST, int BK = kDmaBK, bool PP = false, int STB = 0>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
+  // weight (B) stages in LDS: ST like the activations, or STB > ST with the activations double-
+  // buffered, so that the weight stream runs STB - 2 stages ahead of the activation stream
+  constexpr int SB = STB > 0 ? STB : ST;
+  static_assert(SB == ST || (ST == 2 && SB >= 3 && !PP), "deeper weight ring: two activation buffers");
   static_assert(BK == 32 || BK == 64, "stage depth");
   constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 16, TN = WTN / 16;
   static_assert(WTN % 32 == 0, "paired epilogues need 32-aligned wave columns");
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
   constexpr int PER_STAGE = NP * A_DMA + B_DMA;
   static_assert(ST >= 2 && ST <= 8 && (ST - 2) * PER_STAGE < 64, "ring depth within vmcnt");
   __shared__ uint4 As[ST][NP][BM * CH];
-  __shared__ uint4 Bs[ST][BN * CH];
+  __shared__ uint4 Bs[SB][BN * CH];
 
   const int M = g.M, N = g.N, K = g.K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
   const uint32_t b_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&Bs[0][0] +
                          (uint32_t)(wave_s * B_DMA * 64 * 16);
 
-  auto issue = [&](int t) {   // stage t -> buffer t % ST
+  auto issue_a = [&](int t) {   // activation stage t -> buffer t % ST
     const int buf = t % ST;
     const size_t k0 = (size_t)kbeg + (size_t)t * BK;
 #pragma unroll
@@ -363,8 +367,16 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < A_DMA; ++i)
         dma16(g.a + pl * g.a_ps + k0, a_off[i], a_lds + (uint32_t)((buf * NP + pl) * BM * CH * 16 + i * 64 * 16));
+  };
+  auto issue_b = [&](int t) {   // weight stage t -> buffer t % SB
+    const int buf = t % SB;
+    const size_t k0 = (size_t)kbeg + (size_t)t * BK;
 #pragma unroll
     for (int i = 0; i < B_DMA; ++i) dma16(g.w + k0, b_off[i], b_lds + (uint32_t)(buf * BN * CH * 16 + i * 64 * 16));
+  };
+  auto issue = [&](int t) {
+    issue_a(t);
+    issue_b(t);
   };
 
   f32x4_t acc[TM][TN];
@@ -387,6 +399,50 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
     }
   };
 
+  if constexpr (SB != ST) {
+    // Issue order: B0 .. B(SB-3), then per stage j the pair A(j), B(j + SB - 2).  When stage t is
+    // consumed, the only loads issued after A(t) are those of B(t + SB - 2), so waiting for all but
+    // B_DMA loads lands both A(t) and B(t).  Iteration t refills the buffers of stage t - 1.
+    for (int j = 0; j < SB - 2; ++j)
+      if (j < nk) issue_b(j);
+    if (nk > 0) issue_a(0);
+    if (SB - 2 < nk) issue_b(SB - 2);
+    for (int t = 0; t < nk; ++t) {
+      if (t + SB - 2 < nk) wait_vmcnt<B_DMA>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ++ks) {
+        const int ch = ks * 4 + kc;
+        bf16x8_t af[NP][TM], bw[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = wm * WTM + i * 16 + (lane & 15);
+#pragma unroll
+          for (int pl = 0; pl < NP; ++pl) af[pl][i] = as_bf16x8(As[t % ST][pl][row * CH + dma_swz<CH>(row, ch)]);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int row = wn * WTN + j * 16 + (lane & 15);
+          bw[j] = as_bf16x8(Bs[t % SB][row * CH + dma_swz<CH>(row, ch)]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[pl][i], bw[j], acc[i][j]);
+          if (pl == 0 && ks == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 1 < nk) issue_a(t + 1);
+            if (t + SB - 1 < nk) issue_b(t + SB - 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+  } else {
 #pragma unroll
   for (int t = 0; t < ST - 1; ++t)
     if (t < nk) issue(t);
@@ -483,6 +539,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
         }
       }
     }
+  }
+
   }
 
   gemm_store<TM, TN, WTM, WTN, EPI>(g, acc, m0 + wm * WTM, n0 + wn * WTN, lane, split);
@@ -664,6 +722,11 @@ GemmPlan gemm_plan(int M, int N, int K, int planes, bool qkv) {
   //    25.7 -> 23 us, readout 337 -> 309 us; bit-identical); three planes fill exactly 160 KB
   //    (70B QKV 74.6 -> 67.9 us against 32-deep stages in a 3-deep ring).  Otherwise 32-deep
   //    stages in a ring, 8 waves of 64 x 64.
+  //  * The two-plane 128 x 256 tile keeps a third weight buffer in the 32 KB that two planes leave
+  //    free, so the weight stream runs two stages ahead of the activations (bit-identical; M = 128:
+  //    70B gate/up 259 -> 240 us, down 144 -> 133 us, O and QKV equal; M = 4096: 70B down 3.04 ->
+  //    2.98 ms, O 0.88 -> 0.86 ms, gate/up 0.7% slower; 8B M = 512 gate/up 194 -> 187 us).  With
+  //    32-deep stages and up to 8 weight buffers it was 10-20% slower.
   //  * otherwise 128 x 128 up to M = 512 and 64 x 256 above, one LDS buffer and one register
   //    staging set so that two work-groups fit a CU (the second hides the first's barrier, LDS and
   //    load waits), each wave owning a 64 x 64 tile; the 64 x 256 tile's 4 MB weight panels keep
@@ -780,8 +843,8 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
       k_gemm_dma<2, EPI, 64, 256, 2, 4, 3, 64><<<grid, 512, 0, s>>>(a);
       break;
     case 9: k_gemm_dma<NP, EPI, 64, 128, 1, 4, NP == 2 ? 4 : 3, 64><<<grid, 256, 0, s>>>(a); break;
-    case 10:   // the planner gives it two planes only
-      k_gemm_dma<2, EPI, 128, 256, 4, 2, 2, 64><<<grid, 512, 0, s>>>(a);
+    case 10:   // two planes only: 2 x 32 KB of activations + 3 x 32 KB of weights = 160 KB of LDS
+      k_gemm_dma<2, EPI, 128, 256, 4, 2, 2, 64, false, 3><<<grid, 512, 0, s>>>(a);
       break;
     case 11:   // three planes only: 2 x (3 x 32 KB + 32 KB) = 160 KB of LDS
       if constexpr (NP == 3) k_gemm_dma<3, EPI, 128, 256, 4, 2, 2, 64><<<grid, 512, 0, s>>>(a);
