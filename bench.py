@@ -832,8 +832,8 @@ def stage70b_line(args) -> dict:
     roofline = {"bound": "mfma", "achieved": round(gu_tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": counter_traffic(GEMM_COUNTER_FILE, "gateup", GEMM_SOURCES),
-                "kernel": "k_gemm_dma (gate/up projection + SwiGLU of the 4096-token chunk, 256 x 256 tiles, "
-                          "ping-pong schedule)",
+                "kernel": "k_gemm_dma (gate/up projection + SwiGLU of the 4096-token chunk: 128 x 256 tiles, "
+                          "64-deep stages, two activation-plane and three weight LDS buffers)",
                 "flops_per_launch": gu_flops, "algorithmic_bytes_per_launch": acc.projection_gemm_bytes(shape, "gateup", T),
                 "avg_launch_us": round(gu_avg_s * 1e6, 2), "launches": n_gu,
                 "issued_frac": round(2 * gu_tf / MFMA_BF16_PEAK_TFLOPS, 4),
