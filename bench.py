@@ -111,6 +111,19 @@ def summarize_rocprof(path: str, top: int = 12) -> None:
         for r in rows[:top]:
             print(f"{r['Name'][:110]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                   f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r.get('Percentage', 0)):.1f}")
+    # one template can serve several launch shapes (the prefill and batched-decode projections share
+    # their GEMM tile): the heaviest kernels again, per grid size, from the per-dispatch trace
+    for f in glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True):
+        agg = {}
+        for r in csv.DictReader(open(f)):
+            grid = "x".join(r.get(k, "?") for k in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"))
+            a = agg.setdefault((r["Kernel_Name"][:110], grid), [0, 0])
+            a[0] += 1
+            a[1] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        print(f"# per launch shape ({os.path.basename(f)}): name | grid (work-items x, y, z) | calls | avg us | "
+              "total ms")
+        for (k, grid), (n, ns) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:2 * top]:
+            print(f"{k} | {grid} | {n} | {ns / n / 1e3:.2f} | {ns / 1e6:.2f}")
     for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
         agg = {}
         for r in csv.DictReader(open(f)):
