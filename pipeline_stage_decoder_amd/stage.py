@@ -12,7 +12,9 @@ from dataclasses import dataclass
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpsd_stage.so")
+# PSD_STAGE_LIB selects another build of the same library (the host-sanitized one in the CPU tests)
+LIB_PATH = os.environ.get("PSD_STAGE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "libpsd_stage.so")
 
 STAGE_OK, STAGE_E_INVALID, STAGE_E_UNSUPPORTED, STAGE_E_DOES_NOT_FIT, STAGE_E_ROLE, STAGE_E_RANGE, \
     STAGE_E_HIP = range(7)
