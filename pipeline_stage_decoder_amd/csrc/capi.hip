@@ -408,7 +408,7 @@ hipError_t attn_half(stage* st, int lb, int rows, const float* x_in, const float
     a.dh = dh;
     a.ctx_cap = st->L.ctx_cap;
     a.max_slots = st->s.max_slots;
-    a.chunk = attn_decode_chunk(rows);
+    a.chunk = attn_decode_chunk_for(rows, hkv, st->L.ctx_cap);
     a.nsplit = nsplit_for(rows, st->L.ctx_cap);
     a.scale_log2 = scale_log2;
     a.part_o = st->part_o;

@@ -51,7 +51,7 @@ struct AttnDecodeArgs {
   const int32_t* slots;     // [B]
   const int32_t* pos;       // [B]; keys [0, pos] are attended
   int B, hq, hkv, dh, ctx_cap, max_slots;
-  int chunk;                // keys per split (the last split of a row takes the remainder)
+  int chunk;                // keys per split (a row's last split takes the remainder)
   int nsplit;               // splits allocated per row (>= attn_decode_splits of every row)
   float scale_log2;         // Dh^-1/2 * log2(e)
   float* part_o;            // [B][Hq][nsplit][Dh]
@@ -125,5 +125,9 @@ __host__ __device__ inline int attn_decode_splits(int n, int chunk) {
   const int s = (n + chunk / 2) / chunk;
   return s > 0 ? s : 1;
 }
+// Keys per split for a decode launch of B rows over Hkv heads in a cache of ctx_cap positions:
+// attn_decode_chunk(B), doubled (from 512 up) when the longer splits of a full-length row still
+// give at least 4096 work-groups (eight per CU), so that each streams a longer stretch of K and V.
+int attn_decode_chunk_for(int B, int hkv, int ctx_cap);
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s);
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);

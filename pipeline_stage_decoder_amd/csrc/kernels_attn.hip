@@ -814,6 +814,14 @@ int attn_decode_chunk(int B) {
   return 512;
 }
 
+// 70B-shaped B = 128 at ctx 8192: 1024-key splits (8192 work-groups) against 512 (16384): 14.7 ->
+// 14.4 ms of attention per decode step.  At B = 64, ctx 4096 the doubled chunk would leave 2048
+// work-groups and was ~1% slower, so the rule keeps 512 there.
+int attn_decode_chunk_for(int B, int hkv, int ctx_cap) {
+  const int c = attn_decode_chunk(B);
+  return (c >= 512 && (long)attn_decode_splits(ctx_cap, 2 * c) * B * hkv >= 4096) ? 2 * c : c;
+}
+
 template <int DH>
 void attn_decode_fmt(const AttnDecodeArgs& a, dim3 grid, hipStream_t s) {
   switch (a.kv_fmt) {
@@ -834,7 +842,10 @@ void attn_prefill_fmt(const AttnPrefillArgs& a, dim3 grid, hipStream_t s) {
 }
 
 hipError_t launch_attn_decode(const AttnDecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.nsplit, a.hkv, a.B);
+  // splits of a full-length row (every row holds at most ctx_cap keys); never more than allocated
+  const int ns = attn_decode_splits(a.ctx_cap, a.chunk);
+  if (ns > a.nsplit) return hipErrorInvalidValue;
+  dim3 grid(ns, a.hkv, a.B);
   if (a.dh == 128) attn_decode_fmt<128>(a, grid, s);
   else attn_decode_fmt<64>(a, grid, s);
   return hipGetLastError();
