@@ -694,6 +694,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_norm(GemmArgs g, NormArgs
 struct Cfg {
   int bm, bn;
 };
+// cfg 8 (a 64 x 256 batched-decode tile) is no longer planned; its slot keeps the numbering
 constexpr Cfg kCfgs[] = {{128, 128}, {64, 256}, {64, 128}, {32, 128}, {16, 128}, {256, 256}, {128, 256}, {128, 256}, {64, 256}, {64, 128}, {128, 256}, {128, 256}};
 
 }  // namespace
@@ -726,10 +727,11 @@ GemmPlan gemm_plan(int M, int N, int K, int planes, bool qkv) {
   //  * Batched decode (32 < M <= 128) splits K as many ways as keep the grid within one round of
   //    256 work-groups (each split >= 512 deep), not in powers of two: the three-plane QKV at
   //    M = 128 runs 40 x 6 work-groups instead of 40 x 4 (70B decode step: QKV 1.73 -> 1.47 ms).
-  //  * 32 < M <= 64 (batched decode): 64 x 256 or 64 x 128 LDS-direct tiles with 64-deep stages
-  //    (8B-shaped projections at M = 64: gate/up 55 -> 50 us, down 37 -> 31 us, O 17.5 -> 16 us);
-  //    the wide-N 64 x 256 tile runs 8 waves of 32 x 64 (two per SIMD; four waves of 64 x 64: gate/up
-  //    50.1 -> 43.5 us, readout 292 -> 270 us).
+  //  * 32 < M <= 64 (batched decode): 64 x 128 LDS-direct tiles with 64-deep stages (8B-shaped
+  //    projections at M = 64: gate/up 55 -> 50 us, down 37 -> 31 us, O 17.5 -> 16 us, against
+  //    32-deep stages).  With every weight read cold (the 8B gate/up, 235 MB, otherwise stays in
+  //    the 256 MB memory-side cache between repetitions), 224 unsplit 64 x 128 tiles beat 112
+  //    64 x 256 tiles in two K splits plus their split-K sum: gate/up 59.8 -> 55.5 us; readout equal.
   //  * 64 < M <= 128 (batched decode): 128 x 256 with 64-deep stages in two LDS buffers (K a
   //    multiple of 64), so each row segment a load instruction fetches is a whole 128-byte line
   //    of the activation or weight row (M = 128: 70B gate/up 324 -> 280 us, O 46.5 -> 41 us, 8B O
@@ -750,10 +752,9 @@ GemmPlan gemm_plan(int M, int N, int K, int planes, bool qkv) {
   GemmPlan p{};
   const bool dma_ok = K % kDmaBK == 0 && (uint64_t)(M > N ? M : N) * K * 2 < (1ull << 32);
   if (dma_ok && K % 64 == 0 && M > 32 && M <= 64) {
-    // batched decode rows: 64 x 256 (two planes, wide N) or 64 x 128 tiles with 64-deep stages,
-    // so that every weight row segment a load instruction touches is a whole 128-byte line; K split
-    // until the grid holds ~200 work-groups
-    const int cfg = (planes == 2 && (N + 255) / 256 >= 96) ? 8 : 9;
+    // batched decode rows: 64 x 128 tiles with 64-deep stages, so that every weight row segment a
+    // load instruction touches is a whole 128-byte line; K split to fill one round of work-groups
+    const int cfg = 9;
     const int tiles = (N + kCfgs[cfg].bn - 1) / kCfgs[cfg].bn;
     const int sk = decode_splits(tiles, K);
     p.cfg = cfg;
@@ -851,9 +852,6 @@ void launch_cfg(const GemmArgs& a, const GemmPlan& p, dim3 grid, hipStream_t s) 
     case 7:
       k_gemm_dma<NP, EPI, 128, 256, 2, 4, NP == 2 ? 4 : 3><<<grid, 512, 0, s>>>(a);
       break;
-    case 8:   // the planner gives it two planes only
-      k_gemm_dma<2, EPI, 64, 256, 2, 4, 3, 64><<<grid, 512, 0, s>>>(a);
-      break;
     case 9: k_gemm_dma<NP, EPI, 64, 128, 1, 4, NP == 2 ? 4 : 3, 64><<<grid, 256, 0, s>>>(a); break;
     case 10:   // two planes only: 2 x 32 KB of activations + 3 x 32 KB of weights = 160 KB of LDS
       k_gemm_dma<2, EPI, 128, 256, 4, 2, 2, 64, false, 3><<<grid, 512, 0, s>>>(a);
@@ -880,10 +878,11 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
                        bool* normed) {
   if (normed) *normed = false;
   // the LDS-direct tile takes two planes, K in whole 32-deep stages and operands under 4 GiB
-  if (((p.cfg == 5 || p.cfg == 8 || p.cfg == 10) && a.planes != 2) || (p.cfg == 11 && a.planes != 3) ||
+  if (((p.cfg == 5 || p.cfg == 10) && a.planes != 2) || (p.cfg == 11 && a.planes != 3) ||
       (p.cfg >= 5 && (a.K % kDmaBK != 0 || (uint64_t)(a.M > a.N ? a.M : a.N) * a.K * 2 >= (1ull << 32))))
     return hipErrorInvalidValue;
   if (p.cfg == 5 && a.e.kind == EPI_QKV) return hipErrorInvalidValue;   // not instantiated (see gemm_plan)
+  if (p.cfg == 8) return hipErrorInvalidValue;                           // retired tile: no launch
   if (p.cfg >= 8 && a.K % 64 != 0) return hipErrorInvalidValue;   // 64-deep stages
   dim3 grid(p.tiles_m * p.tiles_n, p.splitk);
   switch (a.e.kind) {

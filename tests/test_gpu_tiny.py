@@ -232,3 +232,34 @@ def test_context_end_and_ragged_capacity(weights):
     st.decode(torch.from_numpy(xd).to(dev), torch.tensor([0], dtype=torch.int32, device=dev),
               torch.tensor([128], dtype=torch.int32, device=dev))       # past the cache: refused per row
     assert st.device_errors(reset=True) > 0
+
+
+def test_empty_calls_are_refused_and_enqueue_nothing(weights):
+    # a row count of zero is a non-positive size: every entry point returns STAGE_E_INVALID with
+    # real buffers passed, and neither the cache nor the output buffer changes
+    from pipeline_stage_decoder_amd import stage as S
+    st = make_stage(TINY, 0, 2, True, True, weights, max_slots=2, max_ctx=64, max_tokens=16)
+    dev = torch.device("cuda")
+    x = torch.from_numpy(hidden_rows(7, 4, TINY.d_model)).to(dev)
+    st.prefill(x, 0, 0)
+    torch.cuda.synchronize()
+    k0, v0 = kv_bits(st, 0, 0, 8)
+    out = torch.full((4, TINY.d_model), 7.0, device=dev)
+    logits = torch.full((4, TINY.vocab), 7.0, device=dev)
+    idx = torch.zeros(4, dtype=torch.int32, device=dev)
+    L, h, p = S.lib(), st._h, S._ptr
+    calls = {
+        "stage_embed": lambda: L.stage_embed(h, 0, p(idx), p(out), 0),
+        "stage_prefill": lambda: L.stage_prefill(h, 0, 4, 0, p(x), p(out), 0),
+        "stage_decode": lambda: L.stage_decode(h, 0, p(idx), p(idx), p(x), p(out), 0),
+        "stage_readout": lambda: L.stage_readout(h, 0, p(x), p(logits), p(out), 0),
+        "stage_mlp": lambda: L.stage_mlp(h, 0, 0, p(x), p(out), 0, 0),
+        "stage_attn": lambda: L.stage_attn(h, 0, 0, 4, 0, p(x), p(out), 0, 0),
+    }
+    for name, call in calls.items():
+        assert call() == S.STAGE_E_INVALID, name
+    torch.cuda.synchronize()
+    k1, v1 = kv_bits(st, 0, 0, 8)
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    assert bool((out == 7.0).all()) and bool((logits == 7.0).all())
+    assert st.device_errors() == 0
