@@ -33,6 +33,7 @@ struct GemmArgs {
   int splitk;          // K splits; each split's K range is a multiple of 64
   float* part;         // [splitk][M][N] f32 partials when splitk > 1
   EpiArgs e;
+  int w_stream;        // set by launch_gemm: one row of M-tiles, each weight byte read once
 };
 
 struct GemmPlan {

@@ -285,6 +285,18 @@ PSD_DEV void dma16(const uint16_t* base, uint32_t lane_off, uint32_t lds_wave_ba
 #pragma clang diagnostic pop
 }
 
+// the same load, non-temporal: for weights that no other work-group reads (a single row of
+// M-tiles), streamed past the caches
+PSD_DEV void dma16_nt(const uint16_t* base, uint32_t lane_off, uint32_t lds_wave_base) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(lane_off), "s"(base), "s"(lds_wave_base)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8)
 template <int n>
@@ -368,11 +380,18 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm_dma(GemmArgs g) {
       for (int i = 0; i < A_DMA; ++i)
         dma16(g.a + pl * g.a_ps + k0, a_off[i], a_lds + (uint32_t)((buf * NP + pl) * BM * CH * 16 + i * 64 * 16));
   };
+  const bool w_nt = g.w_stream != 0;
   auto issue_b = [&](int t) {   // weight stage t -> buffer t % SB
     const int buf = t % SB;
     const size_t k0 = (size_t)kbeg + (size_t)t * BK;
+    if (w_nt) {
 #pragma unroll
-    for (int i = 0; i < B_DMA; ++i) dma16(g.w + k0, b_off[i], b_lds + (uint32_t)(buf * BN * CH * 16 + i * 64 * 16));
+      for (int i = 0; i < B_DMA; ++i)
+        dma16_nt(g.w + k0, b_off[i], b_lds + (uint32_t)(buf * BN * CH * 16 + i * 64 * 16));
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_DMA; ++i) dma16(g.w + k0, b_off[i], b_lds + (uint32_t)(buf * BN * CH * 16 + i * 64 * 16));
+    }
   };
   auto issue = [&](int t) {
     issue_a(t);
@@ -885,19 +904,23 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
   if (p.cfg == 8) return hipErrorInvalidValue;                           // retired tile: no launch
   if (p.cfg >= 8 && a.K % 64 != 0) return hipErrorInvalidValue;   // 64-deep stages
   dim3 grid(p.tiles_m * p.tiles_n, p.splitk);
+  // one row of M-tiles (batched decode): every weight byte is read by one work-group, so the
+  // LDS-direct tiles stream the weights with non-temporal loads
+  GemmArgs g = a;
+  g.w_stream = p.tiles_m == 1;
   switch (a.e.kind) {
     case EPI_QKV:
       if (a.N % 32 != 0) return hipErrorInvalidValue;   // whole head-dim groups (Dh 64 or 128)
-      if (a.planes == 3) launch_cfg<3, EPI_QKV>(a, p, grid, s);
-      else launch_cfg<2, EPI_QKV>(a, p, grid, s);
+      if (a.planes == 3) launch_cfg<3, EPI_QKV>(g, p, grid, s);
+      else launch_cfg<2, EPI_QKV>(g, p, grid, s);
       if (p.splitk > 1) launch_reduce<EPI_QKV>(a, s);
       break;
     case EPI_SWIGLU:
-      launch_cfg<2, EPI_SWIGLU>(a, p, grid, s);
+      launch_cfg<2, EPI_SWIGLU>(g, p, grid, s);
       if (p.splitk > 1) launch_reduce<EPI_SWIGLU>(a, s);
       break;
     case EPI_RESID:
-      launch_cfg<2, EPI_RESID>(a, p, grid, s);
+      launch_cfg<2, EPI_RESID>(g, p, grid, s);
       if (p.splitk > 1) {
         // one work-group per row, every split's loads of a row in flight together
         if (then_norm && a.N % 4 == 0 && a.N <= kReduceNormMaxN && a.e.ldo == a.N) {
@@ -910,7 +933,7 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
       }
       break;
     default:
-      launch_cfg<2, EPI_F32>(a, p, grid, s);
+      launch_cfg<2, EPI_F32>(g, p, grid, s);
       if (p.splitk > 1) launch_reduce<EPI_F32>(a, s);
       break;
   }
