@@ -710,6 +710,74 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_norm(GemmArgs g, NormArgs
   }
 }
 
+// The same sum and norm for a few rows (batched decode): 1024 threads per row, each owning PER
+// float4 columns (i = 4 t + 4096 j), so that every split's partials of the row, its residual and
+// its gains are in flight in one round trip (up to 8 splits).  The summed row goes to LDS and
+// threads 0..255 take its sum of squares over exactly the elements, order and wave combination of
+// block_rms_scale (thread t: i = 4 t + 1024 j, j ascending; waves 0..3), so the RMS scale -- and
+// every output bit -- equals k_rmsnorm's and the 256-thread kernel's.
+template <int PER>
+__global__ __launch_bounds__(1024) void k_splitk_reduce_norm_w(GemmArgs g, NormArgs nrm) {
+  constexpr int SB = 8;
+  __shared__ double red[16];
+  __shared__ float4 vrow[kReduceNormMaxN / 4];
+  const int r = blockIdx.x, N = g.N;
+  const size_t plane = (size_t)g.M * N;
+  const EpiArgs& e = g.e;
+  float4 res[PER], gn[PER], x[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x * 4 + j * 4096;
+    res[j] = gn[j] = x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < N) {
+      res[j] = *(const float4*)(e.resid + (size_t)r * e.ldo + i);
+      gn[j] = *(const float4*)(nrm.gain + i);
+    }
+  }
+  for (int sp0 = 0; sp0 < g.splitk; sp0 += SB) {
+    float4 p[SB][PER];
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = threadIdx.x * 4 + j * 4096;
+        p[u][j] = (sp0 + u < g.splitk && i < N) ? *(const float4*)(g.part + (sp0 + u) * plane + (size_t)r * N + i)
+                                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int u = 0; u < SB; ++u)
+      if (sp0 + u < g.splitk) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          x[j].x += p[u][j].x;
+          x[j].y += p[u][j].y;
+          x[j].z += p[u][j].z;
+          x[j].w += p[u][j].w;
+        }
+      }
+  }
+  float4 v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x * 4 + j * 4096;
+    if (i < N) {
+      v[j] = make_float4(res[j].x + x[j].x, res[j].y + x[j].y, res[j].z + x[j].z, res[j].w + x[j].w);
+      *(float4*)(e.out + (size_t)r * e.ldo + i) = v[j];
+      vrow[i / 4] = v[j];
+    }
+  }
+  __syncthreads();
+  double ss = 0.0;
+  if (threadIdx.x < 256)
+    for (int i = threadIdx.x * 4; i < N; i += 1024) ss = sumsq4(vrow[i / 4], ss);
+  const double rs = block_rms_finish(ss, N, nrm.eps, red);   // waves 4..15 add nothing it reads
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x * 4 + j * 4096;
+    if (i < N) store_norm_planes4(nrm.out_pair + (size_t)r * N + i, nrm.pair_ps, v[j], rs, gn[j]);
+  }
+}
+
 struct Cfg {
   int bm, bn;
 };
@@ -924,8 +992,14 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
       if (p.splitk > 1) {
         // one work-group per row, every split's loads of a row in flight together
         if (then_norm && a.N % 4 == 0 && a.N <= kReduceNormMaxN && a.e.ldo == a.N) {
-          if (a.N <= 4096) k_splitk_reduce_norm<4><<<a.M, 256, 0, s>>>(a, *then_norm);
-          else k_splitk_reduce_norm<kReduceNormMaxN / 1024><<<a.M, 256, 0, s>>>(a, *then_norm);
+          if (a.M < 256) {   // few rows: a 1024-thread work-group per row, one round of loads
+            if (a.N <= 4096) k_splitk_reduce_norm_w<1><<<a.M, 1024, 0, s>>>(a, *then_norm);
+            else k_splitk_reduce_norm_w<kReduceNormMaxN / 4096><<<a.M, 1024, 0, s>>>(a, *then_norm);
+          } else if (a.N <= 4096) {
+            k_splitk_reduce_norm<4><<<a.M, 256, 0, s>>>(a, *then_norm);
+          } else {
+            k_splitk_reduce_norm<kReduceNormMaxN / 1024><<<a.M, 256, 0, s>>>(a, *then_norm);
+          }
           if (normed) *normed = true;
         } else {
           launch_reduce<EPI_RESID>(a, s);
