@@ -361,7 +361,11 @@ PSD_DEV int k_swz(int key) {
   return RC >= 16 ? c * (RC / 16) : c >> 1;
 }
 
-template <int DH, int FMT>
+// NBUF LDS tile buffers: 2 (one tile's global loads in flight while the current one is consumed),
+// or 3 for a 2-byte cache on a grid of at most one work-group per CU, where no second work-group
+// hides the load latency: the loads of tile t + 2 are issued while tile t is consumed, into the
+// register set that tile t + 1 does not occupy.
+template <int DH, int FMT, int NBUF>
 __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
   typedef Kv<FMT> F;
   constexpr bool KF32 = F::pair;
@@ -374,8 +378,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
   constexpr int NPL = KF32 ? 2 : 1;
   constexpr int RC = DH / 8;                               // 16-byte chunks per bf16 K row
   constexpr int PLANE = kKeyTile * RC;                     // uint4 per plane tile
-  __shared__ uint4 kt[2][NPL][PLANE];
-  __shared__ uint4 vt[2][NPL][PLANE];
+  static_assert(NBUF == 2 || (NBUF == 3 && !KF32), "three buffers: 2-byte caches only");
+  __shared__ uint4 kt[NBUF][NPL][PLANE];
+  __shared__ uint4 vt[NBUF][NPL][PLANE];
 
   const int G = a.hq / a.hkv;
   // Work-groups go to the 8 XCDs round-robin in linear block order, so block b takes KV head
@@ -407,16 +412,17 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
   const u32x4* vg = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.vc) +
                                                   ((size_t)a.slot * a.hkv + kvh) * (size_t)a.ctx_cap * DH * EB);
   // a tile is one contiguous byte range of K (kKeyTile rows) and of V (kKeyTile / 8 packed groups)
-  u32x4 kr[PER_THREAD], vr[PER_THREAD];
-  auto gload = [&](int tile) {
+  u32x4 kr[PER_THREAD], vr[PER_THREAD], kr2[PER_THREAD], vr2[PER_THREAD];
+  auto gload_into = [&](int tile, u32x4 (&gk)[PER_THREAD], u32x4 (&gv)[PER_THREAD]) {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       const int q = threadIdx.x + i * 256;
-      kr[i] = kg[(size_t)tile * TILE_CHUNKS + q];
-      vr[i] = vg[(size_t)tile * TILE_CHUNKS + q];
+      gk[i] = kg[(size_t)tile * TILE_CHUNKS + q];
+      gv[i] = vg[(size_t)tile * TILE_CHUNKS + q];
     }
   };
-  auto sstore = [&](int buf) {
+  auto gload = [&](int tile) { gload_into(tile, kr, vr); };
+  auto sstore_from = [&](int buf, const u32x4 (&kr)[PER_THREAD], const u32x4 (&vr)[PER_THREAD]) {
 #pragma unroll
     for (int i = 0; i < PER_THREAD; ++i) {
       const int q = threadIdx.x + i * 256;
@@ -435,15 +441,10 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
       }
     }
   };
+  auto sstore = [&](int buf) { sstore_from(buf, kr, vr); };
 
-  if (tile0 < ntiles) {
-    gload(tile0);
-    sstore(tile0 & 1);
-  }
-  __syncthreads();
-  for (int tile = tile0; tile < ntiles; ++tile) {
-    const int cur = tile & 1;
-    if (tile + 1 < ntiles) gload(tile + 1);
+  // every wave's steps of tile `tile` from LDS buffer `cur`
+  auto consume = [&](int tile, int cur) {
 #pragma unroll
     for (int sub = 0; sub < kKeyTile / 32; ++sub) {
     const int kb = tile * kKeyTile + sub * 32;
@@ -525,8 +526,43 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
       }
     }
     }
-    if (tile + 1 < ntiles) sstore(cur ^ 1);
+  };
+
+  if constexpr (NBUF == 2) {
+    if (tile0 < ntiles) {
+      gload(tile0);
+      sstore(tile0 & 1);
+    }
     __syncthreads();
+    for (int tile = tile0; tile < ntiles; ++tile) {
+      const int cur = tile & 1;
+      if (tile + 1 < ntiles) gload(tile + 1);
+      consume(tile, cur);
+      if (tile + 1 < ntiles) sstore(cur ^ 1);
+      __syncthreads();
+    }
+  } else {
+    // Set 1 holds tile t + 1 while set 2 receives tile t + 2 (the roles swap every tile, so the
+    // loop is unrolled by two).  The loads are unconditional -- past the last tile they re-read
+    // it -- so that at each store the only loads still in flight are the other set's.
+    const int last = ntiles - 1;
+    auto step = [&](int tile, u32x4 (&ldk)[PER_THREAD], u32x4 (&ldv)[PER_THREAD],
+                    const u32x4 (&stk)[PER_THREAD], const u32x4 (&stv)[PER_THREAD]) {
+      gload_into(min(tile + 2, last), ldk, ldv);
+      consume(tile, tile % 3);
+      if (tile + 1 < ntiles) sstore_from((tile + 1) % 3, stk, stv);
+      __syncthreads();
+    };
+    if (tile0 < ntiles) {
+      gload_into(tile0, kr, vr);
+      sstore_from(tile0 % 3, kr, vr);
+      gload_into(min(tile0 + 1, last), kr, vr);
+    }
+    __syncthreads();
+    for (int tile = tile0; tile < ntiles; tile += 2) {
+      step(tile, kr2, vr2, kr, vr);
+      if (tile + 1 < ntiles) step(tile + 1, kr, vr, kr2, vr2);
+    }
   }
 
   float l = st.l;
@@ -846,10 +882,18 @@ void attn_decode_fmt(const AttnDecodeArgs& a, dim3 grid, hipStream_t s) {
 
 template <int DH>
 void attn_prefill_fmt(const AttnPrefillArgs& a, dim3 grid, hipStream_t s) {
+  // at most one work-group per CU: three LDS tile buffers for a 2-byte cache
+  const bool deep = (long)grid.x * grid.y <= 256;
   switch (a.kv_fmt) {
-    case KV_F32: k_attn_prefill<DH, KV_F32><<<grid, 256, 0, s>>>(a); break;
-    case KV_F16: k_attn_prefill<DH, KV_F16><<<grid, 256, 0, s>>>(a); break;
-    default: k_attn_prefill<DH, KV_BF16><<<grid, 256, 0, s>>>(a); break;
+    case KV_F32: k_attn_prefill<DH, KV_F32, 2><<<grid, 256, 0, s>>>(a); break;
+    case KV_F16:
+      if (deep) k_attn_prefill<DH, KV_F16, 3><<<grid, 256, 0, s>>>(a);
+      else k_attn_prefill<DH, KV_F16, 2><<<grid, 256, 0, s>>>(a);
+      break;
+    default:
+      if (deep) k_attn_prefill<DH, KV_BF16, 3><<<grid, 256, 0, s>>>(a);
+      else k_attn_prefill<DH, KV_BF16, 2><<<grid, 256, 0, s>>>(a);
+      break;
   }
 }
 
