@@ -19,6 +19,34 @@ __global__ __launch_bounds__(256) void k_rmsnorm(NormArgs a) {
   }
 }
 
+// The same for rows of exactly PER * 1024 values: each thread loads its PER float4 (and gains) at
+// once instead of one per loop trip, then sums their squares in the same order as
+// block_rms_scale (i = 4 t + 1024 j, j ascending), so the scale and every output bit are equal.
+template <int PER>
+__global__ __launch_bounds__(256) void k_rmsnorm_rows(NormArgs a) {
+  __shared__ double red[4];
+  const int m = blockIdx.x;
+  const float* x = a.x + (size_t)m * a.K;
+  float4 v[PER], g[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    v[j] = *(const float4*)(x + threadIdx.x * 4 + j * 1024);
+    g[j] = *(const float4*)(a.gain + threadIdx.x * 4 + j * 1024);
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) ss = sumsq4(v[j], ss);
+  const double r = block_rms_finish(ss, a.K, a.eps, red);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x * 4 + j * 1024;
+    if (a.out_f32)
+      *(float4*)(a.out_f32 + (size_t)m * a.K + i) = make_float4(
+          norm_mul(v[j].x, r, g[j].x), norm_mul(v[j].y, r, g[j].y), norm_mul(v[j].z, r, g[j].z), norm_mul(v[j].w, r, g[j].w));
+    if (a.out_pair) store_norm_planes4(a.out_pair + (size_t)m * a.K + i, a.pair_ps, v[j], r, g[j]);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_embed(const uint16_t* __restrict__ table, int V, int d,
                                                const int32_t* __restrict__ tokens, float* __restrict__ out,
                                                uint32_t* err) {
@@ -167,7 +195,9 @@ __global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ logits
 
 hipError_t launch_rmsnorm(const NormArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
-  k_rmsnorm<<<a.M, 256, 0, s>>>(a);
+  if (a.K == 4096) k_rmsnorm_rows<4><<<a.M, 256, 0, s>>>(a);
+  else if (a.K == 8192) k_rmsnorm_rows<8><<<a.M, 256, 0, s>>>(a);
+  else k_rmsnorm<<<a.M, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
