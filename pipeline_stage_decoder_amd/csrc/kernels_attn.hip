@@ -615,6 +615,12 @@ PSD_DEV f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// 2^x by the hardware instruction alone: exp2f adds a range fix so that results below 2^-126 come
+// out denormal, which a softmax weight never needs (the instruction flushes them to zero).  It
+// gives exactly 1 for x = 0 and 0 for x = -inf, as the online softmax relies on.
+PSD_DEV float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLazyBase = 8.0f;
+
 // key (within a 32-key step) of S^T row rho = 8a + 4h + r: (a / 2) * 16 + h * 8 + (a % 2) * 4 + r
 PSD_DEV int key_of_row32(int rho) {
   const int a = rho >> 3, h = (rho >> 2) & 1, r = rho & 3;
@@ -735,34 +741,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           sc = mfma32(kf, ql[ks], sc);
         }
         // slot j: key kb + (j / 8) * 16 + half * 8 + j % 8
-        // every key of the step visible to every live column of the wave: no per-key mask
-        const bool all_vis = kb >= a.k_lo && kb + 32 <= kend && kb + 31 <= a.pos0 + c0 / G;
+        // every key of the step visible to every live column of the wave (a wave-uniform test):
+        // the scores without the per-key mask
         float sv[16];
         float mx = kNegInf;
+        if (kb >= a.k_lo && kb + 32 <= kend && kb + 31 <= a.pos0 + c0 / G) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = kb + ((j >> 3) << 4) + (half << 3) + (j & 7);
-          const bool vis = all_vis || (key >= a.k_lo && key < kend && key <= my_pos);
-          sv[j] = vis ? sc[j] * a.scale_log2 : kNegInf;
-          mx = fmaxf(mx, sv[j]);
+          for (int j = 0; j < 16; ++j) {
+            sv[j] = sc[j] * a.scale_log2;
+            mx = fmaxf(mx, sv[j]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = kb + ((j >> 3) << 4) + (half << 3) + (j & 7);
+            const bool vis = key >= a.k_lo && key < kend && key <= my_pos;
+            sv[j] = vis ? sc[j] * a.scale_log2 : kNegInf;
+            mx = fmaxf(mx, sv[j]);
+          }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m, mx);
+        // the column's base moves only when a score exceeds it by more than kLazyBase (2^8): the
+        // weights below are then at most 256, the output and the sum carry the same factor, and
+        // the 64-value rescale runs only when some column of the wave moved
+        const bool move = mx > m + kLazyBase;
+        const float m_new = move ? mx : m;
         const float base = (m_new == kNegInf) ? 0.0f : m_new;
-        const float alpha = exp2f(m - base);
+        const float alpha = exp2_hw(m - base);
         float p0[8], p1[8], ps = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          p0[j] = exp2f(sv[j] - base);
-          p1[j] = exp2f(sv[8 + j] - base);
+          p0[j] = exp2_hw(sv[j] - base);
+          p1[j] = exp2_hw(sv[8 + j] - base);
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) ps += p0[j];
 #pragma unroll
         for (int j = 0; j < 8; ++j) ps += p1[j];
         l = l * alpha + ps;
-        // alpha is exactly 1 (max unmoved) or o is still 0 (no key seen) for every lane: skip
-        if (__any(m_new != m && m != kNegInf)) {
+        // alpha is exactly 1 (base unmoved) or o is still 0 (no key seen) for every lane: skip
+        if (__any(move && m != kNegInf)) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) o[db] *= alpha;
         }
