@@ -35,6 +35,16 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// 2^x by the hardware instruction alone: exp2f adds a range fix so that results below 2^-126 come
+// out denormal, which a softmax weight never needs (the instruction flushes them to zero).  It
+// gives exactly 1 for x = 0 and 0 for x = -inf, as the online softmax relies on.
+PSD_DEV float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Lazy softmax base: a column's running base moves only when a score exceeds it by more than this
+// (log2 units), so its weights stay at most 2^8 = 256 -- the output and the sum carry the same
+// factor, and the output rescale runs only when some column of the wave moved.
+constexpr float kLazyBase = 8.0f;
+
 // Keys of the two S^T MFMAs that A row `rho` (0..15) of chunk c feeds: (rho/4)*8 + c*4 + rho%4.
 PSD_DEV int key_of_row(int rho, int c) { return ((rho >> 2) << 3) + (c << 2) + (rho & 3); }
 
@@ -164,14 +174,14 @@ PSD_DEV void attn_step(Col16<DH, FMT>& st, const uint16_t* __restrict__ kbase, c
   else scores(std::true_type{});
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float m_old = st.m, m_new = fmaxf(st.m, mx);
+  const float m_old = st.m, m_new = mx > st.m + kLazyBase ? mx : st.m;
   // m_new is -inf only if this column has seen no visible key yet; keep everything at zero then.
   const float base = (m_new == kNegInf) ? 0.0f : m_new;
-  const float alpha = exp2f(m_old - base);
+  const float alpha = exp2_hw(m_old - base);
   float p[8], ps = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = exp2f(s[e] - base);
+    p[e] = exp2_hw(s[e] - base);
     ps += p[e];
   }
   st.l = st.l * alpha + ps;
@@ -494,13 +504,13 @@ __global__ __launch_bounds__(256) void k_attn_prefill(AttnPrefillArgs a) {
       else scores(std::true_type{});
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_old = st.m, m_new = fmaxf(st.m, mx);
+      const float m_old = st.m, m_new = mx > st.m + kLazyBase ? mx : st.m;
       const float base = (m_new == kNegInf) ? 0.0f : m_new;
-      const float alpha = exp2f(m_old - base);
+      const float alpha = exp2_hw(m_old - base);
       float p[8], ps = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = exp2f(sv[e] - base);
+        p[e] = exp2_hw(sv[e] - base);
         ps += p[e];
       }
       st.l = st.l * alpha + ps;
@@ -615,11 +625,6 @@ PSD_DEV f32x16_t mfma32(f16x8_t a, f16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// 2^x by the hardware instruction alone: exp2f adds a range fix so that results below 2^-126 come
-// out denormal, which a softmax weight never needs (the instruction flushes them to zero).  It
-// gives exactly 1 for x = 0 and 0 for x = -inf, as the online softmax relies on.
-PSD_DEV float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-constexpr float kLazyBase = 8.0f;
 
 // key (within a 32-key step) of S^T row rho = 8a + 4h + r: (a / 2) * 16 + h * 8 + (a % 2) * 4 + r
 PSD_DEV int key_of_row32(int rho) {
