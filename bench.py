@@ -697,16 +697,21 @@ DECODE_KINDS = ("qkv", "attn", "o", "gateup", "down")
 
 
 def issued_mfma_flops(shape, n_blocks: int, T: int, kv: str, pos0: int = 0) -> int:
-    """MFMA work a prefill issues: activation operands enter as bf16 planes -- three for QKV over a
-    2-byte cache, two otherwise -- so each projection executes planes x its algorithmic flops;
-    attention takes 2 products per score / output term (3 over the F32-grade cache's pairs)."""
+    """MFMA work a prefill issues: activation operands enter as bf16 planes, so each projection
+    executes planes x its algorithmic flops.  Two planes, except the QKV rows whose outputs are
+    rounded into a 2-byte cache: at 256 or more rows only the K/V rows take three (the q rows are
+    a separate two-plane GEMM), below that the fused projection takes three.  Attention takes 2
+    products per score / output term (3 over the F32-grade cache's pairs)."""
     from pipeline_stage_decoder_amd import accounting as acc
     lin = 0
     for kind, (n, k) in acc.projection_shapes(shape).items():
         if kind == "readout":
             continue
-        planes = (2 if kv == "f32" else 3) if kind == "qkv" else 2
-        lin += 2 * T * n * k * planes
+        if kind == "qkv" and kv != "f32":
+            n3 = 2 * shape.n_kv_heads * shape.head_dim if T >= 256 else n
+            lin += 2 * T * k * (2 * (n - n3) + 3 * n3)
+        else:
+            lin += 2 * T * n * k * 2
     attn = acc.prefill_flops(shape, 1, T, pos0=pos0) - acc.prefill_flops(shape, 1, T, pos0=pos0, attn=False)
     return n_blocks * (lin + attn * (3 if kv == "f32" else 2))
 

@@ -155,13 +155,15 @@ Layout make_layout(const stage_model_cfg& m, const stage_stage_cfg& s) {
   L.part_o = take(part_rows * hq * dh * 4);
   L.part_lse = take(part_rows * hq * 4);
   uint64_t gpart = 0;
-  const int shapes[5][2] = {{L.qkv_n, (int)d}, {(int)d, (int)(hq * dh)}, {(int)(2 * F), (int)d},
-                            {(int)d, (int)F}, {(int)V, (int)d}};
+  // the projections, the fused QKV also in its q and K/V row ranges (rows 0, 5, 6: QKV epilogue)
+  const int shapes[7][2] = {{L.qkv_n, (int)d}, {(int)d, (int)(hq * dh)}, {(int)(2 * F), (int)d},
+                            {(int)d, (int)F}, {(int)V, (int)d}, {(int)(hq * dh), (int)d},
+                            {(int)(2 * hkv * dh), (int)d}};
   for (int Mr = 1; Mr <= s.max_tokens; ++Mr)
-    for (int k = 0; k < 5; ++k)
+    for (int k = 0; k < 7; ++k)
       for (int planes = 2; planes <= 3; ++planes) {
         if (shapes[k][0] <= 0) continue;
-        const GemmPlan p = gemm_plan(Mr, shapes[k][0], shapes[k][1], planes, k == 0);
+        const GemmPlan p = gemm_plan(Mr, shapes[k][0], shapes[k][1], planes, k == 0 || k >= 5);
         if (p.splitk > 1) {
           const uint64_t need = (uint64_t)p.splitk * Mr * shapes[k][0] * 4;
           if (need > gpart) gpart = need;
@@ -350,6 +352,27 @@ hipError_t project(stage* st, int kind, int rows, const float* x_f32, const floa
   return launch_gemm(g, p, s, next && next->gain ? &then : nullptr, next ? &next->done : nullptr);
 }
 
+// The QKV projection of norm(x_in) (x_normed: the norm workspace already holds it), its epilogue
+// applying RoPE and writing q and the K/V cache.  Over a 2-byte cache the K/V outputs need the
+// three-plane operand; q goes to attention as a pair and gains nothing from a third plane, so from
+// 256 rows on the fused weight is taken in two row ranges: the q rows over two planes, the K/V
+// rows over three (the norm workspace holds all three; the first two are the pair split).  The
+// q rows' sums are those of the two-plane product, the K/V rows' those of the fused one.  At
+// batched-decode sizes the two launches (each with its own K split and sum) are slower than one.
+hipError_t project_qkv(stage* st, int rows, const float* x_in, const float* gain, const uint16_t* w,
+                       const EpiArgs& e, hipStream_t s, bool x_normed) {
+  const int d = st->m.d_model, qw = st->m.n_q_heads * st->m.head_dim;
+  if (qkv_planes(st) == 2 || gemv_fits(rows, d) || rows < 256)
+    return project(st, STAGE_KT_QKV, rows, x_in, gain, nullptr, 0, w, st->L.qkv_n, d, e, s, qkv_planes(st),
+                   nullptr, x_normed);
+  hipError_t err = project(st, STAGE_KT_QKV, rows, x_in, gain, nullptr, 0, w, qw, d, e, s, 2, nullptr, x_normed);
+  if (err != hipSuccess) return err;
+  EpiArgs ekv = e;
+  ekv.col_off = qw;
+  return project(st, STAGE_KT_QKV, rows, x_in, gain, nullptr, 0, w + (size_t)qw * d, st->L.qkv_n - qw, d, ekv,
+                 s, 3, nullptr, true);
+}
+
 // The MLP half of a block: out = resid + W_down(silu(W_gate h) * W_up h), h = norm(x).
 // x_normed: the norm workspace already holds norm(x); next: see NextNorm (after the down projection).
 hipError_t mlp_half(stage* st, int lb, int rows, const float* x, const float* resid, float* out,
@@ -388,8 +411,7 @@ hipError_t attn_half(stage* st, int lb, int rows, const float* x_in, const float
   e.kc = kc;
   e.vc = vc;
   e.rp = rp;
-  hipError_t err = project(st, STAGE_KT_QKV, rows, x_in, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s,
-                           qkv_planes(st), nullptr, x_normed);
+  hipError_t err = project_qkv(st, rows, x_in, bw.attn_norm, bw.wqkv, e, s, x_normed);
   if (err != hipSuccess) return err;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   if (decode) {
@@ -619,7 +641,7 @@ int ring_run(stage_t* st, int global_block, int slot, int T, int n_ranks, int zi
   e.kc = kc;
   e.vc = vc;
   e.rp = RowPos{nullptr, nullptr, slot, 0};
-  HIP_TRY(st, project(st, STAGE_KT_QKV, T, hin, bw.attn_norm, nullptr, 0, bw.wqkv, st->L.qkv_n, d, e, s, qkv_planes(st)));
+  HIP_TRY(st, project_qkv(st, T, hin, bw.attn_norm, bw.wqkv, e, s, false));
 
   // every rank attends its query chunks to the KV chunks it holds at each hop, merging in hop order
   const auto chunks = ring_chunks(T, n_ranks, zigzag != 0);

@@ -154,6 +154,8 @@ struct EpiArgs {
                                // and then a lo plane (4 bytes per element); KV_F16 also stores
                                // q as binary16 planes
   const double2* rope;         // [ctx_cap][Dh/2] (cos, sin), f64
+  int col_off;                 // fused-QKV stored row of output column 0: a GEMM over a row range of
+                               // the fused weight (a multiple of 32; GEMM paths only, 0 for GEMVs)
   RowPos rp;
   int hq, hkv, dh, ctx_cap, max_slots;
   uint32_t* err;               // device error counter
@@ -253,6 +255,7 @@ PSD_DEV void qkv_store_pair(const EpiArgs& e, int m, int slot, int pos, int col0
 PSD_DEV void qkv_epilogue_pair(const EpiArgs& e, int m, int col0, float x0, float x1) {
   int slot, pos;
   if (!row_slot_pos(e, m, slot, pos)) return;
+  col0 += e.col_off;
   qkv_store_pair(e, m, slot, pos, col0, x0, x1, qkv_rope_cs(e, pos, col0));
 }
 

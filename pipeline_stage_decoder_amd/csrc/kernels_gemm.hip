@@ -86,7 +86,7 @@ PSD_DEV void gemm_store(const GemmArgs& g, const f32x4_t (&acc)[TM][TN], int r0,
           } else {
             int slot, pos;
             if (!row_slot_pos(e, r, slot, pos)) {
-              if (c == 0) atomicAdd(e.err, 1u);
+              if (c + e.col_off == 0) atomicAdd(e.err, 1u);
             } else {
               qkv_epilogue_pair(e, r, c, x0, x1);
             }
@@ -591,11 +591,12 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
         x1.y += b.y;
       }
       int slot, pos;
+      const int s0 = c0 + e.col_off;   // stored row of the fused weight
       if (!row_slot_pos(e, r, slot, pos)) {
-        if (c0 == 0) atomicAdd(e.err, 1u);
+        if (s0 == 0) atomicAdd(e.err, 1u);
       } else {
-        qkv_store_pair(e, r, slot, pos, c0, x0.x, x1.x, qkv_rope_cs(e, pos, c0));
-        qkv_store_pair(e, r, slot, pos, c0 + 1, x0.y, x1.y, qkv_rope_cs(e, pos, c0 + 1));
+        qkv_store_pair(e, r, slot, pos, s0, x0.x, x1.x, qkv_rope_cs(e, pos, s0));
+        qkv_store_pair(e, r, slot, pos, s0 + 1, x0.y, x1.y, qkv_rope_cs(e, pos, s0 + 1));
       }
     }
     return;
@@ -623,7 +624,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
       } else {
         int slot, pos;
         if (!row_slot_pos(e, r, slot, pos)) {
-          if (c0 == 0) atomicAdd(e.err, 1u);
+          if (c0 + e.col_off == 0) atomicAdd(e.err, 1u);
         } else {
           qkv_epilogue_pair(e, r, c0, x0, x1);
         }
@@ -978,7 +979,8 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t s, cons
   g.w_stream = p.tiles_m == 1;
   switch (a.e.kind) {
     case EPI_QKV:
-      if (a.N % 32 != 0) return hipErrorInvalidValue;   // whole head-dim groups (Dh 64 or 128)
+      // whole head-dim groups (Dh 64 or 128), from a stored row that starts a group
+      if (a.N % 32 != 0 || a.e.col_off % 32 != 0 || a.e.col_off < 0) return hipErrorInvalidValue;
       if (a.planes == 3) launch_cfg<3, EPI_QKV>(g, p, grid, s);
       else launch_cfg<2, EPI_QKV>(g, p, grid, s);
       if (p.splitk > 1) launch_reduce<EPI_QKV>(a, s);

@@ -357,6 +357,7 @@ bool gemv1_fits(int B, int K, int N) {
 }
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t s) {
+  if (a.e.kind == EPI_QKV && a.e.col_off != 0) return hipErrorInvalidValue;   // whole fused weight only
   if (gemv1_fits(a.B, a.K, a.N)) {
     switch (a.e.kind) {
       case EPI_F32: launch_one_l<EPI_F32>(a, s); break;
