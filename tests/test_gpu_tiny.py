@@ -11,7 +11,7 @@ import torch
 
 import fixtures as fx
 from oracle import decoder as o
-from tests.gpu_util import gpu_generate, hidden_rows, kv_bits, make_stage, rel_l2, rel_l2_kv, say
+from tests.gpu_util import gpu_generate, hidden_rows, kv_bits, kv_values, make_stage, rel_l2, rel_l2_kv, say
 
 pytestmark = pytest.mark.gpu
 
@@ -177,6 +177,62 @@ def test_device_side_range_checks(weights, bad):
     if bad == "position":
         k, v = kv_bits(st, 0, 1, 2)
         assert not k.any() and not v.any()
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16"])
+def test_wide_decode_batch_splits_the_qkv_rows(weights, kv):
+    # 300 decode rows in 300 slots: from 256 rows on, over a 2-byte cache, the QKV projection runs as
+    # two GEMMs over row ranges of the fused weight (q over two activation planes, K/V over three).
+    # Two steps, so every row attends to two keys and q matters; in the second, three rows are out
+    # of range: one error per bad row and block (not one per GEMM), no K/V written for them, their
+    # outputs x + MLP(x) block by block, and every other row bit-identical to a call whose rows are
+    # all valid
+    B, ctx, dev = 300, 16, torch.device("cuda")
+    say(f"300-row decode, {kv} cache")
+    kw = dict(max_slots=B, max_ctx=ctx, max_tokens=B, kv=kv)
+    st = make_stage(TINY, 0, 2, True, False, weights, **kw)
+    ref = make_stage(TINY, 0, 2, True, False, weights, **kw)
+    ost = oracle_stage(weights, 0, 2, True, False, max_ctx=ctx, kv_dtype=kv)
+
+    def i32(a):
+        return torch.tensor(np.asarray(a), dtype=torch.int32, device=dev)
+
+    slots = np.arange(B)
+    x0, x1 = hidden_rows(11, B, TINY.d_model), hidden_rows(12, B, TINY.d_model)
+    want0 = ost.forward(x0, slots, np.zeros(B, np.int64))
+    for s in (st, ref):
+        got0 = s.decode(torch.from_numpy(x0).to(dev), i32(slots), i32(np.zeros(B))).cpu().numpy()
+        e = rel_l2(got0, want0)
+        say(f"  step 1 vs oracle: {e:.2e}")
+        assert e <= TOL
+    st.device_errors(reset=True)
+    sl, ps = slots.copy(), np.ones(B, np.int64)
+    sl[7], ps[150], sl[299] = B, 100000, -1               # slot past the cache, position past it, negative slot
+    bad = np.array([7, 150, 299])
+    ok = np.setdiff1d(slots, bad)
+    got = st.decode(torch.from_numpy(x1).to(dev), i32(sl), i32(ps)).cpu().numpy()
+    assert st.device_errors(reset=True) == len(bad) * 2      # per bad row and block
+    good = ref.decode(torch.from_numpy(x1).to(dev), i32(slots), i32(np.ones(B))).cpu().numpy()
+    assert ref.device_errors() == 0
+    assert got[ok].tobytes() == good[ok].tobytes()
+    want1 = ost.forward(x1[ok], slots[ok], np.ones(len(ok), np.int64))
+    e = rel_l2(got[ok], want1)
+    say(f"  step 2, {len(ok)} valid rows vs oracle: {e:.2e}")
+    assert e <= TOL
+    want_bad = x1[bad]
+    for b in range(2):
+        want_bad = (want_bad + ost.mlp(b, want_bad)).astype(np.float32)
+    assert rel_l2(got[bad], want_bad) <= TOL
+    # the K/V rows of the fused weight's second range land at the right heads and positions
+    for b in range(2):
+        for slot in (0, 149, 150, 298):
+            k, v = kv_bits(st, b, slot, 2)
+            kc, vc = ost.kv[slot]
+            n = 1 if slot == 150 else 2                        # row 150's second step wrote nothing
+            assert rel_l2_kv(kv_values(kv, k[:n]), kc[b, :n]) <= TOL
+            assert rel_l2_kv(kv_values(kv, v[:n]), vc[b, :n]) <= TOL
+            if n == 1:
+                assert not k[1].any() and not v[1].any()
 
 
 @pytest.mark.parametrize("hq,hkv,dh", [(4, 4, 64), (16, 1, 128), (8, 2, 128)])
