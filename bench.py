@@ -699,16 +699,18 @@ DECODE_KINDS = ("qkv", "attn", "o", "gateup", "down")
 def issued_mfma_flops(shape, n_blocks: int, T: int, kv: str, pos0: int = 0) -> int:
     """MFMA work a prefill issues: activation operands enter as bf16 planes, so each projection
     executes planes x its algorithmic flops.  Two planes, except the QKV rows whose outputs are
-    rounded into a 2-byte cache: at 256 or more rows only the K/V rows take three (the q rows are
-    a separate two-plane GEMM), below that the fused projection takes three.  Attention takes 2
-    products per score / output term (3 over the F32-grade cache's pairs)."""
+    rounded into a 2-byte cache: when the q rows alone make 256 or more 128 x 256 tiles only the
+    K/V rows take three (the q rows are a separate two-plane GEMM), otherwise the fused projection
+    takes three.  Attention takes 2 products per score / output term (3 over the F32-grade cache's
+    pairs)."""
     from pipeline_stage_decoder_amd import accounting as acc
     lin = 0
     for kind, (n, k) in acc.projection_shapes(shape).items():
         if kind == "readout":
             continue
         if kind == "qkv" and kv != "f32":
-            n3 = 2 * shape.n_kv_heads * shape.head_dim if T >= 256 else n
+            q_tiles = -(-T // 128) * -(-(shape.n_q_heads * shape.head_dim) // 256)
+            n3 = 2 * shape.n_kv_heads * shape.head_dim if T >= 256 and q_tiles >= 256 else n
             lin += 2 * T * k * (2 * (n - n3) + 3 * n3)
         else:
             lin += 2 * T * n * k * 2

@@ -354,15 +354,17 @@ hipError_t project(stage* st, int kind, int rows, const float* x_f32, const floa
 
 // The QKV projection of norm(x_in) (x_normed: the norm workspace already holds it), its epilogue
 // applying RoPE and writing q and the K/V cache.  Over a 2-byte cache the K/V outputs need the
-// three-plane operand; q goes to attention as a pair and gains nothing from a third plane, so from
-// 256 rows on the fused weight is taken in two row ranges: the q rows over two planes, the K/V
-// rows over three (the norm workspace holds all three; the first two are the pair split).  The
-// q rows' sums are those of the two-plane product, the K/V rows' those of the fused one.  At
-// batched-decode sizes the two launches (each with its own K split and sum) are slower than one.
+// three-plane operand; q goes to attention as a pair and gains nothing from a third plane, so when
+// the q rows alone fill a round of 256 tiles the fused weight is taken in two row ranges: the q
+// rows over two planes, the K/V rows over three (the norm workspace holds all three; the first two
+// are the pair split).  The q rows' sums are those of the two-plane product, the K/V rows' those
+// of the fused one.  Smaller launches (batched decode, head slices) stay fused: there the two
+// launches, each with its own K split and sum, are slower than one.
 hipError_t project_qkv(stage* st, int rows, const float* x_in, const float* gain, const uint16_t* w,
                        const EpiArgs& e, hipStream_t s, bool x_normed) {
   const int d = st->m.d_model, qw = st->m.n_q_heads * st->m.head_dim;
-  if (qkv_planes(st) == 2 || gemv_fits(rows, d) || rows < 256)
+  const long q_tiles = (long)((rows + 127) / 128) * ((qw + 255) / 256);   // 128 x 256 tiles of the q rows
+  if (qkv_planes(st) == 2 || gemv_fits(rows, d) || rows < 256 || q_tiles < 256)
     return project(st, STAGE_KT_QKV, rows, x_in, gain, nullptr, 0, w, st->L.qkv_n, d, e, s, qkv_planes(st),
                    nullptr, x_normed);
   hipError_t err = project(st, STAGE_KT_QKV, rows, x_in, gain, nullptr, 0, w, qw, d, e, s, 2, nullptr, x_normed);
