@@ -54,6 +54,15 @@ def fill_weights(st, shape, blocks, first, last, seed, gain_sigma=0.0):
     del scratch
 
 
+def cpu_threads() -> int:
+    """Threads the oracle's numpy calls use on this host (the BLAS pool), else the core count."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
+
+
 def cpu_model() -> str:
     """The host CPU's model name (first 'model name' line of /proc/cpuinfo), or 'unknown'."""
     try:
@@ -692,6 +701,81 @@ def pipeline_line(args) -> dict:
     }
 
 
+def tiny_line(args) -> dict:
+    """The tiny decoder (2 blocks, d 256, 4 q / 2 KV heads, Dh 64, F 688, vocab 1024) as two stages
+    on this GPU ([0, 1) + embedding, [1, 2) + final norm + readout): greedy generation of 8 tokens
+    from a 16-token prompt through stage_pipeline_generate, timed whole (median of --steps runs),
+    and the time of one decode step through both stages from the difference between 8-token and
+    1-token runs.  Its weights total under 4 MB, so it is bound by kernel launches, not by HBM or
+    the matrix cores, and carries no roofline.  The oracle runs the same generation on the host,
+    timed whole, and its tokens must equal the GPU's."""
+    import numpy as np
+    import torch
+
+    import fixtures as fx
+    from oracle import decoder as o
+    from pipeline_stage_decoder_amd import stage as S
+
+    shape = fx.TINY
+    plen, n_new, ctx = 16, 8, 64
+    w = fx.draw_stage_weights(shape, 0, 2, True, True, gain_sigma=0.1)
+    parts = ((0, 1, True, False), (1, 2, False, True))
+    stages = []
+    for b0, b1, first, last in parts:
+        st = S.Stage(shape, b0, b1, first, last, max_slots=1, max_ctx=ctx, max_tokens=plen, device=0, kv=args.kv)
+        for (role, blk), t in w.items():
+            if (role == "embed" and not first) or (role in ("final_norm", "readout") and not last):
+                continue
+            if blk >= 0 and not (b0 <= blk < b1):
+                continue
+            st.load_weight(role, blk, t)
+        stages.append(st)
+    prompt = np.asarray(fx.tokens(fx.SEED_TOKENS, fx.token_stream(0), plen, shape.vocab), np.int32)
+    p = torch.tensor(prompt, device="cuda").view(1, 1, plen)
+
+    def median_run(n):
+        for _ in range(max(args.warmup, 1)):
+            S.pipeline_generate(stages, p, n)
+        times, out = [], None
+        for _ in range(max(args.steps, 3)):
+            t0 = time.perf_counter()
+            out = S.pipeline_generate(stages, p, n)
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times)), out
+
+    t_all, out = median_run(n_new)
+    t_one, _ = median_run(1)
+    got = out.cpu().numpy().reshape(-1)
+    step_us = (t_all - t_one) / (n_new - 1) * 1e6
+    log(f"[bench] tiny: {t_all * 1e6:.0f} us for {n_new} tokens, {step_us:.0f} us per decode step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        ost = [o.Stage(o.Dims.of(shape), b0, b1, first, last, w, ctx, kv_dtype=args.kv)
+               for b0, b1, first, last in parts]
+        t0 = time.perf_counter()
+        want, _ = o.generate(ost, prompt, n_new)
+        t_cpu = time.perf_counter() - t0
+        cpu = {"value": round(n_new / t_cpu, 2), "unit": "tok/s", "cores": cpu_threads(), "kind": "oracle",
+               "sample": f"the whole generation ({plen}-token prompt, {n_new} tokens through both stages), "
+                         f"timed once: {t_cpu:.3f} s",
+               "tokens_equal_gpu": bool(np.array_equal(want, got)), "cpu_model": cpu_model()}
+    return {
+        "metric": "stage decode tok/s & HBM GB/s %peak; prefill tok/s & MFMA util",
+        "value": round(n_new / t_all, 1), "unit": "tok/s", "n_gpus": 1, "steps": max(args.steps, 3),
+        "warmup": max(args.warmup, 1), "ms_per_step": round(step_us / 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,0.02) bf16 weights (gains 1 + N(0,0.1)), uniform tokens",
+        "config": {"workload": f"tiny decoder (2 blocks, d 256, 4q/2kv heads, head dim 64, SwiGLU 688, vocab 1024) "
+                               f"as two stages on one GPU; greedy generation of {n_new} tokens from a {plen}-token "
+                               "prompt through the on-device pipeline driver (value: tokens / s of the whole run)",
+                   "kv_cache": args.kv},
+        "us_per_generation": round(t_all * 1e6, 1), "us_per_decode_step": round(step_us, 1),
+        "us_prefill_and_first_token": round(t_one * 1e6, 1), "tokens": got.tolist(),
+        "roofline": None, "cpu_baseline": cpu,
+    }
+
+
 PREFILL_KINDS = ("norm", "qkv", "attn", "o", "gateup", "down")
 DECODE_KINDS = ("qkv", "attn", "o", "gateup", "down")
 
@@ -730,11 +814,7 @@ def cpu_baseline_70b(shape, kv: str, n_blocks: int, T: int, B: int, ctx: int, se
     import fixtures as fx
     from oracle import decoder as o
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+    cores = cpu_threads()
     blk = 20
     w = {(r, blk): fx.draw_weight(shape, r, blk) for r in fx.BLOCK_ROLES}
     st = o.Stage(o.Dims.of(shape), blk, blk + 1, False, False, w, ctx + 1, kv_dtype=kv)
@@ -997,7 +1077,7 @@ def main():
     ap.add_argument("--kv", choices=("f16", "f32", "bf16"), default="f16",
                     help="KV cache format (f16 and f32 are validated against the oracle at full stage depth)")
     ap.add_argument("--workload", choices=("mid-70b", "first-8b", "last-8b", "mlp-slices", "pipeline-8b",
-                                           "attn-parallel", "placement"),
+                                           "attn-parallel", "placement", "tiny"),
                     default="mid-70b",
                     help="mid-70b: the benchmark line (70B-shaped stage; also reports the 8B first stage); "
                          "the others report the remaining workloads")
@@ -1062,6 +1142,9 @@ def main():
         return
     if args.workload == "pipeline-8b":
         print(json.dumps(pipeline_line(args)), flush=True)
+        return
+    if args.workload == "tiny":
+        print(json.dumps(tiny_line(args)), flush=True)
         return
     if args.workload == "mlp-slices":
         print(json.dumps(mlp_slices_line(args)), flush=True)
