@@ -414,6 +414,10 @@ def batched_decode_line(args, workload: str, shape, blocks, first: bool, last: b
     roof = kernel_roofline(kv_launch, kt["attn"][0], kt["attn"][1],
                            f"k_attn_decode + k_attn_merge (split-KV GQA decode over the slots' {args.kv} caches)")
     gbs = step_bytes / (ms / 1e3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] {workload}: timing the CPU oracle on a bounded sample (one block)")
+        cpu = cpu_baseline_block(shape, args.kv, blocks[0], nb, prefill_chunk, B, ctx, last=last)
     return {
         "metric": "stage decode tok/s & HBM GB/s %peak; prefill tok/s & MFMA util",
         "value": round(B / (ms / 1e3), 1), "unit": "tok/s", "n_gpus": 1, "steps": reps * per_graph,
@@ -425,7 +429,7 @@ def batched_decode_line(args, workload: str, shape, blocks, first: bool, last: b
         "decode_step_bytes": step_bytes, "decode_hbm_gbs": round(gbs, 1),
         "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "kernel_ms_per_step": {k: round(v[1], 3) for k, v in kt.items()},
-        **pre, "roofline": roof, "cpu_baseline": None,
+        **pre, "roofline": roof, "cpu_baseline": cpu,
     }
 
 
@@ -474,6 +478,10 @@ def mlp_slices_line(args) -> dict:
                          "mfma_frac": round(fl / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         log(f"[bench] MLP slice T={T}: {per_T[str(T)]}")
     big_t = per_T["4096"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] MLP slices: timing the CPU oracle at T = 64")
+        cpu = cpu_baseline_mlp_slices(sh, n_sl, 64)
     return {
         "metric": "stage decode tok/s & HBM GB/s %peak; prefill tok/s & MFMA util",
         "value": round(4096 / (big_t["us_per_slice"] * n_sl / 1e6), 1), "unit": "tok/s", "n_gpus": 1,
@@ -483,7 +491,7 @@ def mlp_slices_line(args) -> dict:
         "config": {"workload": "sharded-MLP slices: d 8192, 8 slices of width 3584 (F 28672), "
                                "T in {1, 64, 4096}, F32 partials summed in slice order; value = "
                                "T=4096 rows/s through all 8 slices"},
-        "per_T": per_T, "roofline": None, "cpu_baseline": None,
+        "per_T": per_T, "roofline": None, "cpu_baseline": cpu,
     }
 
 
@@ -802,22 +810,36 @@ def issued_mfma_flops(shape, n_blocks: int, T: int, kv: str, pos0: int = 0) -> i
     return n_blocks * (lin + attn * (3 if kv == "f32" else 2))
 
 
-def cpu_baseline_70b(shape, kv: str, n_blocks: int, T: int, B: int, ctx: int, seconds: float = 4.0) -> dict:
-    """The oracle, as it stands, on this host, on one real-shape block of the stage: a 64-row
-    prefill (positions 0..63 of a fresh sequence) and a B = 2 decode step at position ctx over a
-    seeded cache of ctx positions per slot, each repeated for about `seconds`; tok/s of the whole
-    stage extrapolated linearly over blocks (and, for the prefill, over tokens: the timed chunk's
-    rows attend up to T keys, the sample's up to 64, so attention -- about 4% of the chunk's
-    flops -- is under-counted)."""
+def _timed(fn, seconds: float):
+    """Mean seconds of fn over about `seconds` (at least one call) after one untimed call."""
+    fn()
+    reps, t0 = 0, time.perf_counter()
+    while reps < 1 or time.perf_counter() - t0 < seconds:
+        fn()
+        reps += 1
+    return (time.perf_counter() - t0) / reps, reps
+
+
+def cpu_baseline_block(shape, kv: str, blk: int, n_blocks: int, T: int, B: int, ctx: int, last: bool = False,
+                       seconds: float = 4.0) -> dict:
+    """The oracle, as it stands, on this host, on one real-shape block (global block blk) of the
+    stage: a 64-row prefill (positions 0..63 of a fresh sequence) and a B = 2 decode step at
+    position ctx over a seeded cache of ctx positions per slot, each repeated for about `seconds`;
+    with `last`, also the final norm and readout of the 2 decode rows.  tok/s of the whole stage
+    extrapolated linearly over blocks (and, for the prefill, over tokens: the timed chunk's rows
+    attend up to T keys, the sample's up to 64, so attention -- a few % of a chunk's flops -- is
+    under-counted)."""
     import numpy as np
 
     import fixtures as fx
     from oracle import decoder as o
 
     cores = cpu_threads()
-    blk = 20
     w = {(r, blk): fx.draw_weight(shape, r, blk) for r in fx.BLOCK_ROLES}
-    st = o.Stage(o.Dims.of(shape), blk, blk + 1, False, False, w, ctx + 1, kv_dtype=kv)
+    if last:
+        w[("final_norm", -1)] = fx.draw_weight(shape, "final_norm", -1)
+        w[("readout", -1)] = fx.draw_weight(shape, "readout", -1)
+    st = o.Stage(o.Dims.of(shape), blk, blk + 1, False, last, w, ctx + 1, kv_dtype=kv)
     n_s, b_s = 64, 2
     shp = (ctx, shape.n_kv_heads, shape.head_dim)
     for slot in range(b_s):
@@ -827,24 +849,43 @@ def cpu_baseline_70b(shape, kv: str, n_blocks: int, T: int, B: int, ctx: int, se
     xp = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(B), n_s * shape.d_model).reshape(n_s, shape.d_model)
     xd = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(1000), b_s * shape.d_model).reshape(b_s, shape.d_model)
 
-    def timed(fn):
-        fn()
-        reps, t0 = 0, time.perf_counter()
-        while reps < 1 or time.perf_counter() - t0 < seconds:
-            fn()
-            reps += 1
-        return (time.perf_counter() - t0) / reps, reps
-
-    t_pre, r_pre = timed(lambda: st.prefill(xp, b_s, 0))
-    t_dec, r_dec = timed(lambda: st.forward(xd, np.arange(b_s), np.full(b_s, ctx)))
-    return {"value": b_s / (t_dec * n_blocks), "unit": "tok/s", "cores": cores, "kind": "oracle",
+    t_pre, r_pre = _timed(lambda: st.prefill(xp, b_s, 0), seconds)
+    t_dec, r_dec = _timed(lambda: st.forward(xd, np.arange(b_s), np.full(b_s, ctx)), seconds)
+    t_ro, r_ro = _timed(lambda: st.readout(xd), seconds) if last else (0.0, 0)
+    ro = (f" + the final norm and readout of the {b_s} rows ({r_ro} reps, {t_ro:.2f} s each)" if last else "")
+    return {"value": b_s / (t_dec * n_blocks + t_ro), "unit": "tok/s", "cores": cores, "kind": "oracle",
             "sample": f"decode: {r_dec} B={b_s} steps at position {ctx} of 1 of {n_blocks} blocks "
-                      f"({t_dec:.2f} s per block-step); prefill: {r_pre} {n_s}-row prefills of 1 block "
+                      f"({t_dec:.2f} s per block-step){ro}; prefill: {r_pre} {n_s}-row prefills of 1 block "
                       f"({t_pre:.2f} s each); tok/s extrapolated linearly over the stage's {n_blocks} blocks "
                       f"(and the prefill over tokens, to a {T}-token chunk)",
             "prefill_value": n_s / (t_pre * n_blocks), "prefill_unit": "tok/s",
             "seconds_per_block_decode_step": t_dec, "seconds_per_block_prefill_64": t_pre,
-            "cpu_model": cpu_model()}
+            "seconds_readout": t_ro, "cpu_model": cpu_model()}
+
+
+def cpu_baseline_mlp_slices(sh, n_sl: int, T: int = 64, seconds: float = 4.0) -> dict:
+    """The oracle's sliced MLP on this host: T rows through all n_sl slices (each slice's SwiGLU
+    MLP on its own weights, partials summed in slice order in F32), repeated for about `seconds`."""
+    import numpy as np
+
+    import fixtures as fx
+    from oracle import decoder as o
+
+    w = [{r: fx.draw_weight(sh, r, i) for r in ("mlp_norm", "wgate", "wup", "wdown")} for i in range(n_sl)]
+    x = fx.normal_f32(fx.SEED_HIDDEN, fx.hidden_stream(40), T * sh.d_model).reshape(T, sh.d_model)
+    eps = o.Dims.of(sh).rms_eps
+
+    def run():
+        acc_out = np.zeros((T, sh.d_model), np.float32)
+        for wi in w:
+            _, y = o.mlp_full(x, wi["mlp_norm"], wi["wgate"], wi["wup"], wi["wdown"], eps)
+            acc_out = (acc_out + y).astype(np.float32)
+        return acc_out
+
+    t, reps = _timed(run, seconds)
+    return {"value": T / t, "unit": "tok/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{reps} runs of {T} rows through all {n_sl} slices ({t:.2f} s each); rows/s at T = {T}, "
+                      f"not extrapolated to the timed {4096}-row line", "cpu_model": cpu_model()}
 
 
 def stage70b_line(args) -> dict:
@@ -1161,7 +1202,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample (one 70B-shaped block)")
-        cpu = cpu_baseline_70b(fx.LLAMA70B, args.kv, 20, 4096, 128, 8192)
+        cpu = cpu_baseline_block(fx.LLAMA70B, args.kv, 20, 20, 4096, 128, 8192)
     out["cpu_baseline"] = cpu
     if not args.no_first_8b:
         out["first_8b"] = first8b_figures(args)
