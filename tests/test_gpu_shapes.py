@@ -312,12 +312,12 @@ def test_8b_split_equals_unsplit_on_gpu(w8b_first, kv):
 
 @pytest.mark.parametrize("T", [40, 100, 257, 300, 512, 2600])
 def test_8b_mlp_gemm_tiles_ragged_rows(w8b_first, T):
-    # each row count takes another GEMM tiling: 40 the 64-row LDS-direct tiles with 64-deep stages,
-    # 100 the 128 x 256 two-buffer tiles for 64 < M <= 128, 257 / 300 / 512 the 256 x 256 (gate/up)
-    # and 128 x 256 split-K (down) tiles, 2600 the ping-pong schedule for gate/up (1232
-    # work-groups); the last row tile is ragged in every case (clamped reads that must never be
-    # stored).  MLP rows are independent: the oracle checks the first rows, a spread, and the tail
-    # rows.
+    # each row count takes another GEMM plan: 40 the 64 x 128 LDS-direct tiles (M <= 64), 100 one
+    # row of 128 x 256 tiles (64 < M <= 128, non-temporal weight loads), 257 / 300 / 512 / 2600 the
+    # 128 x 256 tiles with three weight buffers -- gate/up unsplit, down split along K into 4 at
+    # 257 / 300 / 512 rows and unsplit at 2600; the last row tile is ragged in every case (clamped
+    # reads that must never be stored).  MLP rows are independent: the oracle checks the first rows, a spread,
+    # and the tail rows.
     s = fx.LLAMA8B
     w = {(r, 0): w8b_first[(r, 0)] for r in ("mlp_norm", "wgate", "wup", "wdown")}
     st = make_stage(s, 0, 1, False, False, w, max_slots=1, max_ctx=64, max_tokens=max(T, 512))
