@@ -245,16 +245,17 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// LDS-direct tiles.  For prefill-sized M (activation pair planes) 8 waves own a 256 x 256 tile,
-// each wave 64 x 128 (two waves per SIMD), K in 32-deep stages; the same kernel serves 128 x 256
-// (three planes, or too few 256 x 256 tiles) and the batched-decode shapes (128 x 256, 64 x 256 and
-// 64 x 128 with 64-deep stages, so every row segment a load instruction fetches is a whole
-// 128-byte line; 128 x 256 of two planes then fits two stage buffers, ST = 2).  Tiles go from
-// global memory straight into LDS (global_load_lds_dwordx4), so no registers stage them and no
-// ds_write is issued: the accumulators, one step's fragments and the addresses fit the 256
-// registers of two waves per SIMD.  ST LDS buffers form a ring: while stage
-// t feeds the MFMAs the loads of stages t + 1 .. t + ST - 2 are in flight, and stage t + ST - 1 is
-// issued into the buffer stage t - 1 has just left.
+// LDS-direct tiles.  When K is a multiple of 64 (every benchmarked projection) 8 waves own a
+// 128 x 256 tile, each wave 32 x 128 (two waves per SIMD), K in 64-deep stages so that every row
+// segment a load instruction fetches is a whole 128-byte line: two activation-plane buffers and
+// three weight buffers (STB = 3) for two planes, two of each for three; the batched decode at
+// M <= 64 takes 64 x 128 tiles.  Otherwise 32-deep stages in a ring of ST buffers, on 256 x 256
+// tiles (waves of 64 x 128) or 128 x 256, with the ping-pong schedule (PP) on grids of several
+// rounds.  Tiles go from global memory straight into LDS (global_load_lds_dwordx4), so no registers
+// stage them and no ds_write is issued: the accumulators, one step's fragments and the addresses
+// fit the 256 registers of two waves per SIMD.  ST LDS buffers form a ring: while stage t feeds the
+// MFMAs the loads of stages t + 1 .. t + ST - 2 are in flight, and stage t + ST - 1 is issued into
+// the buffer stage t - 1 has just left.
 // Rows of a stage are BK / 8 chunks of 16 bytes, XOR-swizzled by row (dma_swz) so that the 8 rows
 // one ds_read_b128 phase reads land in distinct banks.  One load instruction writes 64 consecutive
 // chunks -- lane l's 16 bytes at position l -- so the swizzle is applied on the global side: lane
