@@ -40,8 +40,10 @@
  *    is therefore defined but meaningless, and the other rows of the call are unaffected.
  *  - Activations enter the matrix products as a bf16 "hi" plane and a bf16 "lo" plane
  *    (hi = bf16(v), lo = bf16(v - hi): about 16 significant bits), weights as their bf16 values,
- *    with F32 accumulation; norms and RoPE are evaluated in float64.  The decode projections for
- *    up to 4 rows take the F32 activation directly.  No activation is rounded to bf16 alone.
+ *    with F32 accumulation; norms and RoPE are evaluated in float64.  Over a 2-byte KV cache the
+ *    products whose outputs are rounded into the cache (the K and V rows of the QKV projection)
+ *    take a third plane (bf16(v - hi - lo), about 24 bits).  The decode projections for up to 4
+ *    rows take the F32 activation directly.  No activation is rounded to bf16 alone.
  */
 #ifndef PIPELINE_STAGE_DECODER_STAGE_H
 #define PIPELINE_STAGE_DECODER_STAGE_H
