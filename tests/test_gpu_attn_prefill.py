@@ -16,7 +16,7 @@ import torch
 import fixtures as fx
 from oracle import decoder as o
 from pipeline_stage_decoder_amd.stage import Stage
-from tests.gpu_util import hidden_rows, rel_l2, say
+from tests.gpu_util import hidden_rows, kv_bits, kv_values, rel_l2, rel_l2_kv, say
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -76,4 +76,33 @@ def test_wide_prefill_attention_in_ring_mode(zigzag):
     e, e_plain = rel_l2(got[rows], want), rel_l2(got, plain)
     say(f"  ring vs oracle {e:.2e}; ring vs the plain sublayer on the GPU {e_plain:.2e}")
     assert e <= TOL and e_plain <= TOL
+    assert st.device_errors() == 0
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16"])
+def test_second_chunk_splits_the_qkv_rows_at_an_offset(kv):
+    # one sequence through the attention sublayer in two prefill chunks: 1024 tokens at position 0
+    # (their q rows make 128 GEMM tiles of 128 x 256: the fused three-plane QKV projection), then
+    # 2048 at position 1024 (256 tiles: the q rows over two activation planes and the K/V rows over
+    # three, as two GEMMs over row ranges of the fused weight).  The second chunk's K/V must land at
+    # positions 1024..3071 and its rows attend to both chunks' keys.
+    hq, hkv, dh, T1, T2 = 32, 8, 128, 1024, 2048
+    say(f"two prefill chunks ({T1} at 0, {T2} at {T1}), Hq {hq}, Hkv {hkv}, Dh {dh}, {kv} cache")
+    st, ost, x = setup(hq, hkv, dh, T1 + T2, kv, 82)
+    xt = torch.from_numpy(x).cuda()
+    st.attn(0, xt[:T1], 0, 0)
+    got = st.attn(0, xt[T1:], 0, T1).cpu().numpy()
+    assert np.isfinite(got).all()
+    rows = sample_rows(T2)
+    want = ost.attention(0, x[T1 + rows], np.zeros(len(rows), np.int64), T1 + rows)
+    e = rel_l2(got[rows], want)
+    say(f"  second chunk, {len(rows)} rows vs the oracle: rel L2 (worst row) {e:.2e}")
+    assert e <= TOL
+    k, v = kv_bits(st, 0, 0, T1 + T2)
+    kc, vc = ost.kv[0]
+    for name, g, w in (("K", k, kc), ("V", v, vc)):
+        for lo, hi in ((0, T1), (T1, T1 + T2)):
+            ek = rel_l2_kv(kv_values(kv, g[lo:hi]), w[0, lo:hi])
+            say(f"  {name} positions {lo}..{hi - 1} vs the oracle's cache: {ek:.2e}")
+            assert ek <= TOL
     assert st.device_errors() == 0
