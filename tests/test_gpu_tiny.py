@@ -180,35 +180,38 @@ def test_device_side_range_checks(weights, bad):
 
 
 @pytest.mark.parametrize("kv", ["f16", "bf16"])
-def test_wide_decode_batch_splits_the_qkv_rows(weights, kv):
-    # 300 decode rows in 300 slots: from 256 rows on, over a 2-byte cache, the QKV projection runs as
-    # two GEMMs over row ranges of the fused weight (q over two activation planes, K/V over three).
-    # Two steps, so every row attends to two keys and q matters; in the second, three rows are out
-    # of range: one error per bad row and block (not one per GEMM), no K/V written for them, their
-    # outputs x + MLP(x) block by block, and every other row bit-identical to a call whose rows are
-    # all valid
-    B, ctx, dev = 300, 16, torch.device("cuda")
-    say(f"300-row decode, {kv} cache")
+def test_wide_decode_batch_splits_the_qkv_rows(kv):
+    # 1024 decode rows in 1024 slots of a 2-block stage with 64 query heads of 128 (16 per KV head)
+    # at d 256: the q rows alone make 8 x 32 = 256 GEMM tiles of 128 x 256, so over a 2-byte cache the
+    # QKV projection runs as two GEMMs over row ranges of the fused weight (q over two activation
+    # planes, K/V over three), with per-row slots and positions.  Two steps, so every row attends to
+    # two keys and q matters; in the second, three rows are out of range: one error per bad row and
+    # block (not one per GEMM), no K/V written for them, their outputs x + MLP(x) block by block,
+    # and every other row bit-identical to a call whose rows are all valid
+    B, ctx, dev = 1024, 16, torch.device("cuda")
+    shape = fx.Shape(256, 64, 4, 128, 64, 1024, 2)
+    w = fx.draw_stage_weights(shape, 0, 2, False, False, gain_sigma=0.1)
+    say(f"{B}-row decode, 64 q / 4 KV heads of 128, {kv} cache")
     kw = dict(max_slots=B, max_ctx=ctx, max_tokens=B, kv=kv)
-    st = make_stage(TINY, 0, 2, True, False, weights, **kw)
-    ref = make_stage(TINY, 0, 2, True, False, weights, **kw)
-    ost = oracle_stage(weights, 0, 2, True, False, max_ctx=ctx, kv_dtype=kv)
+    st = make_stage(shape, 0, 2, False, False, w, **kw)
+    ref = make_stage(shape, 0, 2, False, False, w, **kw)
+    ost = o.Stage(o.Dims.of(shape), 0, 2, False, False, w, ctx, kv_dtype=kv)
 
     def i32(a):
         return torch.tensor(np.asarray(a), dtype=torch.int32, device=dev)
 
     slots = np.arange(B)
-    x0, x1 = hidden_rows(11, B, TINY.d_model), hidden_rows(12, B, TINY.d_model)
+    x0, x1 = hidden_rows(11, B, shape.d_model), hidden_rows(12, B, shape.d_model)
     want0 = ost.forward(x0, slots, np.zeros(B, np.int64))
-    for s in (st, ref):
-        got0 = s.decode(torch.from_numpy(x0).to(dev), i32(slots), i32(np.zeros(B))).cpu().numpy()
+    for s_ in (st, ref):
+        got0 = s_.decode(torch.from_numpy(x0).to(dev), i32(slots), i32(np.zeros(B))).cpu().numpy()
         e = rel_l2(got0, want0)
         say(f"  step 1 vs oracle: {e:.2e}")
         assert e <= TOL
     st.device_errors(reset=True)
     sl, ps = slots.copy(), np.ones(B, np.int64)
-    sl[7], ps[150], sl[299] = B, 100000, -1               # slot past the cache, position past it, negative slot
-    bad = np.array([7, 150, 299])
+    sl[7], ps[600], sl[1023] = B, 100000, -1              # slot past the cache, position past it, negative slot
+    bad = np.array([7, 600, 1023])
     ok = np.setdiff1d(slots, bad)
     got = st.decode(torch.from_numpy(x1).to(dev), i32(sl), i32(ps)).cpu().numpy()
     assert st.device_errors(reset=True) == len(bad) * 2      # per bad row and block
@@ -225,10 +228,10 @@ def test_wide_decode_batch_splits_the_qkv_rows(weights, kv):
     assert rel_l2(got[bad], want_bad) <= TOL
     # the K/V rows of the fused weight's second range land at the right heads and positions
     for b in range(2):
-        for slot in (0, 149, 150, 298):
+        for slot in (0, 599, 600, 1022):
             k, v = kv_bits(st, b, slot, 2)
             kc, vc = ost.kv[slot]
-            n = 1 if slot == 150 else 2                        # row 150's second step wrote nothing
+            n = 1 if slot == 600 else 2                        # row 600's second step wrote nothing
             assert rel_l2_kv(kv_values(kv, k[:n]), kc[b, :n]) <= TOL
             assert rel_l2_kv(kv_values(kv, v[:n]), vc[b, :n]) <= TOL
             if n == 1:
