@@ -14,8 +14,10 @@ the stage's kernels at their real shapes on a slice the oracle can follow:
   independent);
 * 8B blocks [0, 2) against [0, 1) + [1, 2): bit-identical hidden rows and KV after a 300-row
   prefill, two B = 1 decode steps and a B = 64 decode step, bf16 and F32 caches;
-* 8B MLP at T in {40, 100, 257, 300, 512}: every GEMM tiling with a ragged last row tile, the
-  oracle on sampled rows and the tail rows.
+* 8B MLP at T in {40, 100, 257, 300, 512, 2600}: every GEMM tiling with a ragged last row tile,
+  the oracle on sampled rows and the tail rows;
+* an irregular shape off the benchmark grid (d 2560, 20 q / 4 KV heads, SwiGLU 6912): a 160-row
+  prefill and B = 3 and B = 70 decode steps over fresh and continuing slots.
 Inputs: seeded bf16 N(0, 0.02) weights with norm gains 1 + N(0, 0.1^2), uniform tokens, F32 N(0,1)
 hidden rows, bf16 N(0,1) cached K/V.
 """
@@ -418,4 +420,45 @@ def test_70b_stage_all_20_blocks_f16_cache():
         e = rel_l2(g, wv)
         say(f"  step {i} rel L2 (worst row) {e:.2e}")
         assert e <= TOL
+    assert st.device_errors() == 0
+
+
+IRREG = fx.Shape(2560, 20, 4, 128, 6912, 1024, 2)
+
+
+@pytest.mark.parametrize("kv", ["f16", "f32"])
+def test_irregular_shape_prefill_and_decode(kv):
+    # a model off the benchmark grid: d 2560 and SwiGLU 6912 (neither a multiple of 2048, so the
+    # B <= 4 decode takes the general GEMV, and the down projection, too wide for its input
+    # staging, the skinny MFMA tiles), 20 query heads over 4 KV heads (groups of 5), a QKV width of
+    # 3584 and 54 gate/up tiles of 256.  A 160-row prefill of slot 0 (the register-staged GEMMs
+    # with a ragged second row tile, the 64-column attention kernel), then a B = 3 decode step
+    # (slot 0 continuing, slots 1 and 2 starting) and a B = 70 step (70 slots at mixed positions).
+    s, T, ctx = IRREG, 160, 256
+    w = fx.draw_stage_weights(s, 0, 2, False, False, gain_sigma=0.1)
+    say(f"irregular shape (d 2560, 20q/4kv, F 6912), {kv} cache: prefill {T}")
+    st = make_stage(s, 0, 2, False, False, w, max_slots=70, max_ctx=ctx, max_tokens=T, kv=kv)
+    ost = o.Stage(o.Dims.of(s), 0, 2, False, False, w, ctx, kv_dtype=kv)
+    dev = torch.device("cuda")
+    x = hidden_rows(51, T, s.d_model)
+    got = st.prefill(torch.from_numpy(x).to(dev), 0, 0).cpu().numpy()
+    want = ost.prefill(x, 0, 0)
+    e = rel_l2(got, want)
+    say(f"  prefill vs oracle: {e:.2e}")
+    assert e <= TOL
+    steps = [(np.array([0, 1, 2]), np.array([T, 0, 0])),
+             (np.arange(70), np.concatenate([[T + 1, 1, 1], np.zeros(67, np.int64)]))]
+    for i, (slots, pos) in enumerate(steps):
+        xd = hidden_rows(52 + i, len(slots), s.d_model)
+        got = st.decode(torch.from_numpy(xd).to(dev), torch.tensor(slots, dtype=torch.int32, device=dev),
+                        torch.tensor(pos, dtype=torch.int32, device=dev)).cpu().numpy()
+        want = ost.forward(xd, slots, pos)
+        e = rel_l2(got, want)
+        say(f"  B = {len(slots)} decode vs oracle: {e:.2e}")
+        assert e <= TOL
+    for b in range(2):
+        k, v = kv_bits(st, b, 0, T + 2)
+        kc, vc = ost.kv[0]
+        assert rel_l2_kv(kv_values(kv, k), kc[b, :T + 2]) <= TOL
+        assert rel_l2_kv(kv_values(kv, v), vc[b, :T + 2]) <= TOL
     assert st.device_errors() == 0
